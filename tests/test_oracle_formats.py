@@ -1,0 +1,113 @@
+"""Pins of the oracle's number formats (CPU only).
+
+BF16 and FP8 E4M3 rounding are pinned to torch's own casts (library
+routines); the FP8 decode table to torch's float8_e4m3fn view and to values
+fixed by the OFP8 specification; E2M1 and the MX scale rule to the OCP MX
+v1.0 definitions checked by exhaustive enumeration / brute-force nearest
+search."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import formats as F
+
+
+def test_fp8_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = F.fp8_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # OFP8: only S.1111.111 is NaN; max 448; min subnormal 2^-9; min normal 2^-6
+    assert list(np.nonzero(nan)[0]) == [0x7F, 0xFF]
+    assert ours[0x7E] == 448.0 and ours[0x01] == 2.0 ** -9 and ours[0x08] == 2.0 ** -6
+
+
+def test_fp8_encode_roundtrip():
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF, 0x80)], dtype=np.uint8)
+    assert np.array_equal(F.fp8_encode(F.fp8_decode(codes)), codes)
+
+
+def test_fp8_round_matches_torch_including_midpoints():
+    pos = F.fp8_decode(np.arange(0, 0x7F, dtype=np.uint8))
+    mids = (pos[:-1] + pos[1:]) / 2
+    rng = np.random.default_rng(1)
+    rnd = rng.uniform(-448, 448, 20000).astype(np.float32).astype(np.float64)
+    small = (rng.standard_normal(20000) * 0.05).astype(np.float32).astype(np.float64)
+    x = np.concatenate([mids, -mids, rnd, small, pos, -pos])
+    ours = F.fp8_round(x)
+    ref = torch.from_numpy(x).to(torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(ours, ref)
+
+
+def test_fp8_saturates():
+    x = np.array([448.0, 463.9, 464.0, 500.0, 1e6, -1e6])
+    assert np.array_equal(F.fp8_round(x), [448, 448, 448, 448, 448, -448])
+
+
+def test_bf16_matches_torch_including_midpoints():
+    rng = np.random.default_rng(2)
+    x = (rng.standard_normal(50000) * np.exp(rng.uniform(-20, 20, 50000))).astype(np.float32)
+    bits = x.view(np.uint32)
+    mids = ((bits & 0xFFFF0000) | 0x8000).view(np.float32)   # exact BF16 midpoints
+    xx = np.concatenate([x, mids]).astype(np.float64)
+    ref = torch.from_numpy(xx.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    assert np.array_equal(F.to_bf16(xx), ref)
+
+
+def test_e2m1_table_and_rne():
+    vals = F.e2m1_decode(np.arange(16))
+    assert list(vals[:8]) == [0, 0.5, 1, 1.5, 2, 3, 4, 6]
+    assert list(vals[9:]) == [-0.5, -1, -1.5, -2, -3, -4, -6]
+    # brute force: nearest representable value, ties to the even code
+    grid = np.arange(-8, 8.0001, 1 / 64)
+    table = F.E2M1_VALUES
+    for x in grid:
+        a = min(abs(x), 6.0)
+        d = np.abs(table - a)
+        best = np.nonzero(d == d.min())[0]
+        pick = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        assert F.e2m1_round(np.array([x]))[0] == np.copysign(table[pick], x) or table[pick] == 0
+
+
+def test_mx_scale_rule():
+    rng = np.random.default_rng(3)
+    x = rng.standard_normal((200, 64)) * np.exp(rng.uniform(-5, 5, (200, 1)))
+    vals, codes, sc = F.mxfp4_quantize(x)
+    blocks = np.abs(x).reshape(200, 2, 32).max(-1)
+    expect = np.floor(np.log2(blocks)).astype(int) - 2 + 127
+    assert np.array_equal(sc.astype(int), expect)
+    # the largest element of each block lands in [4, 6] after scaling
+    Xs = np.ldexp(1.0, sc.astype(int) - 127)
+    scaled_max = np.abs(vals).reshape(200, 2, 32).max(-1) / Xs
+    assert np.all((scaled_max >= 4) & (scaled_max <= 6))
+    assert np.array_equal(F.mxfp4_decode(codes, sc), vals)
+    # a zero block gets the smallest scale and all-zero codes
+    v0, c0, s0 = F.mxfp4_quantize(np.zeros((1, 32)))
+    assert s0[0, 0] == 0 and not c0.any() and not v0.any()
+
+
+def test_fp8_entry_scale():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal((50, 512)) * 3
+    v, codes, s = F.fp8_entry_quantize(x)
+    amax = np.abs(x).max(1)
+    assert np.allclose(s, amax / 448, rtol=1e-7)
+    assert np.all(np.abs(v).max(1) <= 448 * s)
+    # every element within half an E4M3 ulp (relative 2^-4) or the subnormal quantum
+    err = np.abs(v - x)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, s[:, None] * 2.0 ** -10)
+    assert np.all(err <= bound * (1 + 1e-12))
+    assert np.array_equal(F.fp8_decode(codes) * s[:, None], v)
+    v0, c0, s0 = F.fp8_entry_quantize(np.zeros((1, 8)))
+    assert s0[0] == 1.0 and not c0.any()
+
+
+@pytest.mark.parametrize("fmt", ["f32", "bf16"])
+def test_plain_formats_idempotent(fmt):
+    from oracle import csa
+    x = np.random.default_rng(5).standard_normal(1000)
+    y, _ = csa.store_format(x, fmt)
+    z, _ = csa.store_format(y, fmt)
+    assert np.array_equal(y, z)
