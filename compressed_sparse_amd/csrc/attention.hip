@@ -1,0 +1,232 @@
+// Attention over compressed entries: CSA sparse (listed entries) and HCA
+// dense (every visible entry).  [CSA/HCA 混注意力] §1.1 (each query attends
+// only its selected entries), §1.2 (dense attention over the 128x shorter
+// sequence); [读完这篇] §三 CSA 步骤三 (standard attention, KV shared).
+//
+//   q~ = RoPE_pos(q[h]);  l_s = scale * q~ . K_s;  o[h] = softmax(l) V;
+//   lse[h] = log sum exp(l)
+//
+// This file holds the generic path (any head count / width / format, VALU
+// fp32, one workgroup per (query, head), online softmax over chunks of 256
+// entries) and the host entry points, which route the MI355X-shaped cases
+// (64 heads, 512 + 64 dims, BF16 / FP8 caches) to the MFMA kernels.
+#include "attention.hpp"
+
+namespace csa {
+
+__device__ __forceinline__ int64_t attn_pos(const AttnParams& P, int b, int t) {
+  return P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
+}
+
+__device__ __forceinline__ float kv_nope(const AttnParams& P, size_t e, int d) {
+  switch (P.nope_dt) {
+    case CSA_F32: return static_cast<const float*>(P.nope)[e * P.d_nope + d];
+    case CSA_BF16: return bf16_to_f32(static_cast<const bf16_t*>(P.nope)[e * P.d_nope + d]);
+    default: return e4m3_to_f32(static_cast<const uint8_t*>(P.nope)[e * P.d_nope + d]) *
+                    static_cast<const float*>(P.scale)[e];
+  }
+}
+
+__device__ __forceinline__ float kv_rope(const AttnParams& P, size_t e, int d) {
+  return P.rope_dt == CSA_F32 ? static_cast<const float*>(P.rope)[e * P.d_rope + d]
+                              : bf16_to_f32(static_cast<const bf16_t*>(P.rope)[e * P.d_rope + d]);
+}
+
+// grid (H, T, B), 256 threads.
+__global__ void __launch_bounds__(256) attn_generic_kernel(AttnParams P) {
+  extern __shared__ float smem[];
+  const int c = P.d_nope + P.d_rope;
+  float* red = smem;             // 32
+  float* q = smem + 32;          // c
+  float* p = q + c;              // 256 probabilities of the current chunk
+  int* ent = reinterpret_cast<int*>(p + 256);  // 256 entry ids
+  float* o = reinterpret_cast<float*>(ent + 256);  // d_nope accumulators
+  const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int64_t pos = attn_pos(P, b, t);
+  int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
+  if (n > P.cap) n = P.cap;
+  const size_t qrow = (static_cast<size_t>(b) * P.T + t) * P.H + h;
+  for (int j = tid; j < c; j += nt) q[j] = load_elem(P.q, qrow * c + j, P.q_dt);
+  __syncthreads();
+  for (int pp = tid; pp < P.d_rope / 2; pp += nt) {
+    float s, co;
+    rope_sincos(pos, pp, P.d_rope, P.base, &s, &co);
+    float x0 = q[P.d_nope + 2 * pp], x1 = q[P.d_nope + 2 * pp + 1];
+    q[P.d_nope + 2 * pp] = x0 * co - x1 * s;
+    q[P.d_nope + 2 * pp + 1] = x0 * s + x1 * co;
+  }
+  for (int d = tid; d < P.d_nope; d += nt) o[d] = 0.0f;
+  __syncthreads();
+  const int64_t count = P.idx ? P.k : n;
+  const int32_t* list = P.idx ? P.idx + (static_cast<size_t>(b) * P.T + t) * P.k : nullptr;
+  float mx = -INFINITY, sum = 0.0f;
+  for (int64_t base = 0; base < count; base += nt) {
+    const int64_t j = base + tid;
+    int64_t s = -1;
+    if (j < count) s = list ? static_cast<int64_t>(list[j]) : j;
+    if (s >= n) s = -1;
+    float l = -INFINITY;
+    if (s >= 0) {
+      const size_t e = static_cast<size_t>(b) * P.cap + s;
+      float dot = 0.0f;
+      for (int d = 0; d < P.d_nope; ++d) dot = fmaf(q[d], kv_nope(P, e, d), dot);
+      for (int d = 0; d < P.d_rope; ++d) dot = fmaf(q[P.d_nope + d], kv_rope(P, e, d), dot);
+      l = dot * P.scale_qk;
+    }
+    const float cmax = block_max(l, red);
+    const float nmx = fmaxf(mx, cmax);
+    float pe = (s >= 0) ? expf(l - nmx) : 0.0f;
+    const float csum = block_sum(pe, red);
+    const float corr = (nmx == -INFINITY) ? 1.0f : expf(mx - nmx);
+    p[tid] = pe;
+    ent[tid] = static_cast<int>(s);
+    __syncthreads();
+    if (nmx != -INFINITY) {
+      const int lim = static_cast<int>((count - base) < nt ? (count - base) : nt);
+      for (int d = tid; d < P.d_nope; d += nt) {
+        float acc = o[d] * corr;
+        for (int i = 0; i < lim; ++i) {
+          int ss = ent[i];
+          if (ss >= 0) acc = fmaf(p[i], kv_nope(P, static_cast<size_t>(b) * P.cap + ss, d), acc);
+        }
+        o[d] = acc;
+      }
+      sum = sum * corr + csum;
+      mx = nmx;
+    }
+    __syncthreads();
+  }
+  const float inv = sum > 0.0f ? 1.0f / sum : 0.0f;
+  for (int d = tid; d < P.d_nope; d += nt) {
+    float v = o[d] * inv;
+    if (P.o_dt == CSA_F32) static_cast<float*>(P.o)[qrow * P.d_nope + d] = v;
+    else static_cast<bf16_t*>(P.o)[qrow * P.d_nope + d] = f32_to_bf16(v);
+  }
+  if (P.lse && tid == 0) P.lse[qrow] = sum > 0.0f ? mx + logf(sum) : -INFINITY;
+}
+
+static int launch_generic(const AttnParams& P, int B, hipStream_t s) {
+  const int c = P.d_nope + P.d_rope;
+  const size_t lds = (32 + c + 256 + 256 + P.d_nope) * sizeof(float);
+  hipLaunchKernelGGL(attn_generic_kernel, dim3(P.H, P.T, B), dim3(256), lds, s, P);
+  return check_launch("attn_generic_kernel");
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+static int validate_attn(const csa_attn_desc* d, int B, const void* q, const csa_cache* kv,
+                         void* o, float* lse) {
+  if (!d) return fail(CSA_ERR_INVALID_ARG, "attn desc is NULL");
+  if (d->n_heads < 1 || d->n_heads > 65535) return fail(CSA_ERR_INVALID_ARG, "n_heads must be in 1..65535");
+  if (d->d_nope < 1 || d->d_rope < 0 || (d->d_rope & 1) || d->d_nope + d->d_rope > 4096)
+    return fail(CSA_ERR_INVALID_ARG, "d_nope >= 1, d_rope even, width <= 4096");
+  if (d->q_dtype != CSA_F32 && d->q_dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "q_dtype must be F32 or BF16");
+  if (d->o_dtype != CSA_F32 && d->o_dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "o_dtype must be F32 or BF16");
+  if (d->nope_dtype != CSA_F32 && d->nope_dtype != CSA_BF16 && d->nope_dtype != CSA_FP8E4M3)
+    return fail(CSA_ERR_UNSUPPORTED, "nope_dtype must be F32, BF16 or FP8E4M3");
+  if (d->d_rope > 0 && d->rope_dtype != CSA_F32 && d->rope_dtype != CSA_BF16)
+    return fail(CSA_ERR_UNSUPPORTED, "rope_dtype must be F32 or BF16");
+  if (d->m < 1 || d->m > 256) return fail(CSA_ERR_INVALID_ARG, "m must be in 1..256");
+  if (d->capacity < 1 || d->capacity > (int64_t(1) << 31) - 1) return fail(CSA_ERR_INVALID_ARG, "capacity must be in 1..2^31-1");
+  if (!(d->rope_base > 0.0)) return fail(CSA_ERR_INVALID_ARG, "rope_base must be > 0");
+  if (B < 0 || B > 65535) return fail(CSA_ERR_INVALID_ARG, "B must be in 0..65535");
+  if (!q || !kv || !kv->nope || !o) return fail(CSA_ERR_INVALID_ARG, "NULL argument");
+  if (d->nope_dtype == CSA_FP8E4M3 && !kv->scale) return fail(CSA_ERR_INVALID_ARG, "kv scale is NULL");
+  if (d->d_rope > 0 && !kv->rope) return fail(CSA_ERR_INVALID_ARG, "kv rope is NULL");
+  if (!aligned16(q) || !aligned16(kv->nope) || !aligned16(kv->scale) || !aligned16(kv->rope) ||
+      !aligned16(o) || !aligned16(lse))
+    return fail(CSA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  return CSA_OK;
+}
+
+static AttnParams make_attn_params(const csa_attn_desc* d, const void* q, const csa_cache* kv,
+                                   const int32_t* idx, int k, float scale, void* o, float* lse,
+                                   void* ws, size_t ws_bytes) {
+  AttnParams P{};
+  P.H = d->n_heads; P.d_nope = d->d_nope; P.d_rope = d->d_rope;
+  P.q_dt = d->q_dtype; P.o_dt = d->o_dtype; P.nope_dt = d->nope_dtype; P.rope_dt = d->rope_dtype;
+  P.m = d->m; P.base = d->rope_base; P.cap = d->capacity;
+  P.q = q; P.nope = kv->nope; P.scale = kv->scale; P.rope = kv->rope;
+  P.idx = idx; P.k = k; P.scale_qk = scale; P.o = o; P.lse = lse;
+  P.ws = ws; P.ws_bytes = ws_bytes;
+  return P;
+}
+
+size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k) {
+  if (!d || B < 0 || T < 0) return 0;
+  return mfma_attn_ws_bytes(d, op, B, T, pos0, k);
+}
+
+static int dispatch(AttnParams& P, int op, int B, void* stream) {
+  hipStream_t s = as_stream(stream);
+  if (mfma_attn_supported(P)) return launch_mfma_attn(P, op, B, s);
+  return launch_generic(P, B, s);
+}
+
+}  // namespace csa
+
+using namespace csa;
+
+extern "C" int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
+                                       const void* q, const csa_cache* kv, const int32_t* idx, int k,
+                                       float softmax_scale, void* o, float* lse, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  int st = validate_attn(desc, B, q, kv, o, lse);
+  if (st != CSA_OK) return st;
+  if (T < 0 || T > 65535 || pos0 < 0) return fail(CSA_ERR_INVALID_ARG, "T must be in 0..65535, pos0 >= 0");
+  if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
+  if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
+  if (ws_bytes < attn_ws_bytes(desc, CSA_OP_SPARSE_ATTN_PREFILL, B, T, pos0, k))
+    return fail(CSA_ERR_WORKSPACE, "workspace too small");
+  if (B == 0 || T == 0) return CSA_OK;
+  AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes);
+  P.T = T; P.pos0 = pos0; P.pos_dev = nullptr;
+  return dispatch(P, CSA_OP_SPARSE_ATTN_PREFILL, B, stream);
+}
+
+extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
+                                      const void* q, const csa_cache* kv, const int32_t* idx, int k,
+                                      float softmax_scale, void* o, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  int st = validate_attn(desc, B, q, kv, o, lse);
+  if (st != CSA_OK) return st;
+  if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
+  if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
+  if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
+  if (ws_bytes < attn_ws_bytes(desc, CSA_OP_SPARSE_ATTN_DECODE, B, 1, 0, k))
+    return fail(CSA_ERR_WORKSPACE, "workspace too small");
+  if (B == 0) return CSA_OK;
+  AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes);
+  P.T = 1; P.pos0 = 0; P.pos_dev = pos;
+  return dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
+}
+
+extern "C" int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
+                                      const void* q, const csa_cache* kv, float softmax_scale, void* o,
+                                      float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate_attn(desc, B, q, kv, o, lse);
+  if (st != CSA_OK) return st;
+  if (T < 0 || T > 65535 || pos0 < 0) return fail(CSA_ERR_INVALID_ARG, "T must be in 0..65535, pos0 >= 0");
+  if (ws_bytes < attn_ws_bytes(desc, CSA_OP_DENSE_ATTN_PREFILL, B, T, pos0, 0))
+    return fail(CSA_ERR_WORKSPACE, "workspace too small");
+  if (B == 0 || T == 0) return CSA_OK;
+  AttnParams P = make_attn_params(desc, q, kv, nullptr, 0, softmax_scale, o, lse, ws, ws_bytes);
+  P.T = T; P.pos0 = pos0; P.pos_dev = nullptr;
+  return dispatch(P, CSA_OP_DENSE_ATTN_PREFILL, B, stream);
+}
+
+extern "C" int hca_dense_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
+                                     const void* q, const csa_cache* kv, float softmax_scale, void* o,
+                                     float* lse, void* ws, size_t ws_bytes, void* stream) {
+  int st = validate_attn(desc, B, q, kv, o, lse);
+  if (st != CSA_OK) return st;
+  if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
+  if (ws_bytes < attn_ws_bytes(desc, CSA_OP_DENSE_ATTN_DECODE, B, 1, 0, 0))
+    return fail(CSA_ERR_WORKSPACE, "workspace too small");
+  if (B == 0) return CSA_OK;
+  AttnParams P = make_attn_params(desc, q, kv, nullptr, 0, softmax_scale, o, lse, ws, ws_bytes);
+  P.T = 1; P.pos0 = 0; P.pos_dev = pos;
+  return dispatch(P, CSA_OP_DENSE_ATTN_DECODE, B, stream);
+}

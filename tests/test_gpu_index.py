@@ -1,0 +1,155 @@
+"""GPU parity of the lightning indexer + top-k (csa_index_topk_prefill /
+csa_index_topk_decode) against the CPU oracle, through the C ABI.  Key
+caches are filled directly with seeded synthetic values of each storage
+format, so the step is checked on its own."""
+import numpy as np
+import pytest
+import torch
+
+from compressed_sparse_amd import binding as cb
+from compressed_sparse_amd import synth
+from oracle import csa
+from oracle import formats as F
+from tests.helpers import ascending_padded, compare_topk, np64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def key_cache(fmt, B, cap, d, m, seed):
+    desc = cb.cache_desc(m, True, d, 0, "f32", fmt, "f32", cap)
+    kc = cb.KVCache(desc, B)
+    if fmt in ("f32", "bf16"):
+        kc.nope.copy_(synth.normal((B, cap, d), "keys", seed, device=DEV, dtype=synth.TORCH_DTYPE[fmt]))
+        dec = np64(kc.nope)
+    elif fmt == "fp8":
+        kc.nope.copy_(synth.random_fp8_codes((B, cap, d), "keys", seed, device=DEV))
+        kc.scale.copy_(synth.normal((B, cap), "kscale", seed, device=DEV).abs() * 0.01 + 1e-3)
+        dec = F.fp8_decode(kc.nope.cpu().numpy()) * kc.scale.cpu().double().numpy()[..., None]
+    else:
+        kc.nope.copy_(synth.random_e2m1_bytes((B, cap, d // 2), "keys", seed, device=DEV))
+        kc.scale.copy_(synth.random_e8m0((B, cap, d // 32), "kscale", seed=seed, device=DEV))
+        packed = kc.nope.cpu().numpy().astype(np.int64)
+        codes = np.stack([packed & 15, packed >> 4], -1).reshape(B, cap, d)
+        dec = F.mxfp4_decode(codes, kc.scale.cpu().numpy())
+    return kc, dec
+
+
+def oracle_rows(qI, w, K, positions, m, k, qk_fmt, score_fmt):
+    idx, scores = [], []
+    for r, pos in enumerate(positions):
+        n = min(int(csa.n_visible(pos, m)), K.shape[0])
+        I = csa.index_scores(csa.quantize_query(qI[r], qk_fmt), w[r], K, n, score_fmt)
+        scores.append(I)
+        idx.append(csa.topk(I, n, k))
+    return np.array(idx), scores
+
+
+def test_prefill_fp32_tiny_workload_shapes():
+    """fp32 indexer: 4 heads x 32 dims, m = 4, k = 64, 2048 queries."""
+    T, H, d, m, k = 2048, 4, 32, 4, 64
+    cap = T // m
+    kc, K = key_cache("f32", 1, cap, d, m, seed=21)
+    qI = synth.normal((1, T, H, d), "qI", 21, device=DEV)
+    w = synth.normal((1, T, H), "w", 21, device=DEV)
+    desc = cb.index_desc(H, d, "f32", "f32", "f32", "f32", m, cap)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.zeros((1, T, cap), dtype=torch.float32, device=DEV)
+    cb.index_topk_prefill(desc, kc, 0, qI, w, k, idx, scores)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = oracle_rows(np64(qI[0]), np64(w[0]), K[0], np.arange(T), m, k, "f32", "f32")
+    got = idx[0].cpu().numpy()
+    assert ascending_padded(got)
+    differing, bad = compare_topk(got, ref_idx, ref_sc, 1e-6)
+    assert not bad, f"rows {bad[:5]} differ beyond the 1e-6 tie window"
+    assert differing <= 0.01 * T
+    gs = scores[0].cpu().double().numpy()
+    for t in range(0, T, 97):
+        n = len(ref_sc[t])
+        assert np.allclose(gs[t, :n], ref_sc[t], rtol=1e-5, atol=1e-5)
+
+
+def test_prefill_bf16_chunk_at_offset():
+    """BF16 keys and queries (16 heads x 64 dims), queries at positions
+    3072..4095 of a longer prefill, k = 256; includes a ragged query count."""
+    T, H, d, m, k, pos0 = 1000, 16, 64, 4, 256, 3072
+    cap = (pos0 + T) // m + 3
+    kc, K = key_cache("bf16", 1, cap, d, m, seed=22)
+    qI = synth.normal((1, T, H, d), "qI", 22, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((1, T, H), "w", 22, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "bf16", "bf16", "f32", m, cap)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, idx)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = oracle_rows(np64(qI[0]), np64(w[0]), K[0], pos0 + np.arange(T), m, k, "bf16", "f32")
+    got = idx[0].cpu().numpy()
+    assert ascending_padded(got)
+    differing, bad = compare_topk(got, ref_idx, ref_sc, 1e-6)
+    assert not bad and differing <= 0.01 * T
+
+
+def test_decode_fp8_keys_mixed_positions():
+    """FP8 keys with per-entry scale, BF16 queries, fp32 scores; sequences at
+    different positions, including one with a single visible entry and one
+    with none."""
+    B, H, d, m, k, cap = 4, 16, 64, 4, 1024, 8192
+    kc, K = key_cache("fp8", B, cap, d, m, seed=23)
+    positions = [4 * cap - 1, 20000, 5, 2]
+    pos = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    qI = synth.normal((B, H, d), "qI", 23, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((B, H), "w", 23, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "bf16", "fp8", "f32", m, cap)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    cb.index_topk_decode(desc, kc, pos, qI, w, k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert ascending_padded(got)
+    for b in range(B):
+        ri, rs = oracle_rows(np64(qI[b])[None], np64(w[b])[None], K[b], [positions[b]], m, k, "bf16", "f32")
+        differing, bad = compare_topk(got[b:b + 1], ri, rs, 1e-6)
+        assert not bad, f"sequence {b}"
+    assert list(got[2]) == [0] + [-1] * (k - 1)
+    assert (got[3] == -1).all()
+
+
+def test_decode_mxfp4_bf16_scores():
+    """MXFP4 keys and queries (the query is quantised inside the call), fp32
+    accumulation, scores rounded to BF16 before selection.  The GPU's fp32
+    sum and the oracle's fp64 sum may round to neighbouring BF16 values, so
+    indices within one BF16 step of the threshold may differ."""
+    B, H, d, m, k, cap = 2, 16, 64, 4, 1024, 16384
+    kc, K = key_cache("mxfp4", B, cap, d, m, seed=24)
+    positions = [4 * cap - 1, 30001]
+    pos = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    qI = synth.normal((B, H, d), "qI", 24, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((B, H), "w", 24, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "mxfp4", "mxfp4", "bf16", m, cap)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    scores = torch.zeros((B, cap), dtype=torch.float32, device=DEV)
+    cb.index_topk_decode(desc, kc, pos, qI, w, k, idx, scores)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert ascending_padded(got)
+    for b in range(B):
+        ri, rs = oracle_rows(np64(qI[b])[None], np64(w[b])[None], K[b], [positions[b]], m, k, "mxfp4", "bf16")
+        differing, bad = compare_topk(got[b:b + 1], ri, rs, 0.0, kth_rel_window=2.0 ** -7)
+        assert not bad, f"sequence {b}"
+        gs = scores[b].cpu().double().numpy()[:len(rs[0])]
+        # scores equal, or one BF16 step apart
+        assert (np.abs(gs - rs[0]) <= 2.0 ** -7 * np.abs(rs[0])).all()
+        assert (gs == rs[0]).mean() > 0.99
+
+
+def test_k_larger_than_visible():
+    B, H, d, m, k, cap = 2, 4, 32, 4, 64, 100
+    kc, K = key_cache("f32", B, cap, d, m, seed=25)
+    pos = torch.tensor([4 * 50 - 1, 4 * 63], dtype=torch.int64, device=DEV)
+    qI = synth.normal((B, H, d), "qI", 25, device=DEV)
+    w = synth.normal((B, H), "w", 25, device=DEV)
+    desc = cb.index_desc(H, d, "f32", "f32", "f32", "f32", m, cap)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    cb.index_topk_decode(desc, kc, pos, qI, w, k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert list(got[0]) == list(range(50)) + [-1] * 14
+    assert list(got[1]) == list(range(63)) + [-1]
