@@ -1,15 +1,416 @@
-// MFMA attention kernels for the MI355X shapes (placeholder until the
-// kernels land: every case takes the generic path).
+// MFMA attention for the MI355X-shaped cases: 64 query heads sharing one
+// compressed entry of 512 non-RoPE + 64 RoPE dims (MQA), BF16 queries and
+// outputs, BF16 or FP8-with-scale cache.  [CSA/HCA 混注意力] §1.1, §1.2;
+// [读完这篇] §三 CSA 步骤三 (standard attention over the selected entries, KV
+// shared across heads); §1.4 存储格式混 (FP8 non-RoPE dims, BF16 RoPE dims).
+//
+// One workgroup (4 waves) owns one query (all 64 heads) and a range of its
+// entry list.  Entries are gathered 64 at a time into an LDS tile (rows
+// padded to 1168 B so the 32 rows one MFMA operand touches fall on distinct
+// bank groups); FP8 codes are widened to BF16 exactly on the way in and the
+// per-entry scale is applied to the non-RoPE part of the logit.  Wave w owns
+// heads 32*(w/2).. and, for the logits, entries 32*(w%2).. of the tile; for
+// P.V it owns value dims 256*(w%2)...  The next tile's rows are loaded into
+// registers while the current one is multiplied.
+//
+//   S = Q K^T        v_mfma_f32_32x32x16_bf16, Q held in registers (A),
+//                    K rows from LDS (B); non-RoPE and RoPE parts kept apart
+//                    so the FP8 scale applies to the first only
+//   online softmax   row max exchanged between the two waves of a head half
+//                    through LDS, exp2 with log2(e) folded into the scale
+//   O += P V         P (BF16) through LDS as the A operand, V read from the
+//                    same K tile as the B operand (entries along k)
+//
+// Decode splits the entry list over several workgroups per sequence; each
+// writes an unnormalised partial (O, max, sum) and attn_merge_kernel
+// combines them by log-sum-exp.
+#include <cmath>
+
 #include "attention.hpp"
 
 namespace csa {
+namespace {
 
-bool mfma_attn_supported(const AttnParams&) { return false; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-int launch_mfma_attn(const AttnParams&, int, int, hipStream_t) {
-  return fail(CSA_ERR_UNSUPPORTED, "MFMA attention path not built");
+constexpr int NH = 64;       // heads
+constexpr int DN = 512;      // value / non-RoPE dims
+constexpr int DRP = 64;      // RoPE dims
+constexpr int CW = DN + DRP; // entry width
+constexpr int TILE = 64;     // entries per LDS tile
+constexpr int KROW = CW + 8; // padded LDS row (bf16 elements), 1168 B
+constexpr int PROW = TILE + 8;  // padded P row, 144 B
+constexpr int MAX_SPLITS = 32;
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
+
+struct Theta {
+  double t[DRP / 2];  // base^(-2p/d_rope)
+};
+
+struct Prefetch {
+  u32x4 nope[16];  // BF16: 16 chunks of 8 dims; FP8: 8 chunks of 16 codes
+  u32x4 rope[2];
+  float scale;     // thread tid < TILE: the scale of entry tid (0 if invalid)
+};
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// FP8 E4M3 code -> BF16 bits (exact: 3 mantissa bits fit in 7).
+__device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
+  return __float_as_uint(e4m3_to_f32(c)) >> 16;
 }
 
-size_t mfma_attn_ws_bytes(const csa_attn_desc*, int, int, int, int64_t, int) { return 0; }
+struct TileCtx {
+  const AttnParams* P;
+  const int32_t* list;  // sparse: the query's index row; dense: NULL
+  int64_t r1;           // end of this workgroup's list range
+  int64_t n;            // visible entries
+  int b;
+};
+
+template <bool DENSE>
+__device__ __forceinline__ int64_t entry_at(const TileCtx& c, int64_t r) {
+  if (r >= c.r1) return -1;
+  int64_t s = DENSE ? r : static_cast<int64_t>(c.list[r]);
+  return (s >= 0 && s < c.n) ? s : -1;
+}
+
+template <bool FP8, bool DENSE>
+__device__ __forceinline__ void load_tile(Prefetch& pf, const TileCtx& c, int64_t r) {
+  const AttnParams& P = *c.P;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const size_t seq = static_cast<size_t>(c.b) * P.cap;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
+  if (!FP8) {
+    const bf16_t* base = static_cast<const bf16_t*>(P.nope);
+#pragma unroll
+    for (int it = 0; it < 16; ++it) {
+      const int64_t s = entry_at<DENSE>(c, r + w * 16 + it);
+      pf.nope[it] = s >= 0 ? *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + lane * 8) : zero;
+    }
+  } else {
+    const uint8_t* base = static_cast<const uint8_t*>(P.nope);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int64_t s = entry_at<DENSE>(c, r + w * 16 + it * 2 + (lane >> 5));
+      pf.nope[it] = s >= 0 ? *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + (lane & 31) * 16) : zero;
+    }
+  }
+  const bf16_t* rbase = static_cast<const bf16_t*>(P.rope);
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = it * 256 + tid;
+    const int64_t s = entry_at<DENSE>(c, r + q / 8);
+    pf.rope[it] = s >= 0 ? *reinterpret_cast<const u32x4*>(rbase + (seq + s) * DRP + (q % 8) * 8) : zero;
+  }
+  if (tid < TILE) {
+    const int64_t s = entry_at<DENSE>(c, r + tid);
+    pf.scale = s < 0 ? 0.0f : (FP8 ? static_cast<const float*>(P.scale)[seq + s] : 1.0f);
+  }
+}
+
+template <bool FP8>
+__device__ __forceinline__ void store_tile(const Prefetch& pf, bf16_t* ktile, float* s_scale) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (!FP8) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it)
+      *reinterpret_cast<u32x4*>(ktile + (w * 16 + it) * KROW + lane * 8) = pf.nope[it];
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int e = w * 16 + it * 2 + (lane >> 5);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t word = pf.nope[it][q];
+        const uint32_t b0 = e4m3_to_bf16_bits(word & 0xFFu), b1 = e4m3_to_bf16_bits((word >> 8) & 0xFFu);
+        const uint32_t b2 = e4m3_to_bf16_bits((word >> 16) & 0xFFu), b3 = e4m3_to_bf16_bits(word >> 24);
+        const uint32_t p0 = b0 | (b1 << 16), p1 = b2 | (b3 << 16);
+        if (q < 2) { lo[2 * q] = p0; lo[2 * q + 1] = p1; }
+        else { hi[2 * (q - 2)] = p0; hi[2 * (q - 2) + 1] = p1; }
+      }
+      bf16_t* dst = ktile + e * KROW + (lane & 31) * 16;
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 8) = hi;
+    }
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) {
+    const int q = it * 256 + tid;
+    *reinterpret_cast<u32x4*>(ktile + (q / 8) * KROW + DN + (q % 8) * 8) = pf.rope[it];
+  }
+  if (tid < TILE) s_scale[tid] = pf.scale;
+}
+
+// Row (head within the wave's 32) held in register v of a 32x32 MFMA result.
+__device__ __forceinline__ int acc_row(int v, int lane) { return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); }
+
+template <bool FP8, bool DENSE, bool SPLIT>
+__global__ void __launch_bounds__(256, 1)
+attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* part) {
+  __shared__ __attribute__((aligned(16))) bf16_t ktile[TILE * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t pbuf[NH * PROW];
+  __shared__ float s_scale[TILE];
+  __shared__ float s_xchg[2][NH];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int hp = w >> 1, ep = w & 1;
+  const int b = blockIdx.z;
+  const int t = SPLIT ? 0 : blockIdx.x;
+  const int split = SPLIT ? blockIdx.x : 0;
+  const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
+  int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
+  if (n > P.cap) n = P.cap;
+  const int64_t count = DENSE ? n : P.k;
+  const int64_t r0 = static_cast<int64_t>(split) * per_split;
+  int64_t r1 = r0 + per_split;
+  if (r1 > count) r1 = count;
+  const size_t qrow = (static_cast<size_t>(b) * P.T + t) * NH;
+
+  TileCtx c;
+  c.P = &P;
+  c.list = DENSE ? nullptr : P.idx + (static_cast<size_t>(b) * P.T + t) * P.k;
+  c.r1 = r1;
+  c.n = n;
+  c.b = b;
+
+  // --- query fragment (A operand), RoPE on the last 64 dims ---------------
+  const int head = 32 * hp + (lane & 31);
+  bf16x8 qa[CW / 16];
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(P.q) + (qrow + head) * CW + (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < CW / 16; ++s) {
+      u32x4 raw = *reinterpret_cast<const u32x4*>(qp + s * 16);
+      if (s >= DN / 16) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = ((s * 16 + (lane >> 5) * 8 - DN) >> 1) + i;  // pair index
+          const double ang = static_cast<double>(pos) * th.t[p];
+          const double red = ang - rint(ang * 0.15915494309189535) * 6.283185307179586;
+          float sn, cs;
+          sincosf(static_cast<float>(red), &sn, &cs);
+          const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
+          const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
+          raw[i] = static_cast<uint32_t>(f32_to_bf16(x0 * cs - x1 * sn)) |
+                   (static_cast<uint32_t>(f32_to_bf16(x0 * sn + x1 * cs)) << 16);
+        }
+      }
+      qa[s] = as_bf16x8(raw);
+    }
+  }
+
+  const float lscale = P.scale_qk * LOG2E;
+  f32x16 oacc[8];
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x16{};
+  float m_run[16], l_part[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) { m_run[v] = -INFINITY; l_part[v] = 0.0f; }
+
+  const int64_t ntiles = r1 > r0 ? (r1 - r0 + TILE - 1) / TILE : 0;
+  Prefetch pf;
+  if (ntiles > 0) load_tile<FP8, DENSE>(pf, c, r0);
+  for (int64_t j = 0; j < ntiles; ++j) {
+    __syncthreads();  // previous tile's P.V finished with ktile / pbuf
+    store_tile<FP8>(pf, ktile, s_scale);
+    __syncthreads();
+    if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, c, r0 + (j + 1) * TILE);
+
+    // --- S = Q K^T for heads 32hp.., entries 32ep.. ------------------------
+    f32x16 sn = f32x16{}, sr = f32x16{};
+    const bf16_t* krow = ktile + (ep * 32 + (lane & 31)) * KROW + (lane >> 5) * 8;
+#pragma unroll
+    for (int s = 0; s < DN / 16; ++s)
+      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], *reinterpret_cast<const bf16x8*>(krow + s * 16), sn, 0, 0, 0);
+#pragma unroll
+    for (int s = DN / 16; s < CW / 16; ++s)
+      sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], *reinterpret_cast<const bf16x8*>(krow + s * 16), sr, 0, 0, 0);
+
+    const float esc = s_scale[ep * 32 + (lane & 31)];
+    const bool valid = esc != 0.0f;
+    float lg[16], mx[16];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      lg[v] = valid ? (sn[v] * esc + sr[v]) * lscale : -INFINITY;
+      float x = lg[v];
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+      mx[v] = x;
+    }
+    if ((lane & 31) == 0) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s_xchg[ep][32 * hp + acc_row(v, lane)] = mx[v];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const float other = s_xchg[ep ^ 1][32 * hp + acc_row(v, lane)];
+      const float mnew = fmaxf(m_run[v], fmaxf(mx[v], other));
+      const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[v] - mnew);
+      const float p = valid ? exp2f(lg[v] - mnew) : 0.0f;
+      l_part[v] = l_part[v] * alpha + p;
+      m_run[v] = mnew;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) oacc[nb][v] *= alpha;
+      // V rows in the tile are unscaled FP8 codes: the entry scale goes into P
+      pbuf[(32 * hp + acc_row(v, lane)) * PROW + ep * 32 + (lane & 31)] = f32_to_bf16(FP8 ? p * esc : p);
+    }
+    __syncthreads();
+
+    // --- O += P V for heads 32hp.., value dims 256ep.. -----------------------
+    bf16x8 pa[TILE / 16];
+    const bf16_t* prow = pbuf + (32 * hp + (lane & 31)) * PROW + (lane >> 5) * 8;
+#pragma unroll
+    for (int ks = 0; ks < TILE / 16; ++ks) pa[ks] = *reinterpret_cast<const bf16x8*>(prow + ks * 16);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const bf16_t* vcol = ktile + (lane >> 5) * 8 * KROW + ep * 256 + nb * 32 + (lane & 31);
+#pragma unroll
+      for (int ks = 0; ks < TILE / 16; ++ks) {
+        bf16x8 vb;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vb[i] = __builtin_bit_cast(__bf16, vcol[(ks * 16 + i) * KROW]);
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], vb, oacc[nb], 0, 0, 0);
+      }
+    }
+  }
+
+  // --- finish: row sums over the 64 entries of each tile ------------------
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    float x = l_part[v];
+#pragma unroll
+    for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
+    l_part[v] = x;
+  }
+  __syncthreads();
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) s_xchg[ep][32 * hp + acc_row(v, lane)] = l_part[v];
+  }
+  __syncthreads();
+  float ltot[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) ltot[v] = l_part[v] + s_xchg[ep ^ 1][32 * hp + acc_row(v, lane)];
+
+  if (!SPLIT) {
+    bf16_t* out = static_cast<bf16_t*>(P.o) + qrow * DN;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int h = 32 * hp + acc_row(v, lane);
+      const float inv = ltot[v] > 0.0f ? 1.0f / ltot[v] : 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb)
+        out[static_cast<size_t>(h) * DN + ep * 256 + nb * 32 + (lane & 31)] = f32_to_bf16(oacc[nb][v] * inv);
+      if (P.lse && ep == 0 && (lane & 31) == 0)
+        P.lse[qrow + h] = ltot[v] > 0.0f ? (m_run[v] + log2f(ltot[v])) * LN2 : -INFINITY;
+    }
+  } else {
+    // partial: [B][splits][NH][DN] O, then [B][splits][NH][2] (max, sum)
+    const size_t slot = static_cast<size_t>(b) * splits + split;
+    float* po = part + slot * (NH * DN);
+    float* pml = part + static_cast<size_t>(gridDim.z) * splits * (NH * DN) + slot * (2 * NH);
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int h = 32 * hp + acc_row(v, lane);
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) po[h * DN + ep * 256 + nb * 32 + (lane & 31)] = oacc[nb][v];
+      if (ep == 0 && (lane & 31) == 0) {
+        pml[2 * h] = m_run[v];
+        pml[2 * h + 1] = ltot[v];
+      }
+    }
+  }
+}
+
+// Combines split partials by log-sum-exp; grid (B), 512 threads.
+__global__ void __launch_bounds__(512) attn_merge_kernel(AttnParams P, int splits, const float* part, int B) {
+  const int b = blockIdx.x;
+  const float* po = part + static_cast<size_t>(b) * splits * (NH * DN);
+  const float* pml = part + static_cast<size_t>(B) * splits * (NH * DN) + static_cast<size_t>(b) * splits * (2 * NH);
+  bf16_t* out = static_cast<bf16_t*>(P.o) + static_cast<size_t>(b) * NH * DN;
+  for (int x = threadIdx.x; x < NH * DN; x += blockDim.x) {
+    const int h = x / DN;
+    float M = -INFINITY;
+    for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[(s * NH + h) * 2]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != -INFINITY) {
+      for (int s = 0; s < splits; ++s) {
+        const float ms = pml[(s * NH + h) * 2];
+        if (ms == -INFINITY) continue;
+        const float f = exp2f(ms - M);
+        L += pml[(s * NH + h) * 2 + 1] * f;
+        acc += po[static_cast<size_t>(s) * NH * DN + x] * f;
+      }
+    }
+    out[x] = f32_to_bf16(L > 0.0f ? acc / L : 0.0f);
+    if (P.lse && (x % DN) == 0) P.lse[static_cast<size_t>(b) * NH + h] = L > 0.0f ? (M + log2f(L)) * LN2 : -INFINITY;
+  }
+}
+
+Theta make_theta(double base) {
+  Theta th;
+  for (int p = 0; p < DRP / 2; ++p) th.t[p] = std::pow(base, -2.0 * p / DRP);
+  return th;
+}
+
+int decode_splits(int B, int64_t ntiles) {
+  int64_t s = (256 + B - 1) / B;
+  if (s > MAX_SPLITS) s = MAX_SPLITS;
+  if (s > ntiles) s = ntiles;
+  return s < 1 ? 1 : static_cast<int>(s);
+}
+
+}  // namespace
+
+bool mfma_attn_supported(const AttnParams& P) {
+  return P.H == NH && P.d_nope == DN && P.d_rope == DRP && P.q_dt == CSA_BF16 && P.o_dt == CSA_BF16 &&
+         (P.nope_dt == CSA_BF16 || P.nope_dt == CSA_FP8E4M3) && P.rope_dt == CSA_BF16;
+}
+
+size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, int) {
+  if (op != CSA_OP_SPARSE_ATTN_DECODE && op != CSA_OP_DENSE_ATTN_DECODE) return 0;
+  if (d->n_heads != NH || d->d_nope != DN || d->d_rope != DRP) return 0;
+  return static_cast<size_t>(B) * MAX_SPLITS * (NH * DN + 2 * NH) * sizeof(float);
+}
+
+template <bool FP8, bool DENSE, bool SPLIT>
+static void launch_one(const AttnParams& P, dim3 grid, hipStream_t s, int splits, int64_t per, float* part) {
+  hipLaunchKernelGGL((attn_mfma_kernel<FP8, DENSE, SPLIT>), grid, dim3(256), 0, s, P, make_theta(P.base), splits,
+                     per, part);
+}
+
+int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
+  const bool fp8 = P.nope_dt == CSA_FP8E4M3;
+  const bool dense = op == CSA_OP_DENSE_ATTN_PREFILL || op == CSA_OP_DENSE_ATTN_DECODE;
+  const bool decode = op == CSA_OP_SPARSE_ATTN_DECODE || op == CSA_OP_DENSE_ATTN_DECODE;
+  if (!decode) {
+    const int64_t per = dense ? P.cap : P.k;
+    dim3 grid(P.T, 1, B);
+    if (fp8) dense ? launch_one<true, true, false>(P, grid, s, 1, per, nullptr) : launch_one<true, false, false>(P, grid, s, 1, per, nullptr);
+    else dense ? launch_one<false, true, false>(P, grid, s, 1, per, nullptr) : launch_one<false, false, false>(P, grid, s, 1, per, nullptr);
+    return check_launch("attn_mfma_kernel");
+  }
+  const int64_t count = dense ? P.cap : P.k;
+  const int64_t ntiles = (count + TILE - 1) / TILE;
+  const int splits = decode_splits(B, ntiles);
+  const int64_t tiles_per = (ntiles + splits - 1) / splits;
+  const int64_t per = tiles_per * TILE;
+  const size_t need = static_cast<size_t>(B) * splits * (NH * DN + 2 * NH) * sizeof(float);
+  if (!P.ws || P.ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace too small for the split partials");
+  float* part = static_cast<float*>(P.ws);
+  dim3 grid(splits, 1, B);
+  if (fp8) dense ? launch_one<true, true, true>(P, grid, s, splits, per, part) : launch_one<true, false, true>(P, grid, s, splits, per, part);
+  else dense ? launch_one<false, true, true>(P, grid, s, splits, per, part) : launch_one<false, false, true>(P, grid, s, splits, per, part);
+  int st = check_launch("attn_mfma_kernel");
+  if (st != CSA_OK) return st;
+  hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(512), 0, s, P, splits, part, B);
+  return check_launch("attn_merge_kernel");
+}
 
 }  // namespace csa
