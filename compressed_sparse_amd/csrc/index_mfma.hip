@@ -1,0 +1,378 @@
+// MFMA lightning indexer for 16 heads x 64 dims (BF16 or MXFP4 QK product;
+// BF16, FP8-with-scale or MXFP4 keys).  [CSA/HCA 混注意力] §1.4 LIGHTNING
+// INDEXER 的 FP4 计; [读完这篇] §三 CSA 步骤二.
+//
+//   I[s] = sum_h w[h] * ReLU(qI[h] . K[s])
+//
+// index_prefill_fused_kernel: 4 consecutive queries per workgroup, i.e. 64
+//   MFMA rows (query x head) against 32-entry column blocks
+//   (v_mfma_f32_32x32x16_bf16, keys loaded straight from L2 as the B
+//   operand).  The 4 score rows stay in LDS (4 x 8192 fp32) and each wave
+//   then radix-selects one row's top-k, so scores never reach HBM.
+// index_scan_kernel: one query row against a 1024-entry chunk per
+//   workgroup (v_mfma_f32_16x16x32_bf16, rows = the 16 heads); the decode
+//   scan and the fallback for long prefill rows.  FP8 and E2M1 codes widen
+//   to BF16 exactly in registers; the per-entry FP8 scale multiplies the dot
+//   product, the E8M0 block scales are folded into the widened values.
+//
+// Both kernels reduce heads in a fixed order (4 or 8 heads inside a lane,
+// then fixed cross-lane shuffles), so scores are run-to-run deterministic.
+#include "index.hpp"
+
+namespace csa {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int HI = 16;
+constexpr int DI = 64;
+constexpr int QG = 4;          // queries per fused workgroup
+constexpr int FUSED_NMAX = 8192;
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+}
+
+// 8 FP8 codes (two words, first byte first) -> 8 BF16 values (exact).
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  u32x4 o;
+  const uint32_t wd[2] = {w0, w1};
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t word = wd[j];
+    o[2 * j] = (__float_as_uint(e4m3_to_f32(word & 0xFFu)) >> 16) |
+               (__float_as_uint(e4m3_to_f32((word >> 8) & 0xFFu)) & 0xFFFF0000u);
+    o[2 * j + 1] = (__float_as_uint(e4m3_to_f32((word >> 16) & 0xFFu)) >> 16) |
+                   (__float_as_uint(e4m3_to_f32(word >> 24)) & 0xFFFF0000u);
+  }
+  return o;
+}
+
+// 8 E2M1 codes (one word, low nibble first) times 2^ex -> 4 words of BF16 pairs (exact).
+__device__ __forceinline__ void e2m1x8_to_bf16(uint32_t word, float X, u32x4& out) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float a = e2m1_to_f32((word >> (8 * q)) & 15u) * X;
+    const float b = e2m1_to_f32((word >> (8 * q + 4)) & 15u) * X;
+    out[q] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
+  }
+}
+
+// Orders this wave's LDS accesses before the ones that follow.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
+__device__ __forceinline__ uint32_t order_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) return 0x80000000u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------------------
+// fused prefill: scores of 4 queries in LDS, then one wave per row selects
+// ---------------------------------------------------------------------------
+
+// Wave-level radix select of the top-k of row[0..n) (n > k) and ordered
+// compaction of the selected indices into out[0..k).
+__device__ void wave_select(const float* row, int n, int k, int key_bits, int* hist, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = k;
+  for (int shift = 24; shift >= 32 - key_bits; shift -= 8) {
+    for (int i = lane; i < 256; i += 64) hist[i] = 0;
+    wave_lds_sync();
+    for (int s = lane; s < n; s += 64) {
+      const uint32_t key = order_key(row[s]);
+      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+    }
+    wave_lds_sync();
+    // lane i owns bins 255-4i .. 252-4i (descending); inclusive scan from the top
+    int c[4], tot = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; tot += c[j]; }
+    int incl = tot;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int excl = incl - tot;  // count in bins above this lane's bins
+    int bin = -1, above = 0;
+    if (excl < remaining && incl >= remaining) {
+      int cum = excl;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (bin < 0 && cum + c[j] >= remaining) { bin = 255 - 4 * lane - j; above = cum; }
+        cum += c[j];
+      }
+    }
+    const unsigned long long who = __ballot(bin >= 0);
+    const int src = __ffsll(static_cast<long long>(who)) - 1;
+    bin = __shfl(bin, src);
+    above = __shfl(above, src);
+    prefix |= static_cast<uint32_t>(bin) << shift;
+    pmask |= 255u << shift;
+    remaining -= above;
+    wave_lds_sync();
+  }
+  int taken_eq = 0, written = 0;
+  for (int base = 0; base < n; base += 64) {
+    const int s = base + lane;
+    const uint32_t key = s < n ? (order_key(row[s]) & pmask) : 0u;
+    const bool gt = s < n && key > prefix;
+    const bool eq = s < n && key == prefix;
+    const unsigned long long below = (1ull << lane) - 1ull;
+    const unsigned long long eqm = __ballot(eq);
+    const bool take = gt || (eq && taken_eq + __popcll(eqm & below) < remaining);
+    const unsigned long long tm = __ballot(take);
+    if (take) out[written + __popcll(tm & below)] = s;
+    taken_eq += __popcll(eqm);
+    written += __popcll(tm);
+  }
+  for (int j = written + lane; j < k; j += 64) out[j] = -1;
+}
+
+template <bool KFP8>
+__global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams P) {
+  __shared__ float srow[QG][FUSED_NMAX];
+  __shared__ int hist[QG][256];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.y;
+  const int t0 = blockIdx.x * QG;
+  // visible entries of query t0 + q (0 past the end of the rows)
+  auto nvis = [&](int q) -> int {
+    if (t0 + q >= P.T) return 0;
+    int64_t n = (P.pos0 + t0 + q + 1) / P.m;
+    return static_cast<int>(n < P.cap ? n : P.cap);
+  };
+  int nmax = 0;
+  for (int q = 0; q < QG; ++q) nmax = nvis(q) > nmax ? nvis(q) : nmax;
+  // rows that keep every visible entry need no scores
+  const bool need = nmax > P.k;
+  const size_t row0 = static_cast<size_t>(b) * P.T + t0;
+
+  if (need) {
+    // A operands: rows r = 32*rb + (lane & 31) -> query 2rb + r/16, head r%16;
+    // k-step ks covers dims (lane>>5)*32 + ks*8 .. +8 (same map for B)
+    bf16x8 qa[2][4];
+    float wv[2][16];
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const int r = lane & 31;
+      const int q = 2 * rb + (r >> 4);
+      const bool live = t0 + q < P.T;
+      const bf16_t* qp = static_cast<const bf16_t*>(P.qI) + ((row0 + q) * HI + (r & 15)) * DI + (lane >> 5) * 32;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        qa[rb][ks] = as_bf16x8(live ? *reinterpret_cast<const u32x4*>(qp + ks * 8) : z);
+      }
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int rr = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        const int qq = 2 * rb + (rr >> 4);
+        wv[rb][v] = (t0 + qq < P.T) ? P.w[(row0 + qq) * HI + (rr & 15)] : 0.0f;
+      }
+    }
+    const size_t seq = static_cast<size_t>(b) * P.cap;
+    const int nblocks = (nmax + 31) / 32;
+    for (int cb = w; cb < nblocks; cb += 4) {
+      const int s = cb * 32 + (lane & 31);
+      u32x4 kr[4];
+      float ksc = 1.0f;
+      if (s < nmax) {
+        if (KFP8) {
+          const uint8_t* kp = static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
+          const u32x4 c0 = *reinterpret_cast<const u32x4*>(kp);
+          const u32x4 c1 = *reinterpret_cast<const u32x4*>(kp + 16);
+          kr[0] = fp8x8_to_bf16(c0[0], c0[1]);
+          kr[1] = fp8x8_to_bf16(c0[2], c0[3]);
+          kr[2] = fp8x8_to_bf16(c1[0], c1[1]);
+          kr[3] = fp8x8_to_bf16(c1[2], c1[3]);
+          ksc = static_cast<const float*>(P.kscale)[seq + s];
+        } else {
+          const bf16_t* kp = static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
+#pragma unroll
+          for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const u32x4*>(kp + ks * 8);
+        }
+      } else {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kr[ks] = u32x4{0u, 0u, 0u, 0u};
+      }
+      f32x16 acc[2];
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        acc[rb] = f32x16{};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], as_bf16x8(kr[ks]), acc[rb], 0, 0, 0);
+      }
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        float s0 = 0.0f, s1 = 0.0f;  // queries 2rb, 2rb+1 (8 heads of each in this lane)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) s0 = fmaf(wv[rb][v], fmaxf(acc[rb][v] * ksc, 0.0f), s0);
+#pragma unroll
+        for (int v = 8; v < 16; ++v) s1 = fmaf(wv[rb][v], fmaxf(acc[rb][v] * ksc, 0.0f), s1);
+        const float o0 = __shfl_xor(s0, 32), o1 = __shfl_xor(s1, 32);
+        // lanes 0-31 hold head groups {0-3, 8-11}, lanes 32-63 {4-7, 12-15}:
+        // add in a fixed order (lower half first)
+        const float t0s = (lane < 32) ? s0 + o0 : o0 + s0;
+        const float t1s = (lane < 32) ? s1 + o1 : o1 + s1;
+        const int q = 2 * rb + (lane >> 5);
+        float val = (lane < 32) ? t0s : t1s;
+        if (P.score_dt == CSA_BF16) val = round_bf16(val);
+        if (s < nvis(q)) srow[q][s] = val;
+      }
+    }
+  }
+  __syncthreads();
+  // one wave per query row
+  const int q = w;
+  if (t0 + q >= P.T) return;
+  int32_t* out = P.idx + (row0 + q) * P.k;
+  const int n = nvis(q);
+  if (n <= P.k) {
+    for (int j = lane; j < P.k; j += 64) out[j] = j < n ? j : -1;
+    return;
+  }
+  wave_select(srow[q], n, P.k, P.score_dt == CSA_BF16 ? 16 : 32, hist[q], out);
+}
+
+// ---------------------------------------------------------------------------
+// streaming scan: one query row x 1024 entries per workgroup
+// ---------------------------------------------------------------------------
+constexpr int SCAN_CHUNK = 1024;
+
+template <int KFMT, bool QMX>
+__global__ void __launch_bounds__(256) index_scan_kernel(IndexParams P) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.z, t = blockIdx.y;
+  const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
+  int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
+  if (n > P.cap) n = P.cap;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * SCAN_CHUNK;
+  if (c0 >= n) return;
+  const size_t row = static_cast<size_t>(b) * P.T + t;
+  // A operand (16x16x32): head = lane & 15; k-step ks covers dims g*16 + ks*8 .. +8, g = lane >> 4
+  const int g = lane >> 4, h = lane & 15;
+  bf16x8 qa[2];
+  {
+    const bf16_t* qp = static_cast<const bf16_t*>(P.qI) + (row * HI + h) * DI + g * 16;
+    u32x4 r0 = *reinterpret_cast<const u32x4*>(qp);
+    u32x4 r1 = *reinterpret_cast<const u32x4*>(qp + 8);
+    if (QMX) {
+      float x[16];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x[2 * i] = bf16_to_f32(static_cast<bf16_t>(r0[i] & 0xFFFFu));
+        x[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(r0[i] >> 16));
+        x[8 + 2 * i] = bf16_to_f32(static_cast<bf16_t>(r1[i] & 0xFFFFu));
+        x[8 + 2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(r1[i] >> 16));
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
+      am = fmaxf(am, __shfl_xor(am, 16));  // the other half of this 32-dim block
+      const int ex = mx_exponent(am);
+      const float inv = exp2i(-ex), X = exp2i(ex);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = e2m1_to_f32(f32_to_e2m1(x[i] * inv)) * X;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r0[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
+        r1[i] = pack_bf16(x[8 + 2 * i], x[8 + 2 * i + 1]);
+      }
+    }
+    qa[0] = as_bf16x8(r0);
+    qa[1] = as_bf16x8(r1);
+  }
+  float wv[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) wv[v] = P.w[row * HI + g * 4 + v];
+  const size_t seq = static_cast<size_t>(b) * P.cap;
+  float* wsrow = P.ws + row * P.n_stride;
+  float* sorow = P.scores_out ? P.scores_out + row * P.cap : nullptr;
+  int64_t c1 = c0 + SCAN_CHUNK;
+  if (c1 > n) c1 = n;
+  // each wave: 16-entry column blocks w, w+4, ...
+#pragma unroll 2
+  for (int64_t e0 = c0 + w * 16; e0 < c1; e0 += 64) {
+    const int64_t s = e0 + (lane & 15);
+    const bool ok = s < c1;
+    u32x4 k0 = {0u, 0u, 0u, 0u}, k1 = {0u, 0u, 0u, 0u};
+    float ksc = 1.0f;
+    if (ok) {
+      if (KFMT == CSA_BF16) {
+        const bf16_t* kp = static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + g * 16;
+        k0 = *reinterpret_cast<const u32x4*>(kp);
+        k1 = *reinterpret_cast<const u32x4*>(kp + 8);
+      } else if (KFMT == CSA_FP8E4M3) {
+        const u32x4 c = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + g * 16);
+        k0 = fp8x8_to_bf16(c[0], c[1]);
+        k1 = fp8x8_to_bf16(c[2], c[3]);
+        ksc = static_cast<const float*>(P.kscale)[seq + s];
+      } else {  // MXFP4: 16 codes = 8 bytes at dims g*16.., scale of block g/2
+        const u32x2 c = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(P.knope) + (seq + s) * (DI / 2) + g * 8);
+        const int ex = static_cast<int>(static_cast<const uint8_t*>(P.kscale)[(seq + s) * (DI / 32) + (g >> 1)]) - 127;
+        const float X = exp2i(ex);
+        e2m1x8_to_bf16(c[0], X, k0);
+        e2m1x8_to_bf16(c[1], X, k1);
+      }
+    }
+    f32x4 acc = f32x4{};
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(k0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(k1), acc, 0, 0, 0);
+    // lane: entry lane & 15, heads 4g .. 4g+3
+    float sc = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sc = fmaf(wv[v], fmaxf(acc[v] * ksc, 0.0f), sc);
+    // fixed-order head reduction: (g0 + g1) + (g2 + g3)
+    const float x16 = __shfl_xor(sc, 16);
+    const float pair = (g & 1) ? x16 + sc : sc + x16;
+    const float x32 = __shfl_xor(pair, 32);
+    float tot = (g & 2) ? x32 + pair : pair + x32;
+    if (P.score_dt == CSA_BF16) tot = round_bf16(tot);
+    if (ok && g == 0) {
+      wsrow[s] = tot;
+      if (sorow) sorow[s] = tot;
+    }
+  }
+}
+
+}  // namespace
+
+bool index_mfma_supported(const IndexParams& P) {
+  return P.H == HI && P.D == DI && P.q_dt == CSA_BF16 &&
+         ((P.qk_dt == CSA_BF16 && (P.key_dt == CSA_BF16 || P.key_dt == CSA_FP8E4M3)) ||
+          (P.qk_dt == CSA_MXFP4 && P.key_dt == CSA_MXFP4));
+}
+
+bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max) {
+  return index_mfma_supported(P) && P.qk_dt == CSA_BF16 && P.pos_dev == nullptr && n_max <= FUSED_NMAX;
+}
+
+int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
+  dim3 grid((P.T + QG - 1) / QG, B);
+  if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_prefill_fused_kernel<true>, grid, dim3(256), 0, s, P);
+  else hipLaunchKernelGGL(index_prefill_fused_kernel<false>, grid, dim3(256), 0, s, P);
+  return check_launch("index_prefill_fused_kernel");
+}
+
+int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s) {
+  dim3 grid(static_cast<unsigned>((n_max + SCAN_CHUNK - 1) / SCAN_CHUNK), P.T, B);
+  if (P.qk_dt == CSA_MXFP4) hipLaunchKernelGGL((index_scan_kernel<CSA_MXFP4, true>), grid, dim3(256), 0, s, P);
+  else if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL((index_scan_kernel<CSA_FP8E4M3, false>), grid, dim3(256), 0, s, P);
+  else hipLaunchKernelGGL((index_scan_kernel<CSA_BF16, false>), grid, dim3(256), 0, s, P);
+  return check_launch("index_scan_kernel");
+}
+
+}  // namespace csa

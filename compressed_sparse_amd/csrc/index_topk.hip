@@ -9,26 +9,11 @@
 // k-th largest order-preserving key and an ordered compaction writes the
 // selected indices in ascending order (ties at the threshold go to the
 // lower index).
-#include "common.hpp"
+#include "index.hpp"
 
 namespace csa {
 
-struct IndexParams {
-  int H, D, q_dt, qk_dt, key_dt, score_dt, m;
-  int64_t cap;
-  int T;
-  int64_t pos0;
-  const int64_t* pos_dev;  // decode: per-sequence positions (T == 1)
-  const void* qI;
-  const float* w;
-  const void* knope;
-  const void* kscale;
-  int k;
-  int32_t* idx;
-  float* scores_out;  // optional [B][T][cap]
-  float* ws;          // [B][T][n_stride]
-  int64_t n_stride;
-};
+
 
 __device__ __forceinline__ int64_t query_pos(const IndexParams& P, int b, int t) {
   return P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
@@ -195,6 +180,17 @@ __global__ void __launch_bounds__(1024) topk_radix_kernel(IndexParams P, int key
 
 static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
   hipStream_t s = as_stream(stream);
+  if (index_mfma_supported(P)) {
+    // scores stay on chip when every row fits the fused kernel's LDS rows
+    if (!P.scores_out && index_fused_prefill_ok(P, n_max)) return launch_index_fused_prefill(P, B, s);
+    if (n_max > 0) {
+      int st = launch_index_scan(P, B, n_max, s);
+      if (st != CSA_OK) return st;
+    }
+    const int bits = P.score_dt == CSA_BF16 ? 16 : 32;
+    hipLaunchKernelGGL(topk_radix_kernel, dim3(P.T, B), dim3(1024), 0, s, P, bits);
+    return check_launch("topk_radix_kernel");
+  }
   const size_t lds = static_cast<size_t>(P.H) * (P.D + 1) * sizeof(float);
   if (n_max > 0) {
     dim3 grid(static_cast<unsigned>((n_max + 255) / 256), P.T, B);

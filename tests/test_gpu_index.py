@@ -69,23 +69,32 @@ def test_prefill_fp32_tiny_workload_shapes():
         assert np.allclose(gs[t, :n], ref_sc[t], rtol=1e-5, atol=1e-5)
 
 
-def test_prefill_bf16_chunk_at_offset():
-    """BF16 keys and queries (16 heads x 64 dims), queries at positions
-    3072..4095 of a longer prefill, k = 256; includes a ragged query count."""
-    T, H, d, m, k, pos0 = 1000, 16, 64, 4, 256, 3072
+@pytest.mark.parametrize("key_fmt,with_scores", [("bf16", False), ("fp8", False), ("bf16", True)])
+def test_prefill_16x64_chunk_at_offset(key_fmt, with_scores):
+    """16 heads x 64 dims, BF16 queries, BF16 or FP8 keys, queries at
+    positions 3072..4072 of a longer prefill (a ragged last group of 4),
+    k = 256.  Without a score output the scores stay on chip (fused
+    kernel); with one they go through the streaming scan + radix select."""
+    T, H, d, m, k, pos0 = 1001, 16, 64, 4, 256, 3072
     cap = (pos0 + T) // m + 3
-    kc, K = key_cache("bf16", 1, cap, d, m, seed=22)
+    kc, K = key_cache(key_fmt, 1, cap, d, m, seed=22)
     qI = synth.normal((1, T, H, d), "qI", 22, device=DEV, dtype=torch.bfloat16)
     w = synth.normal((1, T, H), "w", 22, device=DEV)
-    desc = cb.index_desc(H, d, "bf16", "bf16", "bf16", "f32", m, cap)
+    desc = cb.index_desc(H, d, "bf16", "bf16", key_fmt, "f32", m, cap)
     idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
-    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, idx)
+    scores = torch.zeros((1, T, cap), dtype=torch.float32, device=DEV) if with_scores else None
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, idx, scores)
     torch.cuda.synchronize()
     ref_idx, ref_sc = oracle_rows(np64(qI[0]), np64(w[0]), K[0], pos0 + np.arange(T), m, k, "bf16", "f32")
     got = idx[0].cpu().numpy()
     assert ascending_padded(got)
     differing, bad = compare_topk(got, ref_idx, ref_sc, 1e-6)
     assert not bad and differing <= 0.01 * T
+    if with_scores:
+        gs = scores[0].cpu().double().numpy()
+        for t in range(0, T, 37):
+            n = len(ref_sc[t])
+            assert np.allclose(gs[t, :n], ref_sc[t], rtol=1e-5, atol=1e-5 * np.abs(ref_sc[t]).max())
 
 
 def test_decode_fp8_keys_mixed_positions():
