@@ -25,6 +25,7 @@
 // writes an unnormalised partial (O, max, sum) and attn_merge_kernel
 // combines them by log-sum-exp.
 #include <cmath>
+#include <utility>
 
 #include "attention.hpp"
 
@@ -63,53 +64,102 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
   return __float_as_uint(e4m3_to_f32(c)) >> 16;
 }
 
-struct TileCtx {
-  const AttnParams* P;
-  const int32_t* list;  // sparse: the query's index row; dense: NULL
-  int64_t r1;           // end of this workgroup's list range
-  int64_t n;            // visible entries
-  int b;
-};
-
-template <bool DENSE>
-__device__ __forceinline__ int64_t entry_at(const TileCtx& c, int64_t r) {
-  if (r >= c.r1) return -1;
-  int64_t s = DENSE ? r : static_cast<int64_t>(c.list[r]);
-  return (s >= 0 && s < c.n) ? s : -1;
+// S = Q K^T over k-steps I: A operand (heads) and B operand (entries) both
+// read from LDS rows (16 B per lane; padded rows keep them conflict-free).
+template <int... I>
+__device__ __forceinline__ void s_mfma(std::integer_sequence<int, I...>, const bf16_t* qrowp, const bf16_t* krow,
+                                       f32x16& acc) {
+  ((acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qrowp + I * 16),
+                                                  *reinterpret_cast<const bf16x8*>(krow + I * 16), acc, 0, 0, 0)),
+   ...);
 }
 
+// Stages the query's 64 heads in LDS (row = head), the last 64 dims turned
+// by RoPE at `pos` (angles reduced in fp64), rounded back to BF16.
+__device__ __forceinline__ void stage_query(bf16_t* qtile, const bf16_t* q, int64_t pos, const Theta& th) {
+  const int tid = threadIdx.x;
+  for (int c = tid; c < NH * (CW / 8); c += 256) {
+    const int h = c / (CW / 8), d0 = (c % (CW / 8)) * 8;
+    u32x4 raw = *reinterpret_cast<const u32x4*>(q + static_cast<size_t>(h) * CW + d0);
+    if (d0 >= DN) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int p = ((d0 - DN) >> 1) + i;
+        const double ang = static_cast<double>(pos) * th.t[p];
+        const float red = static_cast<float>(ang - rint(ang * 0.15915494309189535) * 6.283185307179586);
+        const float sn = __sinf(red), cs = __cosf(red);
+        const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
+        const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
+        raw[i] = static_cast<uint32_t>(f32_to_bf16(x0 * cs - x1 * sn)) |
+                 (static_cast<uint32_t>(f32_to_bf16(x0 * sn + x1 * cs)) << 16);
+      }
+    }
+    *reinterpret_cast<u32x4*>(qtile + h * KROW + d0) = raw;
+  }
+}
+
+// Entry ids of this workgroup's list range, staged in LDS (-1 = skip).
+template <bool DENSE>
+__device__ __forceinline__ int entry_id(const int* s_list, int64_t r_local, int64_t r0, int64_t r1, int64_t n) {
+  if (DENSE) {
+    const int64_t s = r0 + r_local;
+    return s < r1 ? static_cast<int>(s) : -1;
+  }
+  return r_local < r1 - r0 ? s_list[r_local] : -1;
+}
+
+// Issues the global loads of one 64-entry tile (invalid entries read row 0
+// and are zeroed, so nothing branches and no address leaves the cache).
 template <bool FP8, bool DENSE>
-__device__ __forceinline__ void load_tile(Prefetch& pf, const TileCtx& c, int64_t r) {
-  const AttnParams& P = *c.P;
+__device__ __forceinline__ void load_tile(Prefetch& pf, const AttnParams& P, const int* s_list, int64_t rl,
+                                          int64_t r0, int64_t r1, int64_t n, size_t seq) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const size_t seq = static_cast<size_t>(c.b) * P.cap;
   const u32x4 zero = {0u, 0u, 0u, 0u};
+  int ids[16 + 2];
+  if (!FP8) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) ids[it] = entry_id<DENSE>(s_list, rl + w * 16 + it, r0, r1, n);
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) ids[it] = entry_id<DENSE>(s_list, rl + w * 16 + it * 2 + (lane >> 5), r0, r1, n);
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) ids[16 + it] = entry_id<DENSE>(s_list, rl + (it * 256 + tid) / 8, r0, r1, n);
   if (!FP8) {
     const bf16_t* base = static_cast<const bf16_t*>(P.nope);
 #pragma unroll
     for (int it = 0; it < 16; ++it) {
-      const int64_t s = entry_at<DENSE>(c, r + w * 16 + it);
-      pf.nope[it] = s >= 0 ? *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + lane * 8) : zero;
+      const int s = ids[it] < 0 ? 0 : ids[it];
+      pf.nope[it] = *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + lane * 8);
     }
   } else {
     const uint8_t* base = static_cast<const uint8_t*>(P.nope);
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int64_t s = entry_at<DENSE>(c, r + w * 16 + it * 2 + (lane >> 5));
-      pf.nope[it] = s >= 0 ? *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + (lane & 31) * 16) : zero;
+      const int s = ids[it] < 0 ? 0 : ids[it];
+      pf.nope[it] = *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + (lane & 31) * 16);
     }
   }
   const bf16_t* rbase = static_cast<const bf16_t*>(P.rope);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int q = it * 256 + tid;
-    const int64_t s = entry_at<DENSE>(c, r + q / 8);
-    pf.rope[it] = s >= 0 ? *reinterpret_cast<const u32x4*>(rbase + (seq + s) * DRP + (q % 8) * 8) : zero;
+    const int s = ids[16 + it] < 0 ? 0 : ids[16 + it];
+    pf.rope[it] = *reinterpret_cast<const u32x4*>(rbase + (seq + s) * DRP + ((it * 256 + tid) % 8) * 8);
   }
   if (tid < TILE) {
-    const int64_t s = entry_at<DENSE>(c, r + tid);
+    const int s = entry_id<DENSE>(s_list, rl + tid, r0, r1, n);
     pf.scale = s < 0 ? 0.0f : (FP8 ? static_cast<const float*>(P.scale)[seq + s] : 1.0f);
   }
+  // zero the rows of skipped entries (their memory may hold anything)
+  if (!FP8) {
+#pragma unroll
+    for (int it = 0; it < 16; ++it) pf.nope[it] = ids[it] < 0 ? zero : pf.nope[it];
+  } else {
+#pragma unroll
+    for (int it = 0; it < 8; ++it) pf.nope[it] = ids[it] < 0 ? zero : pf.nope[it];
+  }
+#pragma unroll
+  for (int it = 0; it < 2; ++it) pf.rope[it] = ids[16 + it] < 0 ? zero : pf.rope[it];
 }
 
 template <bool FP8>
@@ -149,13 +199,36 @@ __device__ __forceinline__ void store_tile(const Prefetch& pf, bf16_t* ktile, fl
 // Row (head within the wave's 32) held in register v of a 32x32 MFMA result.
 __device__ __forceinline__ int acc_row(int v, int lane) { return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); }
 
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+// B operand of O += P V for value dims [dv0, dv0 + 32) and entries
+// [k0, k0 + 16) from the row-major tile, via two transposing LDS reads:
+// within a 16-lane group, result lane i slot s is element i%4 of the 8 bytes
+// addressed by lane 4s + i/4; lane L = 16G + 4s + q therefore points at
+// entry k0 + 8(G/2) + s (+4 for the second read), dims dv0 + 16(G%2) + 4q.
+__device__ __forceinline__ bf16x8 v_operand(const bf16_t* ktile, int k0, int dv0, int lane) {
+  const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
+  const bf16_t* p = ktile + (k0 + 8 * (G >> 1) + s) * KROW + dv0 + 16 * (G & 1) + 4 * q;
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
+  const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * KROW));
+  const v4s lo = a, hi = b;
+  typedef short v8s __attribute__((ext_vector_type(8)));
+  const v8s all = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, all);
+}
+
+constexpr int MAX_LIST = 1024;  // list entries one workgroup handles
+
 template <bool FP8, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(256, 1)
 attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* part) {
   __shared__ __attribute__((aligned(16))) bf16_t ktile[TILE * KROW];
+  __shared__ __attribute__((aligned(16))) bf16_t qtile[NH * KROW];
   __shared__ __attribute__((aligned(16))) bf16_t pbuf[NH * PROW];
   __shared__ float s_scale[TILE];
   __shared__ float s_xchg[2][NH];
+  __shared__ int s_list[DENSE ? 1 : MAX_LIST];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hp = w >> 1, ep = w & 1;
@@ -170,39 +243,19 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   int64_t r1 = r0 + per_split;
   if (r1 > count) r1 = count;
   const size_t qrow = (static_cast<size_t>(b) * P.T + t) * NH;
+  const size_t seq = static_cast<size_t>(b) * P.cap;
 
-  TileCtx c;
-  c.P = &P;
-  c.list = DENSE ? nullptr : P.idx + (static_cast<size_t>(b) * P.T + t) * P.k;
-  c.r1 = r1;
-  c.n = n;
-  c.b = b;
-
-  // --- query fragment (A operand), RoPE on the last 64 dims ---------------
-  const int head = 32 * hp + (lane & 31);
-  bf16x8 qa[CW / 16];
-  {
-    const bf16_t* qp = static_cast<const bf16_t*>(P.q) + (qrow + head) * CW + (lane >> 5) * 8;
-#pragma unroll
-    for (int s = 0; s < CW / 16; ++s) {
-      u32x4 raw = *reinterpret_cast<const u32x4*>(qp + s * 16);
-      if (s >= DN / 16) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = ((s * 16 + (lane >> 5) * 8 - DN) >> 1) + i;  // pair index
-          const double ang = static_cast<double>(pos) * th.t[p];
-          const double red = ang - rint(ang * 0.15915494309189535) * 6.283185307179586;
-          float sn, cs;
-          sincosf(static_cast<float>(red), &sn, &cs);
-          const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
-          const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
-          raw[i] = static_cast<uint32_t>(f32_to_bf16(x0 * cs - x1 * sn)) |
-                   (static_cast<uint32_t>(f32_to_bf16(x0 * sn + x1 * cs)) << 16);
-        }
-      }
-      qa[s] = as_bf16x8(raw);
+  // the list range of this workgroup, validated once (-1: skip)
+  if (!DENSE) {
+    const int32_t* list = P.idx + (static_cast<size_t>(b) * P.T + t) * P.k;
+    for (int64_t r = tid; r < r1 - r0; r += 256) {
+      const int64_t s = list[r0 + r];
+      s_list[r] = (s >= 0 && s < n) ? static_cast<int>(s) : -1;
     }
   }
+
+  stage_query(qtile, static_cast<const bf16_t*>(P.q) + qrow * CW, pos, th);
+  const bf16_t* qrowp = qtile + (32 * hp + (lane & 31)) * KROW + (lane >> 5) * 8;
 
   const float lscale = P.scale_qk * LOG2E;
   f32x16 oacc[8];
@@ -212,24 +265,21 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
 #pragma unroll
   for (int v = 0; v < 16; ++v) { m_run[v] = -INFINITY; l_part[v] = 0.0f; }
 
+  __syncthreads();  // s_list and the query tile ready
   const int64_t ntiles = r1 > r0 ? (r1 - r0 + TILE - 1) / TILE : 0;
   Prefetch pf;
-  if (ntiles > 0) load_tile<FP8, DENSE>(pf, c, r0);
+  if (ntiles > 0) load_tile<FP8, DENSE>(pf, P, s_list, 0, r0, r1, n, seq);
   for (int64_t j = 0; j < ntiles; ++j) {
     __syncthreads();  // previous tile's P.V finished with ktile / pbuf
     store_tile<FP8>(pf, ktile, s_scale);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, c, r0 + (j + 1) * TILE);
+    if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, P, s_list, (j + 1) * TILE, r0, r1, n, seq);
 
     // --- S = Q K^T for heads 32hp.., entries 32ep.. ------------------------
     f32x16 sn = f32x16{}, sr = f32x16{};
     const bf16_t* krow = ktile + (ep * 32 + (lane & 31)) * KROW + (lane >> 5) * 8;
-#pragma unroll
-    for (int s = 0; s < DN / 16; ++s)
-      sn = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], *reinterpret_cast<const bf16x8*>(krow + s * 16), sn, 0, 0, 0);
-#pragma unroll
-    for (int s = DN / 16; s < CW / 16; ++s)
-      sr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[s], *reinterpret_cast<const bf16x8*>(krow + s * 16), sr, 0, 0, 0);
+    s_mfma(std::make_integer_sequence<int, DN / 16>{}, qrowp, krow, sn);
+    s_mfma(std::make_integer_sequence<int, DRP / 16>{}, qrowp + DN, krow + DN, sr);
 
     const float esc = s_scale[ep * 32 + (lane & 31)];
     const bool valid = esc != 0.0f;
@@ -247,18 +297,26 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       for (int v = 0; v < 16; ++v) s_xchg[ep][32 * hp + acc_row(v, lane)] = mx[v];
     }
     __syncthreads();
+    bool moved = false;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const float other = s_xchg[ep ^ 1][32 * hp + acc_row(v, lane)];
       const float mnew = fmaxf(m_run[v], fmaxf(mx[v], other));
       const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[v] - mnew);
+      moved |= alpha != 1.0f;
       const float p = valid ? exp2f(lg[v] - mnew) : 0.0f;
       l_part[v] = l_part[v] * alpha + p;
       m_run[v] = mnew;
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) oacc[nb][v] *= alpha;
+      mx[v] = alpha;
       // V rows in the tile are unscaled FP8 codes: the entry scale goes into P
       pbuf[(32 * hp + acc_row(v, lane)) * PROW + ep * 32 + (lane & 31)] = f32_to_bf16(FP8 ? p * esc : p);
+    }
+    // rescaling the accumulators is skipped when no row maximum moved
+    if (__ballot(moved)) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) oacc[nb][v] *= mx[v];
     }
     __syncthreads();
 
@@ -269,14 +327,10 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     for (int ks = 0; ks < TILE / 16; ++ks) pa[ks] = *reinterpret_cast<const bf16x8*>(prow + ks * 16);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-      const bf16_t* vcol = ktile + (lane >> 5) * 8 * KROW + ep * 256 + nb * 32 + (lane & 31);
 #pragma unroll
-      for (int ks = 0; ks < TILE / 16; ++ks) {
-        bf16x8 vb;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) vb[i] = __builtin_bit_cast(__bf16, vcol[(ks * 16 + i) * KROW]);
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], vb, oacc[nb], 0, 0, 0);
-      }
+      for (int ks = 0; ks < TILE / 16; ++ks)
+        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], v_operand(ktile, ks * 16, ep * 256 + nb * 32, lane),
+                                                          oacc[nb], 0, 0, 0);
     }
   }
 
@@ -363,14 +417,19 @@ int decode_splits(int B, int64_t ntiles) {
   int64_t s = (256 + B - 1) / B;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
   if (s > ntiles) s = ntiles;
+  const int64_t min_s = (ntiles * TILE + MAX_LIST - 1) / MAX_LIST;  // list range fits LDS
+  if (s < min_s) s = min_s;
   return s < 1 ? 1 : static_cast<int>(s);
 }
 
 }  // namespace
 
 bool mfma_attn_supported(const AttnParams& P) {
-  return P.H == NH && P.d_nope == DN && P.d_rope == DRP && P.q_dt == CSA_BF16 && P.o_dt == CSA_BF16 &&
-         (P.nope_dt == CSA_BF16 || P.nope_dt == CSA_FP8E4M3) && P.rope_dt == CSA_BF16;
+  const bool shape = P.H == NH && P.d_nope == DN && P.d_rope == DRP && P.q_dt == CSA_BF16 && P.o_dt == CSA_BF16 &&
+                     (P.nope_dt == CSA_BF16 || P.nope_dt == CSA_FP8E4M3) && P.rope_dt == CSA_BF16;
+  // sparse prefill keeps one query's whole list in LDS
+  const bool list_fits = P.idx == nullptr || P.pos_dev != nullptr || P.k <= MAX_LIST;
+  return shape && list_fits;
 }
 
 size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, int) {
