@@ -5,22 +5,24 @@
 // shared across heads); §1.4 存储格式混 (FP8 non-RoPE dims, BF16 RoPE dims).
 //
 // One workgroup (4 waves) owns one query (all 64 heads) and a range of its
-// entry list.  Entries are gathered 64 at a time into an LDS tile (rows
-// padded to 1168 B so the 32 rows one MFMA operand touches fall on distinct
-// bank groups); FP8 codes are widened to BF16 exactly on the way in and the
-// per-entry scale is applied to the non-RoPE part of the logit.  Wave w owns
-// heads 32*(w/2).. and, for the logits, entries 32*(w%2).. of the tile; for
-// P.V it owns value dims 256*(w%2)...  The next tile's rows are loaded into
-// registers while the current one is multiplied.
+// entry list.  The query's 64 heads sit in LDS (RoPE applied once); entries
+// are gathered 64 at a time into an LDS tile (rows padded to 1168 B so the
+// 32 rows an MFMA operand touches fall on distinct bank groups), the next
+// tile's rows riding in registers while the current one is multiplied.  FP8
+// codes widen to BF16 exactly on the way in; the per-entry scale multiplies
+// the non-RoPE part of the logit and is folded into P for the values.
 //
-//   S = Q K^T        v_mfma_f32_32x32x16_bf16, Q held in registers (A),
-//                    K rows from LDS (B); non-RoPE and RoPE parts kept apart
-//                    so the FP8 scale applies to the first only
-//   online softmax   row max exchanged between the two waves of a head half
-//                    through LDS, exp2 with log2(e) folded into the scale
-//   O += P V         P (BF16) through LDS as the A operand, V read from the
-//                    same K tile as the B operand (entries along k)
+// Wave w owns heads 32*(w/2).. and, for the logits, entries 32*(w%2).. of a
+// tile; for P.V it owns value dims 256*(w%2)...  Both products run
+// transposed so that one lane holds one head:
 //
+//   S^T = K Q^T      v_mfma_f32_32x32x16_bf16, A = entry rows, B = head rows
+//   softmax          per lane: max / sum over its 16 entries, one cross-lane
+//                    step, one LDS exchange with the partner wave
+//   O^T += V^T P^T   A = V read column-wise from the K tile with
+//                    ds_read_b64_tr_b16, B = P^T rows through LDS
+//
+// LDS operand reads are software-pipelined one group of MFMAs ahead.
 // Decode splits the entry list over several workgroups per sequence; each
 // writes an unnormalised partial (O, max, sum) and attn_merge_kernel
 // combines them by log-sum-exp.
@@ -64,14 +66,30 @@ __device__ __forceinline__ uint32_t e4m3_to_bf16_bits(uint32_t c) {
   return __float_as_uint(e4m3_to_f32(c)) >> 16;
 }
 
-// S = Q K^T over k-steps I: A operand (heads) and B operand (entries) both
-// read from LDS rows (16 B per lane; padded rows keep them conflict-free).
-template <int... I>
-__device__ __forceinline__ void s_mfma(std::integer_sequence<int, I...>, const bf16_t* qrowp, const bf16_t* krow,
-                                       f32x16& acc) {
-  ((acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(*reinterpret_cast<const bf16x8*>(qrowp + I * 16),
-                                                  *reinterpret_cast<const bf16x8*>(krow + I * 16), acc, 0, 0, 0)),
-   ...);
+__device__ __forceinline__ bf16x8 lds_b128(const bf16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// acc += A B over NSTEP k-steps of 16, A and B rows read from LDS (16 B per
+// lane per step, step s at +16s); loads of the next group of 4 steps are
+// issued before the MFMAs of the current group.
+template <int NSTEP>
+__device__ __forceinline__ void mm_lds(const bf16_t* a, const bf16_t* b, f32x16& acc) {
+  static_assert(NSTEP % 4 == 0, "groups of 4 k-steps");
+  bf16x8 ra[2][4], rb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { ra[0][i] = lds_b128(a + 16 * i); rb[0][i] = lds_b128(b + 16 * i); }
+#pragma unroll
+  for (int g = 0; g < NSTEP / 4; ++g) {
+    const int cur = g & 1;
+    if (g + 1 < NSTEP / 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ra[cur ^ 1][i] = lds_b128(a + 16 * (4 * (g + 1) + i));
+        rb[cur ^ 1][i] = lds_b128(b + 16 * (4 * (g + 1) + i));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[cur][i], rb[cur][i], acc, 0, 0, 0);
+  }
 }
 
 // Stages the query's 64 heads in LDS (row = head), the last 64 dims turned
@@ -196,25 +214,26 @@ __device__ __forceinline__ void store_tile(const Prefetch& pf, bf16_t* ktile, fl
   if (tid < TILE) s_scale[tid] = pf.scale;
 }
 
-// Row (head within the wave's 32) held in register v of a 32x32 MFMA result.
+// Entry (row of S^T within the wave's 32) held in register v of a 32x32
+// MFMA result; the lane's column is its head.
 __device__ __forceinline__ int acc_row(int v, int lane) { return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); }
 
 typedef short v4s __attribute__((ext_vector_type(4)));
 
-// B operand of O += P V for value dims [dv0, dv0 + 32) and entries
-// [k0, k0 + 16) from the row-major tile, via two transposing LDS reads:
-// within a 16-lane group, result lane i slot s is element i%4 of the 8 bytes
-// addressed by lane 4s + i/4; lane L = 16G + 4s + q therefore points at
-// entry k0 + 8(G/2) + s (+4 for the second read), dims dv0 + 16(G%2) + 4q.
+// V^T operand (A of O^T += V^T P^T) for value dims [dv0, dv0 + 32) and
+// entries [k0, k0 + 16) from the row-major tile, via two transposing LDS
+// reads: within a 16-lane group, result lane i slot s is element i%4 of the
+// 8 bytes addressed by lane 4s + i/4; lane L = 16G + 4s + q therefore points
+// at entry k0 + 8(G/2) + s (+4 for the second read), dims dv0 + 16(G%2) + 4q,
+// which gives lane l the dims dv0 + l%32 of entries k0 + 8(l/32) .. +8.
 __device__ __forceinline__ bf16x8 v_operand(const bf16_t* ktile, int k0, int dv0, int lane) {
   const int G = lane >> 4, s = (lane >> 2) & 3, q = lane & 3;
   const bf16_t* p = ktile + (k0 + 8 * (G >> 1) + s) * KROW + dv0 + 16 * (G & 1) + 4 * q;
   typedef __attribute__((address_space(3))) v4s lds_v4s;
   const v4s a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p));
   const v4s b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * KROW));
-  const v4s lo = a, hi = b;
   typedef short v8s __attribute__((ext_vector_type(8)));
-  const v8s all = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  const v8s all = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   return __builtin_bit_cast(bf16x8, all);
 }
 
@@ -244,6 +263,7 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   if (r1 > count) r1 = count;
   const size_t qrow = (static_cast<size_t>(b) * P.T + t) * NH;
   const size_t seq = static_cast<size_t>(b) * P.cap;
+  const int head = 32 * hp + (lane & 31);  // this lane's head
 
   // the list range of this workgroup, validated once (-1: skip)
   if (!DENSE) {
@@ -253,131 +273,124 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       s_list[r] = (s >= 0 && s < n) ? static_cast<int>(s) : -1;
     }
   }
-
   stage_query(qtile, static_cast<const bf16_t*>(P.q) + qrow * CW, pos, th);
-  const bf16_t* qrowp = qtile + (32 * hp + (lane & 31)) * KROW + (lane >> 5) * 8;
+  const bf16_t* qop = qtile + head * KROW + (lane >> 5) * 8;                       // B of S^T
+  const bf16_t* kop = ktile + (ep * 32 + (lane & 31)) * KROW + (lane >> 5) * 8;    // A of S^T
+  const bf16_t* pop = pbuf + head * PROW + (lane >> 5) * 8;                        // B of O^T
 
   const float lscale = P.scale_qk * LOG2E;
   f32x16 oacc[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x16{};
-  float m_run[16], l_part[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) { m_run[v] = -INFINITY; l_part[v] = 0.0f; }
+  float m_run = -INFINITY, l_part = 0.0f;
 
   __syncthreads();  // s_list and the query tile ready
   const int64_t ntiles = r1 > r0 ? (r1 - r0 + TILE - 1) / TILE : 0;
   Prefetch pf;
   if (ntiles > 0) load_tile<FP8, DENSE>(pf, P, s_list, 0, r0, r1, n, seq);
   for (int64_t j = 0; j < ntiles; ++j) {
-    __syncthreads();  // previous tile's P.V finished with ktile / pbuf
+    __syncthreads();  // previous tile's O^T finished with ktile / pbuf
     store_tile<FP8>(pf, ktile, s_scale);
     __syncthreads();
     if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, P, s_list, (j + 1) * TILE, r0, r1, n, seq);
 
-    // --- S = Q K^T for heads 32hp.., entries 32ep.. ------------------------
+    // --- S^T = K Q^T: entries 32ep.. x heads 32hp.. --------------------------
     f32x16 sn = f32x16{}, sr = f32x16{};
-    const bf16_t* krow = ktile + (ep * 32 + (lane & 31)) * KROW + (lane >> 5) * 8;
-    s_mfma(std::make_integer_sequence<int, DN / 16>{}, qrowp, krow, sn);
-    s_mfma(std::make_integer_sequence<int, DRP / 16>{}, qrowp + DN, krow + DN, sr);
-
-    const float esc = s_scale[ep * 32 + (lane & 31)];
-    const bool valid = esc != 0.0f;
-    float lg[16], mx[16];
+    if (FP8) {
+      mm_lds<DN / 16>(kop, qop, sn);
+      mm_lds<DRP / 16>(kop + DN, qop + DN, sr);
+    } else {
+      mm_lds<CW / 16>(kop, qop, sn);
+    }
+    float lg[16], esc[16];
+    float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      lg[v] = valid ? (sn[v] * esc + sr[v]) * lscale : -INFINITY;
-      float x = lg[v];
-#pragma unroll
-      for (int o = 1; o < 32; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-      mx[v] = x;
+      esc[v] = s_scale[ep * 32 + acc_row(v, lane)];
+      lg[v] = esc[v] != 0.0f ? (FP8 ? sn[v] * esc[v] + sr[v] : sn[v]) * lscale : -INFINITY;
+      mx = fmaxf(mx, lg[v]);
     }
-    if ((lane & 31) == 0) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) s_xchg[ep][32 * hp + acc_row(v, lane)] = mx[v];
-    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other 16 entries of this head
+    if (lane < 32) s_xchg[ep][head] = mx;
     __syncthreads();
-    bool moved = false;
+    const float mnew = fmaxf(m_run, fmaxf(mx, s_xchg[ep ^ 1][head]));
+    const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run - mnew);
+    m_run = mnew;
+    float psum = 0.0f;
+    uint32_t pk[8];
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      const float other = s_xchg[ep ^ 1][32 * hp + acc_row(v, lane)];
-      const float mnew = fmaxf(m_run[v], fmaxf(mx[v], other));
-      const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run[v] - mnew);
-      moved |= alpha != 1.0f;
-      const float p = valid ? exp2f(lg[v] - mnew) : 0.0f;
-      l_part[v] = l_part[v] * alpha + p;
-      m_run[v] = mnew;
-      mx[v] = alpha;
+      const float p = esc[v] != 0.0f ? exp2f(lg[v] - mnew) : 0.0f;
+      psum += p;
       // V rows in the tile are unscaled FP8 codes: the entry scale goes into P
-      pbuf[(32 * hp + acc_row(v, lane)) * PROW + ep * 32 + (lane & 31)] = f32_to_bf16(FP8 ? p * esc : p);
+      const uint32_t h16 = f32_to_bf16(FP8 ? p * esc[v] : p);
+      pk[v >> 1] = (v & 1) ? (pk[v >> 1] | (h16 << 16)) : h16;
+    }
+    l_part = l_part * alpha + psum;
+    // P^T rows: 4 consecutive entries per register quad -> one 8-byte store each
+#pragma unroll
+    for (int jq = 0; jq < 4; ++jq) {
+      const uint2 val = make_uint2(pk[2 * jq], pk[2 * jq + 1]);
+      *reinterpret_cast<uint2*>(pbuf + head * PROW + ep * 32 + jq * 8 + (lane >> 5) * 4) = val;
     }
     // rescaling the accumulators is skipped when no row maximum moved
-    if (__ballot(moved)) {
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v)
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) oacc[nb][v] *= mx[v];
+      for (int nb = 0; nb < 8; ++nb) oacc[nb] *= alpha;
     }
     __syncthreads();
 
-    // --- O += P V for heads 32hp.., value dims 256ep.. -----------------------
-    bf16x8 pa[TILE / 16];
-    const bf16_t* prow = pbuf + (32 * hp + (lane & 31)) * PROW + (lane >> 5) * 8;
+    // --- O^T += V^T P^T: value dims 256ep.. x heads 32hp.. --------------------
+    bf16x8 pb[TILE / 16];
 #pragma unroll
-    for (int ks = 0; ks < TILE / 16; ++ks) pa[ks] = *reinterpret_cast<const bf16x8*>(prow + ks * 16);
+    for (int ks = 0; ks < TILE / 16; ++ks) pb[ks] = lds_b128(pop + ks * 16);
+    bf16x8 va[3];
+    va[0] = v_operand(ktile, 0, ep * 256, lane);
+    va[1] = v_operand(ktile, 16, ep * 256, lane);
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-#pragma unroll
-      for (int ks = 0; ks < TILE / 16; ++ks)
-        oacc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pa[ks], v_operand(ktile, ks * 16, ep * 256 + nb * 32, lane),
-                                                          oacc[nb], 0, 0, 0);
+    for (int i = 0; i < 8 * (TILE / 16); ++i) {
+      if (i + 2 < 8 * (TILE / 16))
+        va[(i + 2) % 3] = v_operand(ktile, ((i + 2) % 4) * 16, ep * 256 + ((i + 2) / 4) * 32, lane);
+      oacc[i / 4] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], pb[i % 4], oacc[i / 4], 0, 0, 0);
     }
   }
 
-  // --- finish: row sums over the 64 entries of each tile ------------------
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    float x = l_part[v];
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) x += __shfl_xor(x, o);
-    l_part[v] = x;
-  }
+  // --- finish: softmax denominators -------------------------------------
+  l_part += __shfl_xor(l_part, 32);
   __syncthreads();
-  if ((lane & 31) == 0) {
-#pragma unroll
-    for (int v = 0; v < 16; ++v) s_xchg[ep][32 * hp + acc_row(v, lane)] = l_part[v];
-  }
+  if (lane < 32) s_xchg[ep][head] = l_part;
   __syncthreads();
-  float ltot[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) ltot[v] = l_part[v] + s_xchg[ep ^ 1][32 * hp + acc_row(v, lane)];
+  const float ltot = l_part + s_xchg[ep ^ 1][head];
 
+  // O^T layout: lane = head, register (nb, v) = value dim ep*256 + nb*32 + acc_row(v)
   if (!SPLIT) {
-    bf16_t* out = static_cast<bf16_t*>(P.o) + qrow * DN;
+    const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+    bf16_t* out = static_cast<bf16_t*>(P.o) + (qrow + head) * DN + ep * 256;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int h = 32 * hp + acc_row(v, lane);
-      const float inv = ltot[v] > 0.0f ? 1.0f / ltot[v] : 0.0f;
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb)
-        out[static_cast<size_t>(h) * DN + ep * 256 + nb * 32 + (lane & 31)] = f32_to_bf16(oacc[nb][v] * inv);
-      if (P.lse && ep == 0 && (lane & 31) == 0)
-        P.lse[qrow + h] = ltot[v] > 0.0f ? (m_run[v] + log2f(ltot[v])) * LN2 : -INFINITY;
-    }
+      for (int jq = 0; jq < 4; ++jq) {
+        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq + 1] * inv)) << 16);
+        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq + 2] * inv)) |
+                            (static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq + 3] * inv)) << 16);
+        *reinterpret_cast<uint2*>(out + nb * 32 + jq * 8 + (lane >> 5) * 4) = make_uint2(lo, hi);
+      }
+    if (P.lse && ep == 0 && lane < 32) P.lse[qrow + head] = ltot > 0.0f ? (m_run + log2f(ltot)) * LN2 : -INFINITY;
   } else {
     // partial: [B][splits][NH][DN] O, then [B][splits][NH][2] (max, sum)
     const size_t slot = static_cast<size_t>(b) * splits + split;
-    float* po = part + slot * (NH * DN);
+    float* po = part + slot * (NH * DN) + head * DN + ep * 256;
     float* pml = part + static_cast<size_t>(gridDim.z) * splits * (NH * DN) + slot * (2 * NH);
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int h = 32 * hp + acc_row(v, lane);
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) po[h * DN + ep * 256 + nb * 32 + (lane & 31)] = oacc[nb][v];
-      if (ep == 0 && (lane & 31) == 0) {
-        pml[2 * h] = m_run[v];
-        pml[2 * h + 1] = ltot[v];
-      }
+      for (int jq = 0; jq < 4; ++jq)
+        *reinterpret_cast<float4*>(po + nb * 32 + jq * 8 + (lane >> 5) * 4) =
+            make_float4(oacc[nb][4 * jq], oacc[nb][4 * jq + 1], oacc[nb][4 * jq + 2], oacc[nb][4 * jq + 3]);
+    if (ep == 0 && lane < 32) {
+      pml[2 * head] = m_run;
+      pml[2 * head + 1] = ltot;
     }
   }
 }
@@ -417,8 +430,6 @@ int decode_splits(int B, int64_t ntiles) {
   int64_t s = (256 + B - 1) / B;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
   if (s > ntiles) s = ntiles;
-  const int64_t min_s = (ntiles * TILE + MAX_LIST - 1) / MAX_LIST;  // list range fits LDS
-  if (s < min_s) s = min_s;
   return s < 1 ? 1 : static_cast<int>(s);
 }
 
@@ -457,7 +468,11 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   }
   const int64_t count = dense ? P.cap : P.k;
   const int64_t ntiles = (count + TILE - 1) / TILE;
-  const int splits = decode_splits(B, ntiles);
+  int splits = decode_splits(B, ntiles);
+  if (!dense) {  // each workgroup's list range must fit its LDS copy
+    const int min_s = static_cast<int>((ntiles * TILE + MAX_LIST - 1) / MAX_LIST);
+    if (splits < min_s) splits = min_s;
+  }
   const int64_t tiles_per = (ntiles + splits - 1) / splits;
   const int64_t per = tiles_per * TILE;
   const size_t need = static_cast<size_t>(B) * splits * (NH * DN + 2 * NH) * sizeof(float);
