@@ -37,6 +37,9 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NH = 64;       // heads
 constexpr int DN = 512;      // value / non-RoPE dims
@@ -53,10 +56,22 @@ struct Theta {
   double t[DRP / 2];  // base^(-2p/d_rope)
 };
 
-struct Prefetch {
-  u32x4 nope[16];  // BF16: 16 chunks of 8 dims; FP8: 8 chunks of 16 codes
+// Registers of one prefetched tile: wave w holds entries w*16 .. w*16+15, one
+// entry per load (lane l: dims 8l .. 8l+7, 16 B of BF16 or 8 B of FP8), plus
+// two 16-byte RoPE chunks per thread.
+template <bool FP8>
+struct Prefetch;
+template <>
+struct Prefetch<false> {
+  u32x4 nope[16];
   u32x4 rope[2];
-  float scale;     // thread tid < TILE: the scale of entry tid (0 if invalid)
+  float scale;
+};
+template <>
+struct Prefetch<true> {
+  u32x2 nope[16];
+  u32x4 rope[2];
+  float scale;  // thread tid < TILE: the FP8 scale of entry tid
 };
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -73,22 +88,23 @@ __device__ __forceinline__ bf16x8 lds_b128(const bf16_t* p) { return *reinterpre
 // issued before the MFMAs of the current group.
 template <int NSTEP>
 __device__ __forceinline__ void mm_lds(const bf16_t* a, const bf16_t* b, f32x16& acc) {
-  static_assert(NSTEP % 4 == 0, "groups of 4 k-steps");
-  bf16x8 ra[2][4], rb[2][4];
+  constexpr int GS = 2;  // k-steps per group
+  static_assert(NSTEP % GS == 0, "whole groups");
+  bf16x8 ra[2][GS], rb[2][GS];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) { ra[0][i] = lds_b128(a + 16 * i); rb[0][i] = lds_b128(b + 16 * i); }
+  for (int i = 0; i < GS; ++i) { ra[0][i] = lds_b128(a + 16 * i); rb[0][i] = lds_b128(b + 16 * i); }
 #pragma unroll
-  for (int g = 0; g < NSTEP / 4; ++g) {
+  for (int g = 0; g < NSTEP / GS; ++g) {
     const int cur = g & 1;
-    if (g + 1 < NSTEP / 4) {
+    if (g + 1 < NSTEP / GS) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[cur ^ 1][i] = lds_b128(a + 16 * (4 * (g + 1) + i));
-        rb[cur ^ 1][i] = lds_b128(b + 16 * (4 * (g + 1) + i));
+      for (int i = 0; i < GS; ++i) {
+        ra[cur ^ 1][i] = lds_b128(a + 16 * (GS * (g + 1) + i));
+        rb[cur ^ 1][i] = lds_b128(b + 16 * (GS * (g + 1) + i));
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[cur][i], rb[cur][i], acc, 0, 0, 0);
+    for (int i = 0; i < GS; ++i) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ra[cur][i], rb[cur][i], acc, 0, 0, 0);
   }
 }
 
@@ -116,102 +132,77 @@ __device__ __forceinline__ void stage_query(bf16_t* qtile, const bf16_t* q, int6
   }
 }
 
-// Entry ids of this workgroup's list range, staged in LDS (-1 = skip).
-template <bool DENSE>
-__device__ __forceinline__ int entry_id(const int* s_list, int64_t r_local, int64_t r0, int64_t r1, int64_t n) {
-  if (DENSE) {
-    const int64_t s = r0 + r_local;
-    return s < r1 ? static_cast<int>(s) : -1;
-  }
-  return r_local < r1 - r0 ? s_list[r_local] : -1;
+// Two fp32 -> packed BF16 pair (hardware RNE conversion).
+__device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
+  const bf16x2 h = __builtin_convertvector(f32x2{a, b}, bf16x2);
+  return __builtin_bit_cast(uint32_t, h);
 }
 
-// Issues the global loads of one 64-entry tile (invalid entries read row 0
-// and are zeroed, so nothing branches and no address leaves the cache).
+// 4 FP8 E4M3 codes -> 4 BF16 values (exact: 3 mantissa bits fit in 7).
+__device__ __forceinline__ u32x2 fp8x4_to_bf16x4(uint32_t w) {
+  const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(w, false);
+  const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(w, true);
+  return u32x2{pack2_bf16(lo[0], lo[1]), pack2_bf16(hi[0], hi[1])};
+}
+
+// Id of list slot r of this workgroup (its valid ids are compacted to the
+// front of s_list; slots past `nvalid` repeat slot 0, whose row is a real
+// entry, and are masked out of the softmax).
+template <bool DENSE>
+__device__ __forceinline__ int slot_id(const int* s_list, int64_t r, int64_t r0, int64_t nvalid) {
+  const int64_t rr = r < nvalid ? r : 0;
+  return DENSE ? static_cast<int>(r0 + rr) : s_list[rr];
+}
+
+// Issues the global loads of one 64-entry tile starting at slot rl.  Entry
+// ids of the nope rows are wave-uniform, so their addresses are scalar.
 template <bool FP8, bool DENSE>
-__device__ __forceinline__ void load_tile(Prefetch& pf, const AttnParams& P, const int* s_list, int64_t rl,
-                                          int64_t r0, int64_t r1, int64_t n, size_t seq) {
+__device__ __forceinline__ void load_tile(Prefetch<FP8>& pf, const AttnParams& P, const int* s_list, int64_t rl,
+                                          int64_t r0, int64_t nvalid, size_t seq) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const u32x4 zero = {0u, 0u, 0u, 0u};
-  int ids[16 + 2];
-  if (!FP8) {
 #pragma unroll
-    for (int it = 0; it < 16; ++it) ids[it] = entry_id<DENSE>(s_list, rl + w * 16 + it, r0, r1, n);
-  } else {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) ids[it] = entry_id<DENSE>(s_list, rl + w * 16 + it * 2 + (lane >> 5), r0, r1, n);
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) ids[16 + it] = entry_id<DENSE>(s_list, rl + (it * 256 + tid) / 8, r0, r1, n);
-  if (!FP8) {
-    const bf16_t* base = static_cast<const bf16_t*>(P.nope);
-#pragma unroll
-    for (int it = 0; it < 16; ++it) {
-      const int s = ids[it] < 0 ? 0 : ids[it];
-      pf.nope[it] = *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + lane * 8);
-    }
-  } else {
-    const uint8_t* base = static_cast<const uint8_t*>(P.nope);
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int s = ids[it] < 0 ? 0 : ids[it];
-      pf.nope[it] = *reinterpret_cast<const u32x4*>(base + (seq + s) * DN + (lane & 31) * 16);
+  for (int it = 0; it < 16; ++it) {
+    const int id = __builtin_amdgcn_readfirstlane(slot_id<DENSE>(s_list, rl + w * 16 + it, r0, nvalid));
+    if constexpr (!FP8) {
+      const bf16_t* row = static_cast<const bf16_t*>(P.nope) + (seq + id) * DN;
+      pf.nope[it] = *reinterpret_cast<const u32x4*>(row + lane * 8);
+    } else {
+      const uint8_t* row = static_cast<const uint8_t*>(P.nope) + (seq + id) * DN;
+      pf.nope[it] = *reinterpret_cast<const u32x2*>(row + lane * 8);
     }
   }
   const bf16_t* rbase = static_cast<const bf16_t*>(P.rope);
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
-    const int s = ids[16 + it] < 0 ? 0 : ids[16 + it];
-    pf.rope[it] = *reinterpret_cast<const u32x4*>(rbase + (seq + s) * DRP + ((it * 256 + tid) % 8) * 8);
+    const int q = it * 256 + tid;
+    const int id = slot_id<DENSE>(s_list, rl + q / 8, r0, nvalid);
+    pf.rope[it] = *reinterpret_cast<const u32x4*>(rbase + (seq + id) * DRP + (q % 8) * 8);
   }
-  if (tid < TILE) {
-    const int s = entry_id<DENSE>(s_list, rl + tid, r0, r1, n);
-    pf.scale = s < 0 ? 0.0f : (FP8 ? static_cast<const float*>(P.scale)[seq + s] : 1.0f);
+  if constexpr (FP8) {
+    if (tid < TILE) pf.scale = static_cast<const float*>(P.scale)[seq + slot_id<DENSE>(s_list, rl + tid, r0, nvalid)];
   }
-  // zero the rows of skipped entries (their memory may hold anything)
-  if (!FP8) {
-#pragma unroll
-    for (int it = 0; it < 16; ++it) pf.nope[it] = ids[it] < 0 ? zero : pf.nope[it];
-  } else {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) pf.nope[it] = ids[it] < 0 ? zero : pf.nope[it];
-  }
-#pragma unroll
-  for (int it = 0; it < 2; ++it) pf.rope[it] = ids[16 + it] < 0 ? zero : pf.rope[it];
 }
 
 template <bool FP8>
-__device__ __forceinline__ void store_tile(const Prefetch& pf, bf16_t* ktile, float* s_scale) {
+__device__ __forceinline__ void store_tile(const Prefetch<FP8>& pf, bf16_t* ktile, float* s_scale) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  if (!FP8) {
 #pragma unroll
-    for (int it = 0; it < 16; ++it)
-      *reinterpret_cast<u32x4*>(ktile + (w * 16 + it) * KROW + lane * 8) = pf.nope[it];
-  } else {
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int e = w * 16 + it * 2 + (lane >> 5);
-      u32x4 lo, hi;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t word = pf.nope[it][q];
-        const uint32_t b0 = e4m3_to_bf16_bits(word & 0xFFu), b1 = e4m3_to_bf16_bits((word >> 8) & 0xFFu);
-        const uint32_t b2 = e4m3_to_bf16_bits((word >> 16) & 0xFFu), b3 = e4m3_to_bf16_bits(word >> 24);
-        const uint32_t p0 = b0 | (b1 << 16), p1 = b2 | (b3 << 16);
-        if (q < 2) { lo[2 * q] = p0; lo[2 * q + 1] = p1; }
-        else { hi[2 * (q - 2)] = p0; hi[2 * (q - 2) + 1] = p1; }
-      }
-      bf16_t* dst = ktile + e * KROW + (lane & 31) * 16;
-      *reinterpret_cast<u32x4*>(dst) = lo;
-      *reinterpret_cast<u32x4*>(dst + 8) = hi;
+  for (int it = 0; it < 16; ++it) {
+    u32x4 v;
+    if constexpr (!FP8) {
+      v = pf.nope[it];
+    } else {
+      const u32x2 lo = fp8x4_to_bf16x4(pf.nope[it][0]), hi = fp8x4_to_bf16x4(pf.nope[it][1]);
+      v = u32x4{lo[0], lo[1], hi[0], hi[1]};
     }
+    *reinterpret_cast<u32x4*>(ktile + (w * 16 + it) * KROW + lane * 8) = v;
   }
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int q = it * 256 + tid;
     *reinterpret_cast<u32x4*>(ktile + (q / 8) * KROW + DN + (q % 8) * 8) = pf.rope[it];
   }
-  if (tid < TILE) s_scale[tid] = pf.scale;
+  if (FP8 && tid < TILE) s_scale[tid] = pf.scale;
 }
 
 // Entry (row of S^T within the wave's 32) held in register v of a 32x32
@@ -248,6 +239,7 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   __shared__ float s_scale[TILE];
   __shared__ float s_xchg[2][NH];
   __shared__ int s_list[DENSE ? 1 : MAX_LIST];
+  __shared__ int s_cnt[4];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int hp = w >> 1, ep = w & 1;
@@ -265,13 +257,28 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   const size_t seq = static_cast<size_t>(b) * P.cap;
   const int head = 32 * hp + (lane & 31);  // this lane's head
 
-  // the list range of this workgroup, validated once (-1: skip)
-  if (!DENSE) {
+  // the valid ids of this workgroup's list range, compacted into s_list
+  int64_t nvalid;
+  if (DENSE) {
+    nvalid = r1 > r0 ? r1 - r0 : 0;
+  } else {
     const int32_t* list = P.idx + (static_cast<size_t>(b) * P.T + t) * P.k;
-    for (int64_t r = tid; r < r1 - r0; r += 256) {
-      const int64_t s = list[r0 + r];
-      s_list[r] = (s >= 0 && s < n) ? static_cast<int>(s) : -1;
+    int base = 0;
+    for (int64_t c0 = 0; c0 < r1 - r0; c0 += 256) {
+      const int64_t r = c0 + tid;
+      int64_t sid = r < r1 - r0 ? static_cast<int64_t>(list[r0 + r]) : -1;
+      const bool ok = sid >= 0 && sid < n;
+      const unsigned long long bal = __ballot(ok);
+      if (lane == 0) s_cnt[w] = __popcll(bal);
+      __syncthreads();
+      int before = 0, tot = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { before += i < w ? s_cnt[i] : 0; tot += s_cnt[i]; }
+      if (ok) s_list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int>(sid);
+      base += tot;
+      __syncthreads();
     }
+    nvalid = base;
   }
   stage_query(qtile, static_cast<const bf16_t*>(P.q) + qrow * CW, pos, th);
   const bf16_t* qop = qtile + head * KROW + (lane >> 5) * 8;                       // B of S^T
@@ -282,17 +289,20 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   f32x16 oacc[8];
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) oacc[nb] = f32x16{};
+  // running max (log2 domain) and this lane's partial denominator; the max
+  // only moves when a tile's max exceeds it by more than 2^8, so P stays
+  // below 256 and the accumulators are rarely rescaled
   float m_run = -INFINITY, l_part = 0.0f;
 
   __syncthreads();  // s_list and the query tile ready
-  const int64_t ntiles = r1 > r0 ? (r1 - r0 + TILE - 1) / TILE : 0;
-  Prefetch pf;
-  if (ntiles > 0) load_tile<FP8, DENSE>(pf, P, s_list, 0, r0, r1, n, seq);
+  const int64_t ntiles = (nvalid + TILE - 1) / TILE;
+  Prefetch<FP8> pf;
+  if (ntiles > 0) load_tile<FP8, DENSE>(pf, P, s_list, 0, r0, nvalid, seq);
   for (int64_t j = 0; j < ntiles; ++j) {
     __syncthreads();  // previous tile's O^T finished with ktile / pbuf
     store_tile<FP8>(pf, ktile, s_scale);
     __syncthreads();
-    if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, P, s_list, (j + 1) * TILE, r0, r1, n, seq);
+    if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, P, s_list, (j + 1) * TILE, r0, nvalid, seq);
 
     // --- S^T = K Q^T: entries 32ep.. x heads 32hp.. --------------------------
     f32x16 sn = f32x16{}, sr = f32x16{};
@@ -302,42 +312,46 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     } else {
       mm_lds<CW / 16>(kop, qop, sn);
     }
+    const int64_t valid_end = nvalid - j * TILE;  // entries of this tile below it are real
     float lg[16], esc[16];
     float mx = -INFINITY;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      esc[v] = s_scale[ep * 32 + acc_row(v, lane)];
-      lg[v] = esc[v] != 0.0f ? (FP8 ? sn[v] * esc[v] + sr[v] : sn[v]) * lscale : -INFINITY;
+      const int e = ep * 32 + acc_row(v, lane);
+      esc[v] = FP8 ? s_scale[e] : 1.0f;
+      lg[v] = e < valid_end ? (FP8 ? sn[v] * esc[v] + sr[v] : sn[v]) * lscale : -INFINITY;
       mx = fmaxf(mx, lg[v]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other 16 entries of this head
     if (lane < 32) s_xchg[ep][head] = mx;
     __syncthreads();
-    const float mnew = fmaxf(m_run, fmaxf(mx, s_xchg[ep ^ 1][head]));
-    const float alpha = (mnew == -INFINITY) ? 1.0f : exp2f(m_run - mnew);
-    m_run = mnew;
+    mx = fmaxf(mx, s_xchg[ep ^ 1][head]);
+    const bool move = mx > m_run + 8.0f;
+    if (__ballot(move)) {
+      // accumulators are still zero while m_run is -inf: no rescale needed
+      const float alpha = move ? (m_run == -INFINITY ? 0.0f : exp2f(m_run - mx)) : 1.0f;
+      if (__ballot(move && m_run != -INFINITY)) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) oacc[nb] *= alpha;
+      }
+      l_part *= alpha;
+      m_run = move ? mx : m_run;
+    }
     float psum = 0.0f;
     uint32_t pk[8];
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const float p = esc[v] != 0.0f ? exp2f(lg[v] - mnew) : 0.0f;
-      psum += p;
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = exp2f(lg[v] - m_run), p1 = exp2f(lg[v + 1] - m_run);
+      psum += p0 + p1;
       // V rows in the tile are unscaled FP8 codes: the entry scale goes into P
-      const uint32_t h16 = f32_to_bf16(FP8 ? p * esc[v] : p);
-      pk[v >> 1] = (v & 1) ? (pk[v >> 1] | (h16 << 16)) : h16;
+      pk[v >> 1] = FP8 ? pack2_bf16(p0 * esc[v], p1 * esc[v + 1]) : pack2_bf16(p0, p1);
     }
-    l_part = l_part * alpha + psum;
+    l_part += psum;
     // P^T rows: 4 consecutive entries per register quad -> one 8-byte store each
 #pragma unroll
-    for (int jq = 0; jq < 4; ++jq) {
-      const uint2 val = make_uint2(pk[2 * jq], pk[2 * jq + 1]);
-      *reinterpret_cast<uint2*>(pbuf + head * PROW + ep * 32 + jq * 8 + (lane >> 5) * 4) = val;
-    }
-    // rescaling the accumulators is skipped when no row maximum moved
-    if (__ballot(alpha != 1.0f)) {
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) oacc[nb] *= alpha;
-    }
+    for (int jq = 0; jq < 4; ++jq)
+      *reinterpret_cast<uint2*>(pbuf + head * PROW + ep * 32 + jq * 8 + (lane >> 5) * 4) =
+          make_uint2(pk[2 * jq], pk[2 * jq + 1]);
     __syncthreads();
 
     // --- O^T += V^T P^T: value dims 256ep.. x heads 32hp.. --------------------
@@ -370,10 +384,8 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
       for (int jq = 0; jq < 4; ++jq) {
-        const uint32_t lo = static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq] * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq + 1] * inv)) << 16);
-        const uint32_t hi = static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq + 2] * inv)) |
-                            (static_cast<uint32_t>(f32_to_bf16(oacc[nb][4 * jq + 3] * inv)) << 16);
+        const uint32_t lo = pack2_bf16(oacc[nb][4 * jq] * inv, oacc[nb][4 * jq + 1] * inv);
+        const uint32_t hi = pack2_bf16(oacc[nb][4 * jq + 2] * inv, oacc[nb][4 * jq + 3] * inv);
         *reinterpret_cast<uint2*>(out + nb * 32 + jq * 8 + (lane >> 5) * 4) = make_uint2(lo, hi);
       }
     if (P.lse && ep == 0 && lane < 32) P.lse[qrow + head] = ltot > 0.0f ? (m_run + log2f(ltot)) * LN2 : -INFINITY;
