@@ -28,7 +28,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from compressed_sparse_amd import binding as cb  # noqa: E402
-from compressed_sparse_amd import synth  # noqa: E402
+from compressed_sparse_amd import path, synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
@@ -36,41 +36,6 @@ PEAK_HBM_GBS = 8000.0
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
-
-
-def setup_csa_prefill(w):
-    dev = "cuda"
-    T, m = w.tokens, w.m
-    N = T // m
-    tok = synth.token_chunk(w, 0, 0, T, device=dev)
-    qs = synth.query_chunk(w, 0, 0, T, device=dev)
-    prm = synth.compressor_params(w, device=dev)
-    u = lambda t: t[None].contiguous()
-    st = dict(T=T, N=N, tok={k: u(v) for k, v in tok.items()}, q=u(qs["q"]), qI=u(qs["qI"]), w=u(qs["w"]),
-              prm=prm)
-    st["kv"] = cb.KVCache(cb.cache_desc(m, True, w.d_nope, w.d_rope, "bf16", "bf16", "bf16", N), 1)
-    st["keys"] = cb.KVCache(cb.cache_desc(m, True, w.idx_dim, 0, "bf16", "bf16", "f32", N), 1)
-    st["idesc"] = cb.index_desc(w.idx_heads, w.idx_dim, "bf16", "bf16", "bf16", "f32", m, N)
-    st["adesc"] = cb.attn_desc(w.heads, w.d_nope, w.d_rope, "bf16", "bf16", "bf16", "bf16", m, N)
-    st["idx"] = torch.empty((1, T, w.topk), dtype=torch.int32, device=dev)
-    st["o"] = torch.empty((1, T, w.heads, w.d_nope), dtype=torch.bfloat16, device=dev)
-    st["lse"] = torch.empty((1, T, w.heads), dtype=torch.float32, device=dev)
-    st["iws"] = cb.workspace(cb.workspace_bytes(cb.OP_INDEX_TOPK_PREFILL, st["idesc"], 1, T, 0, w.topk))
-    st["aws"] = cb.workspace(cb.workspace_bytes(cb.OP_SPARSE_ATTN_PREFILL, st["adesc"], 1, T, 0, w.topk))
-    return st
-
-
-def csa_prefill_step(w, st, ev=None):
-    t = st["tok"]
-    p = st["prm"]
-    cb.compress_prefill(st["kv"], 0, t["a"], t["za"], p["Ba"], t["b"], t["zb"], p["Bb"])
-    cb.compress_prefill(st["keys"], 0, t["ka"], t["kza"], p["kBa"], t["kb"], t["kzb"], p["kBb"])
-    cb.index_topk_prefill(st["idesc"], st["keys"], 0, st["qI"], st["w"], w.topk, st["idx"], ws=st["iws"])
-    if ev is not None:
-        ev[0].record()
-    cb.sparse_attn_prefill(st["adesc"], st["kv"], 0, st["q"], st["idx"], w.tau, st["o"], st["lse"], ws=st["aws"])
-    if ev is not None:
-        ev[1].record()
 
 
 def attention_pairs(w):
@@ -86,8 +51,8 @@ def cpu_baseline(w, st, budget_s=15.0):
     from oracle import csa
     import threadpoolctl
     cpu = lambda x: x[0].to("cpu", torch.float64).numpy()
-    t = {k: cpu(v) for k, v in st["tok"].items()}
-    p = {k: v.to("cpu", torch.float64).numpy() for k, v in st["prm"].items()}
+    t = {k: cpu(v) for k, v in st.tok.items()}
+    p = {k: v.to("cpu", torch.float64).numpy() for k, v in st.prm.items()}
     t0 = time.perf_counter()
     ent = csa.compress(t["a"], t["za"], p["Ba"], w.m, t["b"], t["zb"], p["Bb"])
     cache = csa.finalize_kv(ent, 0, w.m, w.d_nope, w.rope_base, "bf16", "bf16")
@@ -98,9 +63,9 @@ def cpu_baseline(w, st, budget_s=15.0):
     chunk = 64
     while t_rows < budget_s and rows_done < w.tokens:
         rows = np.sort(order[rows_done:rows_done + chunk])
-        q = st["q"][0, rows].to("cpu", torch.float64).numpy()
-        qI = st["qI"][0, rows].to("cpu", torch.float64).numpy()
-        wt = st["w"][0, rows].to("cpu", torch.float64).numpy()
+        q = st.q[0, rows].to("cpu", torch.float64).numpy()
+        qI = st.qI[0, rows].to("cpu", torch.float64).numpy()
+        wt = st.wt[0, rows].to("cpu", torch.float64).numpy()
         t1 = time.perf_counter()
         csa.csa_rows(rows, rows, q, qI, wt, cache, keys, w.m, w.topk, w.d_nope, w.rope_base, w.tau)
         t_rows += time.perf_counter() - t1
@@ -129,10 +94,10 @@ def main():
         sys.exit(1)
     w = synth.CSA_PREFILL_BF16_32K
     log(f"setup {w.name}")
-    st = setup_csa_prefill(w)
+    st = path.CsaPrefill(w)
     torch.cuda.synchronize()
     for i in range(args.warmup):
-        csa_prefill_step(w, st)
+        st.step()
     torch.cuda.synchronize()
     log("warmup done")
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
@@ -140,7 +105,7 @@ def main():
     torch.cuda.synchronize()
     start.record()
     for i in range(args.steps):
-        csa_prefill_step(w, st, evs[i])
+        st.step(evs[i])
     end.record()
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps

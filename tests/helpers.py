@@ -112,3 +112,20 @@ def compressor_error_bound(x, m, overlap, d_nope):
         r = bound[:, d_nope:].reshape(N, -1, 2).max(-1)
         bound[:, d_nope:] = np.repeat(r, 2, axis=1)
     return bound
+
+
+def topk_explained(gpu_row, ref_row, I, delta, eps):
+    """True when the GPU's top-k set equals the oracle's, or every index in
+    the symmetric difference has an oracle score within delta[s] +
+    max(delta) near the threshold + eps of the oracle's k-th score: a swap
+    that the bounded differences between the two sides' inputs can cause."""
+    g = set(int(x) for x in gpu_row if x >= 0)
+    o = set(int(x) for x in ref_row if x >= 0)
+    if g == o:
+        return True
+    if len(g) != len(o):
+        return False
+    kth = np.min(I[sorted(o)])
+    near = np.abs(I - kth) <= 2 * float(delta.max()) + eps
+    d_thr = float(delta[near].max()) if near.any() else 0.0
+    return all(s < len(I) and abs(I[s] - kth) <= delta[s] + d_thr + eps for s in g ^ o)
