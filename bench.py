@@ -14,8 +14,15 @@ stream it runs on; its algorithmic flop count (2 * pairs * heads * (576 +
 gives the roofline fraction against the 2.5 PFLOP/s dense BF16 MFMA peak.
 The CPU baseline times the fp64 oracle on a bounded row sample of the same
 workload.
+
+The decode workloads (CSA decode at batch 32 / 131072 context, HCA decode at
+batch 16 / 2^20 context, the CSA + HCA pair at batch 4 / 2^20 context) are
+reported under "secondary": consecutive decode steps captured in one HIP
+graph, timed over replays, with their algorithmic HBM bytes per step against
+the 8 TB/s HBM peak.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -36,6 +43,32 @@ PEAK_HBM_GBS = 8000.0
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_csa_prefill_L32768_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "compressed_sparse_amd", "csrc", "attention_mfma.hip")
+
+
+def measured_traffic():
+    """HBM bytes per attention launch from the committed rocprofv3 counter
+    summary, or None when the kernel source has changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = dict(line.split(":", 1) for line in open(TRAFFIC_FILE).read().splitlines() if ":" in line)
+    src = hashlib.sha256(open(ATTN_SRC, "rb").read()).hexdigest()
+    if kv.get("source_sha256", "").strip() != src:
+        return None
+    return float(kv["fetch_bytes_per_launch"]) + float(kv["write_bytes_per_launch"])
+
+
+def copy_calibration():
+    """A plain device copy of 1 GiB (read 1 GiB, write 1 GiB) whose FETCH_SIZE
+    / WRITE_SIZE readings calibrate the counters."""
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def attention_pairs(w):
@@ -77,6 +110,112 @@ def cpu_baseline(w, st, budget_s=15.0):
                       f"of indexer/top-k/attention ({t_rows:.1f} s), extrapolated linearly to {w.tokens} rows"}
 
 
+def decode_bytes_csa(w, n, B):
+    """Algorithmic HBM bytes of one CSA decode step: every visible indexer key
+    once, the k selected split entries, q / qI / w in, o / lse out, the
+    index list written and read, one token into each compressor."""
+    key_b = {"fp8": w.idx_dim + 4, "mxfp4": w.idx_dim // 2 + w.idx_dim // 32, "bf16": 2 * w.idx_dim}[w.key_fmt]
+    ent_b = w.d_nope * (1 if w.nope_fmt == "fp8" else 2) + (4 if w.nope_fmt == "fp8" else 0) + 2 * w.d_rope
+    tok_b = 2 * (4 * w.c + 4 * w.idx_dim)
+    return B * (n * key_b + w.topk * ent_b + 2 * w.heads * w.c + 2 * w.idx_heads * w.idx_dim + 4 * w.idx_heads
+                + 2 * w.heads * w.d_nope + 4 * w.heads + 8 * w.topk + tok_b)
+
+
+def decode_bytes_hca(w, n, B):
+    ent_b = w.d_nope * (1 if w.nope_fmt == "fp8" else 2) + (4 if w.nope_fmt == "fp8" else 0) + 2 * w.d_rope
+    return B * (n * ent_b + 2 * w.heads * w.c + 2 * w.heads * w.d_nope + 4 * w.heads + 2 * 2 * w.c)
+
+
+def time_graph(step_fn, n_steps, replays=20, warmup=3):
+    """Captures n_steps consecutive decode steps in one HIP graph; returns
+    the average ms per step over `replays` replays."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(n_steps):  # eager run also fills caches for the positions
+            step_fn(i)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(n_steps):
+            step_fn(i)
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (replays * n_steps)
+
+
+def secondary_decode(n_steps=8):
+    out = []
+    w = synth.CSA_DECODE_B32_128K
+    log(f"setup {w.name}")
+    lay = path.CsaLayer(w, w.batch, w.tokens // w.m + n_steps)
+    lay.prefill_context(w.tokens)
+    o = lay.alloc_decode_outputs()
+    xs = [lay.decode_inputs([w.tokens + i] * w.batch) for i in range(n_steps)]
+    ms = time_graph(lambda i: lay.decode_step(xs[i], o), n_steps)
+    by = decode_bytes_csa(w, w.tokens // w.m, w.batch)
+    out.append({"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
+                "tokens_per_s": w.batch / (ms * 1e-3),
+                "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "algorithmic_bytes_per_step": by}})
+    del lay, o, xs
+    torch.cuda.empty_cache()
+
+    w = synth.HCA_DECODE_B16_1M
+    log(f"setup {w.name}")
+    lay = path.HcaLayer(w, w.batch, w.tokens // w.m + n_steps)
+    lay.prefill_context(w.tokens)
+    o = lay.alloc_decode_outputs()
+    xs = [lay.decode_inputs([w.tokens + i] * w.batch) for i in range(n_steps)]
+    ms = time_graph(lambda i: lay.decode_step(xs[i], o), n_steps)
+    by = decode_bytes_hca(w, w.tokens // w.m, w.batch)
+    out.append({"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
+                "tokens_per_s": w.batch / (ms * 1e-3),
+                "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "algorithmic_bytes_per_step": by}})
+    del lay, o, xs
+    torch.cuda.empty_cache()
+
+    wc, wh = synth.PAIR_CSA_DECODE_B4_1M, synth.PAIR_HCA_DECODE_B4_1M
+    log(f"setup {wc.name} + {wh.name}")
+    lc = path.CsaLayer(wc, wc.batch, wc.tokens // wc.m + n_steps)
+    lh = path.HcaLayer(wh, wh.batch, wh.tokens // wh.m + n_steps, seed=1)
+    lc.prefill_context(wc.tokens)
+    lh.prefill_context(wh.tokens)
+    oc, oh = lc.alloc_decode_outputs(), lh.alloc_decode_outputs()
+    xc = [lc.decode_inputs([wc.tokens + i] * wc.batch) for i in range(n_steps)]
+    xh = [lh.decode_inputs([wh.tokens + i] * wh.batch) for i in range(n_steps)]
+    ms_c = time_graph(lambda i: lc.decode_step(xc[i], oc), n_steps)
+
+    def pair(i):
+        lc.decode_step(xc[i], oc)
+        lh.decode_step(xh[i], oh)
+    ms = time_graph(pair, n_steps)
+    by_c = decode_bytes_csa(wc, wc.tokens // wc.m, wc.batch)
+    by = by_c + decode_bytes_hca(wh, wh.tokens // wh.m, wh.batch)
+    out.append({"workload": wc.name, "metric": "CSA layer decode us/step (whole batch)", "value": ms_c * 1e3,
+                "unit": "us", "roofline": {"bound": "hbm", "achieved": by_c / (ms_c * 1e-3) / 1e9,
+                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                           "frac": by_c / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                           "algorithmic_bytes_per_step": by_c}})
+    out.append({"workload": wc.name + " + " + wh.name, "metric": "CSA+HCA layer pair decode us/step",
+                "value": ms * 1e3, "unit": "us",
+                "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                             "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                             "algorithmic_bytes_per_step": by}})
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -84,6 +223,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
+    ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X; "
@@ -92,6 +233,8 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calib:
+        copy_calibration()
     w = synth.CSA_PREFILL_BF16_32K
     log(f"setup {w.name}")
     st = path.CsaPrefill(w)
@@ -131,12 +274,16 @@ def main():
                    "indexer": [w.idx_heads, w.idx_dim]},
         "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel (sparse attention prefill)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                     "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "algorithmic_flop_per_launch": flops, "avg_launch_ms": attn_ms},
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline(w, st, args.cpu_budget)
+    if not args.no_secondary:
+        del st
+        torch.cuda.empty_cache()
+        out["secondary"] = secondary_decode()
     print(json.dumps(out), flush=True)
 
 
