@@ -3,7 +3,7 @@
 
 #include <string>
 
-#include "../../include/csa.h"
+#include "csa.h"
 
 namespace csa {
 

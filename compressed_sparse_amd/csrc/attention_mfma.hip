@@ -109,27 +109,53 @@ __device__ __forceinline__ void mm_lds(const bf16_t* a, const bf16_t* b, f32x16&
 }
 
 // Stages the query's 64 heads in LDS (row = head), the last 64 dims turned
-// by RoPE at `pos` (angles reduced in fp64), rounded back to BF16.
+// by RoPE at `pos` (angles reduced in fp64), rounded back to BF16.  Every
+// thread issues all of its loads (16 non-RoPE and 2 RoPE chunks of 8 dims)
+// before the first LDS store.
 __device__ __forceinline__ void stage_query(bf16_t* qtile, const bf16_t* q, int64_t pos, const Theta& th) {
   const int tid = threadIdx.x;
-  for (int c = tid; c < NH * (CW / 8); c += 256) {
-    const int h = c / (CW / 8), d0 = (c % (CW / 8)) * 8;
-    u32x4 raw = *reinterpret_cast<const u32x4*>(q + static_cast<size_t>(h) * CW + d0);
-    if (d0 >= DN) {
+  constexpr int NN = NH * (DN / 8) / 256, NR = NH * (DRP / 8) / 256;
+  u32x4 rn[NN], rr[NR];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = ((d0 - DN) >> 1) + i;
-        const double ang = static_cast<double>(pos) * th.t[p];
-        const float red = static_cast<float>(ang - rint(ang * 0.15915494309189535) * 6.283185307179586);
-        const float sn = __sinf(red), cs = __cosf(red);
-        const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
-        const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
-        raw[i] = static_cast<uint32_t>(f32_to_bf16(x0 * cs - x1 * sn)) |
-                 (static_cast<uint32_t>(f32_to_bf16(x0 * sn + x1 * cs)) << 16);
-      }
-    }
-    *reinterpret_cast<u32x4*>(qtile + h * KROW + d0) = raw;
+  for (int it = 0; it < NN; ++it) {
+    const int c = it * 256 + tid, h = c / (DN / 8), d0 = (c % (DN / 8)) * 8;
+    rn[it] = *reinterpret_cast<const u32x4*>(q + static_cast<size_t>(h) * CW + d0);
   }
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int c = it * 256 + tid, h = c / (DRP / 8), d0 = DN + (c % (DRP / 8)) * 8;
+    rr[it] = *reinterpret_cast<const u32x4*>(q + static_cast<size_t>(h) * CW + d0);
+  }
+#pragma unroll
+  for (int it = 0; it < NN; ++it) {
+    const int c = it * 256 + tid, h = c / (DN / 8), d0 = (c % (DN / 8)) * 8;
+    *reinterpret_cast<u32x4*>(qtile + h * KROW + d0) = rn[it];
+  }
+#pragma unroll
+  for (int it = 0; it < NR; ++it) {
+    const int c = it * 256 + tid, h = c / (DRP / 8), p0 = (c % (DRP / 8)) * 4;
+    u32x4 raw = rr[it];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const double ang = static_cast<double>(pos) * th.t[p0 + i];
+      const float red = static_cast<float>(ang - rint(ang * 0.15915494309189535) * 6.283185307179586);
+      const float sn = __sinf(red), cs = __cosf(red);
+      const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
+      const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
+      raw[i] = static_cast<uint32_t>(f32_to_bf16(x0 * cs - x1 * sn)) |
+               (static_cast<uint32_t>(f32_to_bf16(x0 * sn + x1 * cs)) << 16);
+    }
+    *reinterpret_cast<u32x4*>(qtile + h * KROW + DN + 2 * p0) = raw;
+  }
+}
+
+// Workgroup barrier ordering LDS accesses only: global loads in flight (the
+// next tile's prefetch) stay in flight across it, where __syncthreads()
+// would wait for them.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
 // Two fp32 -> packed BF16 pair (hardware RNE conversion).
@@ -270,13 +296,13 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       const bool ok = sid >= 0 && sid < n;
       const unsigned long long bal = __ballot(ok);
       if (lane == 0) s_cnt[w] = __popcll(bal);
-      __syncthreads();
+      lds_barrier();
       int before = 0, tot = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) { before += i < w ? s_cnt[i] : 0; tot += s_cnt[i]; }
       if (ok) s_list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int>(sid);
       base += tot;
-      __syncthreads();
+      lds_barrier();
     }
     nvalid = base;
   }
@@ -294,14 +320,14 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   // below 256 and the accumulators are rarely rescaled
   float m_run = -INFINITY, l_part = 0.0f;
 
-  __syncthreads();  // s_list and the query tile ready
+  lds_barrier();  // s_list and the query tile ready
   const int64_t ntiles = (nvalid + TILE - 1) / TILE;
   Prefetch<FP8> pf;
   if (ntiles > 0) load_tile<FP8, DENSE>(pf, P, s_list, 0, r0, nvalid, seq);
   for (int64_t j = 0; j < ntiles; ++j) {
-    __syncthreads();  // previous tile's O^T finished with ktile / pbuf
+    lds_barrier();  // previous tile's O^T finished with ktile / pbuf
     store_tile<FP8>(pf, ktile, s_scale);
-    __syncthreads();
+    lds_barrier();
     if (j + 1 < ntiles) load_tile<FP8, DENSE>(pf, P, s_list, (j + 1) * TILE, r0, nvalid, seq);
 
     // --- S^T = K Q^T: entries 32ep.. x heads 32hp.. --------------------------
@@ -324,7 +350,7 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));  // the other 16 entries of this head
     if (lane < 32) s_xchg[ep][head] = mx;
-    __syncthreads();
+    lds_barrier();
     mx = fmaxf(mx, s_xchg[ep ^ 1][head]);
     const bool move = mx > m_run + 8.0f;
     if (__ballot(move)) {
@@ -352,7 +378,7 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     for (int jq = 0; jq < 4; ++jq)
       *reinterpret_cast<uint2*>(pbuf + head * PROW + ep * 32 + jq * 8 + (lane >> 5) * 4) =
           make_uint2(pk[2 * jq], pk[2 * jq + 1]);
-    __syncthreads();
+    lds_barrier();
 
     // --- O^T += V^T P^T: value dims 256ep.. x heads 32hp.. --------------------
     bf16x8 pb[TILE / 16];
@@ -371,9 +397,9 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
 
   // --- finish: softmax denominators -------------------------------------
   l_part += __shfl_xor(l_part, 32);
-  __syncthreads();
+  lds_barrier();
   if (lane < 32) s_xchg[ep][head] = l_part;
-  __syncthreads();
+  lds_barrier();
   const float ltot = l_part + s_xchg[ep ^ 1][head];
 
   // O^T layout: lane = head, register (nb, v) = value dim ep*256 + nb*32 + acc_row(v)
@@ -407,29 +433,44 @@ attn_mfma_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   }
 }
 
-// Combines split partials by log-sum-exp; grid (B), 512 threads.
-__global__ void __launch_bounds__(512) attn_merge_kernel(AttnParams P, int splits, const float* part, int B) {
-  const int b = blockIdx.x;
-  const float* po = part + static_cast<size_t>(b) * splits * (NH * DN);
+// Combines split partials by log-sum-exp; grid (NH, B), one thread per 4
+// value dims (128 threads), the head's split weights computed once in LDS.
+// S >= splits is a power of two: every thread's S partial loads (clamped to
+// the last split) are issued before the weights are known.
+template <int S>
+__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams P, int splits, const float* part, int B) {
+  __shared__ float s_f[S];
+  __shared__ float s_L, s_M;
+  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const float* po = part + static_cast<size_t>(b) * splits * (NH * DN) + static_cast<size_t>(h) * DN + 4 * tid;
+  float4 v[S];
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp)
+    v[sp] = *reinterpret_cast<const float4*>(po + static_cast<size_t>(min(sp, splits - 1)) * NH * DN);
   const float* pml = part + static_cast<size_t>(B) * splits * (NH * DN) + static_cast<size_t>(b) * splits * (2 * NH);
-  bf16_t* out = static_cast<bf16_t*>(P.o) + static_cast<size_t>(b) * NH * DN;
-  for (int x = threadIdx.x; x < NH * DN; x += blockDim.x) {
-    const int h = x / DN;
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) M = fmaxf(M, pml[(s * NH + h) * 2]);
-    float L = 0.0f, acc = 0.0f;
-    if (M != -INFINITY) {
-      for (int s = 0; s < splits; ++s) {
-        const float ms = pml[(s * NH + h) * 2];
-        if (ms == -INFINITY) continue;
-        const float f = exp2f(ms - M);
-        L += pml[(s * NH + h) * 2 + 1] * f;
-        acc += po[static_cast<size_t>(s) * NH * DN + x] * f;
-      }
-    }
-    out[x] = f32_to_bf16(L > 0.0f ? acc / L : 0.0f);
-    if (P.lse && (x % DN) == 0) P.lse[static_cast<size_t>(b) * NH + h] = L > 0.0f ? (M + log2f(L)) * LN2 : -INFINITY;
+  if (tid < 64) {
+    const float ms = tid < splits ? pml[(tid * NH + h) * 2] : -INFINITY;
+    const float ls = tid < splits ? pml[(tid * NH + h) * 2 + 1] : 0.0f;
+    float M = ms;
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+    const float f = (tid < splits && ms != -INFINITY) ? exp2f(ms - M) : 0.0f;
+    float L = ls * f;
+    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
+    if (tid < S) s_f[tid] = f;
+    if (tid == 0) { s_L = L; s_M = M; }
   }
+  __syncthreads();
+  const float L = s_L;
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+  for (int sp = 0; sp < S; ++sp) {
+    const float f = s_f[sp];  // 0 past the last split and for empty splits
+    acc.x += v[sp].x * f; acc.y += v[sp].y * f; acc.z += v[sp].z * f; acc.w += v[sp].w * f;
+  }
+  bf16_t* out = static_cast<bf16_t*>(P.o) + (static_cast<size_t>(b) * NH + h) * DN + 4 * tid;
+  *reinterpret_cast<uint2*>(out) = make_uint2(pack2_bf16(acc.x * inv, acc.y * inv), pack2_bf16(acc.z * inv, acc.w * inv));
+  if (P.lse && tid == 0) P.lse[static_cast<size_t>(b) * NH + h] = L > 0.0f ? (s_M + log2f(L)) * LN2 : -INFINITY;
 }
 
 Theta make_theta(double base) {
@@ -495,7 +536,13 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   else dense ? launch_one<false, true, true>(P, grid, s, splits, per, part) : launch_one<false, false, true>(P, grid, s, splits, per, part);
   int st = check_launch("attn_mfma_kernel");
   if (st != CSA_OK) return st;
-  hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(512), 0, s, P, splits, part, B);
+  const dim3 mg(NH, B);
+  if (splits <= 1) hipLaunchKernelGGL(attn_merge_kernel<1>, mg, dim3(128), 0, s, P, splits, part, B);
+  else if (splits <= 2) hipLaunchKernelGGL(attn_merge_kernel<2>, mg, dim3(128), 0, s, P, splits, part, B);
+  else if (splits <= 4) hipLaunchKernelGGL(attn_merge_kernel<4>, mg, dim3(128), 0, s, P, splits, part, B);
+  else if (splits <= 8) hipLaunchKernelGGL(attn_merge_kernel<8>, mg, dim3(128), 0, s, P, splits, part, B);
+  else if (splits <= 16) hipLaunchKernelGGL(attn_merge_kernel<16>, mg, dim3(128), 0, s, P, splits, part, B);
+  else hipLaunchKernelGGL(attn_merge_kernel<MAX_SPLITS>, mg, dim3(128), 0, s, P, splits, part, B);
   return check_launch("attn_merge_kernel");
 }
 

@@ -34,7 +34,10 @@ __device__ __forceinline__ float* ring_row(const CompressParams& P, int b, int64
   return P.ring + ((static_cast<size_t>(b) * P.R + slot) * P.NT + which) * P.c;
 }
 
-// Weighted value of channel j of entry i, rows fetched by `get(which, t)`.
+// Weighted value of channel j of entry i, rows fetched by `get(which, t)`:
+// an online softmax over the window's rows (C^a rows of window i, then the
+// C^b rows of window i-1).  The rows' loads are issued eight at a time
+// (clamped to the last row, so branch-free) before their softmax steps.
 template <class Get>
 __device__ __forceinline__ float compress_channel(const CompressParams& P, int64_t i, int j, Get get) {
   float mx = -INFINITY, sum = 0.0f, acc = 0.0f;
@@ -50,16 +53,24 @@ __device__ __forceinline__ float compress_channel(const CompressParams& P, int64
       acc += e * v;
     }
   };
-  for (int r = 0; r < P.m; ++r) {
-    int64_t t = i * P.m + r;
-    take(get(RING_ZA, t, j) + P.Ba[r * P.c + j], get(RING_A, t, j));
-  }
-  if (P.overlap && i >= 1) {
-    for (int r = 0; r < P.m; ++r) {
-      int64_t t = (i - 1) * P.m + r;
-      take(get(RING_ZB, t, j) + P.Bb[r * P.c + j], get(RING_B, t, j));
+  constexpr int U = 8;
+  auto side = [&](int zw, int vw, const float* Bw, int64_t t0) {
+    for (int r0 = 0; r0 < P.m; r0 += U) {
+      float z[U], v[U], bw[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int r = r0 + u < P.m ? r0 + u : P.m - 1;
+        z[u] = get(zw, t0 + r, j);
+        v[u] = get(vw, t0 + r, j);
+        bw[u] = Bw[r * P.c + j];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (r0 + u < P.m) take(z[u] + bw[u], v[u]);
     }
-  }
+  };
+  side(RING_ZA, RING_A, P.Ba, i * P.m);
+  if (P.overlap && i >= 1) side(RING_ZB, RING_B, P.Bb, (i - 1) * P.m);
   return acc / sum;
 }
 
@@ -158,26 +169,49 @@ __global__ void __launch_bounds__(256) ring_store_kernel(CompressParams P, int64
   }
 }
 
-__global__ void __launch_bounds__(256) compress_decode_kernel(CompressParams P, const int64_t* pos_dev) {
+template <bool IN_BF16>
+__device__ __forceinline__ float load_in(const void* p, size_t i) {
+  if constexpr (IN_BF16) return bf16_to_f32(static_cast<const bf16_t*>(p)[i]);
+  else return static_cast<const float*>(p)[i];
+}
+
+// Decode: one workgroup per sequence, one thread per channel (looping when
+// the entry is wider than the workgroup).  The thread loads its channel of
+// the new token's rows, stores them into the ring and, when the token
+// completes a window, runs the channel's softmax over the window with the
+// new row taken from its registers; nothing waits for the ring stores.
+template <bool IN_BF16>
+__global__ void __launch_bounds__(1024) compress_decode_kernel(CompressParams P, const int64_t* pos_dev) {
   extern __shared__ float smem[];
-  float* red = smem;
-  float* buf = smem + 32;
-  const int b = blockIdx.x;
+  float* red = smem;        // 32
+  float* buf = smem + 32;   // c: the emitted entry
+  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int64_t pos = pos_dev[b];
   if (pos < 0) return;
-  // 1) the new token enters the ring (each thread its own channels)
-  for (int which = 0; which < P.NT; ++which) {
-    const void* src = which == RING_A ? P.a : which == RING_ZA ? P.za : which == RING_B ? P.b : P.zb;
-    float* dst = ring_row(P, b, pos, which);
-    for (int j = threadIdx.x; j < P.c; j += blockDim.x)
-      dst[j] = load_elem(src, static_cast<size_t>(b) * P.c + j, P.in_dt);
-  }
-  // 2) a completed window emits its entry
-  if ((pos + 1) % P.m != 0) return;
   const int64_t i = (pos + 1) / P.m - 1;
-  if (i >= P.cap) return;
-  auto get = [&](int which, int64_t t, int j) -> float { return ring_row(P, b, t, which)[j]; };
-  for (int j = threadIdx.x; j < P.c; j += blockDim.x) buf[j] = compress_channel(P, i, j, get);
+  const bool emit = (pos + 1) % P.m == 0 && i < P.cap;
+  const size_t row = static_cast<size_t>(b) * P.c;
+  for (int j = tid; j < P.c; j += nt) {
+    float cur[4];
+    cur[RING_A] = load_in<IN_BF16>(P.a, row + j);
+    cur[RING_ZA] = load_in<IN_BF16>(P.za, row + j);
+    cur[RING_B] = cur[RING_ZB] = 0.0f;
+    if (P.NT == 4) {
+      cur[RING_B] = load_in<IN_BF16>(P.b, row + j);
+      cur[RING_ZB] = load_in<IN_BF16>(P.zb, row + j);
+    }
+#pragma unroll
+    for (int wch = 0; wch < 4; ++wch)
+      if (wch < P.NT) ring_row(P, b, pos, wch)[j] = cur[wch];
+    if (emit) {
+      auto get = [&](int which, int64_t t, int jj) -> float {
+        const float v = ring_row(P, b, t, which)[jj];
+        return t == pos ? cur[which] : v;
+      };
+      buf[j] = compress_channel(P, i, j, get);
+    }
+  }
+  if (!emit) return;
   __syncthreads();
   finalize_entry(P, buf, red, b, i);
 }
@@ -295,7 +329,11 @@ extern "C" int csa_compress_decode(const csa_cache_desc* desc, int B, const int6
   CompressParams P = make_params(desc, cache, a, b, za, zb, Ba, Bb);
   P.T = 1;
   P.pos0 = 0;
-  const size_t lds = (32 + P.c) * sizeof(float);
-  hipLaunchKernelGGL(compress_decode_kernel, dim3(B), dim3(256), lds, as_stream(stream), P, pos);
+  const size_t lds = (32 + static_cast<size_t>(P.c)) * sizeof(float);
+  const int threads = P.c >= 1024 ? 1024 : ((P.c + 63) / 64) * 64;
+  if (P.in_dt == CSA_BF16)
+    hipLaunchKernelGGL(compress_decode_kernel<true>, dim3(B), dim3(threads), lds, as_stream(stream), P, pos);
+  else
+    hipLaunchKernelGGL(compress_decode_kernel<false>, dim3(B), dim3(threads), lds, as_stream(stream), P, pos);
   return check_launch("compress_decode_kernel");
 }

@@ -20,7 +20,48 @@ struct IndexParams {
   float* scores_out;  // optional [B][T][cap]
   float* ws;          // [B][T][n_stride] score rows
   int64_t n_stride;
+  // decode multi-workgroup top-k (NULL otherwise): per-row histogram of the
+  // top 11 key bits, candidate count, candidate (key, index) lists and, per
+  // CAND_CHUNK-entry chunk, where its index-ordered candidates start and how
+  // many there are
+  int* ghist;         // [B][HIST_BINS]
+  int* ccount;        // [B]
+  uint32_t* ckey;     // [B][CAND_CAP]
+  int32_t* cidx;      // [B][CAND_CAP]
+  int* cbase;         // [B][nch]
+  int* ccnt;          // [B][nch]
+  int nch;            // chunks per row: ceil(cap / CAND_CHUNK)
 };
+
+constexpr int HIST_BITS = 11;
+constexpr int HIST_BINS = 1 << HIST_BITS;
+constexpr int CAND_CAP = 8192;    // candidates one row may keep in LDS
+constexpr int CAND_CHUNK = 4096;  // entries per candidate workgroup
+constexpr int NCH_MAX = 4096;     // chunks per row the final pass can order (cap <= 16M entries)
+
+// Order-preserving key of a score: larger score -> larger key; -0 == +0.
+__device__ __forceinline__ uint32_t score_key(float x) {
+  uint32_t u = __float_as_uint(x);
+  if ((u << 1) == 0u) return 0x80000000u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// LDS histogram increment, aggregated over the lanes of a wave that hit the
+// same bin (scores concentrate in a few high-bit bins); after a few rounds
+// the remaining lanes (spread bins, little contention) add one by one.
+__device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
+  const int lane = threadIdx.x & 63;
+  for (int round = 0; round < 4; ++round) {
+    const unsigned long long act = __ballot(active);
+    if (act == 0ull) return;
+    const int leader = __ffsll(static_cast<long long>(act)) - 1;
+    const int lb = __shfl(bin, leader);
+    const unsigned long long same = __ballot(active && bin == lb);
+    if (lane == leader) atomicAdd(&hist[lb], __popcll(same));
+    if (bin == lb) active = false;
+  }
+  if (active) atomicAdd(&hist[bin], 1);
+}
 
 bool index_mfma_supported(const IndexParams& P);
 bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max);

@@ -27,6 +27,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int HI = 16;
 constexpr int DI = 64;
@@ -39,29 +40,27 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
-// 8 FP8 codes (two words, first byte first) -> 8 BF16 values (exact).
-__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
-  u32x4 o;
-  const uint32_t wd[2] = {w0, w1};
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t word = wd[j];
-    o[2 * j] = (__float_as_uint(e4m3_to_f32(word & 0xFFu)) >> 16) |
-               (__float_as_uint(e4m3_to_f32((word >> 8) & 0xFFu)) & 0xFFFF0000u);
-    o[2 * j + 1] = (__float_as_uint(e4m3_to_f32((word >> 16) & 0xFFu)) >> 16) |
-                   (__float_as_uint(e4m3_to_f32(word >> 24)) & 0xFFFF0000u);
-  }
-  return o;
+// Hardware widening of FP8 E4M3 / E2M1 codes to BF16 (the scaled
+// conversions with scale 1: exact for every code).  fp8x8: two words, first
+// byte first; e2m1x8: one word, low nibble first.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
 }
 
-// 8 E2M1 codes (one word, low nibble first) times 2^ex -> 4 words of BF16 pairs (exact).
-__device__ __forceinline__ void e2m1x8_to_bf16(uint32_t word, float X, u32x4& out) {
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const float a = e2m1_to_f32((word >> (8 * q)) & 15u) * X;
-    const float b = e2m1_to_f32((word >> (8 * q + 4)) & 15u) * X;
-    out[q] = (__float_as_uint(a) >> 16) | (__float_as_uint(b) & 0xFFFF0000u);
-  }
+__device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
+               fp8x2_to_bf16x2<true>(w1)};
+}
+
+template <int BYTE>
+__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t word) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, BYTE));
+}
+
+__device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t word) {
+  return u32x4{e2m1x2_to_bf16x2<0>(word), e2m1x2_to_bf16x2<1>(word), e2m1x2_to_bf16x2<2>(word),
+               e2m1x2_to_bf16x2<3>(word)};
 }
 
 // Orders this wave's LDS accesses before the ones that follow.
@@ -250,10 +249,13 @@ __global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams
 // ---------------------------------------------------------------------------
 // streaming scan: one query row x 1024 entries per workgroup
 // ---------------------------------------------------------------------------
-constexpr int SCAN_CHUNK = 1024;
+constexpr int SCAN_CHUNK = 2048;
 
 template <int KFMT, bool QMX>
-__global__ void __launch_bounds__(256) index_scan_kernel(IndexParams P) {
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT == CSA_FP8E4M3 ? 3 : 4))) index_scan_kernel(IndexParams P) {
+  // this chunk's top-11-bit key histogram (decode top-k), one per wave so
+  // that no barrier separates the clearing from the counting
+  __shared__ int lhist_w[4][HIST_BINS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.z, t = blockIdx.y;
   const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
@@ -262,88 +264,153 @@ __global__ void __launch_bounds__(256) index_scan_kernel(IndexParams P) {
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * SCAN_CHUNK;
   if (c0 >= n) return;
   const size_t row = static_cast<size_t>(b) * P.T + t;
-  // A operand (16x16x32): head = lane & 15; k-step ks covers dims g*16 + ks*8 .. +8, g = lane >> 4
+  // A operand (16x16x32): head = lane & 15, g = lane >> 4.  BF16 / FP8 keys:
+  // k-step ks covers dims g*16 + ks*8 .. +8.  MXFP4 keys: k-step ks is the
+  // 32-dim scale block ks, dims ks*32 + g*8 .. +8, so that the block scale
+  // multiplies that MFMA's result.
   const int g = lane >> 4, h = lane & 15;
   bf16x8 qa[2];
   {
-    const bf16_t* qp = static_cast<const bf16_t*>(P.qI) + (row * HI + h) * DI + g * 16;
-    u32x4 r0 = *reinterpret_cast<const u32x4*>(qp);
-    u32x4 r1 = *reinterpret_cast<const u32x4*>(qp + 8);
-    if (QMX) {
-      float x[16];
+    const bf16_t* qrow = static_cast<const bf16_t*>(P.qI) + (row * HI + h) * DI;
+    u32x4 r[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_to_f32(static_cast<bf16_t>(r0[i] & 0xFFFFu));
-        x[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(r0[i] >> 16));
-        x[8 + 2 * i] = bf16_to_f32(static_cast<bf16_t>(r1[i] & 0xFFFFu));
-        x[8 + 2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(r1[i] >> 16));
-      }
-      float am = 0.0f;
+    for (int ks = 0; ks < 2; ++ks)
+      r[ks] = *reinterpret_cast<const u32x4*>(qrow + (KFMT == CSA_MXFP4 ? ks * 32 + g * 8 : g * 16 + ks * 8));
+    if (QMX) {  // the query's own MXFP4 rounding, per 32-dim block
 #pragma unroll
-      for (int i = 0; i < 16; ++i) am = fmaxf(am, fabsf(x[i]));
-      am = fmaxf(am, __shfl_xor(am, 16));  // the other half of this 32-dim block
-      const int ex = mx_exponent(am);
-      const float inv = exp2i(-ex), X = exp2i(ex);
+      for (int ks = 0; ks < 2; ++ks) {
+        float x[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = e2m1_to_f32(f32_to_e2m1(x[i] * inv)) * X;
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = bf16_to_f32(static_cast<bf16_t>(r[ks][i] & 0xFFFFu));
+          x[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(r[ks][i] >> 16));
+        }
+        float am = 0.0f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r0[i] = pack_bf16(x[2 * i], x[2 * i + 1]);
-        r1[i] = pack_bf16(x[8 + 2 * i], x[8 + 2 * i + 1]);
+        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
+        am = fmaxf(am, __shfl_xor(am, 16));  // the block's other three groups
+        am = fmaxf(am, __shfl_xor(am, 32));
+        const int ex = mx_exponent(am);
+        const float inv = exp2i(-ex), X = exp2i(ex);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = e2m1_to_f32(f32_to_e2m1(x[i] * inv)) * X;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r[ks][i] = pack_bf16(x[2 * i], x[2 * i + 1]);
       }
     }
-    qa[0] = as_bf16x8(r0);
-    qa[1] = as_bf16x8(r1);
+    qa[0] = as_bf16x8(r[0]);
+    qa[1] = as_bf16x8(r[1]);
   }
   float wv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) wv[v] = P.w[row * HI + g * 4 + v];
   const size_t seq = static_cast<size_t>(b) * P.cap;
-  float* wsrow = P.ws + row * P.n_stride;
-  float* sorow = P.scores_out ? P.scores_out + row * P.cap : nullptr;
-  int64_t c1 = c0 + SCAN_CHUNK;
-  if (c1 > n) c1 = n;
-  // each wave: 16-entry column blocks w, w+4, ...
-#pragma unroll 2
-  for (int64_t e0 = c0 + w * 16; e0 < c1; e0 += 64) {
-    const int64_t s = e0 + (lane & 15);
-    const bool ok = s < c1;
-    u32x4 k0 = {0u, 0u, 0u, 0u}, k1 = {0u, 0u, 0u, 0u};
-    float ksc = 1.0f;
-    if (ok) {
-      if (KFMT == CSA_BF16) {
-        const bf16_t* kp = static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + g * 16;
-        k0 = *reinterpret_cast<const u32x4*>(kp);
-        k1 = *reinterpret_cast<const u32x4*>(kp + 8);
-      } else if (KFMT == CSA_FP8E4M3) {
-        const u32x4 c = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + g * 16);
-        k0 = fp8x8_to_bf16(c[0], c[1]);
-        k1 = fp8x8_to_bf16(c[2], c[3]);
-        ksc = static_cast<const float*>(P.kscale)[seq + s];
-      } else {  // MXFP4: 16 codes = 8 bytes at dims g*16.., scale of block g/2
-        const u32x2 c = *reinterpret_cast<const u32x2*>(static_cast<const uint8_t*>(P.knope) + (seq + s) * (DI / 2) + g * 8);
-        const int ex = static_cast<int>(static_cast<const uint8_t*>(P.kscale)[(seq + s) * (DI / 32) + (g >> 1)]) - 127;
-        const float X = exp2i(ex);
-        e2m1x8_to_bf16(c[0], X, k0);
-        e2m1x8_to_bf16(c[1], X, k1);
+  const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);  // entries of this chunk
+  // wave-uniform bases of this chunk; per-lane offsets are 32-bit
+  float* wsb = P.ws + row * P.n_stride + c0;
+  float* sob = P.scores_out ? P.scores_out + row * P.cap + c0 : nullptr;
+  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) +
+                      (seq + c0) * (KFMT == CSA_BF16 ? 2 * DI : KFMT == CSA_FP8E4M3 ? DI : DI / 2);
+  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * (KFMT == CSA_MXFP4 ? DI / 32 : 4);
+  int* lhist = lhist_w[w];
+  if (P.ghist)
+    for (int i = lane; i < HIST_BINS; i += 64) lhist[i] = 0;
+  // each wave: 16-entry column blocks w, w+4, ...  A batch of NB blocks is
+  // loaded (clamped to the last entry, so branch-free) while the previous
+  // batch is widened, multiplied and reduced over heads (two register sets,
+  // used in turn).
+  constexpr int NB = KFMT == CSA_BF16 ? 4 : 8;
+  auto load = [&](int e0, u32x4 (&ra)[NB], u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int s = min(e0 + 64 * j + (lane & 15), cn - 1);
+      if constexpr (KFMT == CSA_BF16) {
+        ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32));
+        rb[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32 + 16));
+      } else if constexpr (KFMT == CSA_FP8E4M3) {
+        ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * DI + g * 16));
+        rs[j] = *reinterpret_cast<const uint32_t*>(sb + static_cast<uint32_t>(s * 4));
+      } else {  // MXFP4: 8 codes of block 0 and of block 1 at dims ks*32 + g*8, both block scales
+        ra[j][0] = *reinterpret_cast<const uint32_t*>(kb + static_cast<uint32_t>(s * (DI / 2) + g * 4));
+        ra[j][1] = *reinterpret_cast<const uint32_t*>(kb + static_cast<uint32_t>(s * (DI / 2) + g * 4 + 16));
+        rs[j] = *reinterpret_cast<const uint16_t*>(sb + static_cast<uint32_t>(s * (DI / 32)));
       }
     }
-    f32x4 acc = f32x4{};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(k0), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(k1), acc, 0, 0, 0);
-    // lane: entry lane & 15, heads 4g .. 4g+3
-    float sc = 0.0f;
+  };
+  auto compute = [&](int e0, const u32x4 (&ra)[NB], const u32x4 (&rb)[NB], const uint32_t (&rs)[NB]) {
+    f32x4 acc[NB];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sc = fmaf(wv[v], fmaxf(acc[v] * ksc, 0.0f), sc);
-    // fixed-order head reduction: (g0 + g1) + (g2 + g3)
-    const float x16 = __shfl_xor(sc, 16);
-    const float pair = (g & 1) ? x16 + sc : sc + x16;
-    const float x32 = __shfl_xor(pair, 32);
-    float tot = (g & 2) ? x32 + pair : pair + x32;
-    if (P.score_dt == CSA_BF16) tot = round_bf16(tot);
-    if (ok && g == 0) {
-      wsrow[s] = tot;
-      if (sorow) sorow[s] = tot;
+    for (int j = 0; j < NB; ++j) {
+      if constexpr (KFMT == CSA_MXFP4) {  // dot = X0 * (block 0 codes . q) + X1 * (block 1 codes . q)
+        const f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(e2m1x8_to_bf16(ra[j][0])), f32x4{}, 0, 0, 0);
+        const f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(e2m1x8_to_bf16(ra[j][1])), f32x4{}, 0, 0, 0);
+        const float X0 = exp2i(static_cast<int>(rs[j] & 0xFFu) - 127);
+        const float X1 = exp2i(static_cast<int>(rs[j] >> 8) - 127);
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[j][v] = fmaf(a1[v], X1, a0[v] * X0);
+      } else {
+        const u32x4 k0 = KFMT == CSA_FP8E4M3 ? fp8x8_to_bf16(ra[j][0], ra[j][1]) : ra[j];
+        const u32x4 k1 = KFMT == CSA_FP8E4M3 ? fp8x8_to_bf16(ra[j][2], ra[j][3]) : rb[j];
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(k0), f32x4{}, 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(k1), acc[j], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < NB / 4; ++q) {
+      // lane (entry e = lane & 15, group g): partial score of block 4q + i
+      // over heads 4g .. 4g+3 (the positive FP8 scale commutes with ReLU;
+      // ReLU as an integer max: every negative float, -0 included, becomes +0)
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const f32x4 c = acc[4 * q + i];
+        float sc = 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) sc = fmaf(wv[v], __int_as_float(max(__float_as_int(c[v]), 0)), sc);
+        if constexpr (KFMT == CSA_FP8E4M3) sc *= __uint_as_float(rs[4 * q + i]);
+        p[i] = sc;
+      }
+      // butterfly over the four groups: after it, group g holds the full
+      // score of block 4q + g (groups g, g^2 first, then g, g^1)
+      const bool hi = g >= 2, odd = g & 1;
+      const float ka = hi ? p[2] : p[0], kb2 = hi ? p[3] : p[1];
+      const float ra2 = __shfl_xor(hi ? p[0] : p[2], 32), rb2 = __shfl_xor(hi ? p[1] : p[3], 32);
+      const float x = hi ? ra2 + ka : ka + ra2;    // block 2*hi: groups 0 + 2, 1 + 3
+      const float y = hi ? rb2 + kb2 : kb2 + rb2;  // block 2*hi + 1
+      const float r = __shfl_xor(odd ? x : y, 16);
+      float tot = odd ? r + y : x + r;             // block 2*hi + odd = g: (g0 + g2) + (g1 + g3)
+      if (P.score_dt == CSA_BF16) tot = round_bf16(tot);
+      const int s = e0 + 64 * (4 * q + g) + (lane & 15);
+      const bool ok = s < cn;
+      if (ok) {
+        wsb[s] = tot;
+        if (sob) sob[s] = tot;
+      }
+      if (P.ghist) wave_hist_add(lhist, static_cast<int>(score_key(tot) >> (32 - HIST_BITS)), ok);
+    }
+  };
+  u32x4 xa[NB], xb[NB], ya[NB], yb[NB];
+  uint32_t xs[NB], ys[NB];
+  // The loads are unconditional (a batch past the end re-reads the last
+  // entry): a load under a branch would make the compiler wait for every
+  // outstanding load before the next batch's arithmetic.
+  int e0 = w * 16;
+  load(e0, xa, xb, xs);
+  while (e0 < cn) {
+    load(e0 + 64 * NB, ya, yb, ys);
+    compute(e0, xa, xb, xs);
+    e0 += 64 * NB;
+    if (e0 >= cn) break;
+    load(e0 + 64 * NB, xa, xb, xs);
+    compute(e0, ya, yb, ys);
+    e0 += 64 * NB;
+  }
+  if (P.ghist) {
+    __syncthreads();
+    int* gh = P.ghist + static_cast<size_t>(b) * HIST_BINS;
+    for (int i = tid; i < HIST_BINS; i += 256) {
+      const int c = lhist_w[0][i] + lhist_w[1][i] + lhist_w[2][i] + lhist_w[3][i];
+      if (c) atomicAdd(&gh[i], c);
     }
   }
 }

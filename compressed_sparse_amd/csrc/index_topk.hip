@@ -93,89 +93,331 @@ __global__ void __launch_bounds__(256) index_scores_generic(IndexParams P) {
   if (P.scores_out) P.scores_out[row * P.cap + s] = acc;
 }
 
-// Order-preserving key of a score: larger score -> larger key; -0 == +0.
-__device__ __forceinline__ uint32_t score_key(float x) {
-  uint32_t u = __float_as_uint(x);
-  if ((u << 1) == 0u) return 0x80000000u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+// Exclusive prefix sums of two per-thread counts over the workgroup, in
+// thread order (s_part: __shared__ int[34]); *ta and *tb get the totals.
+// Every thread of the workgroup calls it: two barriers inside.
+__device__ __forceinline__ void block_scan2(int a, int b, int* s_part, int* pa, int* pb, int* ta, int* tb) {
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int ya = __shfl_up(ia, o), yb = __shfl_up(ib, o);
+    if (lane >= o) { ia += ya; ib += yb; }
+  }
+  __syncthreads();  // earlier readers of s_part are done
+  if (lane == 63) { s_part[wv] = ia; s_part[17 + wv] = ib; }
+  __syncthreads();
+  int ba = 0, bb = 0, sa = 0, sb = 0;
+  for (int i = 0; i < nw; ++i) {
+    const int xa = s_part[i], xb = s_part[17 + i];
+    if (i < wv) { ba += xa; bb += xb; }
+    sa += xa;
+    sb += xb;
+  }
+  *pa = ba + ia - a;
+  *pb = bb + ib - b;
+  *ta = sa;
+  *tb = sb;
 }
 
-// Exclusive prefix count of `flag` over the workgroup, in thread order.
-// cnt: __shared__ int[17].  Returns the prefix; *total gets the sum.
-__device__ __forceinline__ int block_prefix(bool flag, int* cnt, int* total) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  unsigned long long bal = __ballot(flag);
-  int in_wave = __popcll(bal & ((1ull << lane) - 1ull));
-  __syncthreads();
-  if (lane == 0) cnt[wv] = __popcll(bal);
-  __syncthreads();
-  int before = 0, tot = 0;
-  for (int i = 0; i < nw; ++i) {
-    int c = cnt[i];
-    if (i < wv) before += c;
-    tot += c;
+// Wave 0's part of one radix-select step: the highest 8-bit digit whose bin
+// brings the count of keys taken from the top up to `remaining`.  Lane l
+// holds bins 255-4l .. 252-4l; the digit and the count in the bins above it
+// go to s_sel[0], s_sel[1].
+__device__ __forceinline__ void find_digit(const int* hist, int remaining, int* s_sel) {
+  const int lane = threadIdx.x & 63;
+  int c[4], tot = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; tot += c[j]; }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
   }
-  *total = tot;
-  return before + in_wave;
+  const int excl = incl - tot;
+  if (excl < remaining && incl >= remaining) {
+    int cum = excl;
+    bool found = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if (!found && cum + c[j] >= remaining) {
+        s_sel[0] = 255 - 4 * lane - j;
+        s_sel[1] = cum;
+        found = true;
+      }
+      cum += c[j];
+    }
+  } else if (lane == 63 && incl < remaining) {  // fewer keys than asked for: digit 0
+    s_sel[0] = 0;
+    s_sel[1] = incl - c[3];
+  }
+}
+
+// Radix select by the whole workgroup over cnt keys key_of(i): 8-bit digits
+// from the top over the key's first key_bits bits.  On return *prefix holds
+// the k-th largest key (masked by *pmask) and *rem how many keys equal to it
+// belong to the top k.
+template <typename KeyOf>
+__device__ __forceinline__ void radix_threshold(KeyOf key_of, int64_t cnt, int k, int key_bits, int* hist, int* s_sel,
+                                uint32_t* prefix_out, uint32_t* pmask_out, int* rem_out) {
+  constexpr int U = 4;  // loads in flight per thread
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint32_t prefix = 0, pmask = 0;
+  int remaining = k;
+  for (int shift = 24; shift >= 32 - key_bits; shift -= 8) {
+    for (int i = tid; i < 256; i += nt) hist[i] = 0;
+    __syncthreads();
+    for (int64_t base = 0; base < cnt; base += static_cast<int64_t>(U) * nt) {
+      uint32_t key[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * nt + tid;
+        key[u] = i < cnt ? key_of(i) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t i = base + static_cast<int64_t>(u) * nt + tid;
+        wave_hist_add(hist, (key[u] >> shift) & 255u, i < cnt && (key[u] & pmask) == prefix);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) find_digit(hist, remaining, s_sel);
+    __syncthreads();
+    prefix |= static_cast<uint32_t>(s_sel[0]) << shift;
+    remaining -= s_sel[1];
+    pmask |= 255u << shift;
+  }
+  *prefix_out = prefix;
+  *pmask_out = pmask;
+  *rem_out = remaining;
+}
+
+// Ordered compaction after radix_threshold: the elements whose key is above
+// the threshold, and the first `remaining` equal to it, in element order,
+// their idx_of(i) written to out[0..).  Each thread takes E consecutive
+// elements per tile; one workgroup scan per tile.
+template <typename KeyOf, typename IdxOf>
+__device__ __forceinline__ void ordered_take(KeyOf key_of, IdxOf idx_of, int64_t cnt, uint32_t prefix, uint32_t pmask,
+                             int remaining, int* s_part, int32_t* out) {
+  constexpr int E = 8;
+  const int tid = threadIdx.x, nt = blockDim.x;
+  int gt_done = 0, eq_done = 0;
+  for (int64_t base = 0; base < cnt; base += static_cast<int64_t>(E) * nt) {
+    const int64_t i0 = base + static_cast<int64_t>(tid) * E;
+    uint32_t key[E];
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) key[u] = i0 + u < cnt ? key_of(i0 + u) & pmask : 0u;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      const bool ok = i0 + u < cnt;
+      ngt += ok && key[u] > prefix;
+      neq += ok && key[u] == prefix;
+    }
+    int pg, pe, tg, te;
+    block_scan2(ngt, neq, s_part, &pg, &pe, &tg, &te);
+    int eq_before = eq_done + pe;
+    int pos = gt_done + pg + min(eq_before, remaining);
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+      if (i0 + u >= cnt) break;
+      if (key[u] > prefix) {
+        out[pos++] = idx_of(i0 + u);
+      } else if (key[u] == prefix) {
+        if (eq_before < remaining) out[pos++] = idx_of(i0 + u);
+        ++eq_before;
+      }
+    }
+    gt_done += tg;
+    eq_done += te;
+  }
+}
+
+// Top-k of sc[0..n) (n > k) by one workgroup, ascending indices, ties to the
+// lower index.
+__device__ __forceinline__ void row_radix_select(const float* sc, int64_t n, int k, int key_bits, int32_t* out) {
+  __shared__ int hist[256];
+  __shared__ int s_sel[2];
+  __shared__ int s_part[34];
+  uint32_t prefix, pmask;
+  int remaining;
+  auto key_of = [sc](int64_t i) { return score_key(sc[i]); };
+  radix_threshold(key_of, n, k, key_bits, hist, s_sel, &prefix, &pmask, &remaining);
+  ordered_take(key_of, [](int64_t i) { return static_cast<int32_t>(i); }, n, prefix, pmask, remaining, s_part,
+               out);
 }
 
 // One workgroup (1024 threads) selects the top-k of one query row.
 __global__ void __launch_bounds__(1024) topk_radix_kernel(IndexParams P, int key_bits) {
-  __shared__ int hist[256];
-  __shared__ int cnt[17];
-  __shared__ uint32_t s_prefix;
-  __shared__ int s_remaining;
   const int b = blockIdx.y, t = blockIdx.x;
-  const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t n = visible(query_pos(P, b, t), P.m, P.cap);
   const size_t row = static_cast<size_t>(b) * P.T + t;
-  const float* sc = P.ws + row * P.n_stride;
   int32_t* out = P.idx + row * P.k;
+  if (n <= P.k) {
+    for (int64_t j = threadIdx.x; j < P.k; j += blockDim.x) out[j] = j < n ? static_cast<int32_t>(j) : -1;
+    return;
+  }
+  row_radix_select(P.ws + row * P.n_stride, n, P.k, key_bits, out);
+}
+
+// ---------------------------------------------------------------------------
+// decode top-k across workgroups: the scan kernel has already added every
+// score's top-11-bit bin to ghist; here the threshold bin of each row is
+// found, each CAND_CHUNK-entry chunk compacts its entries at or above it in
+// index order, and one workgroup per row puts the chunks in order and
+// selects exactly among the candidates.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) topk_zero_kernel(IndexParams P) {
+  const int b = blockIdx.x;
+  for (int i = threadIdx.x; i < HIST_BINS; i += blockDim.x) P.ghist[static_cast<size_t>(b) * HIST_BINS + i] = 0;
+  if (threadIdx.x == 0) P.ccount[b] = 0;
+}
+
+// The bin of the k-th largest key of row b (all 256 threads get it).
+__device__ int threshold_bin(const int* gh, int k, int* s_part) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int PER = HIST_BINS / 256;  // bins per thread, thread 0 owns the top bins
+  int c[PER], tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { c[j] = gh[HIST_BINS - 1 - (tid * PER + j)]; tot += c[j]; }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) s_part[w] = incl;
+  __syncthreads();
+  int before = 0;
+  for (int i = 0; i < w; ++i) before += s_part[i];
+  incl += before;
+  const int excl = incl - tot;
+  __syncthreads();
+  if (excl < k && incl >= k) {
+    int cum = excl;
+    for (int j = 0; j < PER; ++j) {
+      if (cum + c[j] >= k) { s_part[4] = HIST_BINS - 1 - (tid * PER + j); break; }
+      cum += c[j];
+    }
+  }
+  __syncthreads();
+  return s_part[4];
+}
+
+__global__ void __launch_bounds__(256) topk_cand_kernel(IndexParams P) {
+  constexpr int PERW = CAND_CHUNK / 4;  // entries per wave
+  constexpr int IT = PERW / 64;
+  __shared__ int s_part[8];
+  __shared__ uint32_t s_ck[CAND_CHUNK];
+  __shared__ int32_t s_ci[CAND_CHUNK];
+  __shared__ int s_wc[4];
+  __shared__ int s_base;
+  const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int64_t n = visible(query_pos(P, b, 0), P.m, P.cap);
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * CAND_CHUNK;
+  if (n <= P.k || c0 >= n) return;
+  const int64_t c1 = c0 + CAND_CHUNK < n ? c0 + CAND_CHUNK : n;
+  const float* sc = P.ws + static_cast<size_t>(b) * P.n_stride;
+  const int64_t e0 = c0 + wv * PERW + lane;
+  float v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) v[it] = e0 + it * 64 < c1 ? sc[e0 + it * 64] : 0.0f;
+  const int bstar = threshold_bin(P.ghist + static_cast<size_t>(b) * HIST_BINS, P.k, s_part);
+  // each wave compacts its quarter of the chunk, in index order, into its
+  // own LDS segment
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int cnt = 0;
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int64_t s = e0 + it * 64;
+    const uint32_t key = score_key(v[it]);
+    const bool take = s < c1 && static_cast<int>(key >> (32 - HIST_BITS)) >= bstar;
+    const unsigned long long m = __ballot(take);
+    if (take) {
+      const int pos = wv * PERW + cnt + __popcll(m & below);
+      s_ck[pos] = key;
+      s_ci[pos] = static_cast<int32_t>(s);
+    }
+    cnt += __popcll(m);
+  }
+  if (lane == 0) s_wc[wv] = cnt;
+  __syncthreads();
+  const int p1 = s_wc[0], p2 = p1 + s_wc[1], p3 = p2 + s_wc[2], tot = p3 + s_wc[3];
+  const size_t cj = static_cast<size_t>(b) * P.nch + blockIdx.x;
+  if (tid == 0) {
+    const int base = tot ? atomicAdd(&P.ccount[b], tot) : 0;  // one global atomic per chunk
+    s_base = base;
+    P.cbase[cj] = base;
+    P.ccnt[cj] = tot;
+  }
+  __syncthreads();
+  const int gbase = s_base;
+  const size_t cb0 = static_cast<size_t>(b) * CAND_CAP;
+  for (int i = tid; i < tot; i += 256) {
+    if (gbase + i >= CAND_CAP) break;
+    const int w = (i >= p1) + (i >= p2) + (i >= p3);
+    const int src = w * PERW + i - (w == 0 ? 0 : w == 1 ? p1 : w == 2 ? p2 : p3);
+    P.ckey[cb0 + gbase + i] = s_ck[src];
+    P.cidx[cb0 + gbase + i] = s_ci[src];
+  }
+}
+
+__global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key_bits) {
+  constexpr int CPT = NCH_MAX / 1024;  // chunks per thread
+  __shared__ uint32_t s_key[CAND_CAP];
+  __shared__ int32_t s_idx[CAND_CAP];
+  __shared__ int s_pre[NCH_MAX];
+  __shared__ int s_cb[NCH_MAX];
+  __shared__ int hist[256];
+  __shared__ int s_sel[2];
+  __shared__ int s_part[34];
+  const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int64_t n = visible(query_pos(P, b, 0), P.m, P.cap);
+  int32_t* out = P.idx + static_cast<size_t>(b) * P.k;
   if (n <= P.k) {
     for (int64_t j = tid; j < P.k; j += nt) out[j] = j < n ? static_cast<int32_t>(j) : -1;
     return;
   }
-  uint32_t prefix = 0, pmask = 0;
-  int remaining = P.k;
-  for (int shift = 24; shift >= 32 - key_bits; shift -= 8) {
-    for (int i = tid; i < 256; i += nt) hist[i] = 0;
-    __syncthreads();
-    for (int64_t s = tid; s < n; s += nt) {
-      uint32_t key = score_key(sc[s]);
-      if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int cum = 0, bin = 255;
-      for (; bin > 0; --bin) {
-        if (cum + hist[bin] >= remaining) break;
-        cum += hist[bin];
-      }
-      s_prefix = prefix | (static_cast<uint32_t>(bin) << shift);
-      s_remaining = remaining - cum;
-    }
-    __syncthreads();
-    prefix = s_prefix;
-    remaining = s_remaining;
-    pmask |= 255u << shift;
+  // where each chunk's candidates go in index order: prefix of the chunk
+  // counts (their sum is the row's candidate count)
+  const int nch = static_cast<int>((n + CAND_CHUNK - 1) / CAND_CHUNK);
+  const size_t rb = static_cast<size_t>(b) * P.nch;
+  int cc[CPT], loc = 0;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int j = tid * CPT + u;
+    cc[u] = j < nch ? P.ccnt[rb + j] : 0;
+    if (j < nch) s_cb[j] = P.cbase[rb + j];
+    loc += cc[u];
   }
-  // keys above the threshold prefix are taken; among keys equal to it (on the
-  // examined bits) the `remaining` lowest indices are taken.
-  int taken_eq = 0, written = 0;
-  for (int64_t base = 0; base < n; base += nt) {
-    const int64_t s = base + tid;
-    uint32_t key = s < n ? (score_key(sc[s]) & pmask) : 0u;
-    bool gt = s < n && key > prefix;
-    bool eq = s < n && key == prefix;
-    int eq_tot, take_tot;
-    int eq_rank = block_prefix(eq, cnt, &eq_tot);
-    bool take = gt || (eq && taken_eq + eq_rank < remaining);
-    int pos = block_prefix(take, cnt, &take_tot);
-    if (take) out[written + pos] = static_cast<int32_t>(s);
-    taken_eq += eq_tot;
-    written += take_tot;
+  int pre, unused, c, unused_tot;
+  block_scan2(loc, 0, s_part, &pre, &unused, &c, &unused_tot);
+  if (c > CAND_CAP) {  // too many candidates: exact select over the whole row
+    row_radix_select(P.ws + static_cast<size_t>(b) * P.n_stride, n, P.k, key_bits, out);
+    return;
   }
-  for (int j = written + tid; j < P.k; j += nt) out[j] = -1;
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int j = tid * CPT + u;
+    if (j < nch) s_pre[j] = pre;
+    pre += cc[u];
+  }
+  __syncthreads();
+  const size_t cb0 = static_cast<size_t>(b) * CAND_CAP;
+  for (int i = tid; i < c; i += nt) {
+    const int32_t s = P.cidx[cb0 + i];
+    const int j = s / CAND_CHUNK;
+    const int d = s_pre[j] + (i - s_cb[j]);
+    s_key[d] = P.ckey[cb0 + i];
+    s_idx[d] = s;
+  }
+  __syncthreads();
+  uint32_t prefix, pmask;
+  int remaining;
+  auto key_of = [](int64_t i) { return s_key[i]; };
+  radix_threshold(key_of, c, P.k, key_bits, hist, s_sel, &prefix, &pmask, &remaining);
+  ordered_take(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, out);
 }
 
 static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
@@ -183,11 +425,22 @@ static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
   if (index_mfma_supported(P)) {
     // scores stay on chip when every row fits the fused kernel's LDS rows
     if (!P.scores_out && index_fused_prefill_ok(P, n_max)) return launch_index_fused_prefill(P, B, s);
+    const int bits = P.score_dt == CSA_BF16 ? 16 : 32;
+    if (P.ghist) {  // decode: histogram in the scan, candidates, exact final select
+      hipLaunchKernelGGL(topk_zero_kernel, dim3(B), dim3(256), 0, s, P);
+      int st = check_launch("topk_zero_kernel");
+      if (st != CSA_OK) return st;
+      if (n_max > 0 && (st = launch_index_scan(P, B, n_max, s)) != CSA_OK) return st;
+      hipLaunchKernelGGL(topk_cand_kernel, dim3(static_cast<unsigned>(P.nch), B),
+                         dim3(256), 0, s, P);
+      if ((st = check_launch("topk_cand_kernel")) != CSA_OK) return st;
+      hipLaunchKernelGGL(topk_final_kernel, dim3(B), dim3(1024), 0, s, P, bits);
+      return check_launch("topk_final_kernel");
+    }
     if (n_max > 0) {
       int st = launch_index_scan(P, B, n_max, s);
       if (st != CSA_OK) return st;
     }
-    const int bits = P.score_dt == CSA_BF16 ? 16 : 32;
     hipLaunchKernelGGL(topk_radix_kernel, dim3(P.T, B), dim3(1024), 0, s, P, bits);
     return check_launch("topk_radix_kernel");
   }
@@ -227,11 +480,22 @@ static int64_t prefill_nmax(const csa_index_desc* d, int T, int64_t pos0) {
   return n < d->capacity ? n : d->capacity;
 }
 
+static int64_t cand_chunks(int64_t cap) { return (cap + CAND_CHUNK - 1) / CAND_CHUNK; }
+
+// decode workspace after the score rows: histograms, counts, candidates,
+// per-chunk candidate bases and counts
+static size_t decode_extra_bytes(int B, int64_t cap) {
+  return static_cast<size_t>(B) * (HIST_BINS * sizeof(int) + 64 + CAND_CAP * (sizeof(uint32_t) + sizeof(int32_t)) +
+                                   2 * cand_chunks(cap) * sizeof(int));
+}
+
 size_t index_ws_bytes(const csa_index_desc* d, int op, int B, int T, int64_t pos0) {
   if (!d || B < 0 || T < 0) return 0;
   int64_t nmax = op == CSA_OP_INDEX_TOPK_DECODE ? d->capacity : prefill_nmax(d, T, pos0);
   int64_t rows = static_cast<int64_t>(B) * (op == CSA_OP_INDEX_TOPK_DECODE ? 1 : T);
-  return static_cast<size_t>(rows * stride_for(nmax) * sizeof(float)) + 256;
+  size_t bytes = static_cast<size_t>(rows * stride_for(nmax) * sizeof(float)) + 256;
+  if (op == CSA_OP_INDEX_TOPK_DECODE) bytes += decode_extra_bytes(B, d->capacity);
+  return bytes;
 }
 
 static int common_index_checks(const csa_index_desc* d, int B, const void* qI, const float* w,
@@ -299,5 +563,16 @@ extern "C" int csa_index_topk_decode(const csa_index_desc* desc, int B, const in
   P.pos0 = 0;
   P.pos_dev = pos;
   P.n_stride = stride_for(desc->capacity);
+  if (index_mfma_supported(P) && cand_chunks(desc->capacity) <= NCH_MAX) {
+    char* extra = reinterpret_cast<char*>(P.ws) + static_cast<size_t>(B) * P.n_stride * sizeof(float);
+    extra += (256 - reinterpret_cast<uintptr_t>(extra) % 256) % 256;
+    P.ghist = reinterpret_cast<int*>(extra);
+    P.ccount = P.ghist + static_cast<size_t>(B) * HIST_BINS;
+    P.ckey = reinterpret_cast<uint32_t*>(P.ccount + ((B + 15) / 16) * 16);
+    P.cidx = reinterpret_cast<int32_t*>(P.ckey + static_cast<size_t>(B) * CAND_CAP);
+    P.nch = static_cast<int>(cand_chunks(desc->capacity));
+    P.cbase = reinterpret_cast<int*>(P.cidx + static_cast<size_t>(B) * CAND_CAP);
+    P.ccnt = P.cbase + static_cast<size_t>(B) * P.nch;
+  }
   return launch_index(P, B, desc->capacity, stream);
 }

@@ -162,3 +162,25 @@ def test_k_larger_than_visible():
     got = idx.cpu().numpy()
     assert list(got[0]) == list(range(50)) + [-1] * 14
     assert list(got[1]) == list(range(63)) + [-1]
+
+
+@pytest.mark.parametrize("n_entries", [6000, 20000])
+def test_decode_all_ties_lowest_indices(n_entries):
+    """Every key equal, so every score ties: the k lowest indices are kept.
+    6000 entries fit the candidate list of the multi-workgroup decode top-k;
+    20000 overflow it and take the whole-row select."""
+    B, H, d, m, k = 2, 16, 64, 4, 1024
+    cap = n_entries
+    kc, K = key_cache("fp8", B, cap, d, m, seed=26)
+    kc.nope.copy_(kc.nope[:, :1].expand(-1, cap, -1))
+    kc.scale.fill_(0.01)
+    pos = torch.tensor([4 * n_entries - 1, 4 * (n_entries // 2)], dtype=torch.int64, device=DEV)
+    qI = synth.normal((B, H, d), "qI", 26, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((B, H), "w", 26, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "bf16", "fp8", "f32", m, cap)
+    idx = torch.empty((B, k), dtype=torch.int32, device=DEV)
+    cb.index_topk_decode(desc, kc, pos, qI, w, k, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    assert list(got[0]) == list(range(k))
+    assert list(got[1]) == list(range(k))
