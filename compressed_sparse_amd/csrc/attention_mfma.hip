@@ -180,15 +180,23 @@ __device__ __forceinline__ int slot_id(const int* s_list, int64_t r, int64_t r0,
   return DENSE ? static_cast<int>(r0 + rr) : s_list[rr];
 }
 
-// Issues the global loads of one 64-entry tile starting at slot rl.  Entry
-// ids of the nope rows are wave-uniform, so their addresses are scalar.
+// Issues the global loads of one 64-entry tile starting at slot rl.  Lane i
+// < 16 of wave w reads the id of the wave's row i from LDS once; the rows'
+// ids then come from v_readlane (wave-uniform, so the row addresses are
+// scalar) without a dependent LDS read per row.
 template <bool FP8, bool DENSE>
 __device__ __forceinline__ void load_tile(Prefetch<FP8>& pf, const AttnParams& P, const int* s_list, int64_t rl,
                                           int64_t r0, int64_t nvalid, size_t seq) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int my_id = slot_id<DENSE>(s_list, rl + w * 16 + (lane & 15), r0, nvalid);
+  int rid[2];
+#pragma unroll
+  for (int it = 0; it < 2; ++it) rid[it] = slot_id<DENSE>(s_list, rl + (it * 256 + tid) / 8, r0, nvalid);
+  int sid = 0;
+  if constexpr (FP8) sid = slot_id<DENSE>(s_list, rl + lane, r0, nvalid);
 #pragma unroll
   for (int it = 0; it < 16; ++it) {
-    const int id = __builtin_amdgcn_readfirstlane(slot_id<DENSE>(s_list, rl + w * 16 + it, r0, nvalid));
+    const int id = __builtin_amdgcn_readlane(my_id, it);
     if constexpr (!FP8) {
       const bf16_t* row = static_cast<const bf16_t*>(P.nope) + (seq + id) * DN;
       pf.nope[it] = *reinterpret_cast<const u32x4*>(row + lane * 8);
@@ -201,11 +209,10 @@ __device__ __forceinline__ void load_tile(Prefetch<FP8>& pf, const AttnParams& P
 #pragma unroll
   for (int it = 0; it < 2; ++it) {
     const int q = it * 256 + tid;
-    const int id = slot_id<DENSE>(s_list, rl + q / 8, r0, nvalid);
-    pf.rope[it] = *reinterpret_cast<const u32x4*>(rbase + (seq + id) * DRP + (q % 8) * 8);
+    pf.rope[it] = *reinterpret_cast<const u32x4*>(rbase + (seq + rid[it]) * DRP + (q % 8) * 8);
   }
   if constexpr (FP8) {
-    if (tid < TILE) pf.scale = static_cast<const float*>(P.scale)[seq + slot_id<DENSE>(s_list, rl + tid, r0, nvalid)];
+    if (tid < TILE) pf.scale = static_cast<const float*>(P.scale)[seq + sid];
   }
 }
 
@@ -516,7 +523,7 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
     const int64_t per = dense ? P.cap : P.k;
     dim3 grid(P.T, 1, B);
     if (fp8) dense ? launch_one<true, true, false>(P, grid, s, 1, per, nullptr) : launch_one<true, false, false>(P, grid, s, 1, per, nullptr);
-    else dense ? launch_one<false, true, false>(P, grid, s, 1, per, nullptr) : launch_one<false, false, false>(P, grid, s, 1, per, nullptr);
+    else launch_attn_bf16(P, dense, grid, s, 1, per, nullptr);
     return check_launch("attn_mfma_kernel");
   }
   const int64_t count = dense ? P.cap : P.k;
@@ -533,7 +540,7 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   float* part = static_cast<float*>(P.ws);
   dim3 grid(splits, 1, B);
   if (fp8) dense ? launch_one<true, true, true>(P, grid, s, splits, per, part) : launch_one<true, false, true>(P, grid, s, splits, per, part);
-  else dense ? launch_one<false, true, true>(P, grid, s, splits, per, part) : launch_one<false, false, true>(P, grid, s, splits, per, part);
+  else launch_attn_bf16(P, dense, grid, s, splits, per, part);
   int st = check_launch("attn_mfma_kernel");
   if (st != CSA_OK) return st;
   const dim3 mg(NH, B);
