@@ -55,7 +55,7 @@ __device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
     const unsigned long long act = __ballot(active);
     if (act == 0ull) return;
     const int leader = __ffsll(static_cast<long long>(act)) - 1;
-    const int lb = __shfl(bin, leader);
+    const int lb = __builtin_amdgcn_readlane(bin, leader);
     const unsigned long long same = __ballot(active && bin == lb);
     if (lane == leader) atomicAdd(&hist[lb], __popcll(same));
     if (bin == lb) active = false;

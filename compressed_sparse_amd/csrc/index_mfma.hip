@@ -81,7 +81,7 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 
 // Wave-level radix select of the top-k of row[0..n) (n > k) and ordered
 // compaction of the selected indices into out[0..k).
-__device__ void wave_select(const float* row, int n, int k, int key_bits, int* hist, int32_t* out) {
+__device__ void wave_radix_select(const float* row, int n, int k, int key_bits, int* hist, int32_t* out) {
   const int lane = threadIdx.x & 63;
   uint32_t prefix = 0, pmask = 0;
   int remaining = k;
@@ -139,10 +139,171 @@ __device__ void wave_select(const float* row, int n, int k, int key_bits, int* h
   for (int j = written + lane; j < k; j += 64) out[j] = -1;
 }
 
+constexpr int SEL_BINS = 1024;  // value-range bins of the fused select
+constexpr int SEL_CB = 256;     // threshold-bin entries ranked directly
+
+// Exact top-k of row[0..n) (n > k) by one wave, ascending indices, ties to
+// the lower index.  The row's scores fall into SEL_BINS equal-width bins
+// between its min and max (a monotone map, so a bin holds a contiguous key
+// range and equal scores share a bin); the histogram finds the bin B that
+// holds the k-th largest score.  Bins above B are taken whole; the entries
+// of B are ranked by (key descending, index ascending) against each other
+// and the best k - |bins above B| taken; one last pass writes the indices
+// in order.  A threshold bin with more than SEL_CB entries (heavy ties)
+// falls back to the radix select.
+__device__ void wave_select(const float* row, int n, int k, int key_bits, int* hist, int* cidx, uint32_t* ckey,
+                            int* crank, int32_t* out) {
+  const int lane = threadIdx.x & 63;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  // lane l reads entries 4(base + l) .. +3 of each 256-entry step (the row
+  // is 16-byte aligned and padded past n)
+  auto quad = [&](int base) { return *reinterpret_cast<const float4*>(row + 4 * (base + lane)); };
+  float mn = INFINITY, mx = -INFINITY;
+  for (int base = 0; 4 * base < n; base += 64) {
+    const float4 v = quad(base);
+    const int s = 4 * (base + lane);
+    if (s < n) { mn = fminf(mn, v.x); mx = fmaxf(mx, v.x); }
+    if (s + 1 < n) { mn = fminf(mn, v.y); mx = fmaxf(mx, v.y); }
+    if (s + 2 < n) { mn = fminf(mn, v.z); mx = fmaxf(mx, v.z); }
+    if (s + 3 < n) { mn = fminf(mn, v.w); mx = fmaxf(mx, v.w); }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    mn = fminf(mn, __shfl_xor(mn, o));
+    mx = fmaxf(mx, __shfl_xor(mx, o));
+  }
+  const float span = mx - mn;
+  float scale = span > 0.0f ? static_cast<float>(SEL_BINS) / span : 0.0f;
+  if (!(scale < 3.0e38f)) scale = 0.0f;  // degenerate range: one bin, radix fallback
+  auto bin_of = [&](float v) { return min(SEL_BINS - 1, static_cast<int>((v - mn) * scale)); };
+  for (int i = lane; i < SEL_BINS; i += 64) hist[i] = 0;
+  wave_lds_sync();
+  for (int base = 0; 4 * base < n; base += 64) {
+    const float4 v = quad(base);
+    const int s = 4 * (base + lane);
+    if (s < n) atomicAdd(&hist[bin_of(v.x)], 1);
+    if (s + 1 < n) atomicAdd(&hist[bin_of(v.y)], 1);
+    if (s + 2 < n) atomicAdd(&hist[bin_of(v.z)], 1);
+    if (s + 3 < n) atomicAdd(&hist[bin_of(v.w)], 1);
+  }
+  wave_lds_sync();
+  // lane l owns bins SEL_BINS-1-16l .. SEL_BINS-16-16l (descending)
+  constexpr int PER = SEL_BINS / 64;
+  int c[PER], tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) { c[j] = hist[SEL_BINS - 1 - PER * lane - j]; tot += c[j]; }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  int bsel = -1, above = 0;
+  if (incl - tot < k && incl >= k) {
+    int cum = incl - tot;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (bsel < 0 && cum + c[j] >= k) { bsel = SEL_BINS - 1 - PER * lane - j; above = cum; }
+      cum += c[j];
+    }
+  }
+  const unsigned long long who = __ballot(bsel >= 0);
+  const int src = __ffsll(static_cast<long long>(who)) - 1;
+  const int B = __builtin_amdgcn_readlane(bsel, src);
+  const int rem = k - __builtin_amdgcn_readlane(above, src);  // entries of bin B to take
+  // the entries of bin B in index order: lanes before this one, then this
+  // lane's earlier elements
+  int cnt = 0;
+  for (int base = 0; 4 * base < n; base += 64) {
+    const float4 v = quad(base);
+    const int s = 4 * (base + lane);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    bool in[4];
+    int mine = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) { in[u] = s + u < n && bin_of(vv[u]) == B; mine += in[u]; }
+    int before = 0, total = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned long long m = __ballot(in[u]);
+      before += __popcll(m & below);
+      total += __popcll(m);
+    }
+    int pos = cnt + before;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      if (in[u]) {
+        if (pos < SEL_CB) { cidx[pos] = s + u; ckey[pos] = order_key(vv[u]); }
+        ++pos;
+      }
+    }
+    cnt += total;
+  }
+  if (cnt > SEL_CB) {
+    wave_lds_sync();
+    wave_radix_select(row, n, k, key_bits, hist, out);
+    return;
+  }
+  wave_lds_sync();
+  // rank of entry e among bin B: entries with a larger key, or an equal key
+  // and a lower index (cidx is ascending, so the lower position)
+  for (int e = lane; e < cnt; e += 64) {
+    const uint32_t ke = ckey[e];
+    int r = 0;
+    for (int f = 0; f < cnt; ++f) {
+      const uint32_t kf = ckey[f];
+      r += (kf > ke || (kf == ke && f < e)) ? 1 : 0;
+    }
+    crank[e] = r;
+  }
+  wave_lds_sync();
+  // ordered output: bins above B, and the entries of B ranked below rem
+  int written = 0, seen = 0;
+  for (int base = 0; 4 * base < n; base += 64) {
+    const float4 v = quad(base);
+    const int s = 4 * (base + lane);
+    const float vv[4] = {v.x, v.y, v.z, v.w};
+    int bn[4];
+    bool inb[4];
+    int bbefore = 0, btotal = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      bn[u] = s + u < n ? bin_of(vv[u]) : -1;
+      inb[u] = bn[u] == B;
+      const unsigned long long m = __ballot(inb[u]);
+      bbefore += __popcll(m & below);
+      btotal += __popcll(m);
+    }
+    int jb = seen + bbefore;
+    bool take[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      take[u] = bn[u] > B;
+      if (inb[u]) { take[u] = crank[jb] < rem; ++jb; }
+    }
+    int tbefore = 0, ttotal = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const unsigned long long m = __ballot(take[u]);
+      tbefore += __popcll(m & below);
+      ttotal += __popcll(m);
+    }
+    int pos = written + tbefore;
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (take[u]) out[pos++] = s + u;
+    written += ttotal;
+    seen += btotal;
+  }
+}
+
 template <bool KFP8>
 __global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams P) {
   __shared__ float srow[QG][FUSED_NMAX];
-  __shared__ int hist[QG][256];
+  __shared__ int hist[QG][SEL_BINS];
+  __shared__ int cidx[QG][SEL_CB];
+  __shared__ uint32_t ckey[QG][SEL_CB];
+  __shared__ int crank[QG][SEL_CB];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int b = blockIdx.y;
   const int t0 = blockIdx.x * QG;
@@ -183,28 +344,33 @@ __global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams
     }
     const size_t seq = static_cast<size_t>(b) * P.cap;
     const int nblocks = (nmax + 31) / 32;
-    for (int cb = w; cb < nblocks; cb += 4) {
+    // raw key rows of one 32-entry block (lane: entry lane%32, dims
+    // (lane/32)*32 .. +32), clamped to the last visible entry: branch-free
+    auto loadk = [&](int cb, u32x4 (&kr)[4], float& ksc) {
+      const int s = min(cb * 32 + (lane & 31), nmax - 1);
+      if (KFP8) {
+        const uint8_t* kp = static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
+        kr[0] = *reinterpret_cast<const u32x4*>(kp);
+        kr[1] = *reinterpret_cast<const u32x4*>(kp + 16);
+        ksc = static_cast<const float*>(P.kscale)[seq + s];
+      } else {
+        const bf16_t* kp = static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const u32x4*>(kp + ks * 8);
+        ksc = 1.0f;
+      }
+    };
+    auto compute = [&](int cb, const u32x4 (&raw)[4], float ksc) {
       const int s = cb * 32 + (lane & 31);
       u32x4 kr[4];
-      float ksc = 1.0f;
-      if (s < nmax) {
-        if (KFP8) {
-          const uint8_t* kp = static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
-          const u32x4 c0 = *reinterpret_cast<const u32x4*>(kp);
-          const u32x4 c1 = *reinterpret_cast<const u32x4*>(kp + 16);
-          kr[0] = fp8x8_to_bf16(c0[0], c0[1]);
-          kr[1] = fp8x8_to_bf16(c0[2], c0[3]);
-          kr[2] = fp8x8_to_bf16(c1[0], c1[1]);
-          kr[3] = fp8x8_to_bf16(c1[2], c1[3]);
-          ksc = static_cast<const float*>(P.kscale)[seq + s];
-        } else {
-          const bf16_t* kp = static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
-#pragma unroll
-          for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const u32x4*>(kp + ks * 8);
-        }
+      if (KFP8) {
+        kr[0] = fp8x8_to_bf16(raw[0][0], raw[0][1]);
+        kr[1] = fp8x8_to_bf16(raw[0][2], raw[0][3]);
+        kr[2] = fp8x8_to_bf16(raw[1][0], raw[1][1]);
+        kr[3] = fp8x8_to_bf16(raw[1][2], raw[1][3]);
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kr[ks] = u32x4{0u, 0u, 0u, 0u};
+        for (int ks = 0; ks < 4; ++ks) kr[ks] = raw[ks];
       }
       f32x16 acc[2];
 #pragma unroll
@@ -231,6 +397,24 @@ __global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams
         if (P.score_dt == CSA_BF16) val = round_bf16(val);
         if (s < nvis(q)) srow[q][s] = val;
       }
+    };
+    // the next block's rows load while this block is multiplied (a block
+    // past the end re-reads the last one; no load sits under a branch)
+    u32x4 ka[4], kb[4];
+    float sa, sb;
+    int cb = w;
+    if (cb < nblocks) {
+      loadk(cb, ka, sa);
+      while (true) {
+        loadk(min(cb + 4, nblocks - 1), kb, sb);
+        compute(cb, ka, sa);
+        cb += 4;
+        if (cb >= nblocks) break;
+        loadk(min(cb + 4, nblocks - 1), ka, sa);
+        compute(cb, kb, sb);
+        cb += 4;
+        if (cb >= nblocks) break;
+      }
     }
   }
   __syncthreads();
@@ -243,7 +427,7 @@ __global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams
     for (int j = lane; j < P.k; j += 64) out[j] = j < n ? j : -1;
     return;
   }
-  wave_select(srow[q], n, P.k, P.score_dt == CSA_BF16 ? 16 : 32, hist[q], out);
+  wave_select(srow[q], n, P.k, P.score_dt == CSA_BF16 ? 16 : 32, hist[q], cidx[q], ckey[q], crank[q], out);
 }
 
 // ---------------------------------------------------------------------------
