@@ -19,7 +19,9 @@ The decode workloads (CSA decode at batch 32 / 131072 context, HCA decode at
 batch 16 / 2^20 context, the CSA + HCA pair at batch 4 / 2^20 context) are
 reported under "secondary": consecutive decode steps captured in one HIP
 graph, timed over replays, with their algorithmic HBM bytes per step against
-the 8 TB/s HBM peak.
+the 8 TB/s HBM peak.  So is HCA prefill at 2^20 context: its last (hardest)
+8192-token chunk, compressor + dense attention over all 8192 entries, with
+the attention's algorithmic flops against the BF16 MFMA peak.
 """
 import argparse
 import hashlib
@@ -45,8 +47,8 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_mfma_csa_prefill_L32768_traffic.txt")
-ATTN_SRC = os.path.join(ROOT, "compressed_sparse_amd", "csrc", "attention_mfma.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_csa_prefill_L32768_traffic.txt")
+ATTN_SRC = os.path.join(ROOT, "compressed_sparse_amd", "csrc", "attention_bf16.hip")
 
 
 def measured_traffic():
@@ -152,8 +154,7 @@ def time_graph(step_fn, n_steps, replays=20, warmup=3):
     return a.elapsed_time(b) / (replays * n_steps)
 
 
-def secondary_decode(n_steps=8):
-    out = []
+def csa_decode_line(n_steps=8):
     w = synth.CSA_DECODE_B32_128K
     log(f"setup {w.name}")
     lay = path.CsaLayer(w, w.batch, w.tokens // w.m + n_steps)
@@ -162,14 +163,14 @@ def secondary_decode(n_steps=8):
     xs = [lay.decode_inputs([w.tokens + i] * w.batch) for i in range(n_steps)]
     ms = time_graph(lambda i: lay.decode_step(xs[i], o), n_steps)
     by = decode_bytes_csa(w, w.tokens // w.m, w.batch)
-    out.append({"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
-                "tokens_per_s": w.batch / (ms * 1e-3),
-                "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "algorithmic_bytes_per_step": by}})
-    del lay, o, xs
-    torch.cuda.empty_cache()
+    return {"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
+            "tokens_per_s": w.batch / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes_per_step": by}}
 
+
+def hca_decode_line(n_steps=8):
     w = synth.HCA_DECODE_B16_1M
     log(f"setup {w.name}")
     lay = path.HcaLayer(w, w.batch, w.tokens // w.m + n_steps)
@@ -178,14 +179,14 @@ def secondary_decode(n_steps=8):
     xs = [lay.decode_inputs([w.tokens + i] * w.batch) for i in range(n_steps)]
     ms = time_graph(lambda i: lay.decode_step(xs[i], o), n_steps)
     by = decode_bytes_hca(w, w.tokens // w.m, w.batch)
-    out.append({"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
-                "tokens_per_s": w.batch / (ms * 1e-3),
-                "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "algorithmic_bytes_per_step": by}})
-    del lay, o, xs
-    torch.cuda.empty_cache()
+    return {"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
+            "tokens_per_s": w.batch / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes_per_step": by}}
 
+
+def pair_decode_lines(n_steps=8):
     wc, wh = synth.PAIR_CSA_DECODE_B4_1M, synth.PAIR_HCA_DECODE_B4_1M
     log(f"setup {wc.name} + {wh.name}")
     lc = path.CsaLayer(wc, wc.batch, wc.tokens // wc.m + n_steps)
@@ -203,17 +204,71 @@ def secondary_decode(n_steps=8):
     ms = time_graph(pair, n_steps)
     by_c = decode_bytes_csa(wc, wc.tokens // wc.m, wc.batch)
     by = by_c + decode_bytes_hca(wh, wh.tokens // wh.m, wh.batch)
-    out.append({"workload": wc.name, "metric": "CSA layer decode us/step (whole batch)", "value": ms_c * 1e3,
-                "unit": "us", "roofline": {"bound": "hbm", "achieved": by_c / (ms_c * 1e-3) / 1e9,
-                                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                           "frac": by_c / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                           "algorithmic_bytes_per_step": by_c}})
-    out.append({"workload": wc.name + " + " + wh.name, "metric": "CSA+HCA layer pair decode us/step",
-                "value": ms * 1e3, "unit": "us",
-                "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                             "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                             "algorithmic_bytes_per_step": by}})
+    return [{"workload": wc.name, "metric": "CSA layer decode us/step (whole batch)", "value": ms_c * 1e3,
+             "unit": "us", "roofline": {"bound": "hbm", "achieved": by_c / (ms_c * 1e-3) / 1e9,
+                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                        "frac": by_c / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                        "algorithmic_bytes_per_step": by_c}},
+            {"workload": wc.name + " + " + wh.name, "metric": "CSA+HCA layer pair decode us/step",
+             "value": ms * 1e3, "unit": "us",
+             "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                          "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                          "algorithmic_bytes_per_step": by}}]
+
+
+def secondary_lines():
+    out = [csa_decode_line()]
+    torch.cuda.empty_cache()
+    out.append(hca_decode_line())
+    torch.cuda.empty_cache()
+    out.extend(pair_decode_lines())
+    torch.cuda.empty_cache()
+    out.append(secondary_hca_prefill())
     return out
+
+def secondary_hca_prefill(steps=5):
+    """The last 8192-token chunk of a 2^20-token HCA prefill: compress the
+    chunk's tokens and run dense attention for its 8192 queries over the
+    8192 entries of the whole context (inputs resident in HBM)."""
+    w = synth.HCA_PREFILL_1M
+    chunk = w.chunk
+    c = w.tokens // chunk - 1
+    log(f"setup {w.name}")
+    lay = path.HcaLayer(w, 1, w.tokens // w.m)
+    lay.prefill_context(w.tokens)
+    tok = synth.token_chunk(w, 0, c, chunk, 0, "cuda")
+    x = {k: v[None].contiguous() for k, v in tok.items()}
+    q = synth.query_chunk(w, 0, c, chunk, 0, "cuda", with_index=False)["q"][None].contiguous()
+    o = torch.empty((1, chunk, w.heads, w.d_nope), dtype=synth.TORCH_DTYPE[w.out_dtype], device="cuda")
+    pos0 = c * chunk
+
+    def step(ev=None):
+        cb.compress_prefill(lay.kv, pos0, x["a"], x["za"], lay.prm["Ba"])
+        if ev is not None:
+            ev[0].record()
+        cb.dense_attn_prefill(lay.adesc, lay.kv, pos0, q, w.tau, o)
+        if ev is not None:
+            ev[1].record()
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(evs[i])
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    attn_ms = float(np.mean([e0.elapsed_time(e1) for e0, e1 in evs]))
+    pairs = int(np.minimum((np.arange(pos0, pos0 + chunk) + 1) // w.m, w.tokens // w.m).sum())
+    flops = 2.0 * pairs * w.heads * (w.c + w.d_nope)
+    ach = flops / (attn_ms * 1e-3) / 1e12
+    return {"workload": w.name + " (last chunk)", "metric": "HCA prefill tokens/s (chunk of 8192 at 2^20 context)",
+            "value": chunk / (ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": ms,
+            "roofline": {"bound": "mfma", "kernel": "dense attention prefill", "achieved": ach,
+                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                         "algorithmic_flop_per_launch": flops, "avg_launch_ms": attn_ms}}
 
 
 def main():
@@ -225,6 +280,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
+    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill"],
+                    help="run just this secondary workload and print its line(s) (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X; "
@@ -235,6 +292,11 @@ def main():
         sys.exit(1)
     if args.copy_calib:
         copy_calibration()
+    if args.only:
+        fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
+              "hca-prefill": secondary_hca_prefill}[args.only]
+        print(json.dumps(fn()), flush=True)
+        return
     w = synth.CSA_PREFILL_BF16_32K
     log(f"setup {w.name}")
     st = path.CsaPrefill(w)
@@ -272,7 +334,7 @@ def main():
         "config": {"workload": w.name, "batch": 1, "seq_len": w.tokens, "heads": w.heads,
                    "kv_dims": [w.d_nope, w.d_rope], "m": w.m, "topk": w.topk,
                    "indexer": [w.idx_heads, w.idx_dim]},
-        "roofline": {"bound": "mfma", "kernel": "attn_mfma_kernel (sparse attention prefill)",
+        "roofline": {"bound": "mfma", "kernel": "attn_bf16_kernel (sparse attention prefill)",
                      "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": achieved / PEAK_BF16_TFLOPS, "traffic": measured_traffic(),
                      "algorithmic_flop_per_launch": flops, "avg_launch_ms": attn_ms},
@@ -283,7 +345,7 @@ def main():
     if not args.no_secondary:
         del st
         torch.cuda.empty_cache()
-        out["secondary"] = secondary_decode()
+        out["secondary"] = secondary_lines()
     print(json.dumps(out), flush=True)
 
 
