@@ -27,8 +27,9 @@ struct AttnParams {
 bool mfma_attn_supported(const AttnParams& P);
 int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s);
 size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k);
-// BF16-cache kernel of the MFMA path; part != NULL writes split partials.
-void launch_attn_bf16(const AttnParams& P, bool dense, dim3 grid, hipStream_t s, int splits, int64_t per,
-                      float* part);
+// BF16-cache kernel of the MFMA path over B sequences (T queries each, or
+// `splits` entry ranges of `per` entries when part != NULL, which then
+// receives the split partials).
+void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, float* part);
 
 }  // namespace csa

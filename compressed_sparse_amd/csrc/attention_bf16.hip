@@ -3,28 +3,38 @@
 // §1.1, §1.2; [读完这篇] §三 CSA 步骤三 (standard attention over the selected
 // entries, one KV shared by all heads).
 //
-// One workgroup (8 waves, two per SIMD so that one wave's softmax and LDS
-// waits overlap the other's MFMAs) owns one query and a range of its entry
-// list, 64 entries per tile.  Per tile the work is S^T = K Q^T (64 x 64 x
-// 576) and O^T += V^T P^T (512 x 64 x 64):
+// A work item is one query (prefill) or one range of a sequence's entries
+// (split decode).  The grid is persistent, one 4-wave workgroup per compute
+// unit, one wave per SIMD with the whole 512-register file, so that each
+// wave keeps its query fragments, its output accumulators and a queue of
+// LDS operand reads in flight.  Items run 64 entries per tile; per tile the
+// work is S^T = K Q^T (64 x 64 x 576) and O^T += V^T P^T (512 x 64 x 64):
 //
-//  * entry rows go HBM/L2 -> LDS by direct loads (global_load_lds_dwordx4),
-//    no VGPR staging, into two tile buffers used in turn: tile j+1 loads
-//    while tile j is multiplied.  Rows are unpadded; the 16-byte chunks of a
-//    row are XOR-swizzled by row so that the MFMA operand reads of 16
-//    consecutive rows (and the transposing V reads) hit distinct banks;
-//  * wave w = (ep, hq) computes S^T for entries 32ep.. x heads 16hq..
-//    (v_mfma_f32_16x16x32_bf16) with the query's B fragments (its 16 heads,
-//    all 576 dims, RoPE applied) held in registers, then that block's
-//    softmax; P^T goes through LDS;
-//  * for O^T (v_mfma_f32_32x32x16_bf16) wave w owns value dims 64w.. for all
-//    64 heads, so each V element is read from LDS once per tile.
+//  * entry rows go HBM/L2 -> LDS by direct loads (buffer_load_dwordx4 ...
+//    lds), no VGPR staging, into two tile buffers used in turn: tile j+1
+//    loads while tile j is multiplied, its loads spread over tile j's MFMAs.  Rows are unpadded; their 16-byte chunks
+//    are XOR-swizzled by row so that MFMA operand reads and transposing V
+//    reads hit distinct banks;
+//  * wave w = (eh, hh) computes the 32 x 32 block of S^T for entries 32eh..
+//    and heads 32hh.. (v_mfma_f32_32x32x16_bf16) with the query's B
+//    fragments (its 32 heads, all 576 dims, RoPE applied) in registers, so
+//    each entry row is read from LDS by two waves only; the two entry halves
+//    of a head agree on the softmax maximum through LDS; P^T goes through
+//    LDS;
+//  * for O^T (v_mfma_f32_32x32x16_bf16) wave w owns value dims 128w.. for
+//    all 64 heads, so each V element is read from LDS once per tile.
 //
 // The softmax running max moves only when a tile's max exceeds it by more
 // than 2^8 (P stays below 256); the waves that own a head's O^T columns
 // rescale them by the factor the softmax waves publish in LDS.
+//
+// While a workgroup finishes an item it already holds the next item's index
+// list, has the next item's first tile in flight and reloads its query
+// fragments behind the last S^T MFMAs.  The finished
+// item's output is staged in the free tile buffer and stored, as whole 1 KB
+// rows, once the next item's first tile has landed, so the stores drain
+// while that tile is multiplied.
 #include <cmath>
-#include <utility>
 
 #include "attention.hpp"
 
@@ -37,7 +47,6 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
 
 constexpr int NH = 64;
 constexpr int DN = 512;
@@ -50,6 +59,10 @@ constexpr int ROPE_OFF = TILE * NROW;      // the RoPE rows follow the 64 non-Ro
 constexpr int KBUF = TILE * (NROW + RROW); // 73,728 B per tile buffer
 constexpr int PROW = TILE + 8;             // padded P^T row (bf16 elements)
 constexpr int MAX_LIST = 1024;
+constexpr int NW = 4;                      // waves per workgroup
+constexpr int NT = 64 * NW;
+constexpr int QS = CW / 16;                // k-steps of S^T (16 dims each)
+constexpr int SPF = 6;                     // S^T A operands in flight
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
@@ -57,20 +70,24 @@ struct Theta {
   double t[DRP / 2];  // base^(-2p/d_rope)
 };
 
-// 16-byte chunk c of row r sits at chunk c ^ swz(r).  LDS serves 128 B (32
-// banks) per cycle: 8 consecutive rows read at one chunk (an MFMA A operand)
-// and the 4 rows x 2 chunks of a transposing V read then fall on distinct
-// 16-byte bank groups.
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 3) + ((r >> 2) & 1); }
-__device__ __forceinline__ int swz_rope(int r) { return swz(r); }
+// 16-byte chunk c of row r sits at chunk c ^ swz(r).  The LDS has 64 banks
+// (256 B); a 128-bit read is served in four passes of 16 lanes (lanes with
+// equal bit 5 and equal parity of bits 2..4), a 64-bit read (also the
+// transposing one) in two passes of 32 lanes (equal bit 5).  With these
+// swizzles the 16 rows of one pass of an S^T A-operand read (rows that
+// differ in bits 0, 1, 2 and 4) and the 4 rows x 4 half-chunks of one pass
+// of a transposing V read land on distinct banks.  RoPE rows are 128 B
+// (8 chunks), two rows per bank line.
+__device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + 2 * ((r >> 2) & 1) + ((r >> 4) & 1); }
+__device__ __forceinline__ int swz_rope(int r) { return 4 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1) + ((r >> 4) & 1); }
 
 // Workgroup barrier for LDS data: this wave's LDS accesses complete, then
-// s_barrier.  Loads in flight (the next tile) are not waited for.
+// s_barrier.  Global loads in flight (the next tile) are not waited for.
 __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// Waits until this wave's direct-to-LDS tile loads (its only vector memory
-// operations in the tile loop) have landed.
-__device__ __forceinline__ void wait_tile_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Waits until all of this wave's vector memory operations have completed
+// (its direct-to-LDS tile loads, query loads and earlier stores).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -79,7 +96,7 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Row of S^T within a wave's 32 held in register v of a 32x32 MFMA result.
+// Row of a 32x32 MFMA result held in register v of this lane.
 __device__ __forceinline__ int acc_row(int v, int lane) { return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); }
 
 template <bool DENSE>
@@ -88,39 +105,174 @@ __device__ __forceinline__ int slot_id(const int* s_list, int64_t r, int64_t r0,
   return DENSE ? static_cast<int>(r0 + rr) : s_list[rr];
 }
 
-constexpr int NW = 8;              // waves per workgroup
-constexpr int ROWS_W = TILE / NW;  // tile rows each wave loads
+// Direct-to-LDS loads of one 64-entry tile into buf: wave w loads rows
+// 16w .. 16w+15.  Load it < 16 is non-RoPE row 16w + it (one 1 KB
+// instruction, lane L fetching the chunk that belongs at slot L); loads 16
+// and 17 are RoPE rows 16w .. 16w+7 and 16w+8 .. 16w+15 (8 rows x 8 chunks
+// each).  my_id: lane i < 16 holds the entry id of row 16w + i.
+template <bool DENSE>
+__device__ __forceinline__ int tile_ids(const int* s_list, int64_t rl, int64_t r0, int64_t nvalid) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  return slot_id<DENSE>(s_list, rl + 16 * w + (lane & 15), r0, nvalid);
+}
 
-// Issues the direct-to-LDS loads of the 64-entry tile at list slot rl into
-// buf: wave w loads rows 8w .. 8w+7 (one 1 KB instruction per non-RoPE row,
-// lane L fetching the chunk that belongs at slot L) and their RoPE rows (one
-// instruction of 8 rows x 8 chunks).
+// Buffer descriptor (raw, byte-addressed, 32-bit data format) over
+// [base, base + bytes).  The loads go through the buffer path so that the
+// compiler keeps counting LDS reads in order around them.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
+                                           0x00020000);
+}
+
+__device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, int my_id, size_t seq, int it) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane offsets are recomputed per load, not kept live
+  const int w = threadIdx.x >> 6;
+  if (it < 16) {
+    const int id = __builtin_amdgcn_readlane(my_id, it);
+    const int r = 16 * w + it;
+    // scalar row base, lane offset of the chunk that belongs at slot `lane`
+    const uint8_t* row = static_cast<const uint8_t*>(P.nope) + (seq + static_cast<size_t>(id)) * NROW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(row, NROW), (lds_void*)(buf + r * NROW), 16, 16 * (lane ^ swz(r)),
+                                             0, 0, 0);
+  } else {
+    const int h = it - 16;
+    const int r = 16 * w + 8 * h + (lane >> 3);
+    const int idr = __shfl(my_id, 8 * h + (lane >> 3));
+    const uint8_t* base = static_cast<const uint8_t*>(P.rope) + seq * RROW;
+    const uint64_t span = static_cast<uint64_t>(P.cap) * RROW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span < 0xFFFFFFFFull ? static_cast<uint32_t>(span) : 0xFFFFFFFFu),
+                                             (lds_void*)(buf + ROPE_OFF + (16 * w + 8 * h) * RROW), 16,
+                                             idr * RROW + 16 * ((lane & 7) ^ swz_rope(r)), 0, 0, 0);
+  }
+}
+
+constexpr int NLOAD = 18;  // loads per wave per tile
+
+// All loads of the tile at list slot rl, back to back.
 template <bool DENSE>
 __device__ __forceinline__ void issue_tile(uint8_t* buf, const AttnParams& P, const int* s_list, int64_t rl,
                                            int64_t r0, int64_t nvalid, size_t seq) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int my_id = slot_id<DENSE>(s_list, rl + w * ROWS_W + (lane & (ROWS_W - 1)), r0, nvalid);
-  const uint8_t* nope = static_cast<const uint8_t*>(P.nope);
-  const bf16_t* rope = static_cast<const bf16_t*>(P.rope);
+  const int my_id = tile_ids<DENSE>(s_list, rl, r0, nvalid);
 #pragma unroll
-  for (int it = 0; it < ROWS_W; ++it) {
-    const int id = __builtin_amdgcn_readlane(my_id, it);
-    const int r = w * ROWS_W + it;
-    // scalar row base + 32-bit lane offset (swz(r) depends on `it` only)
-    const uint8_t* row = nope + (seq + static_cast<size_t>(id)) * NROW;
-    __builtin_amdgcn_global_load_lds(row + static_cast<uint32_t>(16 * (lane ^ swz(r))), buf + r * NROW, 16, 0, 0);
-  }
-  const int r = w * ROWS_W + (lane >> 3);
-  const int idr = __shfl(my_id, lane >> 3);
-  const bf16_t* src = rope + (seq + idr) * DRP + 8 * ((lane & 7) ^ swz_rope(r));
-  __builtin_amdgcn_global_load_lds(src, buf + ROPE_OFF + w * ROWS_W * RROW, 16, 0, 0);
+  for (int it = 0; it < NLOAD; ++it) issue_load(buf, P, my_id, seq, it);
 }
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
+// One work item: query t of sequence b, entries [r0, r1) of its list (or of
+// the cache, dense) among the n visible ones.
+struct Item {
+  int b, t, split;
+  int64_t pos, n, r0, r1;
+  size_t qrow, seq;
+};
 
 template <bool DENSE, bool SPLIT>
-__global__ void __launch_bounds__(512, 1)
-attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* part) {
+__device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int splits, int64_t per_split) {
+  Item I;
+  I.split = SPLIT ? static_cast<int>(it % splits) : 0;
+  const int64_t bt = SPLIT ? it / splits : it;
+  I.t = SPLIT ? 0 : static_cast<int>(bt % P.T);
+  I.b = static_cast<int>(SPLIT ? bt : bt / P.T);
+  // decode (split) items take the sequence's position, prefill ones pos0 + t;
+  // kept in scalar registers
+  if (SPLIT) {
+    const int64_t v = P.pos_dev[I.b];
+    I.pos = static_cast<int64_t>(
+        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)))) << 32) |
+        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v & 0xFFFFFFFF))));
+  } else {
+    I.pos = P.pos0 + I.t;
+  }
+  int64_t n = I.pos < 0 ? 0 : (I.pos + 1) / P.m;
+  I.n = n > P.cap ? P.cap : n;
+  const int64_t count = DENSE ? I.n : P.k;
+  I.r0 = static_cast<int64_t>(I.split) * per_split;
+  I.r1 = I.r0 + per_split < count ? I.r0 + per_split : count;
+  I.qrow = (static_cast<size_t>(I.b) * P.T + I.t) * NH;
+  I.seq = static_cast<size_t>(I.b) * P.cap;
+  return I;
+}
+
+// Item processed by workgroup g of nwg in round r.  Workgroup g runs on XCD
+// g % 8; when nwg is a multiple of 8 each XCD takes nwg / 8 consecutive
+// items per round, so neighbouring queries (whose lists overlap) share an L2.
+__device__ __forceinline__ int64_t item_of(int g, int64_t r, int nwg) {
+  if (nwg % 8) return r * nwg + g;
+  return r * nwg + static_cast<int64_t>(g % 8) * (nwg / 8) + g / 8;
+}
+
+// The item's list entries r0 + tid + 256u, u < 4 (-1 past r1).
+__device__ __forceinline__ void load_list(const AttnParams& P, const Item& I, int tid, int32_t (&lr)[4]) {
+  const int32_t* list = P.idx + (static_cast<size_t>(I.b) * P.T + I.t) * P.k;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int64_t r = u * NT + tid;
+    lr[u] = r < I.r1 - I.r0 ? list[I.r0 + r] : -1;
+  }
+}
+
+// Compacts the valid ids (0 <= id < n) of lr into s_list in list order and
+// returns their count.  Two workgroup barriers.
+__device__ __forceinline__ int compact_list(const int32_t (&lr)[4], int64_t n, int* s_list, int (&s_cnt)[4][NW]) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  bool ok[4];
+  unsigned long long bal[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    ok[u] = lr[u] >= 0 && lr[u] < n;
+    bal[u] = __ballot(ok[u]);
+    if (lane == 0) s_cnt[u][w] = __popcll(bal[u]);
+  }
+  lds_sync();
+  const unsigned long long below = (1ull << lane) - 1ull;
+  int base = 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+      before += i < w ? s_cnt[u][i] : 0;
+      tot += s_cnt[u][i];
+    }
+    if (ok[u]) s_list[base + before + __popcll(bal[u] & below)] = lr[u];
+    base += tot;
+  }
+  lds_sync();
+  return __builtin_amdgcn_readfirstlane(base);
+}
+
+// B fragment k-step s of S^T (32x32x16) for this lane: head 32hh + lane%32,
+// dims 16s + 8(lane/32) .. +8.
+__device__ __forceinline__ bf16x8 load_qs(const AttnParams& P, size_t qrow, int hh, int s) {
+  const int lane = threadIdx.x & 63;
+  const bf16_t* qh = static_cast<const bf16_t*>(P.q) + (qrow + 32 * hh + (lane & 31)) * CW + 8 * (lane >> 5);
+  return *reinterpret_cast<const bf16x8*>(qh + 16 * s);
+}
+
+// Turns the RoPE k-steps (dims 512..575, pairs (2p, 2p+1)) by position pos.
+__device__ __forceinline__ void rope_q(const Theta& th, int64_t pos, bf16x8 (&qf)[QS]) {
+  const int half = (threadIdx.x & 63) >> 5;
+#pragma unroll
+  for (int s = DN / 16; s < QS; ++s) {
+    u32x4 raw = __builtin_bit_cast(u32x4, qf[s]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int p = 8 * (s - DN / 16) + 4 * half + i;
+      const double ang = static_cast<double>(pos) * th.t[p];
+      const float red = static_cast<float>(ang - rint(ang * 0.15915494309189535) * 6.283185307179586);
+      const float sn = __sinf(red), cs = __cosf(red);
+      const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
+      const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
+      raw[i] = pack2_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
+    }
+    qf[s] = __builtin_bit_cast(bf16x8, raw);
+  }
+}
+
+template <bool DENSE, bool SPLIT>
+__global__ void __launch_bounds__(NT, 1)
+attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* part, int64_t nitems, int nbatch) {
   __shared__ __attribute__((aligned(16))) uint8_t kb0[KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t kb1[KBUF];
   __shared__ __attribute__((aligned(16))) bf16_t pbuf[NH * PROW];
@@ -128,262 +280,361 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   __shared__ float s_xchg[2][NH];
   __shared__ float s_alpha[NH];
   __shared__ float s_m[NH];
-  __shared__ int s_cnt[NW];
-  __shared__ int s_mv[4];
+  __shared__ int s_cnt[4][NW];
+  __shared__ int s_mv[2];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int ep = w & 1, hq = w >> 1;  // S^T role: entries 32ep.., heads 16hq..
-  const int b = blockIdx.z;
-  const int t = SPLIT ? 0 : blockIdx.x;
-  const int split = SPLIT ? blockIdx.x : 0;
-  const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
-  int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
-  if (n > P.cap) n = P.cap;
-  const int64_t count = DENSE ? n : P.k;
-  const int64_t r0 = static_cast<int64_t>(split) * per_split;
-  int64_t r1 = r0 + per_split;
-  if (r1 > count) r1 = count;
-  const size_t qrow = (static_cast<size_t>(b) * P.T + t) * NH;
-  const size_t seq = static_cast<size_t>(b) * P.cap;
-  const int head = 16 * hq + (lane & 15);  // this lane's head in the S^T role
-  const int g4 = lane >> 4;                // k-slice / row group of the 16x16 MFMA
+  const int eh = w & 1, hh = w >> 1;       // S^T role: entries 32eh.., heads 32hh..
+  const int head = 32 * hh + (lane & 31);  // this lane's head in the S^T role
+  const int half = lane >> 5;
+  const int g = blockIdx.x, nwg = gridDim.x;
 
-  // the valid ids of this workgroup's list range, compacted into s_list
-  int64_t nvalid;
+  int64_t round = 0;
+  int64_t it = item_of(g, 0, nwg);
+  if (it >= nitems) return;
+  Item I = make_item<DENSE, SPLIT>(P, it, splits, per_split);
+  int nvalid;
   if (DENSE) {
-    nvalid = r1 > r0 ? r1 - r0 : 0;
+    nvalid = static_cast<int>(I.r1 > I.r0 ? I.r1 - I.r0 : 0);
   } else {
-    const int32_t* list = P.idx + (static_cast<size_t>(b) * P.T + t) * P.k;
-    int base = 0;
-    for (int64_t c0 = 0; c0 < r1 - r0; c0 += 64 * NW) {
-      const int64_t r = c0 + tid;
-      const int64_t sid = r < r1 - r0 ? static_cast<int64_t>(list[r0 + r]) : -1;
-      const bool ok = sid >= 0 && sid < n;
-      const unsigned long long bal = __ballot(ok);
-      if (lane == 0) s_cnt[w] = __popcll(bal);
-      lds_sync();
-      int before = 0, tot = 0;
-#pragma unroll
-      for (int i = 0; i < NW; ++i) { before += i < w ? s_cnt[i] : 0; tot += s_cnt[i]; }
-      if (ok) s_list[base + before + __popcll(bal & ((1ull << lane) - 1ull))] = static_cast<int>(sid);
-      base += tot;
-      lds_sync();
-    }
-    nvalid = base;
+    int32_t lr[4];
+    load_list(P, I, tid, lr);
+    nvalid = compact_list(lr, I.n, s_list, s_cnt);
   }
-  const int ntiles = static_cast<int>((nvalid + TILE - 1) / TILE);
-  const int nval = static_cast<int>(nvalid);
-  if (ntiles > 0) issue_tile<DENSE>(kb0, P, s_list, 0, r0, nvalid, seq);
-
-  // B fragments of S^T (16x16x32): lane = head 16hq + lane%16, k-step s holds
-  // dims 32s + 8(lane/16) .. +8; the RoPE steps turned at `pos`
-  constexpr int QS = CW / 32;
+  int ntiles = (nvalid + TILE - 1) / TILE;
+  int par = 0;  // buffer of the next tile: kb0 / kb1
+  if (ntiles > 0) issue_tile<DENSE>(kb0, P, s_list, 0, I.r0, nvalid, I.seq);
   bf16x8 qf[QS];
-  {
-    const bf16_t* qh = static_cast<const bf16_t*>(P.q) + (qrow + head) * CW + 8 * g4;
 #pragma unroll
-    for (int s = 0; s < QS; ++s) qf[s] = *reinterpret_cast<const bf16x8*>(qh + 32 * s);
-#pragma unroll
-    for (int s = DN / 32; s < QS; ++s) {
-      u32x4 raw = __builtin_bit_cast(u32x4, qf[s]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = 16 * (s - DN / 32) + 4 * g4 + i;
-        const double ang = static_cast<double>(pos) * th.t[p];
-        const float red = static_cast<float>(ang - rint(ang * 0.15915494309189535) * 6.283185307179586);
-        const float sn = __sinf(red), cs = __cosf(red);
-        const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
-        const float x1 = bf16_to_f32(static_cast<bf16_t>(raw[i] >> 16));
-        raw[i] = pack2_bf16(x0 * cs - x1 * sn, x0 * sn + x1 * cs);
-      }
-      qf[s] = __builtin_bit_cast(bf16x8, raw);
-    }
-  }
+  for (int s = 0; s < QS; ++s) qf[s] = load_qs(P, I.qrow, hh, s);
 
-  // LDS byte offsets of the S^T A operand (16x16x32): M-block mb rows
-  // 32ep + 16mb + lane%16, k-step s chunk 4s + lane/16
-  int offA[2][4], offR[2][2];
+  // LDS byte offsets of the S^T A operand (32x32x16): row 32eh + lane%32,
+  // k-step s chunk 2s + lane/32.  The swizzle touches the low four chunk
+  // bits, so k-steps 8 apart differ by a constant 256 B.
+  int offA[8], offR[4];
+  {
+    const int r = 32 * eh + (lane & 31);
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    const int r = 32 * ep + 16 * mb + (lane & 15);
+    for (int i = 0; i < 8; ++i) offA[i] = r * NROW + 16 * ((2 * i + half) ^ swz(r));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) offA[mb][i] = r * NROW + 16 * ((4 * i + g4) ^ swz(r));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) offR[mb][i] = ROPE_OFF + r * RROW + 16 * ((4 * i + g4) ^ swz_rope(r));
+    for (int i = 0; i < 4; ++i) offR[i] = ROPE_OFF + r * RROW + 16 * ((2 * i + half) ^ swz_rope(r));
   }
   // V^T operand (transposing reads): within a 16-lane group, result lane i
   // slot s is element i%4 of the 8 bytes addressed by lane 4s + i/4.  Lane
   // L = 16G + 4s + q reads entry 8(G/2) + s (+4 for the second read) of the
-  // k-step, value dims 64w + 32mb + 16(G%2) + 4q .. +4.
+  // 16-entry k-step, value dims 128w + 32mb + 16(G%2) + 4q .. +4.  Rows of
+  // odd k-steps (bit 4 set) have chunk bit 0 flipped: byte offset ^ 16.
   const int G = lane >> 4, sq = (lane >> 2) & 3, q4 = lane & 3;
   const int rowA = 8 * (G >> 1) + sq, rowB = rowA + 4;
-  int offV[2][2];
+  int offV[4][2];
 #pragma unroll
-  for (int mb = 0; mb < 2; ++mb) {
-    // 16-byte chunk 8w + 4mb + 2(G%2) + q/2: high bits w/2, low four bits swizzled
-    const int c = 8 * (w & 1) + 4 * mb + 2 * (G & 1) + (q4 >> 1);
-    offV[mb][0] = rowA * NROW + 16 * (16 * (w >> 1) + (c ^ swz(rowA))) + 8 * (q4 & 1);
-    offV[mb][1] = rowB * NROW + 16 * (16 * (w >> 1) + (c ^ swz(rowB))) + 8 * (q4 & 1);
+  for (int mb = 0; mb < 4; ++mb) {
+    // 16-byte chunk 16w + 4mb + 2(G%2) + q/2: high bits w, low four bits swizzled
+    const int c = 4 * mb + 2 * (G & 1) + (q4 >> 1);
+    offV[mb][0] = rowA * NROW + 16 * (16 * w + (c ^ swz(rowA))) + 8 * (q4 & 1);
+    offV[mb][1] = rowB * NROW + 16 * (16 * w + (c ^ swz(rowB))) + 8 * (q4 & 1);
   }
-  const bf16_t* pop = pbuf + (lane & 31) * PROW + 8 * (lane >> 5);  // + 32 nb rows: heads 32nb..
-
+  const int pop = (lane & 31) * PROW + 8 * half;  // P^T B operand (elements); + 32 nb rows: heads 32nb..
   const float lscale = P.scale_qk * LOG2E;
-  f32x16 oacc[2][2];
-#pragma unroll
-  for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) oacc[mb][nb] = f32x16{};
-  float m_run = -INFINITY, l_part = 0.0f;
+  bool staged = false;  // an output waits in the free tile buffer
+  size_t staged_qrow = 0;
 
-  auto tile = [&](auto parity, int j) {
-    constexpr int PAR = decltype(parity)::value;
-    const uint8_t* cur = PAR ? kb1 : kb0;
-    uint8_t* nxt = PAR ? kb0 : kb1;
-    wait_tile_loads();
-    lds_sync();  // tile j in LDS; every wave done with tile j-1 (its buffer, pbuf, s_alpha)
-    if (j + 1 < ntiles) issue_tile<DENSE>(nxt, P, s_list, static_cast<int64_t>(j + 1) * TILE, r0, nvalid, seq);
-
-    // --- S^T = K Q^T: entries 32ep + 16mb.. x heads 16hq.. ------------------
-    f32x4 sacc[2] = {f32x4{}, f32x4{}};
+  // Stores the staged output rows (16 per wave) from `buf`: row h chunk c
+  // sits at chunk c ^ (h & 15).
+  auto store_staged = [&](const uint8_t* buf) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));  // lane offsets recomputed per call
 #pragma unroll
-    for (int s = 0; s < QS; ++s) {
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        const bf16x8 a = s < DN / 32 ? lds_b128(cur + offA[mb][s & 3] + 256 * (s >> 2))
-                                     : lds_b128(cur + offR[mb][s - DN / 32]);
-        sacc[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[s], sacc[mb], 0, 0, 0);
-      }
-    }
-    // --- softmax: lane holds entries 32ep + 16mb + 4(lane/16) + v of its head
-    const int vend = nval - j * TILE;  // entries of this tile below it are real
-    float mx = -INFINITY;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int e = 32 * ep + 16 * mb + 4 * g4 + v;
-        sacc[mb][v] = e < vend ? sacc[mb][v] * lscale : -INFINITY;
-        mx = fmaxf(mx, sacc[mb][v]);
-      }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    if (lane < 16) s_xchg[ep][head] = mx;
-    lds_sync();
-    mx = fmaxf(mx, s_xchg[ep ^ 1][head]);
-    const bool move = mx > m_run + 8.0f;
-    const bool rescale = move && m_run != -INFINITY;
-    const float alpha = rescale ? exp2f(m_run - mx) : 1.0f;
-    if (move) m_run = mx;
-    l_part *= alpha;
-    if (ep == 0) {
-      if (lane < 16) s_alpha[head] = alpha;
-      const bool any = __ballot(rescale) != 0ull;
-      if (lane == 0) s_mv[hq] = any ? 1 : 0;
-    }
-    float psum = 0.0f;
-#pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
-      const float p0 = __builtin_amdgcn_exp2f(sacc[mb][0] - m_run), p1 = __builtin_amdgcn_exp2f(sacc[mb][1] - m_run);
-      const float p2 = __builtin_amdgcn_exp2f(sacc[mb][2] - m_run), p3 = __builtin_amdgcn_exp2f(sacc[mb][3] - m_run);
-      psum += (p0 + p1) + (p2 + p3);
-      *reinterpret_cast<uint2*>(pbuf + head * PROW + 32 * ep + 16 * mb + 4 * g4) =
-          make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
-    }
-    l_part += psum;
-    lds_sync();
-
-    // --- O^T += V^T P^T: value dims 64w.. x all 64 heads ----------------------
-    if (s_mv[0] | s_mv[1] | s_mv[2] | s_mv[3]) {
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) {
-        const float a = s_alpha[32 * nb + (lane & 31)];
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) oacc[mb][nb] *= a;
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < TILE / 16; ++ks) {
-      bf16x8 pb[2];
-#pragma unroll
-      for (int nb = 0; nb < 2; ++nb) pb[nb] = *reinterpret_cast<const bf16x8*>(pop + 32 * nb * PROW + 16 * ks);
-#pragma unroll
-      for (int mb = 0; mb < 2; ++mb) {
-        typedef __attribute__((address_space(3))) v4s lds_v4s;
-        const v4s x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + offV[mb][0] + 16 * ks * NROW));
-        const v4s y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + offV[mb][1] + 16 * ks * NROW));
-        const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-        for (int nb = 0; nb < 2; ++nb)
-          oacc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb[nb], oacc[mb][nb], 0, 0, 0);
-      }
+    for (int i = 0; i < 16; ++i) {
+      const int h = 16 * w + i;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(buf + h * NROW + 16 * (ln ^ (h & 15)));
+      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.o) + (staged_qrow + h) * DN + 8 * ln) = v;
     }
   };
-  for (int j = 0; j < ntiles; j += 2) {
-    tile(std::integral_constant<int, 0>{}, j);
-    if (j + 1 < ntiles) tile(std::integral_constant<int, 1>{}, j + 1);
-  }
 
-  // --- finish: denominators and maxima to LDS, then each wave its O^T ----
-  l_part += __shfl_xor(l_part, 16);
-  l_part += __shfl_xor(l_part, 32);
-  lds_sync();
-  if (lane < 16) s_xchg[ep][head] = l_part;
-  if (ep == 0 && lane < 16) s_m[head] = m_run;
-  lds_sync();
-  // O^T block (mb, nb): lane = head 32nb + lane%32, register v = value dim
-  // 64w + 32mb + acc_row(v)
+  while (true) {
+    // the next item: its list is read now, compacted and its first tile
+    // issued at the start of this item's last tile, its query loaded behind
+    // this item's last S^T MFMAs
+    const int64_t itn = item_of(g, round + 1, nwg);
+    const bool has_next = itn < nitems;
+    const Item In = make_item<DENSE, SPLIT>(P, has_next ? itn : it, splits, per_split);
+    int32_t lrn[4] = {-1, -1, -1, -1};
+    if (!DENSE && has_next) load_list(P, In, tid, lrn);
+    int nvalid_n = 0;
+    bool next_started = false;
+
+    rope_q(th, I.pos, qf);
+    f32x16 oacc[4][2];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
-    const int h = 32 * nb + (lane & 31);
-    const float ltot = s_xchg[0][h] + s_xchg[1][h];
-    if (!SPLIT) {
-      const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
-      bf16_t* out = static_cast<bf16_t*>(P.o) + (qrow + h) * DN + 64 * w;
+    for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const f32x16& o = oacc[mb][nb];
-          const uint32_t lo = pack2_bf16(o[4 * jq] * inv, o[4 * jq + 1] * inv);
-          const uint32_t hi2 = pack2_bf16(o[4 * jq + 2] * inv, o[4 * jq + 3] * inv);
-          *reinterpret_cast<uint2*>(out + 32 * mb + jq * 8 + (lane >> 5) * 4) = make_uint2(lo, hi2);
+      for (int nb = 0; nb < 2; ++nb) oacc[mb][nb] = f32x16{};
+    float m_run = -INFINITY, l_part = 0.0f;
+
+    // next item's list compacted into s_list, its first tile issued into buf
+    auto start_next = [&](uint8_t* buf) {
+      nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, In.n, s_list, s_cnt);
+      if (nvalid_n > 0) issue_tile<DENSE>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq);
+      next_started = true;
+    };
+
+    // one tile.  The buffers come in as restrict pointers: the tile read,
+    // the tile being loaded and P^T never overlap, and saying so lets the
+    // compiler keep LDS reads (the transposing ones included) from waiting on
+    // the direct-to-LDS loads in flight.
+    auto tile = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bf16_t* __restrict__ pbuf_r,
+                    int j) {
+      const bool last = j + 1 == ntiles;
+      wait_vmem();
+      lds_sync();  // tile j in LDS; every wave done with tile j-1 (its buffer, pbuf, s_alpha)
+      if (staged) {  // the previous item's output, staged in nxt
+        store_staged(nxt);
+        lds_sync();
+        staged = false;
+      }
+      // The next tile's loads (this item's tile j+1, or the next item's first
+      // tile) are spread over this tile's MFMAs: a wave that issues them back
+      // to back stalls until the memory pipeline takes them.  Every tile
+      // issues all of them, without branches in the MFMA loops; with no next
+      // tile they re-read the current item's first entry into the free buffer.
+      int my_id = 0;
+      size_t lseq = I.seq;
+      if (!last) {
+        my_id = tile_ids<DENSE>(s_list, static_cast<int64_t>(j + 1) * TILE, I.r0, nvalid);
+      } else if (has_next) {
+        nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, In.n, s_list, s_cnt);
+        next_started = true;
+        if (nvalid_n > 0) {
+          my_id = tile_ids<DENSE>(s_list, 0, In.r0, nvalid_n);
+          lseq = In.seq;
         }
-      if (P.lse && w == 0 && lane < 32)
-        P.lse[qrow + h] = ltot > 0.0f ? (s_m[h] + log2f(ltot)) * LN2 : -INFINITY;
-    } else {
-      // partial: [B][splits][NH][DN] O, then [B][splits][NH][2] (max, sum)
-      const size_t slot = static_cast<size_t>(b) * splits + split;
-      float* po = part + slot * (NH * DN) + static_cast<size_t>(h) * DN + 64 * w;
+      }
+
+      // --- S^T = K Q^T: entries 32eh.. x heads 32hh.. ------------------------
+      // A operands run SPF k-steps ahead of the MFMAs (scheduling barriers
+      // keep that order); in the item's last tile the query fragments are
+      // reloaded for the next item right after their last use
+      auto aop = [&](int s) -> bf16x8 {
+        return s < DN / 16 ? lds_b128(cur + offA[s & 7] + 256 * (s >> 3)) : lds_b128(cur + offR[s - DN / 16]);
+      };
+      f32x16 sacc = f32x16{};
+      {
+        bf16x8 ring[SPF];
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int s = 0; s < SPF; ++s) ring[s] = aop(s);
 #pragma unroll
-        for (int jq = 0; jq < 4; ++jq) {
-          const f32x16& o = oacc[mb][nb];
-          *reinterpret_cast<float4*>(po + 32 * mb + jq * 8 + (lane >> 5) * 4) =
-              make_float4(o[4 * jq], o[4 * jq + 1], o[4 * jq + 2], o[4 * jq + 3]);
+        for (int s = 0; s < QS; ++s) {
+          const bf16x8 a = ring[s % SPF];
+          if (s + SPF < QS) ring[s % SPF] = aop(s + SPF);
+          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
+          if (s % 7 == 3) issue_load(nxt, P, my_id, lseq, s / 7);  // loads 0..4
+          __builtin_amdgcn_sched_barrier(0);
         }
-      if (w == 0 && lane < 32) {
-        float* pml = part + static_cast<size_t>(gridDim.z) * splits * (NH * DN) + slot * (2 * NH);
-        pml[2 * h] = s_m[h];
-        pml[2 * h + 1] = ltot;
+      }
+      if (last && has_next) {
+#pragma unroll
+        for (int s = 0; s < QS; ++s) qf[s] = load_qs(P, In.qrow, hh, s);
+      }
+
+      // --- softmax: lane holds entries 32eh + acc_row(v) of its head ---------
+      const int vend = nvalid - j * TILE;  // entries of this tile below it are real
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int e = 32 * eh + acc_row(v, lane);
+        sacc[v] = e < vend ? sacc[v] * lscale : -INFINITY;
+        mx = fmaxf(mx, sacc[v]);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (lane < 32) s_xchg[eh][head] = mx;
+      // loads 5..8 (and 9..12 below) stall the wave where it waits anyway
+#pragma unroll
+      for (int q = 5; q < 9; ++q) issue_load(nxt, P, my_id, lseq, q);
+      lds_sync();
+      mx = fmaxf(mx, s_xchg[eh ^ 1][head]);
+      const bool move = mx > m_run + 8.0f;
+      const bool rescale = move && m_run != -INFINITY;
+      const float alpha = rescale ? exp2f(m_run - mx) : 1.0f;
+      if (move) m_run = mx;
+      l_part *= alpha;
+      if (eh == 0) {
+        if (lane < 32) s_alpha[head] = alpha;
+        const bool any = __ballot(rescale) != 0ull;
+        if (lane == 0) s_mv[hh] = any ? 1 : 0;
+      }
+      float psum = 0.0f;
+#pragma unroll
+      for (int jq = 0; jq < 4; ++jq) {
+        const float p0 = __builtin_amdgcn_exp2f(sacc[4 * jq] - m_run);
+        const float p1 = __builtin_amdgcn_exp2f(sacc[4 * jq + 1] - m_run);
+        const float p2 = __builtin_amdgcn_exp2f(sacc[4 * jq + 2] - m_run);
+        const float p3 = __builtin_amdgcn_exp2f(sacc[4 * jq + 3] - m_run);
+        psum += (p0 + p1) + (p2 + p3);
+        *reinterpret_cast<uint2*>(pbuf_r + head * PROW + 32 * eh + 8 * jq + 4 * half) =
+            make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+      }
+      l_part += psum;
+#pragma unroll
+      for (int q = 9; q < 13; ++q) issue_load(nxt, P, my_id, lseq, q);
+      lds_sync();
+
+      // --- O^T += V^T P^T: value dims 128w.. x all 64 heads ---------------------
+      if (s_mv[0] | s_mv[1]) {
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float a = s_alpha[32 * nb + (lane & 31)];
+#pragma unroll
+          for (int mb = 0; mb < 4; ++mb) oacc[mb][nb] *= a;
+        }
+      }
+      // 16 steps (ks, mb): V^T operands run PPF steps ahead of the MFMAs,
+      // P^T operands one k-step ahead
+      {
+        typedef __attribute__((address_space(3))) v4s lds_v4s;
+        constexpr int PPF = 4;
+        auto vop = [&](int t, int i) -> v4s {
+          const int ks = t >> 2, mb = t & 3;
+          const int fl = (ks & 1) ? 16 : 0;
+          return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + (offV[mb][i] ^ fl) + 16 * ks * NROW));
+        };
+        auto pop_ks = [&](int ks, int nb) -> bf16x8 {
+          return *reinterpret_cast<const bf16x8*>(pbuf_r + pop + 32 * nb * PROW + 16 * ks);
+        };
+        v4s vx[PPF], vy[PPF];
+        bf16x8 pbr[2][2];
+        pbr[0][0] = pop_ks(0, 0);
+        pbr[0][1] = pop_ks(0, 1);
+#pragma unroll
+        for (int t = 0; t < PPF; ++t) {
+          vx[t] = vop(t, 0);
+          vy[t] = vop(t, 1);
+        }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          const int ks = t >> 2;
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vx[t % PPF], vy[t % PPF], 0, 1, 2, 3, 4, 5, 6, 7));
+          if (t + PPF < 16) {
+            vx[t % PPF] = vop(t + PPF, 0);
+            vy[t % PPF] = vop(t + PPF, 1);
+          }
+          if ((t & 3) == 0 && ks + 1 < 4) {
+            pbr[(ks + 1) & 1][0] = pop_ks(ks + 1, 0);
+            pbr[(ks + 1) & 1][1] = pop_ks(ks + 1, 1);
+          }
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb)
+            oacc[t & 3][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[ks & 1][nb], oacc[t & 3][nb], 0, 0, 0);
+          // loads 13..17
+          if (t % 3 == 1) issue_load(nxt, P, my_id, lseq, 13 + t / 3);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    };
+    for (int j = 0; j < ntiles; ++j) {
+      tile(par ? kb1 : kb0, par ? kb0 : kb1, pbuf, j);
+      par ^= 1;
+    }
+
+    // --- finish: denominators and maxima to LDS, then each wave its O^T ----
+    l_part += __shfl_xor(l_part, 32);
+    lds_sync();  // every wave done with the last tile: its buffer is free
+    if (lane < 32) s_xchg[eh][head] = l_part;
+    if (eh == 0 && lane < 32) s_m[head] = m_run;
+    lds_sync();
+    uint8_t* stage = par ? kb0 : kb1;  // not the buffer of the next item's first tile
+    // O^T block (mb, nb): lane = head 32nb + lane%32, register v = value dim
+    // 128w + 32mb + acc_row(v)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      const int h = 32 * nb + (lane & 31);
+      const float ltot = s_xchg[0][h] + s_xchg[1][h];
+      if (!SPLIT) {
+        const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const f32x16& o = oacc[mb][nb];
+            const uint32_t lo = pack2_bf16(o[4 * jq] * inv, o[4 * jq + 1] * inv);
+            const uint32_t hi2 = pack2_bf16(o[4 * jq + 2] * inv, o[4 * jq + 3] * inv);
+            // dims 128w + 32mb + 8jq + 4half: chunk 16w + 4mb + jq, byte 8half
+            const int c = 16 * w + 4 * mb + jq;
+            *reinterpret_cast<uint2*>(stage + h * NROW + 16 * (c ^ (h & 15)) + 8 * half) = make_uint2(lo, hi2);
+          }
+        if (P.lse && w == 0 && lane < 32)
+          P.lse[I.qrow + h] = ltot > 0.0f ? (s_m[h] + log2f(ltot)) * LN2 : -INFINITY;
+      } else {
+        // partial: [B][splits][NH][DN] O, then [B][splits][NH][2] (max, sum)
+        const size_t slot = static_cast<size_t>(I.b) * splits + I.split;
+        float* po = part + slot * (NH * DN) + static_cast<size_t>(h) * DN + 128 * w;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+          for (int jq = 0; jq < 4; ++jq) {
+            const f32x16& o = oacc[mb][nb];
+            *reinterpret_cast<float4*>(po + 32 * mb + jq * 8 + half * 4) =
+                make_float4(o[4 * jq], o[4 * jq + 1], o[4 * jq + 2], o[4 * jq + 3]);
+          }
+        if (w == 0 && lane < 32) {
+          float* pml = part + static_cast<size_t>(nbatch) * splits * (NH * DN) + slot * (2 * NH);
+          pml[2 * h] = s_m[h];
+          pml[2 * h + 1] = ltot;
+        }
       }
     }
+    // the output stays staged until the next item's first tile has landed,
+    // when there is one; else it is stored now
+    const bool defer = !SPLIT && has_next && next_started && nvalid_n > 0;
+    staged_qrow = I.qrow;
+    if (!SPLIT && !defer) {
+      lds_sync();  // every wave's part of the rows written
+      store_staged(stage);
+    }
+    if (!has_next) break;
+    if (!next_started) {  // this item had no tile: start the next one now
+      wait_vmem();  // earlier loads into the free buffers have landed
+      if (par == 0) start_next(kb0);
+      else start_next(kb1);
+#pragma unroll
+      for (int s = 0; s < QS; ++s) qf[s] = load_qs(P, In.qrow, hh, s);
+    }
+    staged = defer;
+    I = In;
+    it = itn;
+    nvalid = nvalid_n;
+    ntiles = (nvalid + TILE - 1) / TILE;
+    ++round;
   }
+  wait_vmem();  // no load into this workgroup's LDS outlives it
 }
 
 }  // namespace
 
-void launch_attn_bf16(const AttnParams& P, bool dense, dim3 grid, hipStream_t s, int splits, int64_t per,
-                      float* part) {
+// One persistent workgroup per compute unit (at most one item each when the
+// items are fewer).
+void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, float* part) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  int& cu = cus[dev & 63];
+  if (cu == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+    cu = v;
+  }
   Theta th;
   for (int p = 0; p < DRP / 2; ++p) th.t[p] = std::pow(P.base, -2.0 * p / DRP);
   const bool split = part != nullptr;
+  const int64_t nitems = static_cast<int64_t>(B) * (split ? splits : P.T);
+  if (nitems <= 0) return;
+  const dim3 grid(static_cast<unsigned>(nitems < cu ? nitems : cu));
   if (dense) {
-    if (split) hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, dim3(512), 0, s, P, th, splits, per, part);
-    else hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, dim3(512), 0, s, P, th, splits, per, part);
+    if (split) hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
+    else hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
   } else {
-    if (split) hipLaunchKernelGGL((attn_bf16_kernel<false, true>), grid, dim3(512), 0, s, P, th, splits, per, part);
-    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, dim3(512), 0, s, P, th, splits, per, part);
+    if (split) hipLaunchKernelGGL((attn_bf16_kernel<false, true>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
+    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
   }
 }
 

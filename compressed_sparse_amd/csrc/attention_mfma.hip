@@ -523,7 +523,7 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
     const int64_t per = dense ? P.cap : P.k;
     dim3 grid(P.T, 1, B);
     if (fp8) dense ? launch_one<true, true, false>(P, grid, s, 1, per, nullptr) : launch_one<true, false, false>(P, grid, s, 1, per, nullptr);
-    else launch_attn_bf16(P, dense, grid, s, 1, per, nullptr);
+    else launch_attn_bf16(P, dense, B, s, 1, per, nullptr);
     return check_launch("attn_mfma_kernel");
   }
   const int64_t count = dense ? P.cap : P.k;
@@ -540,7 +540,7 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   float* part = static_cast<float*>(P.ws);
   dim3 grid(splits, 1, B);
   if (fp8) dense ? launch_one<true, true, true>(P, grid, s, splits, per, part) : launch_one<true, false, true>(P, grid, s, splits, per, part);
-  else launch_attn_bf16(P, dense, grid, s, splits, per, part);
+  else launch_attn_bf16(P, dense, B, s, splits, per, part);
   int st = check_launch("attn_mfma_kernel");
   if (st != CSA_OK) return st;
   const dim3 mg(NH, B);
