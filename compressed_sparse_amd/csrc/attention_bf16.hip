@@ -25,8 +25,9 @@
 //    all 64 heads, so each V element is read from LDS once per tile.
 //
 // The softmax running max moves only when a tile's max exceeds it by more
-// than 2^8 (P stays below 256); the waves that own a head's O^T columns
-// rescale them by the factor the softmax waves publish in LDS.
+// than 2^8 (P stays below 256); only then do the two entry halves of a head
+// exchange maxima, and the waves that own a head's O^T columns rescale them
+// by the factor the softmax waves publish in LDS.
 //
 // While a workgroup finishes an item it already holds the next item's index
 // list, has the next item's first tile in flight and reloads its query
@@ -281,7 +282,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   __shared__ float s_alpha[NH];
   __shared__ float s_m[NH];
   __shared__ int s_cnt[4][NW];
-  __shared__ int s_mv[2];
+  __shared__ int s_flag[NW];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int eh = w & 1, hh = w >> 1;       // S^T role: entries 32eh.., heads 32hh..
@@ -365,6 +366,8 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     bool next_started = false;
 
     rope_q(th, I.pos, qf);
+    // entry ids of the tile whose loads the current tile issues (read ahead)
+    int my_id_pf = ntiles > 1 ? tile_ids<DENSE>(s_list, TILE, I.r0, nvalid) : 0;
     f32x16 oacc[4][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -401,7 +404,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       int my_id = 0;
       size_t lseq = I.seq;
       if (!last) {
-        my_id = tile_ids<DENSE>(s_list, static_cast<int64_t>(j + 1) * TILE, I.r0, nvalid);
+        my_id = my_id_pf;
       } else if (has_next) {
         nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, In.n, s_list, s_cnt);
         next_started = true;
@@ -438,6 +441,13 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       }
 
       // --- softmax: lane holds entries 32eh + acc_row(v) of its head ---------
+      // P = exp2(S - m_run) with the running reference m_run of the head,
+      // which both entry halves hold alike.  While no score of the tile
+      // exceeds m_run + 8 (P < 256) no wave needs the other half's maximum,
+      // so one barrier (P^T written) serves the tile.  Otherwise (the first
+      // tile of an item, or a jump of the maximum) a wave flags it, and after
+      // that barrier all waves agree on the new reference from the maxima
+      // they published, rewrite P^T, rescale l and O^T, and meet once more.
       const int vend = nvalid - j * TILE;  // entries of this tile below it are real
       float mx = -INFINITY;
 #pragma unroll
@@ -448,39 +458,38 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (lane < 32) s_xchg[eh][head] = mx;
-      // loads 5..8 (and 9..12 below) stall the wave where it waits anyway
+      const bool bad = m_run == -INFINITY || !(mx <= m_run + 8.0f);
+      const bool wave_bad = __ballot(bad) != 0ull;
+      if (lane == 0) s_flag[w] = wave_bad ? 1 : 0;
+      auto write_p = [&]() -> float {
+        float ps = 0.0f;
 #pragma unroll
-      for (int q = 5; q < 9; ++q) issue_load(nxt, P, my_id, lseq, q);
-      lds_sync();
-      mx = fmaxf(mx, s_xchg[eh ^ 1][head]);
-      const bool move = mx > m_run + 8.0f;
-      const bool rescale = move && m_run != -INFINITY;
-      const float alpha = rescale ? exp2f(m_run - mx) : 1.0f;
-      if (move) m_run = mx;
-      l_part *= alpha;
-      if (eh == 0) {
-        if (lane < 32) s_alpha[head] = alpha;
-        const bool any = __ballot(rescale) != 0ull;
-        if (lane == 0) s_mv[hh] = any ? 1 : 0;
-      }
+        for (int jq = 0; jq < 4; ++jq) {
+          const float p0 = __builtin_amdgcn_exp2f(sacc[4 * jq] - m_run);
+          const float p1 = __builtin_amdgcn_exp2f(sacc[4 * jq + 1] - m_run);
+          const float p2 = __builtin_amdgcn_exp2f(sacc[4 * jq + 2] - m_run);
+          const float p3 = __builtin_amdgcn_exp2f(sacc[4 * jq + 3] - m_run);
+          ps += (p0 + p1) + (p2 + p3);
+          *reinterpret_cast<uint2*>(pbuf_r + head * PROW + 32 * eh + 8 * jq + 4 * half) =
+              make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+        }
+        return ps;
+      };
       float psum = 0.0f;
+      if (!wave_bad) psum = write_p();
+      // loads 5..12 stall the wave where it waits anyway
 #pragma unroll
-      for (int jq = 0; jq < 4; ++jq) {
-        const float p0 = __builtin_amdgcn_exp2f(sacc[4 * jq] - m_run);
-        const float p1 = __builtin_amdgcn_exp2f(sacc[4 * jq + 1] - m_run);
-        const float p2 = __builtin_amdgcn_exp2f(sacc[4 * jq + 2] - m_run);
-        const float p3 = __builtin_amdgcn_exp2f(sacc[4 * jq + 3] - m_run);
-        psum += (p0 + p1) + (p2 + p3);
-        *reinterpret_cast<uint2*>(pbuf_r + head * PROW + 32 * eh + 8 * jq + 4 * half) =
-            make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
-      }
-      l_part += psum;
-#pragma unroll
-      for (int q = 9; q < 13; ++q) issue_load(nxt, P, my_id, lseq, q);
+      for (int q = 5; q < 13; ++q) issue_load(nxt, P, my_id, lseq, q);
       lds_sync();
-
-      // --- O^T += V^T P^T: value dims 128w.. x all 64 heads ---------------------
-      if (s_mv[0] | s_mv[1]) {
+      if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {
+        const float mall = fmaxf(mx, s_xchg[eh ^ 1][head]);
+        const bool move = m_run == -INFINITY || mall > m_run + 8.0f;
+        const float alpha = move && m_run != -INFINITY ? exp2f(m_run - mall) : 1.0f;
+        if (move) m_run = mall;
+        l_part *= alpha;
+        if (eh == 0 && lane < 32) s_alpha[head] = alpha;
+        psum = write_p();
+        lds_sync();
 #pragma unroll
         for (int nb = 0; nb < 2; ++nb) {
           const float a = s_alpha[32 * nb + (lane & 31)];
@@ -488,6 +497,9 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
           for (int mb = 0; mb < 4; ++mb) oacc[mb][nb] *= a;
         }
       }
+      l_part += psum;
+
+      // --- O^T += V^T P^T: value dims 128w.. x all 64 heads ---------------------
       // 16 steps (ks, mb): V^T operands run PPF steps ahead of the MFMAs,
       // P^T operands one k-step ahead
       {
@@ -533,6 +545,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     };
     for (int j = 0; j < ntiles; ++j) {
       tile(par ? kb1 : kb0, par ? kb0 : kb1, pbuf, j);
+      if (j + 2 < ntiles) my_id_pf = tile_ids<DENSE>(s_list, static_cast<int64_t>(j + 2) * TILE, I.r0, nvalid);
       par ^= 1;
     }
 
