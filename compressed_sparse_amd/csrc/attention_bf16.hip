@@ -54,11 +54,23 @@ constexpr int DN = 512;
 constexpr int DRP = 64;
 constexpr int CW = DN + DRP;
 constexpr int TILE = 64;
-constexpr int NROW = DN * 2;               // bytes of one non-RoPE row in LDS
+constexpr int NROW = DN * 2;               // bytes of one BF16 non-RoPE row (and of a staged output row)
 constexpr int RROW = DRP * 2;              // bytes of one RoPE row
-constexpr int ROPE_OFF = TILE * NROW;      // the RoPE rows follow the 64 non-RoPE rows
-constexpr int KBUF = TILE * (NROW + RROW); // 73,728 B per tile buffer
 constexpr int PROW = TILE + 8;             // padded P^T row (bf16 elements)
+
+// Tile buffer layout: 64 non-RoPE rows (BF16 1 KB, or FP8 codes 512 B),
+// then 64 RoPE rows, then (FP8) the 64 entry scales.  An FP8 buffer is
+// padded to 64 KB so that an item's output (64 rows of 1 KB) can be staged
+// in it.
+template <bool FP8>
+struct Lay {
+  static constexpr int NROWB = FP8 ? DN : DN * 2;
+  static constexpr int ROPE_OFF = TILE * NROWB;
+  static constexpr int SC_OFF = ROPE_OFF + TILE * RROW;
+  static constexpr int BYTES = SC_OFF + (FP8 ? TILE * 4 : 0);
+  static constexpr int KBUF = BYTES > TILE * NROW ? BYTES : TILE * NROW;
+  static constexpr int NLOAD = FP8 ? 11 : 18;  // loads per wave per tile
+};
 constexpr int MAX_LIST = 1024;
 constexpr int NW = 4;                      // waves per workgroup
 constexpr int NT = 64 * NW;
@@ -81,6 +93,20 @@ struct Theta {
 // (8 chunks), two rows per bank line.
 __device__ __forceinline__ int swz(int r) { return 4 * (r & 3) + 2 * ((r >> 2) & 1) + ((r >> 4) & 1); }
 __device__ __forceinline__ int swz_rope(int r) { return 4 * ((r >> 1) & 1) + 2 * ((r >> 2) & 1) + ((r >> 4) & 1); }
+// FP8 rows (512 B, 32 chunks): an S^T A-operand pass reads one chunk of 16
+// rows differing in bits 0, 1, 2 and 4; a transposing 8-bit V read pass
+// reads 8 consecutive rows x 2 chunks x 2 halves.
+__device__ __forceinline__ int swzf(int r) { return 2 * (r & 7) + ((r >> 4) & 1); }
+
+// 8 FP8 E4M3 codes (low byte first) widened to BF16, exactly.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_bf16x2(uint32_t word) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
+}
+__device__ __forceinline__ bf16x8 fp8x8_bf16(uint32_t w0, uint32_t w1) {
+  return __builtin_bit_cast(bf16x8, u32x4{fp8x2_bf16x2<false>(w0), fp8x2_bf16x2<true>(w0), fp8x2_bf16x2<false>(w1),
+                                          fp8x2_bf16x2<true>(w1)});
+}
 
 // Workgroup barrier for LDS data: this wave's LDS accesses complete, then
 // s_barrier.  Global loads in flight (the next tile) are not waited for.
@@ -120,44 +146,62 @@ __device__ __forceinline__ int tile_ids(const int* s_list, int64_t rl, int64_t r
 // Buffer descriptor (raw, byte-addressed, 32-bit data format) over
 // [base, base + bytes).  The loads go through the buffer path so that the
 // compiler keeps counting LDS reads in order around them.
+__device__ __forceinline__ uint32_t span(uint64_t b) { return b < 0xFFFFFFFFull ? static_cast<uint32_t>(b) : 0xFFFFFFFFu; }
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
                                            0x00020000);
 }
 
+// Load `it` of this wave's share of one tile.  BF16: it < 16 is non-RoPE row
+// 16w + it (one 1 KB instruction, lane L fetching the chunk that belongs at
+// slot L).  FP8: it < 8 is rows 16w + 2it (lanes 0..31) and 16w + 2it + 1
+// (lanes 32..63), it == 10 the scales of rows 16w .. 16w+15.  Then the
+// RoPE rows 16w .. 16w+7 and 16w+8 .. 16w+15 (8 rows x 8 chunks each).
+template <bool FP8>
 __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, int my_id, size_t seq, int it) {
   typedef __attribute__((address_space(3))) void lds_void;
+  typedef Lay<FP8> L;
   int lane = threadIdx.x & 63;
   asm volatile("" : "+v"(lane));  // lane offsets are recomputed per load, not kept live
   const int w = threadIdx.x >> 6;
-  if (it < 16) {
+  const uint64_t cap = static_cast<uint64_t>(P.cap);
+  if (!FP8 && it < 16) {
     const int id = __builtin_amdgcn_readlane(my_id, it);
     const int r = 16 * w + it;
     // scalar row base, lane offset of the chunk that belongs at slot `lane`
     const uint8_t* row = static_cast<const uint8_t*>(P.nope) + (seq + static_cast<size_t>(id)) * NROW;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(row, NROW), (lds_void*)(buf + r * NROW), 16, 16 * (lane ^ swz(r)),
                                              0, 0, 0);
+  } else if (FP8 && it < 8) {
+    const int ida = __builtin_amdgcn_readlane(my_id, 2 * it), idb = __builtin_amdgcn_readlane(my_id, 2 * it + 1);
+    const int id = lane < 32 ? ida : idb;
+    const int r = 16 * w + 2 * it + (lane >> 5);
+    const uint8_t* base = static_cast<const uint8_t*>(P.nope) + seq * DN;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * DN)), (lds_void*)(buf + (16 * w + 2 * it) * DN), 16,
+                                             id * DN + 16 * ((lane & 31) ^ swzf(r)), 0, 0, 0);
+  } else if (FP8 && it == 10) {
+    const uint8_t* base = static_cast<const uint8_t*>(P.scale) + seq * 4;
+    if (lane < 16)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * 4)), (lds_void*)(buf + L::SC_OFF + 64 * w), 4,
+                                               my_id * 4, 0, 0, 0);
   } else {
-    const int h = it - 16;
+    const int h = it - (FP8 ? 8 : 16);
     const int r = 16 * w + 8 * h + (lane >> 3);
     const int idr = __shfl(my_id, 8 * h + (lane >> 3));
     const uint8_t* base = static_cast<const uint8_t*>(P.rope) + seq * RROW;
-    const uint64_t span = static_cast<uint64_t>(P.cap) * RROW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span < 0xFFFFFFFFull ? static_cast<uint32_t>(span) : 0xFFFFFFFFu),
-                                             (lds_void*)(buf + ROPE_OFF + (16 * w + 8 * h) * RROW), 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * RROW)),
+                                             (lds_void*)(buf + L::ROPE_OFF + (16 * w + 8 * h) * RROW), 16,
                                              idr * RROW + 16 * ((lane & 7) ^ swz_rope(r)), 0, 0, 0);
   }
 }
 
-constexpr int NLOAD = 18;  // loads per wave per tile
-
 // All loads of the tile at list slot rl, back to back.
-template <bool DENSE>
+template <bool FP8, bool DENSE>
 __device__ __forceinline__ void issue_tile(uint8_t* buf, const AttnParams& P, const int* s_list, int64_t rl,
                                            int64_t r0, int64_t nvalid, size_t seq) {
   const int my_id = tile_ids<DENSE>(s_list, rl, r0, nvalid);
 #pragma unroll
-  for (int it = 0; it < NLOAD; ++it) issue_load(buf, P, my_id, seq, it);
+  for (int it = 0; it < Lay<FP8>::NLOAD; ++it) issue_load<FP8>(buf, P, my_id, seq, it);
 }
 
 // One work item: query t of sequence b, entries [r0, r1) of its list (or of
@@ -244,11 +288,16 @@ __device__ __forceinline__ int compact_list(const int32_t (&lr)[4], int64_t n, i
 }
 
 // B fragment k-step s of S^T (32x32x16) for this lane: head 32hh + lane%32,
-// dims 16s + 8(lane/32) .. +8.
+// dims 16s + 8(lane/32) .. +8.  FP8 non-RoPE k-steps come in pairs that
+// share one 16-byte A read per lane: k-step s then holds dims
+// 32(s/2) + 16(lane/32) + 8(s%2) .. +8 (the same permutation of k on both
+// operands).
+template <bool FP8>
 __device__ __forceinline__ bf16x8 load_qs(const AttnParams& P, size_t qrow, int hh, int s) {
-  const int lane = threadIdx.x & 63;
-  const bf16_t* qh = static_cast<const bf16_t*>(P.q) + (qrow + 32 * hh + (lane & 31)) * CW + 8 * (lane >> 5);
-  return *reinterpret_cast<const bf16x8*>(qh + 16 * s);
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const bf16_t* qh = static_cast<const bf16_t*>(P.q) + (qrow + 32 * hh + (lane & 31)) * CW;
+  const int d = FP8 && s < DN / 16 ? 32 * (s >> 1) + 16 * half + 8 * (s & 1) : 16 * s + 8 * half;
+  return *reinterpret_cast<const bf16x8*>(qh + d);
 }
 
 // Turns the RoPE k-steps (dims 512..575, pairs (2p, 2p+1)) by position pos.
@@ -271,11 +320,12 @@ __device__ __forceinline__ void rope_q(const Theta& th, int64_t pos, bf16x8 (&qf
   }
 }
 
-template <bool DENSE, bool SPLIT>
+template <bool FP8, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(NT, 1)
 attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* part, int64_t nitems, int nbatch) {
-  __shared__ __attribute__((aligned(16))) uint8_t kb0[KBUF];
-  __shared__ __attribute__((aligned(16))) uint8_t kb1[KBUF];
+  typedef Lay<FP8> L;
+  __shared__ __attribute__((aligned(16))) uint8_t kb0[L::KBUF];
+  __shared__ __attribute__((aligned(16))) uint8_t kb1[L::KBUF];
   __shared__ __attribute__((aligned(16))) bf16_t pbuf[NH * PROW];
   __shared__ int s_list[DENSE ? 1 : MAX_LIST];
   __shared__ float s_xchg[2][NH];
@@ -304,21 +354,22 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   }
   int ntiles = (nvalid + TILE - 1) / TILE;
   int par = 0;  // buffer of the next tile: kb0 / kb1
-  if (ntiles > 0) issue_tile<DENSE>(kb0, P, s_list, 0, I.r0, nvalid, I.seq);
+  if (ntiles > 0) issue_tile<FP8, DENSE>(kb0, P, s_list, 0, I.r0, nvalid, I.seq);
   bf16x8 qf[QS];
 #pragma unroll
-  for (int s = 0; s < QS; ++s) qf[s] = load_qs(P, I.qrow, hh, s);
+  for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
 
   // LDS byte offsets of the S^T A operand (32x32x16): row 32eh + lane%32,
-  // k-step s chunk 2s + lane/32.  The swizzle touches the low four chunk
-  // bits, so k-steps 8 apart differ by a constant 256 B.
+  // chunk 2i + lane/32 of the non-RoPE row (BF16: k-step i, FP8: k-steps 2i
+  // and 2i + 1) and of the RoPE row.  The swizzle touches the low four chunk
+  // bits, so reads 8 apart differ by a constant 256 B.
   int offA[8], offR[4];
   {
     const int r = 32 * eh + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) offA[i] = r * NROW + 16 * ((2 * i + half) ^ swz(r));
+    for (int i = 0; i < 8; ++i) offA[i] = r * L::NROWB + 16 * ((2 * i + half) ^ (FP8 ? swzf(r) : swz(r)));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) offR[i] = ROPE_OFF + r * RROW + 16 * ((2 * i + half) ^ swz_rope(r));
+    for (int i = 0; i < 4; ++i) offR[i] = L::ROPE_OFF + r * RROW + 16 * ((2 * i + half) ^ swz_rope(r));
   }
   // V^T operand (transposing reads): within a 16-lane group, result lane i
   // slot s is element i%4 of the 8 bytes addressed by lane 4s + i/4.  Lane
@@ -327,13 +378,25 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   // odd k-steps (bit 4 set) have chunk bit 0 flipped: byte offset ^ 16.
   const int G = lane >> 4, sq = (lane >> 2) & 3, q4 = lane & 3;
   const int rowA = 8 * (G >> 1) + sq, rowB = rowA + 4;
+  // FP8 (8-bit transposing reads): within a 16-lane group, result lane i
+  // byte k is byte i%8 of the 8 bytes addressed by lane 2k + i/8.  Lane
+  // L = 16G + 2k + h reads entry 8(G/2) + k of the k-step, value dims
+  // 128w + 32mb + 16(G%2) + 8h .. +8: chunk 8w + 2mb + G%2, byte 8h.
   int offV[4][2];
 #pragma unroll
   for (int mb = 0; mb < 4; ++mb) {
-    // 16-byte chunk 16w + 4mb + 2(G%2) + q/2: high bits w, low four bits swizzled
-    const int c = 4 * mb + 2 * (G & 1) + (q4 >> 1);
-    offV[mb][0] = rowA * NROW + 16 * (16 * w + (c ^ swz(rowA))) + 8 * (q4 & 1);
-    offV[mb][1] = rowB * NROW + 16 * (16 * w + (c ^ swz(rowB))) + 8 * (q4 & 1);
+    if (FP8) {
+      const int k8 = (lane & 15) >> 1, h8 = lane & 1;
+      const int row = 8 * (G >> 1) + k8;
+      const int c = 8 * (w & 1) + 2 * mb + (G & 1);
+      offV[mb][0] = row * DN + 16 * (16 * (w >> 1) + (c ^ swzf(row))) + 8 * h8;
+      offV[mb][1] = 0;
+    } else {
+      // 16-byte chunk 16w + 4mb + 2(G%2) + q/2: high bits w, low four bits swizzled
+      const int c = 4 * mb + 2 * (G & 1) + (q4 >> 1);
+      offV[mb][0] = rowA * NROW + 16 * (16 * w + (c ^ swz(rowA))) + 8 * (q4 & 1);
+      offV[mb][1] = rowB * NROW + 16 * (16 * w + (c ^ swz(rowB))) + 8 * (q4 & 1);
+    }
   }
   const int pop = (lane & 31) * PROW + 8 * half;  // P^T B operand (elements); + 32 nb rows: heads 32nb..
   const float lscale = P.scale_qk * LOG2E;
@@ -378,7 +441,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     // next item's list compacted into s_list, its first tile issued into buf
     auto start_next = [&](uint8_t* buf) {
       nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, In.n, s_list, s_cnt);
-      if (nvalid_n > 0) issue_tile<DENSE>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq);
+      if (nvalid_n > 0) issue_tile<FP8, DENSE>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq);
       next_started = true;
     };
 
@@ -418,26 +481,55 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       // A operands run SPF k-steps ahead of the MFMAs (scheduling barriers
       // keep that order); in the item's last tile the query fragments are
       // reloaded for the next item right after their last use
-      auto aop = [&](int s) -> bf16x8 {
-        return s < DN / 16 ? lds_b128(cur + offA[s & 7] + 256 * (s >> 3)) : lds_b128(cur + offR[s - DN / 16]);
+      // one A read per unit: BF16 36 units of one k-step; FP8 16 units of two
+      // non-RoPE k-steps (16 codes widened in registers) and 4 RoPE k-steps
+      constexpr int NU = FP8 ? DN / 32 + DRP / 16 : QS;
+      constexpr int NUN = FP8 ? DN / 32 : DN / 16;  // non-RoPE units
+      auto aop = [&](int u) -> u32x4 {
+        return u < NUN ? *reinterpret_cast<const u32x4*>(cur + offA[u & 7] + 256 * (u >> 3))
+                       : *reinterpret_cast<const u32x4*>(cur + offR[u - NUN]);
       };
       f32x16 sacc = f32x16{};
+      f32x16 sacr = f32x16{};  // FP8: the RoPE part, unscaled
       {
-        bf16x8 ring[SPF];
+        u32x4 ring[SPF];
 #pragma unroll
-        for (int s = 0; s < SPF; ++s) ring[s] = aop(s);
+        for (int u = 0; u < SPF; ++u) ring[u] = aop(u);
 #pragma unroll
-        for (int s = 0; s < QS; ++s) {
-          const bf16x8 a = ring[s % SPF];
-          if (s + SPF < QS) ring[s % SPF] = aop(s + SPF);
-          sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[s], sacc, 0, 0, 0);
-          if (s % 7 == 3) issue_load(nxt, P, my_id, lseq, s / 7);  // loads 0..4
+        for (int u = 0; u < NU; ++u) {
+          const u32x4 a = ring[u % SPF];
+          if (u + SPF < NU) ring[u % SPF] = aop(u + SPF);
+          if (FP8 && u < NUN) {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_bf16(a[0], a[1]), qf[2 * u], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_bf16(a[2], a[3]), qf[2 * u + 1], sacc, 0, 0, 0);
+          } else if (FP8) {
+            sacr = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[DN / 16 + u - NUN], sacr, 0,
+                                                           0, 0);
+          } else {
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[u], sacc, 0, 0, 0);
+          }
+          if (FP8 ? u % 5 == 2 : u % 7 == 3) issue_load<FP8>(nxt, P, my_id, lseq, FP8 ? u / 5 : u / 7);  // loads 0..3 / 0..4
           __builtin_amdgcn_sched_barrier(0);
         }
       }
       if (last && has_next) {
 #pragma unroll
-        for (int s = 0; s < QS; ++s) qf[s] = load_qs(P, In.qrow, hh, s);
+        for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, In.qrow, hh, s);
+      }
+      // FP8: S = scale_e (q . codes_e) + (q_rope . k_rope_e); P^T carries the
+      // scale into O (the V rows in LDS are unscaled codes)
+      float esc[16];
+      if (FP8) {
+#pragma unroll
+        for (int jq = 0; jq < 4; ++jq) {
+          const float4 sc = *reinterpret_cast<const float4*>(cur + L::SC_OFF + 4 * (32 * eh + 8 * jq + 4 * half));
+          esc[4 * jq] = sc.x;
+          esc[4 * jq + 1] = sc.y;
+          esc[4 * jq + 2] = sc.z;
+          esc[4 * jq + 3] = sc.w;
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) sacc[v] = sacc[v] * esc[v] + sacr[v];
       }
 
       // --- softmax: lane holds entries 32eh + acc_row(v) of its head ---------
@@ -470,16 +562,19 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
           const float p2 = __builtin_amdgcn_exp2f(sacc[4 * jq + 2] - m_run);
           const float p3 = __builtin_amdgcn_exp2f(sacc[4 * jq + 3] - m_run);
           ps += (p0 + p1) + (p2 + p3);
+          const float f0 = FP8 ? esc[4 * jq] : 1.0f, f1 = FP8 ? esc[4 * jq + 1] : 1.0f;
+          const float f2 = FP8 ? esc[4 * jq + 2] : 1.0f, f3 = FP8 ? esc[4 * jq + 3] : 1.0f;
           *reinterpret_cast<uint2*>(pbuf_r + head * PROW + 32 * eh + 8 * jq + 4 * half) =
-              make_uint2(pack2_bf16(p0, p1), pack2_bf16(p2, p3));
+              make_uint2(pack2_bf16(p0 * f0, p1 * f1), pack2_bf16(p2 * f2, p3 * f3));
         }
         return ps;
       };
       float psum = 0.0f;
       if (!wave_bad) psum = write_p();
-      // loads 5..12 stall the wave where it waits anyway
+      // loads 5..12 (FP8: 4..7 and the scales) stall the wave where it waits anyway
 #pragma unroll
-      for (int q = 5; q < 13; ++q) issue_load(nxt, P, my_id, lseq, q);
+      for (int q = FP8 ? 4 : 5; q < (FP8 ? 8 : 13); ++q) issue_load<FP8>(nxt, P, my_id, lseq, q);
+      if (FP8) issue_load<FP8>(nxt, P, my_id, lseq, 10);
       lds_sync();
       if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {
         const float mall = fmaxf(mx, s_xchg[eh ^ 1][head]);
@@ -505,31 +600,48 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       {
         typedef __attribute__((address_space(3))) v4s lds_v4s;
         constexpr int PPF = 4;
-        auto vop = [&](int t, int i) -> v4s {
+        // one V^T operand per step: BF16 two 16-bit transposing reads, FP8
+        // one 8-bit transposing read widened in registers
+        typedef int v2i __attribute__((ext_vector_type(2)));
+        typedef __attribute__((address_space(3))) v2i lds_v2i;
+        struct VOp {
+          v4s x, y;
+        };
+        auto vop = [&](int t) -> VOp {
           const int ks = t >> 2, mb = t & 3;
           const int fl = (ks & 1) ? 16 : 0;
-          return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + (offV[mb][i] ^ fl) + 16 * ks * NROW));
+          VOp r;
+          if (FP8) {
+            const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(cur + (offV[mb][0] ^ fl) + 16 * ks * DN));
+            r.x = __builtin_bit_cast(v4s, c);
+            r.y = r.x;
+          } else {
+            r.x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + (offV[mb][0] ^ fl) + 16 * ks * NROW));
+            r.y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + (offV[mb][1] ^ fl) + 16 * ks * NROW));
+          }
+          return r;
+        };
+        auto vval = [&](const VOp& o) -> bf16x8 {
+          if (FP8) {
+            const v2i c = __builtin_bit_cast(v2i, o.x);
+            return fp8x8_bf16(static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1]));
+          }
+          return __builtin_bit_cast(bf16x8, __builtin_shufflevector(o.x, o.y, 0, 1, 2, 3, 4, 5, 6, 7));
         };
         auto pop_ks = [&](int ks, int nb) -> bf16x8 {
           return *reinterpret_cast<const bf16x8*>(pbuf_r + pop + 32 * nb * PROW + 16 * ks);
         };
-        v4s vx[PPF], vy[PPF];
+        VOp vr[PPF];
         bf16x8 pbr[2][2];
         pbr[0][0] = pop_ks(0, 0);
         pbr[0][1] = pop_ks(0, 1);
 #pragma unroll
-        for (int t = 0; t < PPF; ++t) {
-          vx[t] = vop(t, 0);
-          vy[t] = vop(t, 1);
-        }
+        for (int t = 0; t < PPF; ++t) vr[t] = vop(t);
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           const int ks = t >> 2;
-          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(vx[t % PPF], vy[t % PPF], 0, 1, 2, 3, 4, 5, 6, 7));
-          if (t + PPF < 16) {
-            vx[t % PPF] = vop(t + PPF, 0);
-            vy[t % PPF] = vop(t + PPF, 1);
-          }
+          const bf16x8 va = vval(vr[t % PPF]);
+          if (t + PPF < 16) vr[t % PPF] = vop(t + PPF);
           if ((t & 3) == 0 && ks + 1 < 4) {
             pbr[(ks + 1) & 1][0] = pop_ks(ks + 1, 0);
             pbr[(ks + 1) & 1][1] = pop_ks(ks + 1, 1);
@@ -537,8 +649,8 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
             oacc[t & 3][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[ks & 1][nb], oacc[t & 3][nb], 0, 0, 0);
-          // loads 13..17
-          if (t % 3 == 1) issue_load(nxt, P, my_id, lseq, 13 + t / 3);
+          // loads 13..17 (FP8: 8, 9)
+          if (FP8 ? t % 8 == 3 : t % 3 == 1) issue_load<FP8>(nxt, P, my_id, lseq, FP8 ? 8 + t / 8 : 13 + t / 3);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -610,7 +722,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       if (par == 0) start_next(kb0);
       else start_next(kb1);
 #pragma unroll
-      for (int s = 0; s < QS; ++s) qf[s] = load_qs(P, In.qrow, hh, s);
+      for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, In.qrow, hh, s);
     }
     staged = defer;
     I = In;
@@ -642,13 +754,27 @@ void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int
   const int64_t nitems = static_cast<int64_t>(B) * (split ? splits : P.T);
   if (nitems <= 0) return;
   const dim3 grid(static_cast<unsigned>(nitems < cu ? nitems : cu));
-  if (dense) {
-    if (split) hipLaunchKernelGGL((attn_bf16_kernel<true, true>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
-    else hipLaunchKernelGGL((attn_bf16_kernel<true, false>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
+  const bool fp8 = P.nope_dt == CSA_FP8E4M3;
+#define CSA_ATTN_LAUNCH(F, D, S) \
+  hipLaunchKernelGGL((attn_bf16_kernel<F, D, S>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B)
+  if (fp8) {
+    if (dense) {
+      if (split) CSA_ATTN_LAUNCH(true, true, true);
+      else CSA_ATTN_LAUNCH(true, true, false);
+    } else {
+      if (split) CSA_ATTN_LAUNCH(true, false, true);
+      else CSA_ATTN_LAUNCH(true, false, false);
+    }
   } else {
-    if (split) hipLaunchKernelGGL((attn_bf16_kernel<false, true>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
-    else hipLaunchKernelGGL((attn_bf16_kernel<false, false>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B);
+    if (dense) {
+      if (split) CSA_ATTN_LAUNCH(false, true, true);
+      else CSA_ATTN_LAUNCH(false, true, false);
+    } else {
+      if (split) CSA_ATTN_LAUNCH(false, false, true);
+      else CSA_ATTN_LAUNCH(false, false, false);
+    }
   }
+#undef CSA_ATTN_LAUNCH
 }
 
 }  // namespace csa
