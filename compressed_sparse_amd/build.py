@@ -28,8 +28,10 @@ FLAGS = [
 
 
 # per-source extra flags: the BF16 attention kernel keeps the query in
-# registers; MFMA results in VGPR form leave the AGPRs for the rest
-EXTRA = {"attention_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# registers and the indexer's epilogue works on every MFMA result; MFMA
+# results in VGPR form save the copies out of AGPRs
+EXTRA = {"attention_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "index_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def sources():

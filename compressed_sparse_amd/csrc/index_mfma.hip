@@ -69,6 +69,10 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// ReLU as an integer max: every negative float, -0 included, becomes +0
+// (one instruction; the float max would first quiet NaNs)
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
 __device__ __forceinline__ uint32_t order_key(float x) {
   uint32_t u = __float_as_uint(x);
   if ((u << 1) == 0u) return 0x80000000u;
@@ -76,12 +80,37 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// fused prefill: scores of 4 queries in LDS, then one wave per row selects
+// fused prefill: scores of 4 queries in LDS, then two waves per row select
 // ---------------------------------------------------------------------------
+
+constexpr int FW = 8;           // waves per fused workgroup
+constexpr int SEL_BINS = 2048;  // value-range bins of the fused select (16-bit counts, two per word)
+constexpr int SEL_HW = SEL_BINS / 2;  // histogram words per row
+constexpr int SEL_CBH = 128;    // threshold-bin entries ranked directly, per half row
+constexpr int KD = 8;           // key blocks in flight per wave (scoring)
+constexpr int HSTEPS = FUSED_NMAX / 512;  // 256-entry steps in half a row, at most
+
+// Inclusive prefix sum over the wave's lanes (row shifts within 16 lanes,
+// then the row broadcasts)
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
+__device__ __forceinline__ int mbcnt(unsigned long long m) {
+  return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
+}
 
 // Wave-level radix select of the top-k of row[0..n) (n > k) and ordered
 // compaction of the selected indices into out[0..k).
-__device__ void wave_radix_select(const float* row, int n, int k, int key_bits, int* hist, int32_t* out) {
+__device__ __forceinline__ void wave_radix_select(const float* row, int n, int k, int key_bits, int* hist,
+                                                  int32_t* out) {
   const int lane = threadIdx.x & 63;
   uint32_t prefix = 0, pmask = 0;
   int remaining = k;
@@ -139,178 +168,52 @@ __device__ void wave_radix_select(const float* row, int n, int k, int key_bits, 
   for (int j = written + lane; j < k; j += 64) out[j] = -1;
 }
 
-constexpr int SEL_BINS = 1024;  // value-range bins of the fused select
-constexpr int SEL_CB = 256;     // threshold-bin entries ranked directly
-
-// Exact top-k of row[0..n) (n > k) by one wave, ascending indices, ties to
-// the lower index.  The row's scores fall into SEL_BINS equal-width bins
-// between its min and max (a monotone map, so a bin holds a contiguous key
-// range and equal scores share a bin); the histogram finds the bin B that
-// holds the k-th largest score.  Bins above B are taken whole; the entries
-// of B are ranked by (key descending, index ascending) against each other
-// and the best k - |bins above B| taken; one last pass writes the indices
-// in order.  A threshold bin with more than SEL_CB entries (heavy ties)
-// falls back to the radix select.
-__device__ void wave_select(const float* row, int n, int k, int key_bits, int* hist, int* cidx, uint32_t* ckey,
-                            int* crank, int32_t* out) {
-  const int lane = threadIdx.x & 63;
-  const unsigned long long below = (1ull << lane) - 1ull;
-  // lane l reads entries 4(base + l) .. +3 of each 256-entry step (the row
-  // is 16-byte aligned and padded past n)
-  auto quad = [&](int base) { return *reinterpret_cast<const float4*>(row + 4 * (base + lane)); };
-  float mn = INFINITY, mx = -INFINITY;
-  for (int base = 0; 4 * base < n; base += 64) {
-    const float4 v = quad(base);
-    const int s = 4 * (base + lane);
-    if (s < n) { mn = fminf(mn, v.x); mx = fmaxf(mx, v.x); }
-    if (s + 1 < n) { mn = fminf(mn, v.y); mx = fmaxf(mx, v.y); }
-    if (s + 2 < n) { mn = fminf(mn, v.z); mx = fmaxf(mx, v.z); }
-    if (s + 3 < n) { mn = fminf(mn, v.w); mx = fmaxf(mx, v.w); }
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    mn = fminf(mn, __shfl_xor(mn, o));
-    mx = fmaxf(mx, __shfl_xor(mx, o));
-  }
-  const float span = mx - mn;
-  float scale = span > 0.0f ? static_cast<float>(SEL_BINS) / span : 0.0f;
-  if (!(scale < 3.0e38f)) scale = 0.0f;  // degenerate range: one bin, radix fallback
-  auto bin_of = [&](float v) { return min(SEL_BINS - 1, static_cast<int>((v - mn) * scale)); };
-  for (int i = lane; i < SEL_BINS; i += 64) hist[i] = 0;
-  wave_lds_sync();
-  for (int base = 0; 4 * base < n; base += 64) {
-    const float4 v = quad(base);
-    const int s = 4 * (base + lane);
-    if (s < n) atomicAdd(&hist[bin_of(v.x)], 1);
-    if (s + 1 < n) atomicAdd(&hist[bin_of(v.y)], 1);
-    if (s + 2 < n) atomicAdd(&hist[bin_of(v.z)], 1);
-    if (s + 3 < n) atomicAdd(&hist[bin_of(v.w)], 1);
-  }
-  wave_lds_sync();
-  // lane l owns bins SEL_BINS-1-16l .. SEL_BINS-16-16l (descending)
-  constexpr int PER = SEL_BINS / 64;
-  int c[PER], tot = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) { c[j] = hist[SEL_BINS - 1 - PER * lane - j]; tot += c[j]; }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
-  int bsel = -1, above = 0;
-  if (incl - tot < k && incl >= k) {
-    int cum = incl - tot;
-#pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (bsel < 0 && cum + c[j] >= k) { bsel = SEL_BINS - 1 - PER * lane - j; above = cum; }
-      cum += c[j];
-    }
-  }
-  const unsigned long long who = __ballot(bsel >= 0);
-  const int src = __ffsll(static_cast<long long>(who)) - 1;
-  const int B = __builtin_amdgcn_readlane(bsel, src);
-  const int rem = k - __builtin_amdgcn_readlane(above, src);  // entries of bin B to take
-  // the entries of bin B in index order: lanes before this one, then this
-  // lane's earlier elements
-  int cnt = 0;
-  for (int base = 0; 4 * base < n; base += 64) {
-    const float4 v = quad(base);
-    const int s = 4 * (base + lane);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-    bool in[4];
-    int mine = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) { in[u] = s + u < n && bin_of(vv[u]) == B; mine += in[u]; }
-    int before = 0, total = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned long long m = __ballot(in[u]);
-      before += __popcll(m & below);
-      total += __popcll(m);
-    }
-    int pos = cnt + before;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      if (in[u]) {
-        if (pos < SEL_CB) { cidx[pos] = s + u; ckey[pos] = order_key(vv[u]); }
-        ++pos;
-      }
-    }
-    cnt += total;
-  }
-  if (cnt > SEL_CB) {
-    wave_lds_sync();
-    wave_radix_select(row, n, k, key_bits, hist, out);
-    return;
-  }
-  wave_lds_sync();
-  // rank of entry e among bin B: entries with a larger key, or an equal key
-  // and a lower index (cidx is ascending, so the lower position)
-  for (int e = lane; e < cnt; e += 64) {
-    const uint32_t ke = ckey[e];
-    int r = 0;
-    for (int f = 0; f < cnt; ++f) {
-      const uint32_t kf = ckey[f];
-      r += (kf > ke || (kf == ke && f < e)) ? 1 : 0;
-    }
-    crank[e] = r;
-  }
-  wave_lds_sync();
-  // ordered output: bins above B, and the entries of B ranked below rem
-  int written = 0, seen = 0;
-  for (int base = 0; 4 * base < n; base += 64) {
-    const float4 v = quad(base);
-    const int s = 4 * (base + lane);
-    const float vv[4] = {v.x, v.y, v.z, v.w};
-    int bn[4];
-    bool inb[4];
-    int bbefore = 0, btotal = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      bn[u] = s + u < n ? bin_of(vv[u]) : -1;
-      inb[u] = bn[u] == B;
-      const unsigned long long m = __ballot(inb[u]);
-      bbefore += __popcll(m & below);
-      btotal += __popcll(m);
-    }
-    int jb = seen + bbefore;
-    bool take[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      take[u] = bn[u] > B;
-      if (inb[u]) { take[u] = crank[jb] < rem; ++jb; }
-    }
-    int tbefore = 0, ttotal = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const unsigned long long m = __ballot(take[u]);
-      tbefore += __popcll(m & below);
-      ttotal += __popcll(m);
-    }
-    int pos = written + tbefore;
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (take[u]) out[pos++] = s + u;
-    written += ttotal;
-    seen += btotal;
-  }
-}
-
+// index_prefill_fused_kernel: queries t0 .. t0+3 of sequence b.
+//
+// Scoring: 8 waves take 16-entry key blocks in turn (two waves per SIMD, so
+// one multiplies while the other reduces), each for all 64 (query, head)
+// rows; every lane ends with the weighted ReLU sum of one query and entry,
+// and the row's extremes are kept on the way.
+//
+// Select, exact top-k of each row with n > k (ascending indices, ties to the
+// lower index), by the row's two waves, one per half of its 256-entry
+// steps.  Scores map monotonically onto t = (s - min) * (BINS-2) / (max -
+// min) + 1, bin floor(t) in 1 .. BINS-1; the row's tail up to a whole step
+// holds -inf (bin 0).  A shared histogram gives the bin B of the k-th
+// largest score; entries with t >= B+1 are taken, those of bin B are ranked
+// by (score descending, index ascending) and the best k - |above B| taken.
+// Each half compacts its taken indices, in order, into the front of its own
+// part of the row (a position never passes an entry still to be read), and
+// the two runs are copied out back to back.  A row whose scores are all
+// equal keeps its first k entries; a range too narrow for the bins, or a
+// threshold bin of more than SEL_CBH entries in a half (heavy ties), takes
+// the radix select.
 template <bool KFP8>
-__global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams P) {
-  __shared__ float srow[QG][FUSED_NMAX];
-  __shared__ int hist[QG][SEL_BINS];
-  __shared__ int cidx[QG][SEL_CB];
-  __shared__ uint32_t ckey[QG][SEL_CB];
-  __shared__ int crank[QG][SEL_CB];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+__global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexParams P) {
+  __shared__ __align__(16) float srow[QG][FUSED_NMAX];
+  // select state (histograms, bin-B candidates, ranks); while scoring, the
+  // same bytes stage each wave's key block
+  __shared__ __align__(16) int sel_mem[QG * SEL_HW + 3 * QG * 2 * SEL_CBH];
+  static_assert(sizeof(sel_mem) >= FW * 2048, "key stage");
+  int (*hist)[SEL_HW] = reinterpret_cast<int (*)[SEL_HW]>(sel_mem);
+  int (*cidx)[2][SEL_CBH] = reinterpret_cast<int (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW);
+  uint32_t (*ckey)[2][SEL_CBH] = reinterpret_cast<uint32_t (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW + QG * 2 * SEL_CBH);
+  int (*crank)[2][SEL_CBH] = reinterpret_cast<int (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW + 2 * QG * 2 * SEL_CBH);
+  __shared__ float s_mm[FW][QG][2];  // per wave and row: min, max of the scores it wrote
+  __shared__ int s_cnt[QG][2][2];    // per row and half: bin-B entries, entries above B
+  __shared__ int s_sink[FW][64];     // stores of lanes with nothing to store
+  // the wave index is uniform: saying so keeps the loops below scalar
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
   const int t0 = blockIdx.x * QG;
-  // visible entries of query t0 + q (0 past the end of the rows)
+  // visible entries of query t0 + q (0 past the end of the rows): one 64-bit
+  // division per workgroup, (pos0 + t0 + 1) = qb m + rb
+  const int64_t base = P.pos0 + t0 + 1;
+  const int64_t qb = base / P.m;
+  const int rb0 = static_cast<int>(base - qb * P.m);
   auto nvis = [&](int q) -> int {
     if (t0 + q >= P.T) return 0;
-    int64_t n = (P.pos0 + t0 + q + 1) / P.m;
+    const int64_t n = qb + (rb0 + q) / P.m;
     return static_cast<int>(n < P.cap ? n : P.cap);
   };
   int nmax = 0;
@@ -320,114 +223,357 @@ __global__ void __launch_bounds__(256, 1) index_prefill_fused_kernel(IndexParams
   const size_t row0 = static_cast<size_t>(b) * P.T + t0;
 
   if (need) {
-    // A operands: rows r = 32*rb + (lane & 31) -> query 2rb + r/16, head r%16;
-    // k-step ks covers dims (lane>>5)*32 + ks*8 .. +8 (same map for B)
-    bf16x8 qa[2][4];
-    float wv[2][16];
+    // 16x16x32 MFMAs over 16-entry key blocks.  Row r of head block j holds
+    // query r/4, head 4j + r%4, so that lane l's four accumulators are the
+    // 16 heads (head 4j + i in element i of block j) of query l/16 against
+    // entry l%16.  K-step ks, lane group g = l/16 covers dims 32ks + 8g
+    // (BF16 keys: one k-step reads 64 contiguous bytes of each of 16 rows)
+    // or 16g + 8ks (FP8 keys: one 16-byte read covers both k-steps); the
+    // query follows the same map.
+    const int g = lane >> 4, e16 = lane & 15;
+    bf16x8 qa[4][2];
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-      const int r = lane & 31;
-      const int q = 2 * rb + (r >> 4);
-      const bool live = t0 + q < P.T;
-      const bf16_t* qp = static_cast<const bf16_t*>(P.qI) + ((row0 + q) * HI + (r & 15)) * DI + (lane >> 5) * 32;
+    for (int j = 0; j < 4; ++j) {
+      const int qq = e16 >> 2, hh = 4 * j + (e16 & 3);
+      const bool live = t0 + qq < P.T;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
+      for (int ks = 0; ks < 2; ++ks) {
+        const int d0 = KFP8 ? 16 * g + 8 * ks : 32 * ks + 8 * g;
+        const bf16_t* qp = static_cast<const bf16_t*>(P.qI) + ((row0 + qq) * HI + hh) * DI + d0;
         const u32x4 z = {0u, 0u, 0u, 0u};
-        qa[rb][ks] = as_bf16x8(live ? *reinterpret_cast<const u32x4*>(qp + ks * 8) : z);
-      }
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int rr = (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        const int qq = 2 * rb + (rr >> 4);
-        wv[rb][v] = (t0 + qq < P.T) ? P.w[(row0 + qq) * HI + (rr & 15)] : 0.0f;
+        qa[j][ks] = as_bf16x8(live ? *reinterpret_cast<const u32x4*>(qp) : z);
       }
     }
-    const size_t seq = static_cast<size_t>(b) * P.cap;
-    const int nblocks = (nmax + 31) / 32;
-    // raw key rows of one 32-entry block (lane: entry lane%32, dims
-    // (lane/32)*32 .. +32), clamped to the last visible entry: branch-free
-    auto loadk = [&](int cb, u32x4 (&kr)[4], float& ksc) {
-      const int s = min(cb * 32 + (lane & 31), nmax - 1);
-      if (KFP8) {
-        const uint8_t* kp = static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
-        kr[0] = *reinterpret_cast<const u32x4*>(kp);
-        kr[1] = *reinterpret_cast<const u32x4*>(kp + 16);
-        ksc = static_cast<const float*>(P.kscale)[seq + s];
-      } else {
-        const bf16_t* kp = static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + (lane >> 5) * 32;
+    float wv[16];  // weights of this lane's query g
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kr[ks] = *reinterpret_cast<const u32x4*>(kp + ks * 8);
+    for (int v = 0; v < 16; ++v) wv[v] = (t0 + g < P.T) ? P.w[(row0 + g) * HI + v] : 0.0f;
+    const int nv = nvis(g);
+    float mnv = INFINITY, mxv = -INFINITY;
+    const size_t seq = static_cast<size_t>(b) * P.cap;
+    const int nblocks = (nmax + 15) / 16;
+    // Key blocks arrive by coalesced reads (BF16: lane l reads 16 bytes of
+    // row 8i + l/8 at chunk l%8, i = 0, 1; FP8: row l/4, chunk l%4), pass
+    // through this wave's 2 KB LDS stage and are read back in the MFMA's
+    // layout.  Stage chunk c of row r sits at chunk c ^ ((r/2)%8) (BF16,
+    // 128-byte rows) or c ^ ((r/4)%4) (FP8, 64-byte rows): both the writes
+    // and the reads of 16 lanes then cover distinct bank groups.
+    uint8_t* stage = reinterpret_cast<uint8_t*>(sel_mem) + 2048 * w;
+    auto loadk = [&](int cb, u32x4 (&kr)[2], float& ksc) {
+      if (KFP8) {
+        const int s = min(cb * 16 + (lane >> 2), nmax - 1);
+        kr[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + 16 * (lane & 3));
+        kr[1] = kr[0];
+        ksc = static_cast<const float*>(P.kscale)[seq + min(cb * 16 + e16, nmax - 1)];
+      } else {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int s = min(cb * 16 + 8 * i + (lane >> 3), nmax - 1);
+          kr[i] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + 8 * (lane & 7));
+        }
         ksc = 1.0f;
       }
     };
-    auto compute = [&](int cb, const u32x4 (&raw)[4], float ksc) {
-      const int s = cb * 32 + (lane & 31);
-      u32x4 kr[4];
+    // block registers -> stage -> B operands (k-steps 0, 1)
+    auto restage = [&](const u32x4 (&kr)[2], u32x4 (&kb)[2]) {
+      wave_lds_sync();  // the previous block's reads are done
       if (KFP8) {
-        kr[0] = fp8x8_to_bf16(raw[0][0], raw[0][1]);
-        kr[1] = fp8x8_to_bf16(raw[0][2], raw[0][3]);
-        kr[2] = fp8x8_to_bf16(raw[1][0], raw[1][1]);
-        kr[3] = fp8x8_to_bf16(raw[1][2], raw[1][3]);
+        const int r = lane >> 2;
+        *reinterpret_cast<u32x4*>(stage + 64 * r + 16 * ((lane & 3) ^ ((r >> 2) & 3))) = kr[0];
       } else {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) kr[ks] = raw[ks];
+        for (int i = 0; i < 2; ++i) {
+          const int r = 8 * i + (lane >> 3);
+          *reinterpret_cast<u32x4*>(stage + 128 * r + 16 * ((lane & 7) ^ ((r >> 1) & 7))) = kr[i];
+        }
       }
-      f32x16 acc[2];
+      wave_lds_sync();
+      if (KFP8) {
+        const u32x4 raw = *reinterpret_cast<const u32x4*>(stage + 64 * e16 + 16 * (g ^ ((e16 >> 2) & 3)));
+        kb[0] = fp8x8_to_bf16(raw[0], raw[1]);
+        kb[1] = fp8x8_to_bf16(raw[2], raw[3]);
+      } else {
 #pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        acc[rb] = f32x16{};
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-          acc[rb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qa[rb][ks], as_bf16x8(kr[ks]), acc[rb], 0, 0, 0);
-      }
-#pragma unroll
-      for (int rb = 0; rb < 2; ++rb) {
-        float s0 = 0.0f, s1 = 0.0f;  // queries 2rb, 2rb+1 (8 heads of each in this lane)
-#pragma unroll
-        for (int v = 0; v < 8; ++v) s0 = fmaf(wv[rb][v], fmaxf(acc[rb][v] * ksc, 0.0f), s0);
-#pragma unroll
-        for (int v = 8; v < 16; ++v) s1 = fmaf(wv[rb][v], fmaxf(acc[rb][v] * ksc, 0.0f), s1);
-        const float o0 = __shfl_xor(s0, 32), o1 = __shfl_xor(s1, 32);
-        // lanes 0-31 hold head groups {0-3, 8-11}, lanes 32-63 {4-7, 12-15}:
-        // add in a fixed order (lower half first)
-        const float t0s = (lane < 32) ? s0 + o0 : o0 + s0;
-        const float t1s = (lane < 32) ? s1 + o1 : o1 + s1;
-        const int q = 2 * rb + (lane >> 5);
-        float val = (lane < 32) ? t0s : t1s;
-        if (P.score_dt == CSA_BF16) val = round_bf16(val);
-        if (s < nvis(q)) srow[q][s] = val;
+        for (int ks = 0; ks < 2; ++ks)
+          kb[ks] = *reinterpret_cast<const u32x4*>(stage + 128 * e16 + 16 * ((4 * ks + g) ^ ((e16 >> 1) & 7)));
       }
     };
-    // the next block's rows load while this block is multiplied (a block
-    // past the end re-reads the last one; no load sits under a branch)
-    u32x4 ka[4], kb[4];
-    float sa, sb;
-    int cb = w;
-    if (cb < nblocks) {
-      loadk(cb, ka, sa);
-      while (true) {
-        loadk(min(cb + 4, nblocks - 1), kb, sb);
-        compute(cb, ka, sa);
-        cb += 4;
-        if (cb >= nblocks) break;
-        loadk(min(cb + 4, nblocks - 1), ka, sa);
-        compute(cb, kb, sb);
-        cb += 4;
-        if (cb >= nblocks) break;
+    auto compute = [&](int cb, const u32x4 (&kb)[2], float ksc) {
+      f32x4 acc[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j][0], as_bf16x8(kb[0]), f32x4{}, 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j][1], as_bf16x8(kb[1]), acc[j], 0, 0, 0);
+      }
+      // heads 0..15 in order
+      float val = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) val = fmaf(wv[4 * j + i], relu(acc[j][i] * ksc), val);
+      if (P.score_dt == CSA_BF16) val = round_bf16(val);
+      const int s = cb * 16 + e16;
+      if (s < nv) {
+        srow[g][s] = val;
+        mnv = fminf(mnv, val);
+        mxv = fmaxf(mxv, val);
+      }
+    };
+    // KD blocks of keys in flight per wave: block c + FW KD loads into the
+    // registers block c has just staged (a block past the end re-reads the
+    // last one, so no load sits under a branch)
+    u32x4 kr[KD][2];
+    float ks[KD];
+    const int lastb = nblocks - 1;
+#pragma unroll
+    for (int i = 0; i < KD; ++i) loadk(min(w + FW * i, lastb), kr[i], ks[i]);
+    for (int cb = w; cb < nblocks; cb += FW * KD) {
+#pragma unroll
+      for (int i = 0; i < KD; ++i) {
+        const int c = cb + FW * i;
+        if (c < nblocks) {
+          u32x4 kb[2];
+          restage(kr[i], kb);
+          const float ksc = ks[i];
+          loadk(min(c + FW * KD, lastb), kr[i], ks[i]);
+          compute(c, kb, ksc);
+        } else {
+          loadk(min(c + FW * KD, lastb), kr[i], ks[i]);
+        }
+      }
+    }
+    // per-row extremes of this wave's scores (the 16 lanes of query g)
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) {
+      mnv = fminf(mnv, __shfl_xor(mnv, o));
+      mxv = fmaxf(mxv, __shfl_xor(mxv, o));
+    }
+    if (e16 == 0) {
+      s_mm[w][g][0] = mnv;
+      s_mm[w][g][1] = mxv;
+    }
+  }
+  __syncthreads();
+
+  // ---- select: row q, half hf; every wave passes the same barriers ----
+  const int q = w & 3, hf = w >> 2;
+  const bool live = t0 + q < P.T;
+  const int k = P.k;
+  const int n = live ? __builtin_amdgcn_readfirstlane(nvis(q)) : 0;
+  int32_t* out = P.idx + (row0 + q) * k;
+  float* row = srow[q];
+  float mn = INFINITY, mx = -INFINITY;
+  if (n > k) {
+#pragma unroll
+    for (int j = 0; j < FW; ++j) {
+      mn = fminf(mn, s_mm[j][q][0]);
+      mx = fmaxf(mx, s_mm[j][q][1]);
+    }
+  }
+  const float span = mx - mn;
+  const float scale = static_cast<float>(SEL_BINS - 2) / span;
+  // 0: no row, 1: every entry kept, 2: every score equal, 3: radix select,
+  // 4: binned select
+  int mode = !live ? 0 : n <= k ? 1 : !(span > 0.0f) ? 2 : !(scale < 3.0e38f) ? 3 : 4;
+  const int nq = (n + 255) >> 8, nqh = (nq + 1) >> 1;
+  const int c0 = hf * nqh, nc = min(nq, c0 + nqh) - c0;  // this half's steps: c0 .. c0 + nc
+  const unsigned long long below = (1ull << lane) - 1ull;
+  // this half's scores as t = (s - min) * (BINS-2) / (max - min) + 1, read
+  // once; entries past n get -inf
+  float4 tq[HSTEPS];
+  if (mode == 4) {
+    for (int i = lane + 64 * hf; i < SEL_HW; i += 128) hist[q][i] = 0;
+#pragma unroll
+    for (int i = 0; i < HSTEPS; ++i) {
+      if (i < nc) {
+        const float4 v = *reinterpret_cast<const float4*>(row + 4 * (64 * (c0 + i) + lane));
+        tq[i] = float4{fmaf(v.x - mn, scale, 1.0f), fmaf(v.y - mn, scale, 1.0f), fmaf(v.z - mn, scale, 1.0f),
+                       fmaf(v.w - mn, scale, 1.0f)};
+        if (c0 + i == nq - 1) {
+          const int s = 4 * (64 * (c0 + i) + lane);
+          if (s >= n) tq[i].x = -INFINITY;
+          if (s + 1 >= n) tq[i].y = -INFINITY;
+          if (s + 2 >= n) tq[i].z = -INFINITY;
+          if (s + 3 >= n) tq[i].w = -INFINITY;
+        }
       }
     }
   }
   __syncthreads();
-  // one wave per query row
-  const int q = w;
-  if (t0 + q >= P.T) return;
-  int32_t* out = P.idx + (row0 + q) * P.k;
-  const int n = nvis(q);
-  if (n <= P.k) {
-    for (int j = lane; j < P.k; j += 64) out[j] = j < n ? j : -1;
-    return;
+  auto binof = [](float t) {
+    return static_cast<int>(__builtin_amdgcn_fmed3f(t, 0.0f, static_cast<float>(SEL_BINS - 1)));
+  };
+  if (mode == 4) {
+#pragma unroll
+    for (int i = 0; i < HSTEPS; ++i) {
+      if (i < nc) {
+        const float tt[4] = {tq[i].x, tq[i].y, tq[i].z, tq[i].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int bn = binof(tt[u]);  // bin 2w + h counts in bits 16h .. 16h+15 of word w
+          atomicAdd(&hist[q][bn >> 1], 1 << (16 * (bn & 1)));
+        }
+      }
+    }
   }
-  wave_select(srow[q], n, P.k, P.score_dt == CSA_BF16 ? 16 : 32, hist[q], cidx[q], ckey[q], crank[q], out);
+  __syncthreads();
+  // the bin B of the k-th largest score (both waves of the row): lane l owns
+  // bins BINS-1-PER*l .. BINS-PER-PER*l (descending; words HW-16(l+1) ..
+  // HW-16l-1); the k largest scores lie in bins >= 1, so the search never
+  // reaches bin 0
+  int B = 1, rem = 0;
+  if (mode == 4) {
+    constexpr int PER = SEL_BINS / 64;
+    int cnts[PER], tot = 0;
+#pragma unroll
+    for (int j = 0; j < PER / 2; j += 4) {
+      const int4 h4 = *reinterpret_cast<const int4*>(&hist[q][SEL_HW - (PER / 2) * (lane + 1) + j]);
+      const int hw[4] = {h4.x, h4.y, h4.z, h4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {  // word (PER/2)(HW/(PER/2) - l - 1) + j + u: bins 2(..) (low), +1 (high)
+        const int jj = PER - 2 * (j + u);  // descending position of the word's high bin, plus 2
+        cnts[jj - 2] = static_cast<int>(static_cast<uint32_t>(hw[u]) >> 16);
+        cnts[jj - 1] = hw[u] & 0xFFFF;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) tot += cnts[j];
+    const int incl = wave_incl_scan(tot);
+    int bsel = -1, above = 0;
+    if (incl - tot < k && incl >= k) {
+      int cum = incl - tot;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) {
+        if (bsel < 0 && cum + cnts[j] >= k) { bsel = SEL_BINS - 1 - PER * lane - j; above = cum; }
+        cum += cnts[j];
+      }
+    }
+    const unsigned long long who = __ballot(bsel >= 0);
+    const int src = __ffsll(static_cast<long long>(who)) - 1;
+    B = __builtin_amdgcn_readlane(bsel, src);
+    rem = k - __builtin_amdgcn_readlane(above, src);  // entries of bin B to take
+  }
+  // bin > B  <=>  t >= B+1;  bin == B  <=>  B <= t < B+1 (t stays below BINS)
+  const float tb = static_cast<float>(B), tb1 = static_cast<float>(B + 1);
+  // this half's entries of bin B, in index order; hasb marks the steps
+  // that hold one (uniform)
+  uint32_t hasb = 0;
+  if (mode == 4) {
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < HSTEPS; ++i) {
+      if (i < nc) {
+        const float tt[4] = {tq[i].x, tq[i].y, tq[i].z, tq[i].w};
+        bool in[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) in[u] = tt[u] >= tb && tt[u] < tb1;
+        if (__ballot(in[0] || in[1] || in[2] || in[3])) {
+          hasb |= 1u << i;
+          const int s = 4 * (64 * (c0 + i) + lane);
+          int pos = cnt, total = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const unsigned long long m = __ballot(in[u]);
+            pos += mbcnt(m);
+            total += __popcll(m);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            if (in[u]) {
+              if (pos < SEL_CBH) { cidx[q][hf][pos] = s + u; ckey[q][hf][pos] = order_key(row[s + u]); }
+              ++pos;
+            }
+          }
+          cnt += total;
+        }
+      }
+    }
+    if (lane == 0) s_cnt[q][hf][0] = cnt;
+  }
+  __syncthreads();
+  const int cnt0 = s_cnt[q][0][0], cnt1 = s_cnt[q][1][0];
+  if (mode == 4 && (cnt0 > SEL_CBH || cnt1 > SEL_CBH)) mode = 3;
+  // rank of each bin-B entry among both halves' (half 0 first: index order):
+  // entries with a larger key, or an equal key and a lower index.  The
+  // candidates' keys sit in lanes (two per lane and half) and are read back
+  // one by one with readlane.
+  if (mode == 4) {
+    uint32_t kk[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {
+      const int ch = hh ? cnt1 : cnt0;
+      kk[hh][0] = lane < ch ? ckey[q][hh][lane] : 0u;
+      kk[hh][1] = lane + 64 < ch ? ckey[q][hh][lane + 64] : 0u;
+    }
+    const int cnth = hf ? cnt1 : cnt0, g0 = hf ? cnt0 : 0;
+    const uint32_t ke0 = hf ? kk[1][0] : kk[0][0], ke1 = hf ? kk[1][1] : kk[0][1];
+    const int ge0 = g0 + lane, ge1 = g0 + lane + 64;
+    int r0 = 0, r1 = 0;
+    for (int f = 0; f < cnt0 + cnt1; ++f) {
+      const int hh = f < cnt0 ? 0 : 1, e = hh ? f - cnt0 : f;
+      const uint32_t kf = __builtin_amdgcn_readlane(e < 64 ? kk[hh][0] : kk[hh][1], e & 63);
+      r0 += (kf > ke0 || (kf == ke0 && f < ge0)) ? 1 : 0;
+      r1 += (kf > ke1 || (kf == ke1 && f < ge1)) ? 1 : 0;
+    }
+    if (lane < cnth) crank[q][hf][lane] = r0;
+    if (lane + 64 < cnth) crank[q][hf][lane + 64] = r1;
+  }
+  __syncthreads();
+  // ordered output of each half: entries above B and the chosen entries of
+  // bin B, compacted (every score is in registers by now) into the row:
+  // half 0 from element 0, half 1 from element FUSED_NMAX/2 (k is at most
+  // 2048); positions from a prefix sum of each lane's take count
+  if (mode == 4) {
+    int* outl = reinterpret_cast<int*>(row) + (hf ? FUSED_NMAX / 2 : 0);
+    int* sink = &s_sink[w][lane];
+    int written = 0, seen = 0;
+#pragma unroll
+    for (int i = 0; i < HSTEPS; ++i) {
+      if (i < nc) {
+        const int s = 4 * (64 * (c0 + i) + lane);
+        const float tt[4] = {tq[i].x, tq[i].y, tq[i].z, tq[i].w};
+        bool take[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) take[u] = tt[u] >= tb1;
+        if (hasb & (1u << i)) {
+          bool inb[4];
+          int jb = seen, btotal = 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            inb[u] = tt[u] >= tb && !take[u];
+            const unsigned long long m = __ballot(inb[u]);
+            jb += mbcnt(m);
+            btotal += __popcll(m);
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            if (inb[u]) { take[u] = crank[q][hf][jb] < rem; ++jb; }
+          seen += btotal;
+        }
+        const int tk = (take[0] ? 1 : 0) + (take[1] ? 1 : 0) + (take[2] ? 1 : 0) + (take[3] ? 1 : 0);
+        const int incl = wave_incl_scan(tk);
+        int pos = written + incl - tk;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          *(take[u] ? outl + pos : sink) = s + u;
+          pos += take[u] ? 1 : 0;
+        }
+        written += __builtin_amdgcn_readlane(incl, 63);
+      }
+    }
+    if (hf == 0 && lane == 0) s_cnt[q][0][1] = written;
+  }
+  __syncthreads();
+  if (mode == 4) {
+    const int* o = reinterpret_cast<const int*>(row);
+    const int base1 = s_cnt[q][0][1];  // half 0's run
+    for (int j = lane + 64 * hf; j < k; j += 128) out[j] = j < base1 ? o[j] : o[FUSED_NMAX / 2 + j - base1];
+  } else if (mode == 3) {
+    if (hf == 0) wave_radix_select(row, n, k, P.score_dt == CSA_BF16 ? 16 : 32, hist[q], out);
+  } else if (mode == 2) {
+    for (int j = lane + 64 * hf; j < k; j += 128) out[j] = j;
+  } else if (mode == 1) {
+    for (int j = lane + 64 * hf; j < k; j += 128) out[j] = j < n ? j : -1;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -613,8 +759,8 @@ bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max) {
 
 int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
   dim3 grid((P.T + QG - 1) / QG, B);
-  if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_prefill_fused_kernel<true>, grid, dim3(256), 0, s, P);
-  else hipLaunchKernelGGL(index_prefill_fused_kernel<false>, grid, dim3(256), 0, s, P);
+  if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_prefill_fused_kernel<true>, grid, dim3(64 * FW), 0, s, P);
+  else hipLaunchKernelGGL(index_prefill_fused_kernel<false>, grid, dim3(64 * FW), 0, s, P);
   return check_launch("index_prefill_fused_kernel");
 }
 

@@ -184,3 +184,44 @@ def test_decode_all_ties_lowest_indices(n_entries):
     got = idx.cpu().numpy()
     assert list(got[0]) == list(range(k))
     assert list(got[1]) == list(range(k))
+
+
+@pytest.mark.parametrize("pattern", ["all_equal", "three_values", "bf16_ties"])
+def test_prefill_fused_ties(pattern):
+    """Fused prefill select under ties, against the oracle (ties to the
+    lower index): every score equal (one value between the extremes), keys
+    of three values (a threshold bin far larger than the candidate list:
+    radix fallback), and BF16-rounded scores of random keys (many exact
+    ties inside the threshold bin)."""
+    T, H, d, m, k, pos0 = 67, 16, 64, 4, 256, 4096
+    cap = (pos0 + T) // m
+    kc, K = key_cache("bf16", 1, cap, d, m, seed=27)
+    score_fmt = "f32"
+    if pattern == "all_equal":
+        kc.nope.zero_()
+    elif pattern == "three_values":
+        r = torch.arange(cap, device=DEV) % 3
+        row = synth.normal((1, 1, d), "krow", 27, device=DEV, dtype=torch.bfloat16)
+        kc.nope.copy_(row * (r.to(torch.bfloat16) - 1)[None, :, None])
+    else:
+        score_fmt = "bf16"
+    K = np64(kc.nope)[0]
+    qI = synth.normal((1, T, H, d), "qI", 27, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((1, T, H), "w", 27, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "bf16", "bf16", score_fmt, m, cap)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, idx)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = oracle_rows(np64(qI[0]), np64(w[0]), K, pos0 + np.arange(T), m, k, "bf16", score_fmt)
+    got = idx[0].cpu().numpy()
+    assert ascending_padded(got)
+    if pattern == "bf16_ties":
+        # the two sides round to BF16 from different fp32 / fp64 sums: an
+        # entry may land one BF16 step apart, so differences must sit within
+        # a few BF16 steps of the k-th score
+        _, bad = compare_topk(got, ref_idx, ref_sc, 1e-6, kth_rel_window=2.0 ** -6)
+        assert not bad
+    else:
+        # scores are exact here (products of zeros or of one key row), so
+        # the sets, ties included, match exactly
+        assert (got == ref_idx).all(), np.nonzero((got != ref_idx).any(1))[0][:5]
