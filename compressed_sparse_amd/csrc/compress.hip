@@ -13,6 +13,11 @@
 
 namespace csa {
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 struct CompressParams {
   int m, overlap, d_nope, d_rope, c, in_dt, nope_dt, rope_dt;
   int R, NT;
@@ -34,44 +39,55 @@ __device__ __forceinline__ float* ring_row(const CompressParams& P, int b, int64
   return P.ring + ((static_cast<size_t>(b) * P.R + slot) * P.NT + which) * P.c;
 }
 
+constexpr int CW_ROWS = 4;  // window rows per softmax batch
+
+// One batch of a window's softmax for one channel: logits lg (-inf past the
+// window) and values vv of CW_ROWS rows folded into the running max mx,
+// weight sum sw and weighted sum acc, with one rescale per batch.  Every
+// path (prefill kernels, decode) goes through this, in the same row order,
+// so they agree bit for bit.
+__device__ __forceinline__ void softmax_batch(const float (&lg)[CW_ROWS], const float (&vv)[CW_ROWS], float& mx,
+                                              float& sw, float& acc) {
+  float bm = lg[0];
+#pragma unroll
+  for (int u = 1; u < CW_ROWS; ++u) bm = fmaxf(bm, lg[u]);
+  const float nm = fmaxf(mx, bm);
+  const float sc = __expf(mx - nm);  // 0 on the first batch
+  float s = 0.0f, a = 0.0f;
+#pragma unroll
+  for (int u = 0; u < CW_ROWS; ++u) {
+    const float e = __expf(lg[u] - nm);  // 0 past the window
+    s += e;
+    a = fmaf(e, vv[u], a);
+  }
+  sw = fmaf(sw, sc, s);
+  acc = fmaf(acc, sc, a);
+  mx = nm;
+}
+
 // Weighted value of channel j of entry i, rows fetched by `get(which, t)`:
-// an online softmax over the window's rows (C^a rows of window i, then the
-// C^b rows of window i-1).  The rows' loads are issued eight at a time
-// (clamped to the last row, so branch-free) before their softmax steps.
+// the window's rows (C^a rows of window i, then the C^b rows of window
+// i-1) in batches of CW_ROWS (clamped to the last row, so branch-free).
 template <class Get>
 __device__ __forceinline__ float compress_channel(const CompressParams& P, int64_t i, int j, Get get) {
-  float mx = -INFINITY, sum = 0.0f, acc = 0.0f;
-  auto take = [&](float logit, float v) {
-    if (logit > mx) {
-      float sc = expf(mx - logit);  // 0 on the first row
-      sum = sum * sc + 1.0f;
-      acc = acc * sc + v;
-      mx = logit;
-    } else {
-      float e = expf(logit - mx);
-      sum += e;
-      acc += e * v;
-    }
-  };
-  constexpr int U = 8;
-  auto side = [&](int zw, int vw, const float* Bw, int64_t t0) {
-    for (int r0 = 0; r0 < P.m; r0 += U) {
-      float z[U], v[U], bw[U];
+  const int nrow = P.m + ((P.overlap && i >= 1) ? P.m : 0);
+  float mx = -INFINITY, sw = 0.0f, acc = 0.0f;
+  for (int r0 = 0; r0 < nrow; r0 += CW_ROWS) {
+    float lg[CW_ROWS], vv[CW_ROWS];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int r = r0 + u < P.m ? r0 + u : P.m - 1;
-        z[u] = get(zw, t0 + r, j);
-        v[u] = get(vw, t0 + r, j);
-        bw[u] = Bw[r * P.c + j];
-      }
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-        if (r0 + u < P.m) take(z[u] + bw[u], v[u]);
+    for (int u = 0; u < CW_ROWS; ++u) {
+      const int rho = min(r0 + u, nrow - 1);
+      const bool sa = rho < P.m;
+      const int r = sa ? rho : rho - P.m;
+      const int64_t t = sa ? i * P.m + r : (i - 1) * P.m + r;
+      const float z = get(sa ? RING_ZA : RING_ZB, t, j);
+      vv[u] = get(sa ? RING_A : RING_B, t, j);
+      const float bw = (sa ? P.Ba : P.Bb)[r * P.c + j];
+      lg[u] = r0 + u < nrow ? z + bw : -INFINITY;
     }
-  };
-  side(RING_ZA, RING_A, P.Ba, i * P.m);
-  if (P.overlap && i >= 1) side(RING_ZB, RING_B, P.Bb, (i - 1) * P.m);
-  return acc / sum;
+    softmax_batch(lg, vv, mx, sw, acc);
+  }
+  return acc / sw;
 }
 
 // RoPE + storage of the entry held in buf[0..c).  All threads call it.
@@ -156,6 +172,202 @@ __global__ void __launch_bounds__(256) compress_prefill_kernel(CompressParams P,
   finalize_entry(P, buf, red, b, i);
 }
 
+// Lanes per entry: enough for the 8-channel groups and the RoPE pairs, a
+// power of two, so that a wave holds 64 / lanes entries.
+__host__ __device__ inline int wave_lanes_per_entry(int ng, int np) {
+  const int need = ng > np ? ng : np;
+  int l = 1;
+  while (l < need) l <<= 1;
+  return l;
+}
+
+// Prefill, a group of lanes per entry (a whole wave for 576-wide entries,
+// 8 lanes for 64-wide ones; workgroup: 4 waves).  Lane l of the group owns
+// the eight channels 8l .. 8l+7 of the non-RoPE part (l < d_nope / 8) and
+// the RoPE pair d_nope + 2l, +1 (l < d_rope / 2), so the rotation stays in
+// the lane and every load is a whole 16-byte (8-byte, 4-byte) piece.  A batch
+// of CW_ROWS window rows is loaded at once; the softmax of each channel
+// then runs over the batch with one rescale per batch (the window's rows:
+// C^a rows of window i, then the C^b rows of window i-1).  Scale reductions
+// of the storage formats run across lanes.
+template <bool IN_BF16>
+__global__ void __launch_bounds__(256, 2) compress_prefill_wave_kernel(CompressParams P, int64_t i_first,
+                                                                    int64_t i_end) {
+  const int lane = threadIdx.x & 63;
+  const int b = blockIdx.y;
+  const int ng = P.d_nope / 8, np = P.d_rope / 2;
+  const int lpe = wave_lanes_per_entry(ng, np), epw = 64 / lpe, ll = lane & (lpe - 1);
+  const int64_t i0 = i_first + (4 * static_cast<int64_t>(blockIdx.x) + (threadIdx.x >> 6)) * epw;
+  if (i0 >= i_end) return;
+  const int64_t i = i0 + lane / lpe;  // this lane's entry
+  const bool ok = i < i_end;
+  const bool hg = ok && ll < ng, hp = ok && ll < np;
+  const int jg = 8 * ll, jp = P.d_nope + 2 * ll;  // this lane's channels
+  const int nrow = P.m + ((P.overlap && i >= 1) ? P.m : 0);
+  const int nrow_w = P.overlap ? 2 * P.m : P.m;  // the wave's longest window
+  // 8 + 2 channels: running max, sum of weights, weighted sum
+  float mx[10], sw[10], acc[10];
+#pragma unroll
+  for (int c = 0; c < 10; ++c) { mx[c] = -INFINITY; sw[c] = 0.0f; acc[c] = 0.0f; }
+  for (int r0 = 0; r0 < nrow_w; r0 += CW_ROWS) {
+    float lg[CW_ROWS][10], vv[CW_ROWS][10];
+#pragma unroll
+    for (int u = 0; u < CW_ROWS; ++u) {
+      const int rho = min(r0 + u, nrow - 1);
+      const bool sa = rho < P.m;  // side a (C^a of window i) or side b (C^b of window i-1)
+      const int r = sa ? rho : rho - P.m;
+      const int64_t t = sa ? i * P.m + r : (i - 1) * P.m + r;
+      const float* bw = (sa ? P.Ba : P.Bb) + static_cast<size_t>(r) * P.c;
+      float z[10], v[10];
+      if (t >= P.pos0) {
+        const size_t row = (static_cast<size_t>(b) * P.T + (t - P.pos0)) * P.c;
+        const void* zs = sa ? P.za : P.zb;
+        const void* vs = sa ? P.a : P.b;
+        if constexpr (IN_BF16) {
+          const bf16_t* zp = static_cast<const bf16_t*>(zs) + row;
+          const bf16_t* vp = static_cast<const bf16_t*>(vs) + row;
+          u32x4 zq = {0u, 0u, 0u, 0u}, vq = zq;
+          uint32_t zr = 0u, vr = 0u;
+          if (hg) { zq = *reinterpret_cast<const u32x4*>(zp + jg); vq = *reinterpret_cast<const u32x4*>(vp + jg); }
+          if (hp) { zr = *reinterpret_cast<const uint32_t*>(zp + jp); vr = *reinterpret_cast<const uint32_t*>(vp + jp); }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            z[2 * c] = __uint_as_float(zq[c] << 16); z[2 * c + 1] = __uint_as_float(zq[c] & 0xFFFF0000u);
+            v[2 * c] = __uint_as_float(vq[c] << 16); v[2 * c + 1] = __uint_as_float(vq[c] & 0xFFFF0000u);
+          }
+          z[8] = __uint_as_float(zr << 16); z[9] = __uint_as_float(zr & 0xFFFF0000u);
+          v[8] = __uint_as_float(vr << 16); v[9] = __uint_as_float(vr & 0xFFFF0000u);
+        } else {
+          const float* zp = static_cast<const float*>(zs) + row;
+          const float* vp = static_cast<const float*>(vs) + row;
+          f32x4 z0 = {}, z1 = {}, v0 = {}, v1 = {};
+          f32x2 z2 = {}, v2 = {};
+          if (hg) {
+            z0 = *reinterpret_cast<const f32x4*>(zp + jg); z1 = *reinterpret_cast<const f32x4*>(zp + jg + 4);
+            v0 = *reinterpret_cast<const f32x4*>(vp + jg); v1 = *reinterpret_cast<const f32x4*>(vp + jg + 4);
+          }
+          if (hp) { z2 = *reinterpret_cast<const f32x2*>(zp + jp); v2 = *reinterpret_cast<const f32x2*>(vp + jp); }
+#pragma unroll
+          for (int c = 0; c < 4; ++c) { z[c] = z0[c]; z[4 + c] = z1[c]; v[c] = v0[c]; v[4 + c] = v1[c]; }
+          z[8] = z2[0]; z[9] = z2[1]; v[8] = v2[0]; v[9] = v2[1];
+        }
+      } else {  // rows before this call: the fp32 ring
+        const float* zp = ring_row(P, b, t, sa ? RING_ZA : RING_ZB);
+        const float* vp = ring_row(P, b, t, sa ? RING_A : RING_B);
+#pragma unroll
+        for (int c = 0; c < 10; ++c) { z[c] = 0.0f; v[c] = 0.0f; }
+        if (hg)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) { z[c] = zp[jg + c]; v[c] = vp[jg + c]; }
+        if (hp) { z[8] = zp[jp]; z[9] = zp[jp + 1]; v[8] = vp[jp]; v[9] = vp[jp + 1]; }
+      }
+      float bb[10];
+#pragma unroll
+      for (int c = 0; c < 10; ++c) bb[c] = 0.0f;
+      if (hg) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(bw + jg), b1 = *reinterpret_cast<const f32x4*>(bw + jg + 4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) { bb[c] = b0[c]; bb[4 + c] = b1[c]; }
+      }
+      if (hp) { bb[8] = bw[jp]; bb[9] = bw[jp + 1]; }
+      const bool live = r0 + u < nrow;
+#pragma unroll
+      for (int c = 0; c < 10; ++c) {
+        lg[u][c] = live ? z[c] + bb[c] : -INFINITY;
+        vv[u][c] = v[c];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 10; ++c) {
+      float l1[CW_ROWS], v1[CW_ROWS];
+#pragma unroll
+      for (int u = 0; u < CW_ROWS; ++u) { l1[u] = lg[u][c]; v1[u] = vv[u][c]; }
+      softmax_batch(l1, v1, mx[c], sw[c], acc[c]);
+    }
+  }
+  float x[10];
+#pragma unroll
+  for (int c = 0; c < 10; ++c) x[c] = acc[c] / sw[c];
+  // RoPE of the pair at the entry's last position
+  if (hp) {
+    float sn, co;
+    rope_sincos(i * P.m + P.m - 1, ll, P.d_rope, P.base, &sn, &co);
+    const double x0 = x[8], x1 = x[9];
+    x[8] = static_cast<float>(x0 * co - x1 * sn);
+    x[9] = static_cast<float>(x0 * sn + x1 * co);
+  }
+  const size_t e = static_cast<size_t>(b) * P.cap + i;
+  switch (P.nope_dt) {
+    case CSA_F32:
+      if (hg) {
+        float* dst = static_cast<float*>(P.nope) + e * P.d_nope + jg;
+        *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
+        *reinterpret_cast<f32x4*>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
+      }
+      break;
+    case CSA_BF16:
+      if (hg) {
+        u32x4 o;
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          o[c] = static_cast<uint32_t>(f32_to_bf16(x[2 * c])) | (static_cast<uint32_t>(f32_to_bf16(x[2 * c + 1])) << 16);
+        *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.nope) + e * P.d_nope + jg) = o;
+      }
+      break;
+    case CSA_FP8E4M3: {
+      float am = 0.0f;
+      if (hg)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(x[c]));
+      for (int o = 1; o < lpe; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));  // over the entry's lanes
+      const float s = am > 0.0f ? am / 448.0f : 1.0f;
+      if (hg) {
+        uint32_t w0 = 0u, w1 = 0u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          w0 |= f32_to_e4m3(x[c] / s) << (8 * c);
+          w1 |= f32_to_e4m3(x[4 + c] / s) << (8 * c);
+        }
+        *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(P.nope) + e * P.d_nope + jg) = u32x2{w0, w1};
+      }
+      if (ok && ll == 0) static_cast<float*>(P.scale)[e] = s;
+      break;
+    }
+    case CSA_MXFP4: {
+      // block of 32 channels = lanes 4k .. 4k+3
+      float am = 0.0f;
+      if (hg)
+#pragma unroll
+        for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(x[c]));
+      am = fmaxf(am, __shfl_xor(am, 1));
+      am = fmaxf(am, __shfl_xor(am, 2));
+      const int ex = mx_exponent(am);
+      const float inv = exp2i(-ex);
+      if (hg) {
+        uint32_t wd = 0u;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) wd |= f32_to_e2m1(x[c] * inv) << (4 * c);
+        *reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(P.nope) + e * (P.d_nope / 2) + 4 * ll) = wd;
+        if ((ll & 3) == 0) static_cast<uint8_t*>(P.scale)[e * (P.d_nope / 32) + ll / 4] = static_cast<uint8_t>(ex + 127);
+      }
+      break;
+    }
+  }
+  if (hp) {
+    if (P.rope_dt == CSA_F32) {
+      *reinterpret_cast<f32x2*>(static_cast<float*>(P.rope) + e * P.d_rope + 2 * ll) = f32x2{x[8], x[9]};
+    } else {
+      const uint32_t o = static_cast<uint32_t>(f32_to_bf16(x[8])) | (static_cast<uint32_t>(f32_to_bf16(x[9])) << 16);
+      *reinterpret_cast<uint32_t*>(static_cast<bf16_t*>(P.rope) + e * P.d_rope + 2 * ll) = o;
+    }
+  }
+}
+
+// the wave kernel's shapes: one 8-channel group and one RoPE pair per lane
+static bool compress_wave_ok(const CompressParams& P) {
+  return P.d_nope % 8 == 0 && P.d_nope <= 512 && P.d_rope <= 128 && P.c % 8 == 0;
+}
+
 // Copies token rows [t_first, pos0 + T) into the ring (after the entries of
 // the same call have read the older rows).
 __global__ void __launch_bounds__(256) ring_store_kernel(CompressParams P, int64_t t_first) {
@@ -206,7 +418,9 @@ __global__ void __launch_bounds__(1024) compress_decode_kernel(CompressParams P,
     if (emit) {
       auto get = [&](int which, int64_t t, int jj) -> float {
         const float v = ring_row(P, b, t, which)[jj];
-        return t == pos ? cur[which] : v;
+        const float c = which == RING_A ? cur[RING_A] : which == RING_ZA ? cur[RING_ZA]
+                      : which == RING_B ? cur[RING_B] : cur[RING_ZB];  // selects, not an indexed array
+        return t == pos ? c : v;
       };
       buf[j] = compress_channel(P, i, j, get);
     }
@@ -305,9 +519,19 @@ extern "C" int csa_compress_prefill(const csa_cache_desc* desc, int B, int T, in
   hipStream_t s = as_stream(stream);
   const size_t lds = (32 + P.c) * sizeof(float);
   if (i_end > i_first) {
-    hipLaunchKernelGGL(compress_prefill_kernel, dim3(static_cast<unsigned>(i_end - i_first), B), dim3(256),
-                       lds, s, P, i_first);
-    if ((st = check_launch("compress_prefill_kernel")) != CSA_OK) return st;
+    if (compress_wave_ok(P)) {
+      const int per_wg = 4 * (64 / wave_lanes_per_entry(P.d_nope / 8, P.d_rope / 2));  // entries
+      const dim3 grid(static_cast<unsigned>((i_end - i_first + per_wg - 1) / per_wg), B);
+      if (P.in_dt == CSA_BF16)
+        hipLaunchKernelGGL(compress_prefill_wave_kernel<true>, grid, dim3(256), 0, s, P, i_first, i_end);
+      else
+        hipLaunchKernelGGL(compress_prefill_wave_kernel<false>, grid, dim3(256), 0, s, P, i_first, i_end);
+      if ((st = check_launch("compress_prefill_wave_kernel")) != CSA_OK) return st;
+    } else {
+      hipLaunchKernelGGL(compress_prefill_kernel, dim3(static_cast<unsigned>(i_end - i_first), B), dim3(256),
+                         lds, s, P, i_first);
+      if ((st = check_launch("compress_prefill_kernel")) != CSA_OK) return st;
+    }
   }
   const int64_t t_first = (pos0 + T - P.R > pos0) ? pos0 + T - P.R : pos0;
   hipLaunchKernelGGL(ring_store_kernel, dim3(static_cast<unsigned>(pos0 + T - t_first), B), dim3(256), 0, s,
