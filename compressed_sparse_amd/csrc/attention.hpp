@@ -30,6 +30,6 @@ size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t 
 // BF16-cache kernel of the MFMA path over B sequences (T queries each, or
 // `splits` entry ranges of `per` entries when part != NULL, which then
 // receives the split partials).
-void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, float* part);
+void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, void* part);
 
 }  // namespace csa

@@ -322,7 +322,7 @@ __device__ __forceinline__ void rope_q(const Theta& th, int64_t pos, bf16x8 (&qf
 
 template <bool FP8, bool DENSE, bool SPLIT>
 __global__ void __launch_bounds__(NT, 1)
-attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* part, int64_t nitems, int nbatch) {
+attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* part, int64_t nitems, int nbatch) {
   typedef Lay<FP8> L;
   __shared__ __attribute__((aligned(16))) uint8_t kb0[L::KBUF];
   __shared__ __attribute__((aligned(16))) uint8_t kb1[L::KBUF];
@@ -403,16 +403,16 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
   bool staged = false;  // an output waits in the free tile buffer
   size_t staged_qrow = 0;
 
-  // Stores the staged output rows (16 per wave) from `buf`: row h chunk c
-  // sits at chunk c ^ (h & 15).
-  auto store_staged = [&](const uint8_t* buf) {
+  // Stores the staged output rows (16 per wave) from `buf` to rows dst +
+  // h * DN: row h chunk c sits at chunk c ^ (h & 15).
+  auto store_staged = [&](const uint8_t* buf, bf16_t* dst) {
     int ln = lane;
     asm volatile("" : "+v"(ln));  // lane offsets recomputed per call
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int h = 16 * w + i;
       const u32x4 v = *reinterpret_cast<const u32x4*>(buf + h * NROW + 16 * (ln ^ (h & 15)));
-      *reinterpret_cast<u32x4*>(static_cast<bf16_t*>(P.o) + (staged_qrow + h) * DN + 8 * ln) = v;
+      *reinterpret_cast<u32x4*>(dst + static_cast<size_t>(h) * DN + 8 * ln) = v;
     }
   };
 
@@ -455,7 +455,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
       wait_vmem();
       lds_sync();  // tile j in LDS; every wave done with tile j-1 (its buffer, pbuf, s_alpha)
       if (staged) {  // the previous item's output, staged in nxt
-        store_staged(nxt);
+        store_staged(nxt, static_cast<bf16_t*>(P.o) + staged_qrow * DN);
         lds_sync();
         staged = false;
       }
@@ -670,51 +670,40 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
     uint8_t* stage = par ? kb0 : kb1;  // not the buffer of the next item's first tile
     // O^T block (mb, nb): lane = head 32nb + lane%32, register v = value dim
     // 128w + 32mb + acc_row(v)
+    // partials of a decode split: normalised BF16 rows [B][splits][NH][DN],
+    // then the log2-sum-exp per head, fp32 [B][splits][NH]
+    const size_t slot = static_cast<size_t>(I.b) * splits + I.split;
+    bf16_t* part_o = static_cast<bf16_t*>(part);
+    float* part_lse = reinterpret_cast<float*>(part_o + static_cast<size_t>(nbatch) * splits * (NH * DN));
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int h = 32 * nb + (lane & 31);
       const float ltot = s_xchg[0][h] + s_xchg[1][h];
-      if (!SPLIT) {
-        const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
+      const float inv = ltot > 0.0f ? 1.0f / ltot : 0.0f;
 #pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
+      for (int mb = 0; mb < 4; ++mb)
 #pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const f32x16& o = oacc[mb][nb];
-            const uint32_t lo = pack2_bf16(o[4 * jq] * inv, o[4 * jq + 1] * inv);
-            const uint32_t hi2 = pack2_bf16(o[4 * jq + 2] * inv, o[4 * jq + 3] * inv);
-            // dims 128w + 32mb + 8jq + 4half: chunk 16w + 4mb + jq, byte 8half
-            const int c = 16 * w + 4 * mb + jq;
-            *reinterpret_cast<uint2*>(stage + h * NROW + 16 * (c ^ (h & 15)) + 8 * half) = make_uint2(lo, hi2);
-          }
-        if (P.lse && w == 0 && lane < 32)
-          P.lse[I.qrow + h] = ltot > 0.0f ? (s_m[h] + log2f(ltot)) * LN2 : -INFINITY;
-      } else {
-        // partial: [B][splits][NH][DN] O, then [B][splits][NH][2] (max, sum)
-        const size_t slot = static_cast<size_t>(I.b) * splits + I.split;
-        float* po = part + slot * (NH * DN) + static_cast<size_t>(h) * DN + 128 * w;
-#pragma unroll
-        for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-          for (int jq = 0; jq < 4; ++jq) {
-            const f32x16& o = oacc[mb][nb];
-            *reinterpret_cast<float4*>(po + 32 * mb + jq * 8 + half * 4) =
-                make_float4(o[4 * jq], o[4 * jq + 1], o[4 * jq + 2], o[4 * jq + 3]);
-          }
-        if (w == 0 && lane < 32) {
-          float* pml = part + static_cast<size_t>(nbatch) * splits * (NH * DN) + slot * (2 * NH);
-          pml[2 * h] = s_m[h];
-          pml[2 * h + 1] = ltot;
+        for (int jq = 0; jq < 4; ++jq) {
+          const f32x16& o = oacc[mb][nb];
+          const uint32_t lo = pack2_bf16(o[4 * jq] * inv, o[4 * jq + 1] * inv);
+          const uint32_t hi2 = pack2_bf16(o[4 * jq + 2] * inv, o[4 * jq + 3] * inv);
+          // dims 128w + 32mb + 8jq + 4half: chunk 16w + 4mb + jq, byte 8half
+          const int c = 16 * w + 4 * mb + jq;
+          *reinterpret_cast<uint2*>(stage + h * NROW + 16 * (c ^ (h & 15)) + 8 * half) = make_uint2(lo, hi2);
         }
+      if (w == 0 && lane < 32) {
+        const float l2 = ltot > 0.0f ? s_m[h] + log2f(ltot) : -INFINITY;
+        if (SPLIT) part_lse[slot * NH + h] = l2;
+        else if (P.lse) P.lse[I.qrow + h] = l2 * LN2;
       }
     }
     // the output stays staged until the next item's first tile has landed,
-    // when there is one; else it is stored now
+    // when there is one; else (and for split partials) it is stored now
     const bool defer = !SPLIT && has_next && next_started && nvalid_n > 0;
     staged_qrow = I.qrow;
-    if (!SPLIT && !defer) {
+    if (!defer) {
       lds_sync();  // every wave's part of the rows written
-      store_staged(stage);
+      store_staged(stage, SPLIT ? part_o + slot * (NH * DN) : static_cast<bf16_t*>(P.o) + staged_qrow * DN);
     }
     if (!has_next) break;
     if (!next_started) {  // this item had no tile: start the next one now
@@ -738,7 +727,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, float* p
 
 // One persistent workgroup per compute unit (at most one item each when the
 // items are fewer).
-void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, float* part) {
+void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, void* part) {
   static int cus[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;

@@ -5,7 +5,8 @@
 //
 // Prefill runs one query per work item; decode splits each sequence's entry
 // list (CSA) or visible entries (HCA) over several work items, each writing
-// an unnormalised partial (O, max, sum) that attn_merge_kernel combines.
+// a partial (O normalised by its own weights, as BF16, and the log2 of its
+// weight sum) that attn_merge_kernel combines.
 #include <cmath>
 
 #include "attention.hpp"
@@ -29,28 +30,31 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
-// Combines split partials by log-sum-exp; grid (NH, B), one thread per 4
-// value dims (128 threads), the head's split weights computed once in LDS.
-// S >= splits is a power of two: every thread's S partial loads (clamped to
-// the last split) are issued before the weights are known.
+// Combines split partials by log-sum-exp: O = sum_s 2^(l_s - M) O_s / sum_s
+// 2^(l_s - M), l_s the split's log2 weight sum and M their maximum; grid
+// (NH, B), one thread per 4 value dims (128 threads), the head's split
+// weights computed once in LDS.  S >= splits is a power of two: every
+// thread's S partial loads (clamped to the last split) are issued before
+// the weights are known.
 template <int S>
-__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams P, int splits, const float* part, int B) {
+__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams P, int splits, const void* part, int B) {
   __shared__ float s_f[S];
   __shared__ float s_L, s_M;
   const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const float* po = part + static_cast<size_t>(b) * splits * (NH * DN) + static_cast<size_t>(h) * DN + 4 * tid;
-  float4 v[S];
+  const bf16_t* po = static_cast<const bf16_t*>(part) + static_cast<size_t>(b) * splits * (NH * DN) +
+                     static_cast<size_t>(h) * DN + 4 * tid;
+  uint2 v[S];
 #pragma unroll
   for (int sp = 0; sp < S; ++sp)
-    v[sp] = *reinterpret_cast<const float4*>(po + static_cast<size_t>(min(sp, splits - 1)) * NH * DN);
-  const float* pml = part + static_cast<size_t>(B) * splits * (NH * DN) + static_cast<size_t>(b) * splits * (2 * NH);
+    v[sp] = *reinterpret_cast<const uint2*>(po + static_cast<size_t>(min(sp, splits - 1)) * NH * DN);
+  const float* pl = reinterpret_cast<const float*>(static_cast<const bf16_t*>(part) + static_cast<size_t>(B) * splits * (NH * DN)) +
+                    static_cast<size_t>(b) * splits * NH;
   if (tid < 64) {
-    const float ms = tid < splits ? pml[(tid * NH + h) * 2] : -INFINITY;
-    const float ls = tid < splits ? pml[(tid * NH + h) * 2 + 1] : 0.0f;
-    float M = ms;
+    const float ls = tid < splits ? pl[tid * NH + h] : -INFINITY;
+    float M = ls;
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = (tid < splits && ms != -INFINITY) ? exp2f(ms - M) : 0.0f;
-    float L = ls * f;
+    const float f = ls != -INFINITY ? exp2f(ls - M) : 0.0f;
+    float L = f;
     for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
     if (tid < S) s_f[tid] = f;
     if (tid == 0) { s_L = L; s_M = M; }
@@ -62,11 +66,19 @@ __global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams P, int split
 #pragma unroll
   for (int sp = 0; sp < S; ++sp) {
     const float f = s_f[sp];  // 0 past the last split and for empty splits
-    acc.x += v[sp].x * f; acc.y += v[sp].y * f; acc.z += v[sp].z * f; acc.w += v[sp].w * f;
+    acc.x = fmaf(__uint_as_float(v[sp].x << 16), f, acc.x);
+    acc.y = fmaf(__uint_as_float(v[sp].x & 0xFFFF0000u), f, acc.y);
+    acc.z = fmaf(__uint_as_float(v[sp].y << 16), f, acc.z);
+    acc.w = fmaf(__uint_as_float(v[sp].y & 0xFFFF0000u), f, acc.w);
   }
   bf16_t* out = static_cast<bf16_t*>(P.o) + (static_cast<size_t>(b) * NH + h) * DN + 4 * tid;
   *reinterpret_cast<uint2*>(out) = make_uint2(pack2_bf16(acc.x * inv, acc.y * inv), pack2_bf16(acc.z * inv, acc.w * inv));
   if (P.lse && tid == 0) P.lse[static_cast<size_t>(b) * NH + h] = L > 0.0f ? (s_M + log2f(L)) * LN2 : -INFINITY;
+}
+
+// bytes of the split partials of B sequences
+size_t part_bytes(int B, int splits) {
+  return static_cast<size_t>(B) * splits * NH * (DN * sizeof(bf16_t) + sizeof(float));
 }
 
 int decode_splits(int B, int64_t ntiles) {
@@ -89,7 +101,7 @@ bool mfma_attn_supported(const AttnParams& P) {
 size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, int) {
   if (op != CSA_OP_SPARSE_ATTN_DECODE && op != CSA_OP_DENSE_ATTN_DECODE) return 0;
   if (d->n_heads != NH || d->d_nope != DN || d->d_rope != DRP) return 0;
-  return static_cast<size_t>(B) * MAX_SPLITS * (NH * DN + 2 * NH) * sizeof(float);
+  return part_bytes(B, MAX_SPLITS);
 }
 
 int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
@@ -109,9 +121,9 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   }
   const int64_t tiles_per = (ntiles + splits - 1) / splits;
   const int64_t per = tiles_per * TILE;
-  const size_t need = static_cast<size_t>(B) * splits * (NH * DN + 2 * NH) * sizeof(float);
+  const size_t need = part_bytes(B, splits);
   if (!P.ws || P.ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace too small for the split partials");
-  float* part = static_cast<float*>(P.ws);
+  void* part = P.ws;
   launch_attn_bf16(P, dense, B, s, splits, per, part);
   int st = check_launch("attn_bf16_kernel");
   if (st != CSA_OK) return st;
