@@ -79,8 +79,12 @@ constexpr int SPF = 6;                     // S^T A operands in flight
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float LN2 = 0.6931471805599453f;
 
+// RoPE frequencies theta_p = base^(-2p/d_rope) = r^p, r = base^(-2/d_rope):
+// the uniform powers a lane needs to form its own 16 (held in scalar
+// registers; a per-lane table here would be read with lane-dependent
+// offsets and kept live in vector registers across the item loop)
 struct Theta {
-  double t[DRP / 2];  // base^(-2p/d_rope)
+  double r1, r2, r3, r4, r8;
 };
 
 // 16-byte chunk c of row r sits at chunk c ^ swz(r).  The LDS has 64 banks
@@ -222,10 +226,11 @@ __device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int s
   // decode (split) items take the sequence's position, prefill ones pos0 + t;
   // kept in scalar registers
   if (SPLIT) {
-    const int64_t v = P.pos_dev[I.b];
-    I.pos = static_cast<int64_t>(
-        (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v >> 32)))) << 32) |
-        static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<int>(v & 0xFFFFFFFF))));
+    // a scalar load (constant address space, uniform index): a vector load
+    // here would make its wait drain every load and gather in flight
+    typedef const __attribute__((address_space(4))) int64_t cpos_t;
+    const int bb = __builtin_amdgcn_readfirstlane(I.b);
+    I.pos = reinterpret_cast<cpos_t*>(reinterpret_cast<uintptr_t>(P.pos_dev))[bb];
   } else {
     I.pos = P.pos0 + I.t;
   }
@@ -301,15 +306,20 @@ __device__ __forceinline__ bf16x8 load_qs(const AttnParams& P, size_t qrow, int 
 }
 
 // Turns the RoPE k-steps (dims 512..575, pairs (2p, 2p+1)) by position pos.
+// Lane pair p = 8(s - DN/16) + 4 half + i: theta_p = r^(4 half) r^(8(s -
+// DN/16)) r^i, a few fp64 products (relative error ~1e-15).
 __device__ __forceinline__ void rope_q(const Theta& th, int64_t pos, bf16x8 (&qf)[QS]) {
-  const int half = (threadIdx.x & 63) >> 5;
+  int half = (threadIdx.x & 63) >> 5;
+  asm volatile("" : "+v"(half));  // formed per call: kept out of registers between items
+  double tj = half ? th.r4 : 1.0;
 #pragma unroll
   for (int s = DN / 16; s < QS; ++s) {
     u32x4 raw = __builtin_bit_cast(u32x4, qf[s]);
+    if (s > DN / 16) tj *= th.r8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int p = 8 * (s - DN / 16) + 4 * half + i;
-      const double ang = static_cast<double>(pos) * th.t[p];
+      const double theta = i == 0 ? tj : i == 1 ? tj * th.r1 : i == 2 ? tj * th.r2 : tj * th.r3;
+      const double ang = static_cast<double>(pos) * theta;
       const float red = static_cast<float>(ang - rint(ang * 0.15915494309189535) * 6.283185307179586);
       const float sn = __sinf(red), cs = __cosf(red);
       const float x0 = bf16_to_f32(static_cast<bf16_t>(raw[i] & 0xFFFFu));
@@ -738,7 +748,11 @@ void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int
     cu = v;
   }
   Theta th;
-  for (int p = 0; p < DRP / 2; ++p) th.t[p] = std::pow(P.base, -2.0 * p / DRP);
+  th.r1 = std::pow(P.base, -2.0 / DRP);
+  th.r2 = std::pow(P.base, -4.0 / DRP);
+  th.r3 = std::pow(P.base, -6.0 / DRP);
+  th.r4 = std::pow(P.base, -8.0 / DRP);
+  th.r8 = std::pow(P.base, -16.0 / DRP);
   const bool split = part != nullptr;
   const int64_t nitems = static_cast<int64_t>(B) * (split ? splits : P.T);
   if (nitems <= 0) return;
