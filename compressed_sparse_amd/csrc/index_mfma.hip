@@ -579,7 +579,7 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
 // ---------------------------------------------------------------------------
 // streaming scan: one query row x 1024 entries per workgroup
 // ---------------------------------------------------------------------------
-constexpr int SCAN_CHUNK = 2048;
+constexpr int SCAN_CHUNK = 1024;
 
 template <int KFMT, bool QMX>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT == CSA_FP8E4M3 ? 3 : 4))) index_scan_kernel(IndexParams P) {
@@ -649,7 +649,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   // loaded (clamped to the last entry, so branch-free) while the previous
   // batch is widened, multiplied and reduced over heads (two register sets,
   // used in turn).
-  constexpr int NB = KFMT == CSA_BF16 ? 4 : 8;
+  constexpr int NB = 4;
   auto load = [&](int e0, u32x4 (&ra)[NB], u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
