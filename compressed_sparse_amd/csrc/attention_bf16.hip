@@ -172,10 +172,11 @@ __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, in
   if (!FP8 && it < 16) {
     const int id = __builtin_amdgcn_readlane(my_id, it);
     const int r = 16 * w + it;
-    // scalar row base, lane offset of the chunk that belongs at slot `lane`
-    const uint8_t* row = static_cast<const uint8_t*>(P.nope) + (seq + static_cast<size_t>(id)) * NROW;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(row, NROW), (lds_void*)(buf + r * NROW), 16, 16 * (lane ^ swz(r)),
-                                             0, 0, 0);
+    // one descriptor for the sequence's rows; the row as the scalar offset,
+    // the lane's chunk (the one that belongs at slot `lane`) as the vector one
+    const uint8_t* base = static_cast<const uint8_t*>(P.nope) + seq * NROW;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * NROW)), (lds_void*)(buf + r * NROW), 16,
+                                             16 * (lane ^ swz(r)), id * NROW, 0, 0);
   } else if (FP8 && it < 8) {
     const int ida = __builtin_amdgcn_readlane(my_id, 2 * it), idb = __builtin_amdgcn_readlane(my_id, 2 * it + 1);
     const int id = lane < 32 ? ida : idb;
