@@ -117,8 +117,10 @@ static int launch_generic(const AttnParams& P, int B, hipStream_t s) {
 // host side
 // ---------------------------------------------------------------------------
 static int validate_attn(const csa_attn_desc* d, int B, const void* q, const csa_cache* kv,
-                         void* o, float* lse) {
+                         void* o, float* lse, float softmax_scale) {
   if (!d) return fail(CSA_ERR_INVALID_ARG, "attn desc is NULL");
+  if (!(softmax_scale > 0.0f) || !(softmax_scale < INFINITY))
+    return fail(CSA_ERR_INVALID_ARG, "softmax_scale must be positive and finite");
   if (d->n_heads < 1 || d->n_heads > 65535) return fail(CSA_ERR_INVALID_ARG, "n_heads must be in 1..65535");
   if (d->d_nope < 1 || d->d_rope < 0 || (d->d_rope & 1) || d->d_nope + d->d_rope > 4096)
     return fail(CSA_ERR_INVALID_ARG, "d_nope >= 1, d_rope even, width <= 4096");
@@ -173,7 +175,7 @@ extern "C" int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, 
                                        const void* q, const csa_cache* kv, const int32_t* idx, int k,
                                        float softmax_scale, void* o, float* lse, void* ws,
                                        size_t ws_bytes, void* stream) {
-  int st = validate_attn(desc, B, q, kv, o, lse);
+  int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
   if (T < 0 || T > 65535 || pos0 < 0) return fail(CSA_ERR_INVALID_ARG, "T must be in 0..65535, pos0 >= 0");
   if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
@@ -190,7 +192,7 @@ extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const in
                                       const void* q, const csa_cache* kv, const int32_t* idx, int k,
                                       float softmax_scale, void* o, float* lse, void* ws,
                                       size_t ws_bytes, void* stream) {
-  int st = validate_attn(desc, B, q, kv, o, lse);
+  int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
   if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
@@ -206,7 +208,7 @@ extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const in
 extern "C" int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
                                       const void* q, const csa_cache* kv, float softmax_scale, void* o,
                                       float* lse, void* ws, size_t ws_bytes, void* stream) {
-  int st = validate_attn(desc, B, q, kv, o, lse);
+  int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
   if (T < 0 || T > 65535 || pos0 < 0) return fail(CSA_ERR_INVALID_ARG, "T must be in 0..65535, pos0 >= 0");
   if (ws_bytes < attn_ws_bytes(desc, CSA_OP_DENSE_ATTN_PREFILL, B, T, pos0, 0))
@@ -220,7 +222,7 @@ extern "C" int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, i
 extern "C" int hca_dense_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
                                      const void* q, const csa_cache* kv, float softmax_scale, void* o,
                                      float* lse, void* ws, size_t ws_bytes, void* stream) {
-  int st = validate_attn(desc, B, q, kv, o, lse);
+  int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
   if (ws_bytes < attn_ws_bytes(desc, CSA_OP_DENSE_ATTN_DECODE, B, 1, 0, 0))

@@ -551,15 +551,22 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       // tile of an item, or a jump of the maximum) a wave flags it, and after
       // that barrier all waves agree on the new reference from the maxima
       // they published, rewrite P^T, rescale l and O^T, and meet once more.
+      // the scores stay unscaled: the positive scale commutes with the max,
+      // and exp2 takes fma(s, scale, -m)
       const int vend = nvalid - j * TILE;  // entries of this tile below it are real
       float mx = -INFINITY;
+      if (vend >= TILE) {  // a full tile (all but an item's last): no mask
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int e = 32 * eh + acc_row(v, lane);
-        sacc[v] = e < vend ? sacc[v] * lscale : -INFINITY;
-        mx = fmaxf(mx, sacc[v]);
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
+      } else {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int e = 32 * eh + acc_row(v, lane);
+          sacc[v] = e < vend ? sacc[v] : -INFINITY;
+          mx = fmaxf(mx, sacc[v]);
+        }
       }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * lscale;
       if (lane < 32) s_xchg[eh][head] = mx;
       const bool bad = m_run == -INFINITY || !(mx <= m_run + 8.0f);
       const bool wave_bad = __ballot(bad) != 0ull;
@@ -568,10 +575,10 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
         float ps = 0.0f;
 #pragma unroll
         for (int jq = 0; jq < 4; ++jq) {
-          const float p0 = __builtin_amdgcn_exp2f(sacc[4 * jq] - m_run);
-          const float p1 = __builtin_amdgcn_exp2f(sacc[4 * jq + 1] - m_run);
-          const float p2 = __builtin_amdgcn_exp2f(sacc[4 * jq + 2] - m_run);
-          const float p3 = __builtin_amdgcn_exp2f(sacc[4 * jq + 3] - m_run);
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[4 * jq], lscale, -m_run));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[4 * jq + 1], lscale, -m_run));
+          const float p2 = __builtin_amdgcn_exp2f(fmaf(sacc[4 * jq + 2], lscale, -m_run));
+          const float p3 = __builtin_amdgcn_exp2f(fmaf(sacc[4 * jq + 3], lscale, -m_run));
           ps += (p0 + p1) + (p2 + p3);
           const float f0 = FP8 ? esc[4 * jq] : 1.0f, f1 = FP8 ? esc[4 * jq + 1] : 1.0f;
           const float f2 = FP8 ? esc[4 * jq + 2] : 1.0f, f3 = FP8 ? esc[4 * jq + 3] : 1.0f;

@@ -203,7 +203,9 @@ int csa_index_topk_decode(const csa_index_desc* desc, int B, const int64_t* pos,
  *   idx : device int32 [B][T][k] (CSA only)
  *   o   : device [B][T][H][d_nope] of o_dtype
  *   lse : device float [B][T][H] or NULL
- *   ws  : device workspace of csa_workspace_bytes(...) bytes (may be 0) */
+ *   ws  : device workspace of csa_workspace_bytes(...) bytes (may be 0)
+ * In all four attention calls softmax_scale must be positive and finite
+ * (CSA_ERR_INVALID_ARG otherwise). */
 int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
                             const void* q, const csa_cache* kv, const int32_t* idx, int k,
                             float softmax_scale, void* o, float* lse, void* ws,

@@ -87,3 +87,21 @@ def test_index_and_attention_validation():
     kv = cb.Cache(0x1000, 0, 0x2000, 0x3000)   # FP8 without a scale buffer
     assert L.csa_sparse_attn_decode(ctypes.byref(adesc), 1, P, P, ctypes.byref(kv), P, 1024, 0.1, P, None, P, 1 << 30, None) == 1
     assert L.csa_workspace_bytes(99, ctypes.byref(adesc), 1, 1, 0, 0) == 0
+
+
+@pytest.mark.parametrize("scale", [0.0, -0.125, float("inf"), float("nan")])
+def test_attention_rejects_nonpositive_scale(scale):
+    # the kernels take the running maximum over unscaled scores, which is
+    # only order-preserving for a positive, finite scale
+    L = cb.lib()
+    adesc = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    P = fake(0x4000)
+    args = (P, P, ctypes.byref(kv))
+    assert L.csa_sparse_attn_prefill(ctypes.byref(adesc), 1, 16, 0, P, ctypes.byref(kv), P, 1024, scale, P, None,
+                                     P, 1 << 30, None) == 1
+    assert b"softmax_scale" in L.csa_last_error()
+    assert L.csa_sparse_attn_decode(ctypes.byref(adesc), 1, *args, P, 1024, scale, P, None, P, 1 << 30, None) == 1
+    assert L.hca_dense_attn_prefill(ctypes.byref(adesc), 1, 16, 0, P, ctypes.byref(kv), scale, P, None, P, 1 << 30,
+                                    None) == 1
+    assert L.hca_dense_attn_decode(ctypes.byref(adesc), 1, *args, scale, P, None, P, 1 << 30, None) == 1
