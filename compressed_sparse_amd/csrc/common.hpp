@@ -84,23 +84,25 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
   return sign | (code > 0x7Eu ? 0x7Eu : code);
 }
 
-// E2M1 code (4 bits, bit 3 = sign) -> fp32.
+// E2M1 code (4 bits, bit 3 = sign) -> fp32, assembled bitwise (no table,
+// no branches): magnitudes 0, 0.5 and, for m >= 2, (1 + (m & 1) / 2) *
+// 2^((m >> 1) - 1), i.e. 1, 1.5, 2, 3, 4, 6.
 __device__ __forceinline__ float e2m1_to_f32(uint32_t c) {
-  const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
-  float v = mag[c & 7u];
-  return (c & 8u) ? -v : v;
+  const uint32_t m = c & 7u;
+  const uint32_t mag = m >= 2u ? (((m >> 1) + 126u) << 23) | ((m & 1u) << 22) : (m ? 0x3F000000u : 0u);
+  return __uint_as_float(mag | ((c & 8u) << 28));
 }
 
-// fp32 (already divided by the block scale) -> E2M1 code, RNE, clamped to 6.
+// fp32 (already divided by the block scale) -> E2M1 code, RNE, clamped to 6:
+// the magnitude code counts the rounding boundaries at or below |x| (ties
+// go to the even code), NaN gives 7.
 __device__ __forceinline__ uint32_t f32_to_e2m1(float x) {
-  float a = fabsf(x);
-  uint32_t c = (a <= 0.25f) ? 0u
-             : (a < 0.75f) ? 1u
-             : (a <= 1.25f) ? 2u
-             : (a < 1.75f) ? 3u
-             : (a <= 2.5f) ? 4u
-             : (a < 3.5f) ? 5u
-             : (a <= 5.0f) ? 6u : 7u;
+  const float a = fabsf(x);
+  const uint32_t n = static_cast<uint32_t>(a > 0.25f) + static_cast<uint32_t>(a >= 0.75f) +
+                     static_cast<uint32_t>(a > 1.25f) + static_cast<uint32_t>(a >= 1.75f) +
+                     static_cast<uint32_t>(a > 2.5f) + static_cast<uint32_t>(a >= 3.5f) +
+                     static_cast<uint32_t>(a > 5.0f);
+  const uint32_t c = a == a ? n : 7u;
   return (x < 0.0f && c != 0u) ? (c | 8u) : c;
 }
 

@@ -31,6 +31,9 @@ struct IndexParams {
   int* cbase;         // [B][nch]
   int* ccnt;          // [B][nch]
   int nch;            // chunks per row: ceil(cap / CAND_CHUNK)
+  // MXFP4 scan: per query row the A operand of the scaled MFMA, 64 lanes x
+  // 16 bytes of E2M1 codes, then 64 int32 E8M0 scales (QPACK_ROW_BYTES)
+  uint8_t* qpack;
 };
 
 constexpr int HIST_BITS = 11;
@@ -63,7 +66,14 @@ __device__ __forceinline__ void wave_hist_add(int* hist, int bin, bool active) {
   if (active) atomicAdd(&hist[bin], 1);
 }
 
+constexpr int QPACK_ROW_BYTES = 64 * 16 + 64 * 4;
+
 bool index_mfma_supported(const IndexParams& P);
+// MXFP4 keys and query: the scaled-MFMA scan, which needs
+// launch_index_mx_prep (query operands; for decode also the cleared
+// histogram and candidate count) before it
+bool index_scan_mx(const IndexParams& P);
+int launch_index_mx_prep(const IndexParams& P, int rows, hipStream_t s);
 bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max);
 int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s);
 int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s);

@@ -11,11 +11,15 @@
 //   then radix-selects one row's top-k, so scores never reach HBM.
 // index_scan_kernel: one query row against a 1024-entry chunk per
 //   workgroup (v_mfma_f32_16x16x32_bf16, rows = the 16 heads); the decode
-//   scan and the fallback for long prefill rows.  FP8 and E2M1 codes widen
-//   to BF16 exactly in registers; the per-entry FP8 scale multiplies the dot
-//   product, the E8M0 block scales are folded into the widened values.
+//   scan and the fallback for long prefill rows, BF16 or FP8 keys.  FP8
+//   codes widen to BF16 exactly in registers; the per-entry FP8 scale
+//   multiplies the dot product.
+// index_scan_mx_kernel: the same for MXFP4 keys and query, on the scaled
+//   FP4 MFMA (v_mfma_scale_f32_32x32x64_f8f6f4): codes go in as they are
+//   stored and the hardware applies both operands' E8M0 block scales.  The
+//   query's MXFP4 operand is formed once per row by index_mx_prep_kernel.
 //
-// Both kernels reduce heads in a fixed order (4 or 8 heads inside a lane,
+// All kernels reduce heads in a fixed order (4 or 8 heads inside a lane,
 // then fixed cross-lane shuffles), so scores are run-to-run deterministic.
 #include "index.hpp"
 
@@ -40,9 +44,8 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
 }
 
-// Hardware widening of FP8 E4M3 / E2M1 codes to BF16 (the scaled
-// conversions with scale 1: exact for every code).  fp8x8: two words, first
-// byte first; e2m1x8: one word, low nibble first.
+// Hardware widening of FP8 E4M3 codes to BF16 (the scaled conversion with
+// scale 1: exact for every code); two words, first byte first.
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, 1.0f, HI));
@@ -51,16 +54,6 @@ __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t word) {
 __device__ __forceinline__ u32x4 fp8x8_to_bf16(uint32_t w0, uint32_t w1) {
   return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0), fp8x2_to_bf16x2<false>(w1),
                fp8x2_to_bf16x2<true>(w1)};
-}
-
-template <int BYTE>
-__device__ __forceinline__ uint32_t e2m1x2_to_bf16x2(uint32_t word) {
-  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(word, 1.0f, BYTE));
-}
-
-__device__ __forceinline__ u32x4 e2m1x8_to_bf16(uint32_t word) {
-  return u32x4{e2m1x2_to_bf16x2<0>(word), e2m1x2_to_bf16x2<1>(word), e2m1x2_to_bf16x2<2>(word),
-               e2m1x2_to_bf16x2<3>(word)};
 }
 
 // Orders this wave's LDS accesses before the ones that follow.
@@ -581,7 +574,21 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
 // ---------------------------------------------------------------------------
 constexpr int SCAN_CHUNK = 1024;
 
-template <int KFMT, bool QMX>
+// Clears a wave's LDS histogram (four bins per store).
+__device__ __forceinline__ void clear_hist(int* hist, int lane) {
+#pragma unroll
+  for (int i = 0; i < HIST_BINS / 256; ++i) reinterpret_cast<u32x4*>(hist)[lane + 64 * i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// Adds a workgroup's four wave histograms to the row's global histogram.
+__device__ __forceinline__ void flush_hist(const int (*lhist_w)[HIST_BINS], int* gh, int tid) {
+  for (int i = tid; i < HIST_BINS; i += 256) {
+    const int c = lhist_w[0][i] + lhist_w[1][i] + lhist_w[2][i] + lhist_w[3][i];
+    if (c) atomicAdd(&gh[i], c);
+  }
+}
+
+template <int KFMT>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT == CSA_FP8E4M3 ? 3 : 4))) index_scan_kernel(IndexParams P) {
   // this chunk's top-11-bit key histogram (decode top-k), one per wave so
   // that no barrier separates the clearing from the counting
@@ -594,42 +601,14 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * SCAN_CHUNK;
   if (c0 >= n) return;
   const size_t row = static_cast<size_t>(b) * P.T + t;
-  // A operand (16x16x32): head = lane & 15, g = lane >> 4.  BF16 / FP8 keys:
-  // k-step ks covers dims g*16 + ks*8 .. +8.  MXFP4 keys: k-step ks is the
-  // 32-dim scale block ks, dims ks*32 + g*8 .. +8, so that the block scale
-  // multiplies that MFMA's result.
+  // A operand (16x16x32): head = lane & 15, g = lane >> 4; k-step ks covers
+  // dims g*16 + ks*8 .. +8
   const int g = lane >> 4, h = lane & 15;
   bf16x8 qa[2];
   {
     const bf16_t* qrow = static_cast<const bf16_t*>(P.qI) + (row * HI + h) * DI;
-    u32x4 r[2];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-      r[ks] = *reinterpret_cast<const u32x4*>(qrow + (KFMT == CSA_MXFP4 ? ks * 32 + g * 8 : g * 16 + ks * 8));
-    if (QMX) {  // the query's own MXFP4 rounding, per 32-dim block
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[2 * i] = bf16_to_f32(static_cast<bf16_t>(r[ks][i] & 0xFFFFu));
-          x[2 * i + 1] = bf16_to_f32(static_cast<bf16_t>(r[ks][i] >> 16));
-        }
-        float am = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) am = fmaxf(am, fabsf(x[i]));
-        am = fmaxf(am, __shfl_xor(am, 16));  // the block's other three groups
-        am = fmaxf(am, __shfl_xor(am, 32));
-        const int ex = mx_exponent(am);
-        const float inv = exp2i(-ex), X = exp2i(ex);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = e2m1_to_f32(f32_to_e2m1(x[i] * inv)) * X;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) r[ks][i] = pack_bf16(x[2 * i], x[2 * i + 1]);
-      }
-    }
-    qa[0] = as_bf16x8(r[0]);
-    qa[1] = as_bf16x8(r[1]);
+    for (int ks = 0; ks < 2; ++ks) qa[ks] = as_bf16x8(*reinterpret_cast<const u32x4*>(qrow + g * 16 + ks * 8));
   }
   float wv[4];
 #pragma unroll
@@ -639,12 +618,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   // wave-uniform bases of this chunk; per-lane offsets are 32-bit
   float* wsb = P.ws + row * P.n_stride + c0;
   float* sob = P.scores_out ? P.scores_out + row * P.cap + c0 : nullptr;
-  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) +
-                      (seq + c0) * (KFMT == CSA_BF16 ? 2 * DI : KFMT == CSA_FP8E4M3 ? DI : DI / 2);
-  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * (KFMT == CSA_MXFP4 ? DI / 32 : 4);
+  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + (seq + c0) * (KFMT == CSA_BF16 ? 2 * DI : DI);
+  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * 4;
   int* lhist = lhist_w[w];
-  if (P.ghist)
-    for (int i = lane; i < HIST_BINS; i += 64) lhist[i] = 0;
+  if (P.ghist) clear_hist(lhist, lane);
   // each wave: 16-entry column blocks w, w+4, ...  A batch of NB blocks is
   // loaded (clamped to the last entry, so branch-free) while the previous
   // batch is widened, multiplied and reduced over heads (two register sets,
@@ -657,13 +634,9 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
       if constexpr (KFMT == CSA_BF16) {
         ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32));
         rb[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32 + 16));
-      } else if constexpr (KFMT == CSA_FP8E4M3) {
+      } else {
         ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * DI + g * 16));
         rs[j] = *reinterpret_cast<const uint32_t*>(sb + static_cast<uint32_t>(s * 4));
-      } else {  // MXFP4: 8 codes of block 0 and of block 1 at dims ks*32 + g*8, both block scales
-        ra[j][0] = *reinterpret_cast<const uint32_t*>(kb + static_cast<uint32_t>(s * (DI / 2) + g * 4));
-        ra[j][1] = *reinterpret_cast<const uint32_t*>(kb + static_cast<uint32_t>(s * (DI / 2) + g * 4 + 16));
-        rs[j] = *reinterpret_cast<const uint16_t*>(sb + static_cast<uint32_t>(s * (DI / 32)));
       }
     }
   };
@@ -671,19 +644,10 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
     f32x4 acc[NB];
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      if constexpr (KFMT == CSA_MXFP4) {  // dot = X0 * (block 0 codes . q) + X1 * (block 1 codes . q)
-        const f32x4 a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(e2m1x8_to_bf16(ra[j][0])), f32x4{}, 0, 0, 0);
-        const f32x4 a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(e2m1x8_to_bf16(ra[j][1])), f32x4{}, 0, 0, 0);
-        const float X0 = exp2i(static_cast<int>(rs[j] & 0xFFu) - 127);
-        const float X1 = exp2i(static_cast<int>(rs[j] >> 8) - 127);
-#pragma unroll
-        for (int v = 0; v < 4; ++v) acc[j][v] = fmaf(a1[v], X1, a0[v] * X0);
-      } else {
-        const u32x4 k0 = KFMT == CSA_FP8E4M3 ? fp8x8_to_bf16(ra[j][0], ra[j][1]) : ra[j];
-        const u32x4 k1 = KFMT == CSA_FP8E4M3 ? fp8x8_to_bf16(ra[j][2], ra[j][3]) : rb[j];
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(k0), f32x4{}, 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(k1), acc[j], 0, 0, 0);
-      }
+      const u32x4 k0 = KFMT == CSA_FP8E4M3 ? fp8x8_to_bf16(ra[j][0], ra[j][1]) : ra[j];
+      const u32x4 k1 = KFMT == CSA_FP8E4M3 ? fp8x8_to_bf16(ra[j][2], ra[j][3]) : rb[j];
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[0], as_bf16x8(k0), f32x4{}, 0, 0, 0);
+      acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[1], as_bf16x8(k1), acc[j], 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < NB / 4; ++q) {
@@ -737,11 +701,138 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   }
   if (P.ghist) {
     __syncthreads();
-    int* gh = P.ghist + static_cast<size_t>(b) * HIST_BINS;
-    for (int i = tid; i < HIST_BINS; i += 256) {
-      const int c = lhist_w[0][i] + lhist_w[1][i] + lhist_w[2][i] + lhist_w[3][i];
-      if (c) atomicAdd(&gh[i], c);
+    flush_hist(lhist_w, P.ghist + static_cast<size_t>(b) * HIST_BINS, tid);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// MXFP4 keys and query
+// ---------------------------------------------------------------------------
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// One query row per workgroup.  Wave 0 rounds the row's query to MXFP4 (per
+// head and 32-dim block: the OCP MX shared exponent e of the block's largest
+// magnitude, E2M1 codes of q / 2^e) and stores it as the A operand of the
+// scaled 32x32x64 MFMA: lane l holds head l % 32 (heads 16.. are zero) and
+// dims 32 (l / 32) .. +32, 16 bytes of codes (low nibble first), and the
+// E8M0 byte e + 127.  Decode: the row's histogram and candidate count are
+// cleared too.
+__global__ void __launch_bounds__(256) index_mx_prep_kernel(IndexParams P) {
+  const size_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int h = tid & 31, kb = tid >> 5;
+    u32x4 codes = {0u, 0u, 0u, 0u};
+    int e8 = 127;
+    if (h < HI) {
+      const u32x4* src =
+          reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(P.qI) + (r * HI + h) * DI + 32 * kb);
+      float x[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 v = src[i];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          x[8 * i + 2 * j] = bf16_to_f32(static_cast<bf16_t>(v[j] & 0xFFFFu));
+          x[8 * i + 2 * j + 1] = bf16_to_f32(static_cast<bf16_t>(v[j] >> 16));
+        }
+      }
+      float am = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
+      const int ex = mx_exponent(am);
+      const float inv = exp2i(-ex);
+#pragma unroll
+      for (int i = 0; i < 32; ++i) codes[i >> 3] |= f32_to_e2m1(x[i] * inv) << (4 * (i & 7));
+      e8 = ex + 127;
     }
+    uint8_t* dst = P.qpack + r * QPACK_ROW_BYTES;
+    reinterpret_cast<u32x4*>(dst)[tid] = codes;
+    reinterpret_cast<int*>(dst + 64 * 16)[tid] = e8;
+  }
+  if (P.ghist) {  // decode: one row per sequence
+    for (int i = tid; i < HIST_BINS; i += blockDim.x) P.ghist[r * HIST_BINS + i] = 0;
+    if (tid == 0) P.ccount[r] = 0;
+  }
+}
+
+// Per 32-entry block one scaled MFMA: 32 (16 real) heads x 32 entries x 64
+// dims, E2M1 codes of both operands with both E8M0 block scales applied in
+// the MFMA (exact products, fp32 sum).  Accumulator lane l holds entry l % 32
+// and heads 4 (l / 32) + v, 8 + 4 (l / 32) + v (v < 4); its ReLU-weighted
+// partial sum and that of lane l ^ 32 make the score, combined for two blocks
+// at once by one cross-half lane swap (lanes 0..31: block A, 32..63: block
+// B).  Wave w takes the 64-entry block pairs w, w + 4, ..; all its key loads
+// are issued before the first MFMA.
+constexpr int MX_PAIRS = SCAN_CHUNK / 256;  // block pairs per wave
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) index_scan_mx_kernel(IndexParams P) {
+  __shared__ int lhist_w[4][HIST_BINS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int b = blockIdx.z, t = blockIdx.y;
+  const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
+  int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
+  if (n > P.cap) n = P.cap;
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * SCAN_CHUNK;
+  if (c0 >= n) return;
+  const size_t row = static_cast<size_t>(b) * P.T + t;
+  const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);
+  const size_t seq = static_cast<size_t>(b) * P.cap;
+  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + (seq + c0) * (DI / 2);
+  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * (DI / 32);
+  // every key load first (clamped to the last entry: branch-free)
+  u32x4 kc[MX_PAIRS][2];
+  uint32_t ks[MX_PAIRS][2];
+#pragma unroll
+  for (int p = 0; p < MX_PAIRS; ++p)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int s = min(64 * (w + 4 * p) + 32 * j + (lane & 31), cn - 1);
+      kc[p][j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * (DI / 2) + 16 * (lane >> 5)));
+      ks[p][j] = sb[static_cast<uint32_t>(s * (DI / 32) + (lane >> 5))];
+    }
+  const uint8_t* qp = P.qpack + row * QPACK_ROW_BYTES;
+  const u32x4 qc = reinterpret_cast<const u32x4*>(qp)[lane];
+  const int qs = reinterpret_cast<const int*>(qp + 64 * 16)[lane];
+  const i32x8 qa = {static_cast<int>(qc[0]), static_cast<int>(qc[1]), static_cast<int>(qc[2]), static_cast<int>(qc[3]),
+                    0, 0, 0, 0};
+  float wv[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) wv[v] = P.w[row * HI + (v & 4 ? 8 : 0) + 4 * (lane >> 5) + (v & 3)];
+  float* wsb = P.ws + row * P.n_stride + c0;
+  float* sob = P.scores_out ? P.scores_out + row * P.cap + c0 : nullptr;
+  int* lhist = lhist_w[w];
+  if (P.ghist) clear_hist(lhist, lane);
+#pragma unroll
+  for (int p = 0; p < MX_PAIRS; ++p) {
+    float part[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const i32x8 kv = {static_cast<int>(kc[p][j][0]), static_cast<int>(kc[p][j][1]), static_cast<int>(kc[p][j][2]),
+                        static_cast<int>(kc[p][j][3]), 0, 0, 0, 0};
+      // formats 4, 4: E2M1 A and B; scale bytes in bits 0..7 of qs and ks
+      const f32x16 acc =
+          __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kv, f32x16{}, 4, 4, 0, qs, 0, static_cast<int>(ks[p][j]));
+      float sc = 0.0f;
+#pragma unroll
+      for (int v = 0; v < 8; ++v) sc = fmaf(wv[v], relu(acc[v]), sc);
+      part[j] = sc;
+    }
+    // lanes 0..31: part A of lanes l and l + 32; lanes 32..63: part B of l - 32 and l
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]), __float_as_uint(part[1]), false, false);
+    float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (P.score_dt == CSA_BF16) tot = round_bf16(tot);
+    const int s = 64 * (w + 4 * p) + lane;
+    const bool ok = s < cn;
+    if (ok) {
+      wsb[s] = tot;
+      if (sob) sob[s] = tot;
+    }
+    if (P.ghist) wave_hist_add(lhist, static_cast<int>(score_key(tot) >> (32 - HIST_BITS)), ok);
+  }
+  if (P.ghist) {
+    __syncthreads();
+    flush_hist(lhist_w, P.ghist + static_cast<size_t>(b) * HIST_BINS, tid);
   }
 }
 
@@ -751,6 +842,15 @@ bool index_mfma_supported(const IndexParams& P) {
   return P.H == HI && P.D == DI && P.q_dt == CSA_BF16 &&
          ((P.qk_dt == CSA_BF16 && (P.key_dt == CSA_BF16 || P.key_dt == CSA_FP8E4M3)) ||
           (P.qk_dt == CSA_MXFP4 && P.key_dt == CSA_MXFP4));
+}
+
+bool index_scan_mx(const IndexParams& P) {
+  return index_mfma_supported(P) && P.qk_dt == CSA_MXFP4;
+}
+
+int launch_index_mx_prep(const IndexParams& P, int rows, hipStream_t s) {
+  hipLaunchKernelGGL(index_mx_prep_kernel, dim3(rows), dim3(P.ghist ? 256 : 64), 0, s, P);
+  return check_launch("index_mx_prep_kernel");
 }
 
 bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max) {
@@ -766,9 +866,9 @@ int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
 
 int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((n_max + SCAN_CHUNK - 1) / SCAN_CHUNK), P.T, B);
-  if (P.qk_dt == CSA_MXFP4) hipLaunchKernelGGL((index_scan_kernel<CSA_MXFP4, true>), grid, dim3(256), 0, s, P);
-  else if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL((index_scan_kernel<CSA_FP8E4M3, false>), grid, dim3(256), 0, s, P);
-  else hipLaunchKernelGGL((index_scan_kernel<CSA_BF16, false>), grid, dim3(256), 0, s, P);
+  if (P.qk_dt == CSA_MXFP4) hipLaunchKernelGGL(index_scan_mx_kernel, grid, dim3(256), 0, s, P);
+  else if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_scan_kernel<CSA_FP8E4M3>, grid, dim3(256), 0, s, P);
+  else hipLaunchKernelGGL(index_scan_kernel<CSA_BF16>, grid, dim3(256), 0, s, P);
   return check_launch("index_scan_kernel");
 }
 

@@ -427,8 +427,13 @@ static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
     if (!P.scores_out && index_fused_prefill_ok(P, n_max)) return launch_index_fused_prefill(P, B, s);
     const int bits = P.score_dt == CSA_BF16 ? 16 : 32;
     if (P.ghist) {  // decode: histogram in the scan, candidates, exact final select
-      hipLaunchKernelGGL(topk_zero_kernel, dim3(B), dim3(256), 0, s, P);
-      int st = check_launch("topk_zero_kernel");
+      int st;
+      if (index_scan_mx(P)) {
+        st = launch_index_mx_prep(P, B, s);  // clears the histograms too
+      } else {
+        hipLaunchKernelGGL(topk_zero_kernel, dim3(B), dim3(256), 0, s, P);
+        st = check_launch("topk_zero_kernel");
+      }
       if (st != CSA_OK) return st;
       if (n_max > 0 && (st = launch_index_scan(P, B, n_max, s)) != CSA_OK) return st;
       hipLaunchKernelGGL(topk_cand_kernel, dim3(static_cast<unsigned>(P.nch), B),
@@ -438,8 +443,8 @@ static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
       return check_launch("topk_final_kernel");
     }
     if (n_max > 0) {
-      int st = launch_index_scan(P, B, n_max, s);
-      if (st != CSA_OK) return st;
+      int st = index_scan_mx(P) ? launch_index_mx_prep(P, B * P.T, s) : CSA_OK;
+      if (st != CSA_OK || (st = launch_index_scan(P, B, n_max, s)) != CSA_OK) return st;
     }
     hipLaunchKernelGGL(topk_radix_kernel, dim3(P.T, B), dim3(1024), 0, s, P, bits);
     return check_launch("topk_radix_kernel");
@@ -494,8 +499,20 @@ size_t index_ws_bytes(const csa_index_desc* d, int op, int B, int T, int64_t pos
   int64_t nmax = op == CSA_OP_INDEX_TOPK_DECODE ? d->capacity : prefill_nmax(d, T, pos0);
   int64_t rows = static_cast<int64_t>(B) * (op == CSA_OP_INDEX_TOPK_DECODE ? 1 : T);
   size_t bytes = static_cast<size_t>(rows * stride_for(nmax) * sizeof(float)) + 256;
+  if (d->qk_dtype == CSA_MXFP4) bytes += static_cast<size_t>(rows) * QPACK_ROW_BYTES + 256;
   if (op == CSA_OP_INDEX_TOPK_DECODE) bytes += decode_extra_bytes(B, d->capacity);
   return bytes;
+}
+
+// Workspace after the score rows: the MXFP4 query operands (when the
+// scaled-MFMA scan runs), then whatever follows; each part 256-byte aligned.
+static char* align256(char* p) { return p + (256 - reinterpret_cast<uintptr_t>(p) % 256) % 256; }
+
+static char* place_qpack(IndexParams& P, int64_t rows) {
+  char* p = align256(reinterpret_cast<char*>(P.ws) + static_cast<size_t>(rows) * P.n_stride * sizeof(float));
+  if (P.qk_dt != CSA_MXFP4) return p;
+  P.qpack = reinterpret_cast<uint8_t*>(p);
+  return align256(p + static_cast<size_t>(rows) * QPACK_ROW_BYTES);
 }
 
 static int common_index_checks(const csa_index_desc* d, int B, const void* qI, const float* w,
@@ -545,6 +562,7 @@ extern "C" int csa_index_topk_prefill(const csa_index_desc* desc, int B, int T, 
   P.pos_dev = nullptr;
   const int64_t nmax = prefill_nmax(desc, T, pos0);
   P.n_stride = stride_for(nmax);
+  place_qpack(P, static_cast<int64_t>(B) * T);
   return launch_index(P, B, nmax, stream);
 }
 
@@ -563,9 +581,8 @@ extern "C" int csa_index_topk_decode(const csa_index_desc* desc, int B, const in
   P.pos0 = 0;
   P.pos_dev = pos;
   P.n_stride = stride_for(desc->capacity);
+  char* extra = place_qpack(P, B);
   if (index_mfma_supported(P) && cand_chunks(desc->capacity) <= NCH_MAX) {
-    char* extra = reinterpret_cast<char*>(P.ws) + static_cast<size_t>(B) * P.n_stride * sizeof(float);
-    extra += (256 - reinterpret_cast<uintptr_t>(extra) % 256) % 256;
     P.ghist = reinterpret_cast<int*>(extra);
     P.ccount = P.ghist + static_cast<size_t>(B) * HIST_BINS;
     P.ckey = reinterpret_cast<uint32_t*>(P.ccount + ((B + 15) / 16) * 16);

@@ -225,3 +225,28 @@ def test_prefill_fused_ties(pattern):
         # scores are exact here (products of zeros or of one key row), so
         # the sets, ties included, match exactly
         assert (got == ref_idx).all(), np.nonzero((got != ref_idx).any(1))[0][:5]
+
+
+def test_prefill_mxfp4_bf16_scores():
+    """MXFP4 keys and queries in prefill (the scaled-MFMA scan over every
+    query row, then the per-row select), same tolerance as decode."""
+    B, T, H, d, m, k, cap = 2, 48, 16, 64, 4, 1024, 8192
+    pos0 = 4 * 8000 + 1
+    kc, K = key_cache("mxfp4", B, cap, d, m, seed=26)
+    qI = synth.normal((B, T, H, d), "qI", 26, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((B, T, H), "w", 26, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "mxfp4", "mxfp4", "bf16", m, cap)
+    idx = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.zeros((B, T, cap), dtype=torch.float32, device=DEV)
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, idx, scores)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for b in range(B):
+        assert ascending_padded(got[b])
+        ri, rs = oracle_rows(np64(qI[b]), np64(w[b]), K[b], pos0 + np.arange(T), m, k, "mxfp4", "bf16")
+        differing, bad = compare_topk(got[b], ri, rs, 0.0, kth_rel_window=2.0 ** -7)
+        assert not bad, f"sequence {b}: rows {bad[:5]}"
+        for t in range(T):
+            gs = scores[b, t].cpu().double().numpy()[:len(rs[t])]
+            assert (np.abs(gs - rs[t]) <= 2.0 ** -7 * np.abs(rs[t])).all()
+            assert (gs == rs[t]).mean() > 0.99
