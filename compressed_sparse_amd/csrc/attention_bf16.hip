@@ -165,19 +165,25 @@ template <bool FP8>
 __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, int my_id, size_t seq, int it) {
   typedef __attribute__((address_space(3))) void lds_void;
   typedef Lay<FP8> L;
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));  // lane offsets are recomputed per load, not kept live
-  const int w = threadIdx.x >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // rows, LDS addresses: scalar
   const uint64_t cap = static_cast<uint64_t>(P.cap);
   if (!FP8 && it < 16) {
     const int id = __builtin_amdgcn_readlane(my_id, it);
     const int r = 16 * w + it;
     // one descriptor for the sequence's rows; the row as the scalar offset,
-    // the lane's chunk (the one that belongs at slot `lane`) as the vector one
+    // the lane's chunk (the one that belongs at slot `lane`) as the vector
+    // one: 16 lane ^ 16 swz(r), the swizzle passed through a scalar so that
+    // each load forms its offset with one XOR instead of keeping 16 live
+    int sw = 16 * swz(r);
+    asm volatile("" : "+s"(sw));
     const uint8_t* base = static_cast<const uint8_t*>(P.nope) + seq * NROW;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * NROW)), (lds_void*)(buf + r * NROW), 16,
-                                             16 * (lane ^ swz(r)), id * NROW, 0, 0);
-  } else if (FP8 && it < 8) {
+                                             (16 * static_cast<int>(threadIdx.x & 63)) ^ sw, id * NROW, 0, 0);
+    return;
+  }
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane offsets are recomputed per load, not kept live
+  if (FP8 && it < 8) {
     const int ida = __builtin_amdgcn_readlane(my_id, 2 * it), idb = __builtin_amdgcn_readlane(my_id, 2 * it + 1);
     const int id = lane < 32 ? ida : idb;
     const int r = 16 * w + 2 * it + (lane >> 5);
@@ -554,18 +560,16 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       // the scores stay unscaled: the positive scale commutes with the max,
       // and exp2 takes fma(s, scale, -m)
       const int vend = nvalid - j * TILE;  // entries of this tile below it are real
-      float mx = -INFINITY;
-      if (vend >= TILE) {  // a full tile (all but an item's last): no mask
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-      } else {
+      if (vend < TILE) {  // an item's last tile: entries past the list are masked
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int e = 32 * eh + acc_row(v, lane);
           sacc[v] = e < vend ? sacc[v] : -INFINITY;
-          mx = fmaxf(mx, sacc[v]);
         }
       }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
       mx = fmaxf(mx, __shfl_xor(mx, 32)) * lscale;
       if (lane < 32) s_xchg[eh][head] = mx;
       const bool bad = m_run == -INFINITY || !(mx <= m_run + 8.0f);
