@@ -181,16 +181,23 @@ __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, in
                                              (16 * static_cast<int>(threadIdx.x & 63)) ^ sw, id * NROW, 0, 0);
     return;
   }
-  int lane = threadIdx.x & 63;
-  asm volatile("" : "+v"(lane));  // lane offsets are recomputed per load, not kept live
   if (FP8 && it < 8) {
+    // rows 16w + 2it (lanes 0..31) and 16w + 2it + 1 (lanes 32..63).  Their
+    // swizzle swzf(16w + 2it + h) = 4 (it & 3) + 2h + (w & 1), disjoint bits:
+    // the chunk offset is a per-lane constant XOR a scalar
     const int ida = __builtin_amdgcn_readlane(my_id, 2 * it), idb = __builtin_amdgcn_readlane(my_id, 2 * it + 1);
-    const int id = lane < 32 ? ida : idb;
-    const int r = 16 * w + 2 * it + (lane >> 5);
+    const int ln = threadIdx.x & 63;
+    int sw = 64 * (it & 3);
+    asm volatile("" : "+s"(sw));
+    const int lf = 16 * ((ln & 31) ^ (2 * (ln >> 5)) ^ (w & 1));
     const uint8_t* base = static_cast<const uint8_t*>(P.nope) + seq * DN;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * DN)), (lds_void*)(buf + (16 * w + 2 * it) * DN), 16,
-                                             id * DN + 16 * ((lane & 31) ^ swzf(r)), 0, 0, 0);
-  } else if (FP8 && it == 10) {
+                                             (ln < 32 ? ida : idb) * DN + (lf ^ sw), 0, 0, 0);
+    return;
+  }
+  int lane = threadIdx.x & 63;
+  asm volatile("" : "+v"(lane));  // lane offsets are recomputed per load, not kept live
+  if (FP8 && it == 10) {
     const uint8_t* base = static_cast<const uint8_t*>(P.scale) + seq * 4;
     if (lane < 16)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc(base, span(cap * 4)), (lds_void*)(buf + L::SC_OFF + 64 * w), 4,
