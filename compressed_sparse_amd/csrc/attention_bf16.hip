@@ -476,6 +476,24 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     auto tile = [&](const uint8_t* __restrict__ cur, uint8_t* __restrict__ nxt, bf16_t* __restrict__ pbuf_r,
                     int j) {
       const bool last = j + 1 == ntiles;
+      // the buffer's base folded into the operand lane offsets once per tile
+      // (28 adds; the reads then take the fixed base kb0 and immediates, where
+      // each read would otherwise add the base itself)
+      const int cb = __builtin_amdgcn_readfirstlane(static_cast<int>(cur - kb0));
+      int tA[8], tR[4], tV[4][2][2];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) { tA[i] = offA[i] + cb; asm volatile("" : "+v"(tA[i])); }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { tR[i] = offR[i] + cb; asm volatile("" : "+v"(tR[i])); }
+#pragma unroll
+      for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int k = 0; k < (FP8 ? 1 : 2); ++k) {
+          tV[mb][k][0] = offV[mb][k] + cb;
+          tV[mb][k][1] = (offV[mb][k] ^ 16) + cb;
+          asm volatile("" : "+v"(tV[mb][k][0]));
+          asm volatile("" : "+v"(tV[mb][k][1]));
+        }
       wait_vmem();
       lds_sync();  // tile j in LDS; every wave done with tile j-1 (its buffer, pbuf, s_alpha)
       if (staged) {  // the previous item's output, staged in nxt
@@ -510,8 +528,8 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       constexpr int NU = FP8 ? DN / 32 + DRP / 16 : QS;
       constexpr int NUN = FP8 ? DN / 32 : DN / 16;  // non-RoPE units
       auto aop = [&](int u) -> u32x4 {
-        return u < NUN ? *reinterpret_cast<const u32x4*>(cur + offA[u & 7] + 256 * (u >> 3))
-                       : *reinterpret_cast<const u32x4*>(cur + offR[u - NUN]);
+        return u < NUN ? *reinterpret_cast<const u32x4*>(kb0 + tA[u & 7] + 256 * (u >> 3))
+                       : *reinterpret_cast<const u32x4*>(kb0 + tR[u - NUN]);
       };
       f32x16 sacc = f32x16{};
       f32x16 sacr = f32x16{};  // FP8: the RoPE part, unscaled
@@ -638,15 +656,14 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
         };
         auto vop = [&](int t) -> VOp {
           const int ks = t >> 2, mb = t & 3;
-          const int fl = (ks & 1) ? 16 : 0;
           VOp r;
           if (FP8) {
-            const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(cur + (offV[mb][0] ^ fl) + 16 * ks * DN));
+            const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(kb0 + tV[mb][0][ks & 1] + 16 * ks * DN));
             r.x = __builtin_bit_cast(v4s, c);
             r.y = r.x;
           } else {
-            r.x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + (offV[mb][0] ^ fl) + 16 * ks * NROW));
-            r.y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(cur + (offV[mb][1] ^ fl) + 16 * ks * NROW));
+            r.x = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(kb0 + tV[mb][0][ks & 1] + 16 * ks * NROW));
+            r.y = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(kb0 + tV[mb][1][ks & 1] + 16 * ks * NROW));
           }
           return r;
         };
