@@ -632,11 +632,13 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
         if (eh == 0 && lane < 32) s_alpha[head] = alpha;
         psum = write_p();
         lds_sync();
+        if (j > 0) {  // an item's first tile starts from m_run = -inf: alpha = 1, O^T = 0
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
-          const float a = s_alpha[32 * nb + (lane & 31)];
+          for (int nb = 0; nb < 2; ++nb) {
+            const float a = s_alpha[32 * nb + (lane & 31)];
 #pragma unroll
-          for (int mb = 0; mb < 4; ++mb) oacc[mb][nb] *= a;
+            for (int mb = 0; mb < 4; ++mb) oacc[mb][nb] *= a;
+          }
         }
       }
       l_part += psum;
