@@ -31,6 +31,7 @@ struct IndexParams {
   int* cbase;         // [B][nch]
   int* ccnt;          // [B][nch]
   int nch;            // chunks per row: ceil(cap / CAND_CHUNK)
+  int* csel;          // [B][2]: the histogram bin of the k-th key, keys in higher bins
   // MXFP4 scan: per query row the A operand of the scaled MFMA, 64 lanes x
   // 16 bytes of E2M1 codes, then 64 int32 E8M0 scales (QPACK_ROW_BYTES)
   uint8_t* qpack;

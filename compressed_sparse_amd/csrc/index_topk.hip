@@ -155,17 +155,23 @@ __device__ __forceinline__ void find_digit(const int* hist, int remaining, int* 
 }
 
 // Radix select by the whole workgroup over cnt keys key_of(i): 8-bit digits
-// from the top over the key's first key_bits bits.  On return *prefix holds
-// the k-th largest key (masked by *pmask) and *rem how many keys equal to it
-// belong to the top k.
+// over the key's first key_bits bits, below the bits already known (the
+// keys matching prefix0 under pmask0 hold the k-th largest; k counts from
+// the largest of them; the next digit ends at bit top_shift).  The last
+// digit may overlap known bits (it then starts at bit 0).  On return
+// *prefix holds the k-th largest key (masked by *pmask) and *rem how many
+// keys equal to it belong to the top k.
 template <typename KeyOf>
 __device__ __forceinline__ void radix_threshold(KeyOf key_of, int64_t cnt, int k, int key_bits, int* hist, int* s_sel,
-                                uint32_t* prefix_out, uint32_t* pmask_out, int* rem_out) {
+                                uint32_t* prefix_out, uint32_t* pmask_out, int* rem_out, uint32_t prefix0 = 0u,
+                                uint32_t pmask0 = 0u, int top_shift = 24) {
   constexpr int U = 4;  // loads in flight per thread
   const int tid = threadIdx.x, nt = blockDim.x;
-  uint32_t prefix = 0, pmask = 0;
+  uint32_t prefix = prefix0, pmask = pmask0;
   int remaining = k;
-  for (int shift = 24; shift >= 32 - key_bits; shift -= 8) {
+  for (int sd = top_shift;; sd -= 8) {
+    const int shift = sd < 0 ? 0 : sd;
+    if (shift + 8 <= 32 - key_bits) break;  // only bits below the key's width left
     for (int i = tid; i < 256; i += nt) hist[i] = 0;
     __syncthreads();
     for (int64_t base = 0; base < cnt; base += static_cast<int64_t>(U) * nt) {
@@ -187,6 +193,7 @@ __device__ __forceinline__ void radix_threshold(KeyOf key_of, int64_t cnt, int k
     prefix |= static_cast<uint32_t>(s_sel[0]) << shift;
     remaining -= s_sel[1];
     pmask |= 255u << shift;
+    if (shift == 0) break;
   }
   *prefix_out = prefix;
   *pmask_out = pmask;
@@ -274,7 +281,8 @@ __global__ void __launch_bounds__(256) topk_zero_kernel(IndexParams P) {
   if (threadIdx.x == 0) P.ccount[b] = 0;
 }
 
-// The bin of the k-th largest key of row b (all 256 threads get it).
+// The bin of the k-th largest key of row b (all 256 threads get it); the
+// number of keys in higher bins is left in s_part[5].
 __device__ int threshold_bin(const int* gh, int k, int* s_part) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   constexpr int PER = HIST_BINS / 256;  // bins per thread, thread 0 owns the top bins
@@ -297,7 +305,7 @@ __device__ int threshold_bin(const int* gh, int k, int* s_part) {
   if (excl < k && incl >= k) {
     int cum = excl;
     for (int j = 0; j < PER; ++j) {
-      if (cum + c[j] >= k) { s_part[4] = HIST_BINS - 1 - (tid * PER + j); break; }
+      if (cum + c[j] >= k) { s_part[4] = HIST_BINS - 1 - (tid * PER + j); s_part[5] = cum; break; }
       cum += c[j];
     }
   }
@@ -324,6 +332,10 @@ __global__ void __launch_bounds__(256) topk_cand_kernel(IndexParams P) {
 #pragma unroll
   for (int it = 0; it < IT; ++it) v[it] = e0 + it * 64 < c1 ? sc[e0 + it * 64] : 0.0f;
   const int bstar = threshold_bin(P.ghist + static_cast<size_t>(b) * HIST_BINS, P.k, s_part);
+  if (blockIdx.x == 0 && tid == 0) {  // for the final select: the known top bits
+    P.csel[2 * b] = bstar;
+    P.csel[2 * b + 1] = s_part[5];
+  }
   // each wave compacts its quarter of the chunk, in index order, into its
   // own LDS segment
   const unsigned long long below = (1ull << lane) - 1ull;
@@ -413,10 +425,15 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
     s_idx[d] = s;
   }
   __syncthreads();
+  // the k-th key lies in the histogram's bin (its top HIST_BITS bits), with
+  // `above` candidates in higher bins: the select starts below those bits
   uint32_t prefix, pmask;
   int remaining;
   auto key_of = [](int64_t i) { return s_key[i]; };
-  radix_threshold(key_of, c, P.k, key_bits, hist, s_sel, &prefix, &pmask, &remaining);
+  const uint32_t bstar = static_cast<uint32_t>(P.csel[2 * b]);
+  const int above = P.csel[2 * b + 1];
+  radix_threshold(key_of, c, P.k - above, key_bits, hist, s_sel, &prefix, &pmask, &remaining,
+                  bstar << (32 - HIST_BITS), ~0u << (32 - HIST_BITS), 32 - HIST_BITS - 8);
   ordered_take(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, out);
 }
 
@@ -491,7 +508,7 @@ static int64_t cand_chunks(int64_t cap) { return (cap + CAND_CHUNK - 1) / CAND_C
 // per-chunk candidate bases and counts
 static size_t decode_extra_bytes(int B, int64_t cap) {
   return static_cast<size_t>(B) * (HIST_BINS * sizeof(int) + 64 + CAND_CAP * (sizeof(uint32_t) + sizeof(int32_t)) +
-                                   2 * cand_chunks(cap) * sizeof(int));
+                                   2 * cand_chunks(cap) * sizeof(int) + 2 * sizeof(int));
 }
 
 size_t index_ws_bytes(const csa_index_desc* d, int op, int B, int T, int64_t pos0) {
@@ -590,6 +607,7 @@ extern "C" int csa_index_topk_decode(const csa_index_desc* desc, int B, const in
     P.nch = static_cast<int>(cand_chunks(desc->capacity));
     P.cbase = reinterpret_cast<int*>(P.cidx + static_cast<size_t>(B) * CAND_CAP);
     P.ccnt = P.cbase + static_cast<size_t>(B) * P.nch;
+    P.csel = P.ccnt + static_cast<size_t>(B) * P.nch;
   }
   return launch_index(P, B, desc->capacity, stream);
 }
