@@ -105,3 +105,14 @@ def test_attention_rejects_nonpositive_scale(scale):
     assert L.hca_dense_attn_prefill(ctypes.byref(adesc), 1, 16, 0, P, ctypes.byref(kv), scale, P, None, P, 1 << 30,
                                     None) == 1
     assert L.hca_dense_attn_decode(ctypes.byref(adesc), 1, *args, scale, P, None, P, 1 << 30, None) == 1
+
+
+def test_mxfp4_workspace_holds_query_operands():
+    # MXFP4 QK: per query row 64 lanes x 16 bytes of codes + 64 int32 scales
+    # for the scaled-MFMA scan, on top of the BF16-QK workspace
+    mx = cb.index_desc(16, 64, "bf16", "mxfp4", "mxfp4", "bf16", 4, 262144)
+    bf = cb.index_desc(16, 64, "bf16", "bf16", "mxfp4", "bf16", 4, 262144)
+    for op, B, T in ((cb.OP_INDEX_TOPK_DECODE, 4, 1), (cb.OP_INDEX_TOPK_PREFILL, 2, 48)):
+        a = cb.workspace_bytes(op, mx, B, T, 4 * 8000, 1024)
+        b = cb.workspace_bytes(op, bf, B, T, 4 * 8000, 1024)
+        assert a - b >= B * T * (64 * 16 + 64 * 4)
