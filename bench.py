@@ -24,6 +24,7 @@ the 8 TB/s HBM peak.  So is HCA prefill at 2^20 context: its last (hardest)
 the attention's algorithmic flops against the BF16 MFMA peak.
 """
 import argparse
+import dataclasses
 import hashlib
 import json
 import os
@@ -224,6 +225,8 @@ def secondary_lines():
     out.extend(pair_decode_lines())
     torch.cuda.empty_cache()
     out.append(secondary_hca_prefill())
+    torch.cuda.empty_cache()
+    out.append(secondary_mxfp4_prefill_indexer())
     return out
 
 def secondary_hca_prefill(steps=5):
@@ -271,6 +274,37 @@ def secondary_hca_prefill(steps=5):
                          "algorithmic_flop_per_launch": flops, "avg_launch_ms": attn_ms}}
 
 
+def secondary_mxfp4_prefill_indexer(steps=5):
+    """Lightning indexer + top-k of the 32768-token prefill with MXFP4 keys
+    and query and BF16 scores (the 2^20-context pair's precision): the
+    scaled-MFMA scan over every query row writes the score rows, the per-row
+    select reads them back.  Keys from the MXFP4 compressor, inputs resident."""
+    w = dataclasses.replace(synth.CSA_PREFILL_BF16_32K, name="csa_prefill_L32768_mxfp4_indexer",
+                            key_fmt="mxfp4", qk_fmt="mxfp4", score_fmt="bf16")
+    log(f"setup {w.name}")
+    st = path.CsaPrefill(w)
+    st.step()
+
+    def run():
+        cb.index_topk_prefill(st.idesc, st.keys, 0, st.qI, st.wt, w.topk, st.idx, ws=st.iws)
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        run()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    visible = int(((np.arange(w.tokens) + 1) // w.m).sum())
+    by = 2.0 * visible * 4  # score rows written by the scan and read by the select
+    return {"workload": w.name, "metric": "MXFP4 prefill indexer + top-k tokens/s (L=32768, k=1024)",
+            "value": w.tokens / (ms * 1e-3), "unit": "tokens/s", "ms_per_launch": ms,
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, "algorithmic_bytes_per_launch": by}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,7 +314,7 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
-    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill"],
+    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill", "mxfp4-indexer"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -294,7 +328,7 @@ def main():
         copy_calibration()
     if args.only:
         fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
-              "hca-prefill": secondary_hca_prefill}[args.only]
+              "hca-prefill": secondary_hca_prefill, "mxfp4-indexer": secondary_mxfp4_prefill_indexer}[args.only]
         print(json.dumps(fn()), flush=True)
         return
     w = synth.CSA_PREFILL_BF16_32K
