@@ -77,6 +77,10 @@ bool index_scan_mx(const IndexParams& P);
 int launch_index_mx_prep(const IndexParams& P, int rows, hipStream_t s);
 bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max);
 int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s);
+// prefill rows of at most FUSED_NMAX entries whose scores a scan kernel
+// wrote to the workspace: the fused kernel's select alone
+bool index_ws_select_ok(const IndexParams& P, int64_t n_max);
+int launch_index_ws_select(const IndexParams& P, int B, hipStream_t s);
 int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s);
 
 }  // namespace csa

@@ -181,7 +181,9 @@ __device__ __forceinline__ void wave_radix_select(const float* row, int n, int k
 // equal keeps its first k entries; a range too narrow for the bins, or a
 // threshold bin of more than SEL_CBH entries in a half (heavy ties), takes
 // the radix select.
-template <bool KFP8>
+// FROM_WS: no scoring; the 4 rows' scores come from the workspace rows a
+// scan kernel wrote (MXFP4 prefill), then the same select.
+template <bool KFP8, bool FROM_WS>
 __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexParams P) {
   __shared__ __align__(16) float srow[QG][FUSED_NMAX];
   // select state (histograms, bin-B candidates, ranks); while scoring, the
@@ -216,6 +218,49 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
   const size_t row0 = static_cast<size_t>(b) * P.T + t0;
 
   if (need) {
+   if constexpr (FROM_WS) {
+    // lane l of wave w reads entries 4(64w + l) + 2048i .. +3 of each row
+    // (FUSED_NMAX/2048 16-byte loads per row, all issued before any is
+    // used; the rows are n_stride >= n long, so a load past n stays in the
+    // row and its values are dropped), keeping the wave's extremes
+    constexpr int NL = FUSED_NMAX / (4 * 64 * FW);
+    float4 v[QG][NL];
+#pragma unroll
+    for (int qq = 0; qq < QG; ++qq)
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int e = 4 * (64 * w + lane) + 4 * 64 * FW * i;
+        const int ec = min(e, static_cast<int>(P.n_stride) - 4);
+        v[qq][i] = nvis(qq) > e ? *reinterpret_cast<const float4*>(P.ws + (row0 + qq) * P.n_stride + ec)
+                                : float4{0.0f, 0.0f, 0.0f, 0.0f};
+      }
+#pragma unroll
+    for (int qq = 0; qq < QG; ++qq) {
+      const int nv = nvis(qq);
+      float mnv = INFINITY, mxv = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int e = 4 * (64 * w + lane) + 4 * 64 * FW * i;
+        const float x[4] = {v[qq][i].x, v[qq][i].y, v[qq][i].z, v[qq][i].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (e + c < nv) {
+            srow[qq][e + c] = x[c];
+            mnv = fminf(mnv, x[c]);
+            mxv = fmaxf(mxv, x[c]);
+          }
+      }
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        mnv = fminf(mnv, __shfl_xor(mnv, o));
+        mxv = fmaxf(mxv, __shfl_xor(mxv, o));
+      }
+      if (lane == 0) {
+        s_mm[w][qq][0] = mnv;
+        s_mm[w][qq][1] = mxv;
+      }
+    }
+   } else {
     // 16x16x32 MFMAs over 16-entry key blocks.  Row r of head block j holds
     // query r/4, head 4j + r%4, so that lane l's four accumulators are the
     // 16 heads (head 4j + i in element i of block j) of query l/16 against
@@ -344,6 +389,7 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
       s_mm[w][g][0] = mnv;
       s_mm[w][g][1] = mxv;
     }
+   }
   }
   __syncthreads();
 
@@ -859,9 +905,19 @@ bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max) {
 
 int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
   dim3 grid((P.T + QG - 1) / QG, B);
-  if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_prefill_fused_kernel<true>, grid, dim3(64 * FW), 0, s, P);
-  else hipLaunchKernelGGL(index_prefill_fused_kernel<false>, grid, dim3(64 * FW), 0, s, P);
+  if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * FW), 0, s, P);
+  else hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * FW), 0, s, P);
   return check_launch("index_prefill_fused_kernel");
+}
+
+bool index_ws_select_ok(const IndexParams& P, int64_t n_max) {
+  return index_mfma_supported(P) && P.pos_dev == nullptr && n_max <= FUSED_NMAX;
+}
+
+int launch_index_ws_select(const IndexParams& P, int B, hipStream_t s) {
+  dim3 grid((P.T + QG - 1) / QG, B);
+  hipLaunchKernelGGL((index_prefill_fused_kernel<false, true>), grid, dim3(64 * FW), 0, s, P);
+  return check_launch("index_prefill_fused_kernel (select)");
 }
 
 int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s) {

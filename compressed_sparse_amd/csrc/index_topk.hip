@@ -463,6 +463,7 @@ static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
       int st = index_scan_mx(P) ? launch_index_mx_prep(P, B * P.T, s) : CSA_OK;
       if (st != CSA_OK || (st = launch_index_scan(P, B, n_max, s)) != CSA_OK) return st;
     }
+    if (index_ws_select_ok(P, n_max)) return launch_index_ws_select(P, B, s);
     hipLaunchKernelGGL(topk_radix_kernel, dim3(P.T, B), dim3(1024), 0, s, P, bits);
     return check_launch("topk_radix_kernel");
   }
