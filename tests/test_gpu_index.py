@@ -74,7 +74,8 @@ def test_prefill_16x64_chunk_at_offset(key_fmt, with_scores):
     """16 heads x 64 dims, BF16 queries, BF16 or FP8 keys, queries at
     positions 3072..4072 of a longer prefill (a ragged last group of 4),
     k = 256.  Without a score output the scores stay on chip (fused
-    kernel); with one they go through the streaming scan + radix select."""
+    kernel); with one the streaming scan writes them and the fused kernel's
+    select reads them back."""
     T, H, d, m, k, pos0 = 1001, 16, 64, 4, 256, 3072
     cap = (pos0 + T) // m + 3
     kc, K = key_cache(key_fmt, 1, cap, d, m, seed=22)
@@ -250,3 +251,22 @@ def test_prefill_mxfp4_bf16_scores():
             gs = scores[b, t].cpu().double().numpy()[:len(rs[t])]
             assert (np.abs(gs - rs[t]) <= 2.0 ** -7 * np.abs(rs[t])).all()
             assert (gs == rs[t]).mean() > 0.99
+
+
+def test_prefill_rows_longer_than_fused_limit():
+    """Rows with more than 8192 visible entries: streaming scan, then the
+    one-workgroup-per-row radix select."""
+    T, H, d, m, k, pos0 = 40, 16, 64, 4, 1024, 4 * 9000
+    cap = (pos0 + T) // m + 1
+    kc, K = key_cache("bf16", 1, cap, d, m, seed=27)
+    qI = synth.normal((1, T, H, d), "qI", 27, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((1, T, H), "w", 27, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "bf16", "bf16", "f32", m, cap)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device=DEV)
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, idx)
+    torch.cuda.synchronize()
+    ref_idx, ref_sc = oracle_rows(np64(qI[0]), np64(w[0]), K[0], pos0 + np.arange(T), m, k, "bf16", "f32")
+    got = idx[0].cpu().numpy()
+    assert ascending_padded(got)
+    differing, bad = compare_topk(got, ref_idx, ref_sc, 1e-6)
+    assert not bad and differing <= 0.05 * T
