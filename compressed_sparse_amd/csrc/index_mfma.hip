@@ -882,6 +882,87 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   }
 }
 
+// Prefill form: the A operand's rows 16..31 carry the next query's heads,
+// so one scaled MFMA scores 32 entries against two consecutive queries
+// (t0, t0 + 1).  Lane l's accumulators 0..7 are query t0's partial sums,
+// 8..15 query t0 + 1's (same heads); one cross-half swap leaves lanes
+// 0..31 with query t0's scores of the block's entries and lanes 32..63 with
+// query t0 + 1's.  Wave w takes the blocks w, w + 4, .. of the chunk.
+constexpr int MX2_BLOCKS = SCAN_CHUNK / 128;  // 32-entry blocks per wave
+
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) index_scan_mx2_kernel(IndexParams P) {
+  const int lane = threadIdx.x & 63, w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int b = blockIdx.z, t0 = 2 * blockIdx.y;
+  const bool two = t0 + 1 < P.T;
+  auto vis = [&](int t) -> int64_t {
+    const int64_t pos = P.pos0 + t;
+    const int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
+    return n < P.cap ? n : P.cap;
+  };
+  const int64_t n0 = vis(t0), n1 = two ? vis(t0 + 1) : n0;  // n1 >= n0
+  const int64_t c0 = static_cast<int64_t>(blockIdx.x) * SCAN_CHUNK;
+  if (c0 >= n1) return;
+  const size_t row0 = static_cast<size_t>(b) * P.T + t0;
+  const int cn = static_cast<int>(n1 - c0 < SCAN_CHUNK ? n1 - c0 : SCAN_CHUNK);
+  const int cn0 = static_cast<int>(n0 - c0 < 0 ? 0 : (n0 - c0 < SCAN_CHUNK ? n0 - c0 : SCAN_CHUNK));
+  const size_t seq = static_cast<size_t>(b) * P.cap;
+  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + (seq + c0) * (DI / 2);
+  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * (DI / 32);
+  u32x4 kc[MX2_BLOCKS];
+  uint32_t ks[MX2_BLOCKS];
+#pragma unroll
+  for (int j = 0; j < MX2_BLOCKS; ++j) {
+    const int s = min(32 * (w + 4 * j) + (lane & 31), cn - 1);
+    kc[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * (DI / 2) + 16 * (lane >> 5)));
+    ks[j] = sb[static_cast<uint32_t>(s * (DI / 32) + (lane >> 5))];
+  }
+  // A operand: row l % 32 = (query (l % 32) / 16, head l % 16), block l / 32
+  const int qsel = (lane >> 4) & 1;
+  u32x4 qc = {0u, 0u, 0u, 0u};
+  int qs = 127;
+  if (!qsel || two) {
+    const uint8_t* qp = P.qpack + (row0 + qsel) * QPACK_ROW_BYTES;
+    const int ql = (lane & 15) + 32 * (lane >> 5);
+    qc = reinterpret_cast<const u32x4*>(qp)[ql];
+    qs = reinterpret_cast<const int*>(qp + 64 * 16)[ql];
+  }
+  const i32x8 qa = {static_cast<int>(qc[0]), static_cast<int>(qc[1]), static_cast<int>(qc[2]), static_cast<int>(qc[3]),
+                    0, 0, 0, 0};
+  float wv0[8], wv1[8];
+#pragma unroll
+  for (int v = 0; v < 8; ++v) {
+    const int h = (v & 4 ? 8 : 0) + 4 * (lane >> 5) + (v & 3);
+    wv0[v] = P.w[row0 * HI + h];
+    wv1[v] = two ? P.w[(row0 + 1) * HI + h] : 0.0f;
+  }
+  const int mine = lane >> 5;  // 0: query t0, 1: query t0 + 1
+  float* wsb = P.ws + (row0 + mine) * P.n_stride + c0;
+  float* sob = P.scores_out ? P.scores_out + (row0 + mine) * P.cap + c0 : nullptr;
+  const int lim = mine ? (two ? cn : 0) : cn0;
+#pragma unroll
+  for (int j = 0; j < MX2_BLOCKS; ++j) {
+    const i32x8 kv = {static_cast<int>(kc[j][0]), static_cast<int>(kc[j][1]), static_cast<int>(kc[j][2]),
+                      static_cast<int>(kc[j][3]), 0, 0, 0, 0};
+    const f32x16 acc =
+        __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa, kv, f32x16{}, 4, 4, 0, qs, 0, static_cast<int>(ks[j]));
+    float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+    for (int v = 0; v < 8; ++v) {
+      p0 = fmaf(wv0[v], relu(acc[v]), p0);
+      p1 = fmaf(wv1[v], relu(acc[v + 8]), p1);
+    }
+    // lanes 0..31: query t0, heads of lanes l and l + 32; lanes 32..63: query t0 + 1
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+    float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    if (P.score_dt == CSA_BF16) tot = round_bf16(tot);
+    const int s = 32 * (w + 4 * j) + (lane & 31);
+    if (s < lim) {
+      wsb[s] = tot;
+      if (sob) sob[s] = tot;
+    }
+  }
+}
+
 }  // namespace
 
 bool index_mfma_supported(const IndexParams& P) {
@@ -922,6 +1003,10 @@ int launch_index_ws_select(const IndexParams& P, int B, hipStream_t s) {
 
 int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s) {
   dim3 grid(static_cast<unsigned>((n_max + SCAN_CHUNK - 1) / SCAN_CHUNK), P.T, B);
+  if (P.qk_dt == CSA_MXFP4 && !P.ghist && !P.pos_dev) {  // prefill: two queries per workgroup
+    hipLaunchKernelGGL(index_scan_mx2_kernel, dim3(grid.x, (P.T + 1) / 2, B), dim3(256), 0, s, P);
+    return check_launch("index_scan_mx2_kernel");
+  }
   if (P.qk_dt == CSA_MXFP4) hipLaunchKernelGGL(index_scan_mx_kernel, grid, dim3(256), 0, s, P);
   else if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_scan_kernel<CSA_FP8E4M3>, grid, dim3(256), 0, s, P);
   else hipLaunchKernelGGL(index_scan_kernel<CSA_BF16>, grid, dim3(256), 0, s, P);

@@ -228,10 +228,12 @@ def test_prefill_fused_ties(pattern):
         assert (got == ref_idx).all(), np.nonzero((got != ref_idx).any(1))[0][:5]
 
 
-def test_prefill_mxfp4_bf16_scores():
-    """MXFP4 keys and queries in prefill (the scaled-MFMA scan over every
-    query row, then the per-row select), same tolerance as decode."""
-    B, T, H, d, m, k, cap = 2, 48, 16, 64, 4, 1024, 8192
+@pytest.mark.parametrize("T", [48, 47])
+def test_prefill_mxfp4_bf16_scores(T):
+    """MXFP4 keys and queries in prefill (the scaled-MFMA scan, two query
+    rows per MFMA; an odd T leaves the last workgroup one row), then the
+    select, same tolerance as decode."""
+    B, H, d, m, k, cap = 2, 16, 64, 4, 1024, 8192
     pos0 = 4 * 8000 + 1
     kc, K = key_cache("mxfp4", B, cap, d, m, seed=26)
     qI = synth.normal((B, T, H, d), "qI", 26, device=DEV, dtype=torch.bfloat16)
