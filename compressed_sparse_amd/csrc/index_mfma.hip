@@ -756,18 +756,21 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
 // ---------------------------------------------------------------------------
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// One query row per workgroup.  Wave 0 rounds the row's query to MXFP4 (per
+// One wave per query row (decode: one row per workgroup, whose other waves
+// clear the row's histogram).  The wave rounds the row's query to MXFP4 (per
 // head and 32-dim block: the OCP MX shared exponent e of the block's largest
 // magnitude, E2M1 codes of q / 2^e) and stores it as the A operand of the
 // scaled 32x32x64 MFMA: lane l holds head l % 32 (heads 16.. are zero) and
 // dims 32 (l / 32) .. +32, 16 bytes of codes (low nibble first), and the
 // E8M0 byte e + 127.  Decode: the row's histogram and candidate count are
 // cleared too.
-__global__ void __launch_bounds__(256) index_mx_prep_kernel(IndexParams P) {
-  const size_t r = blockIdx.x;
-  const int tid = threadIdx.x;
-  if (tid < 64) {
-    const int h = tid & 31, kb = tid >> 5;
+__global__ void __launch_bounds__(256) index_mx_prep_kernel(IndexParams P, int rows) {
+  // decode: one row per workgroup (its waves then clear the histogram);
+  // prefill: one row per wave
+  const int tid = threadIdx.x, lane = tid & 63;
+  const size_t r = P.ghist ? blockIdx.x : static_cast<size_t>(blockIdx.x) * 4 + (tid >> 6);
+  if ((P.ghist ? tid < 64 : true) && r < static_cast<size_t>(rows)) {
+    const int h = lane & 31, kb = lane >> 5;
     u32x4 codes = {0u, 0u, 0u, 0u};
     int e8 = 127;
     if (h < HI) {
@@ -793,8 +796,8 @@ __global__ void __launch_bounds__(256) index_mx_prep_kernel(IndexParams P) {
       e8 = ex + 127;
     }
     uint8_t* dst = P.qpack + r * QPACK_ROW_BYTES;
-    reinterpret_cast<u32x4*>(dst)[tid] = codes;
-    reinterpret_cast<int*>(dst + 64 * 16)[tid] = e8;
+    reinterpret_cast<u32x4*>(dst)[lane] = codes;
+    reinterpret_cast<int*>(dst + 64 * 16)[lane] = e8;
   }
   if (P.ghist) {  // decode: one row per sequence
     for (int i = tid; i < HIST_BINS; i += blockDim.x) P.ghist[r * HIST_BINS + i] = 0;
@@ -976,7 +979,7 @@ bool index_scan_mx(const IndexParams& P) {
 }
 
 int launch_index_mx_prep(const IndexParams& P, int rows, hipStream_t s) {
-  hipLaunchKernelGGL(index_mx_prep_kernel, dim3(rows), dim3(P.ghist ? 256 : 64), 0, s, P);
+  hipLaunchKernelGGL(index_mx_prep_kernel, dim3(P.ghist ? rows : (rows + 3) / 4), dim3(256), 0, s, P, rows);
   return check_launch("index_mx_prep_kernel");
 }
 
