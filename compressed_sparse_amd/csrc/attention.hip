@@ -163,7 +163,12 @@ size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0,
 
 static int dispatch(AttnParams& P, int op, int B, void* stream) {
   hipStream_t s = as_stream(stream);
-  if (mfma_attn_supported(P)) return launch_mfma_attn(P, op, B, s);
+  if (mfma_attn_supported(P)) {
+    if (!mfma_attn_capacity_ok(P))
+      return fail(CSA_ERR_UNSUPPORTED, "capacity too large: each cache buffer of a sequence must stay below 2^31 bytes "
+                                       "(2^21 BF16 or 2^22 FP8 entries of 512 dims)");
+    return launch_mfma_attn(P, op, B, s);
+  }
   return launch_generic(P, B, s);
 }
 

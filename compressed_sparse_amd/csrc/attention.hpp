@@ -25,6 +25,8 @@ struct AttnParams {
 
 // MFMA path (64 heads, 512 + 64 dims, BF16 q, BF16 / FP8 cache).
 bool mfma_attn_supported(const AttnParams& P);
+// false when a sequence's cache rows would need byte offsets of 2^31 or more
+bool mfma_attn_capacity_ok(const AttnParams& P);
 int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s);
 size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k);
 // BF16-cache kernel of the MFMA path over B sequences (T queries each, or

@@ -35,6 +35,7 @@
 // item's output is staged in the free tile buffer and stored, as whole 1 KB
 // rows, once the next item's first tile has landed, so the stores drain
 // while that tile is multiplied.
+#include <atomic>
 #include <cmath>
 
 #include "attention.hpp"
@@ -776,14 +777,17 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
 // One persistent workgroup per compute unit (at most one item each when the
 // items are fewer).
 void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, void* part) {
-  static int cus[64] = {0};
+  // compute units per device, looked up once; concurrent first calls store
+  // the same value
+  static std::atomic<int> cus[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) dev = 0;
-  int& cu = cus[dev & 63];
+  int cu = cus[dev & 63].load(std::memory_order_relaxed);
   if (cu == 0) {
     int v = 0;
     if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
     cu = v;
+    cus[dev & 63].store(cu, std::memory_order_relaxed);
   }
   Theta th;
   th.r1 = std::pow(P.base, -2.0 / DRP);

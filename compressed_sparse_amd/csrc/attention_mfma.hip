@@ -81,27 +81,50 @@ size_t part_bytes(int B, int splits) {
   return static_cast<size_t>(B) * splits * NH * (DN * sizeof(bf16_t) + sizeof(float));
 }
 
-int decode_splits(int B, int64_t ntiles) {
-  int64_t s = (256 + B - 1) / B;
+// Decode splits of one sequence: a function of its entry count alone (the
+// list length k, or the capacity for dense), never of the batch size, so a
+// sequence's partials, their merge and its output bits are the same in any
+// batch.  A sparse split covers one 64-entry tile (k = 1024: 16 splits); a
+// dense split at least DENSE_TILES tiles, at most MAX_SPLITS splits.
+constexpr int DENSE_TILES = 4;
+int decode_splits(bool dense, int64_t count) {
+  const int64_t ntiles = (count + TILE - 1) / TILE;
+  const int64_t per = dense ? DENSE_TILES : 1;
+  int64_t s = (ntiles + per - 1) / per;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
-  if (s > ntiles) s = ntiles;
   return s < 1 ? 1 : static_cast<int>(s);
+}
+
+// Gather offsets of the MFMA kernel are 32-bit byte offsets within one
+// sequence's rows (row id times row bytes): every cache buffer of a
+// sequence must stay below 2^31 bytes.
+bool offsets_fit(const AttnParams& P) {
+  const int64_t nope_row = P.nope_dt == CSA_FP8E4M3 ? DN : DN * 2;
+  const int64_t lim = int64_t(1) << 31;
+  return P.cap <= lim / nope_row && P.cap <= lim / (DRP * 2);
+}
+
+bool mfma_shape(int H, int d_nope, int d_rope, int q_dt, int o_dt, int nope_dt, int rope_dt) {
+  return H == NH && d_nope == DN && d_rope == DRP && q_dt == CSA_BF16 && o_dt == CSA_BF16 &&
+         (nope_dt == CSA_BF16 || nope_dt == CSA_FP8E4M3) && rope_dt == CSA_BF16;
 }
 
 }  // namespace
 
 bool mfma_attn_supported(const AttnParams& P) {
-  const bool shape = P.H == NH && P.d_nope == DN && P.d_rope == DRP && P.q_dt == CSA_BF16 && P.o_dt == CSA_BF16 &&
-                     (P.nope_dt == CSA_BF16 || P.nope_dt == CSA_FP8E4M3) && P.rope_dt == CSA_BF16;
+  const bool shape = mfma_shape(P.H, P.d_nope, P.d_rope, P.q_dt, P.o_dt, P.nope_dt, P.rope_dt);
   // sparse prefill keeps one query's whole list in LDS
   const bool list_fits = P.idx == nullptr || P.pos_dev != nullptr || P.k <= MAX_LIST;
   return shape && list_fits;
 }
 
-size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, int) {
+bool mfma_attn_capacity_ok(const AttnParams& P) { return offsets_fit(P); }
+
+size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, int k) {
   if (op != CSA_OP_SPARSE_ATTN_DECODE && op != CSA_OP_DENSE_ATTN_DECODE) return 0;
-  if (d->n_heads != NH || d->d_nope != DN || d->d_rope != DRP) return 0;
-  return part_bytes(B, MAX_SPLITS);
+  if (!mfma_shape(d->n_heads, d->d_nope, d->d_rope, d->q_dtype, d->o_dtype, d->nope_dtype, d->rope_dtype)) return 0;
+  const bool dense = op == CSA_OP_DENSE_ATTN_DECODE;
+  return part_bytes(B, decode_splits(dense, dense ? d->capacity : k));
 }
 
 int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
@@ -114,11 +137,7 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   }
   const int64_t count = dense ? P.cap : P.k;
   const int64_t ntiles = (count + TILE - 1) / TILE;
-  int splits = decode_splits(B, ntiles);
-  if (!dense) {  // each workgroup's list range must fit its LDS copy
-    const int min_s = static_cast<int>((ntiles * TILE + MAX_LIST - 1) / MAX_LIST);
-    if (splits < min_s) splits = min_s;
-  }
+  const int splits = decode_splits(dense, count);
   const int64_t tiles_per = (ntiles + splits - 1) / splits;
   const int64_t per = tiles_per * TILE;
   const size_t need = part_bytes(B, splits);

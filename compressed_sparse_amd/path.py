@@ -26,8 +26,12 @@ def _stack(tensors):
 
 
 class CsaLayer:
-    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0):
+    """seq_ids: the seeded sequence held in each batch slot (default 0..B-1)."""
+
+    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None):
         self.w, self.B, self.cap, self.device, self.seed = w, B, capacity, device, seed
+        self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
+        assert len(self.seq_ids) == B
         act = w.act_dtype
         self.kv = cb.KVCache(cb.cache_desc(w.m, w.overlap, w.d_nope, w.d_rope, act, w.nope_fmt, w.rope_fmt,
                                            capacity, w.rope_base), B, device)
@@ -40,6 +44,9 @@ class CsaLayer:
         self.iws = None
         self.aws = None
 
+    def caches(self):
+        return [self.kv, self.keys]
+
     # -- context ----------------------------------------------------------
     def prefill_context(self, T, chunk=None):
         """Compresses tokens [0, T) of every sequence into the caches."""
@@ -47,7 +54,7 @@ class CsaLayer:
         p = self.prm
         for c in range(math.ceil(T / chunk)):
             n = min(chunk, T - c * chunk)
-            toks = [synth.token_chunk(self.w, b, c, chunk, self.seed, self.device) for b in range(self.B)]
+            toks = [synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device) for sid in self.seq_ids]
             x = {k: _stack([t[k][:n] for t in toks]) for k in toks[0]}
             cb.compress_prefill(self.kv, c * chunk, x["a"], x["za"], p["Ba"], x.get("b"), x.get("zb"), p.get("Bb"))
             cb.compress_prefill(self.keys, c * chunk, x["ka"], x["kza"], p["kBa"], x.get("kb"), x.get("kzb"),
@@ -56,16 +63,29 @@ class CsaLayer:
     # -- decode -----------------------------------------------------------
     def decode_inputs(self, positions, chunk=None):
         """Token projections and queries of each sequence at its position."""
+        return self.decode_input_steps([positions], chunk)[0]
+
+    def decode_input_steps(self, steps, chunk=None):
+        """decode_inputs for a list of steps (each a list of positions, one per
+        sequence); every seeded chunk is drawn once."""
         chunk = chunk or self.w.chunk
-        toks, qs = [], []
-        for b, pos in enumerate(positions):
-            c, r = divmod(int(pos), chunk)
-            toks.append({k: v[r] for k, v in synth.token_chunk(self.w, b, c, chunk, self.seed, self.device).items()})
-            qs.append({k: v[r] for k, v in synth.query_chunk(self.w, b, c, chunk, self.seed, self.device).items()})
-        x = {k: _stack([t[k] for t in toks]) for k in toks[0]}
-        x.update({k: _stack([q[k] for q in qs]) for k in qs[0]})
-        x["pos"] = torch.tensor([int(p) for p in positions], dtype=torch.int64, device=self.device)
-        return x
+        per = [[None] * self.B for _ in steps]
+        for b, sid in enumerate(self.seq_ids):  # one sequence's chunks alive at a time
+            drawn = {}
+            for i, positions in enumerate(steps):
+                c, r = divmod(int(positions[b]), chunk)
+                if c not in drawn:
+                    d = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
+                    d.update(synth.query_chunk(self.w, sid, c, chunk, self.seed, self.device))
+                    drawn[c] = d
+                per[i][b] = {k: v[r].clone() for k, v in drawn[c].items()}  # rows, not views of the chunk
+            del drawn
+        out = []
+        for i, positions in enumerate(steps):
+            x = {k: _stack([p[k] for p in per[i]]) for k in per[i][0]}
+            x["pos"] = torch.tensor([int(p) for p in positions], dtype=torch.int64, device=self.device)
+            out.append(x)
+        return out
 
     def alloc_decode_outputs(self):
         w = self.w
@@ -93,8 +113,12 @@ class CsaLayer:
 
 
 class HcaLayer:
-    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0):
+    """seq_ids: the seeded sequence held in each batch slot (default 0..B-1)."""
+
+    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None):
         self.w, self.B, self.cap, self.device, self.seed = w, B, capacity, device, seed
+        self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
+        assert len(self.seq_ids) == B
         self.kv = cb.KVCache(cb.cache_desc(w.m, False, w.d_nope, w.d_rope, w.act_dtype, w.nope_fmt, w.rope_fmt,
                                            capacity, w.rope_base), B, device)
         self.adesc = cb.attn_desc(w.heads, w.d_nope, w.d_rope, w.act_dtype, w.out_dtype, w.nope_fmt, w.rope_fmt,
@@ -102,9 +126,12 @@ class HcaLayer:
         self.prm = synth.compressor_params(w, seed, device)
         self.aws = None
 
+    def caches(self):
+        return [self.kv]
+
     def compress_chunk(self, c, chunk, n=None):
         n = n or chunk
-        toks = [synth.token_chunk(self.w, b, c, chunk, self.seed, self.device) for b in range(self.B)]
+        toks = [synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device) for sid in self.seq_ids]
         x = {k: _stack([t[k][:n] for t in toks]) for k in toks[0]}
         cb.compress_prefill(self.kv, c * chunk, x["a"], x["za"], self.prm["Ba"])
 
@@ -118,16 +145,28 @@ class HcaLayer:
         cb.dense_attn_prefill(self.adesc, self.kv, c * chunk, q, self.w.tau, o, lse)
 
     def decode_inputs(self, positions, chunk=None):
+        return self.decode_input_steps([positions], chunk)[0]
+
+    def decode_input_steps(self, steps, chunk=None):
+        """decode_inputs for a list of steps; every seeded chunk is drawn once."""
         chunk = chunk or self.w.chunk
-        toks, qs = [], []
-        for b, pos in enumerate(positions):
-            c, r = divmod(int(pos), chunk)
-            toks.append({k: v[r] for k, v in synth.token_chunk(self.w, b, c, chunk, self.seed, self.device).items()})
-            qs.append(synth.query_chunk(self.w, b, c, chunk, self.seed, self.device, with_index=False)["q"][r])
-        x = {k: _stack([t[k] for t in toks]) for k in toks[0]}
-        x["q"] = _stack(qs)
-        x["pos"] = torch.tensor([int(p) for p in positions], dtype=torch.int64, device=self.device)
-        return x
+        per = [[None] * self.B for _ in steps]
+        for b, sid in enumerate(self.seq_ids):  # one sequence's chunks alive at a time
+            drawn = {}
+            for i, positions in enumerate(steps):
+                c, r = divmod(int(positions[b]), chunk)
+                if c not in drawn:
+                    d = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
+                    d["q"] = synth.query_chunk(self.w, sid, c, chunk, self.seed, self.device, with_index=False)["q"]
+                    drawn[c] = d
+                per[i][b] = {k: v[r].clone() for k, v in drawn[c].items()}  # rows, not views of the chunk
+            del drawn
+        out = []
+        for i, positions in enumerate(steps):
+            x = {k: _stack([p[k] for p in per[i]]) for k in per[i][0]}
+            x["pos"] = torch.tensor([int(p) for p in positions], dtype=torch.int64, device=self.device)
+            out.append(x)
+        return out
 
     def alloc_decode_outputs(self):
         w = self.w
@@ -139,6 +178,39 @@ class HcaLayer:
     def decode_step(self, x, out):
         cb.compress_decode(self.kv, x["pos"], x["a"], x["za"], self.prm["Ba"])
         cb.dense_attn_decode(self.adesc, self.kv, x["pos"], x["q"], self.w.tau, out["o"], out["lse"], ws=self.aws)
+
+
+class DecodeGraph:
+    """n consecutive decode steps of one or more layers captured in one HIP
+    graph.  Every run starts from the same state: the graph first restores
+    the staging rings of the layers' caches from a snapshot taken before
+    capture (a device copy, no memset), so each replay recomputes the same
+    steps from the same inputs; entries the steps complete are rewritten with
+    the same values before any later step reads them.  An eager run of the
+    same steps (warm-up) precedes capture."""
+
+    def __init__(self, layers, step_fn, n_steps):
+        self.rings = [c.ring for lay in layers for c in lay.caches()]
+        self.snaps = [r.clone() for r in self.rings]
+        self.step_fn, self.n = step_fn, n_steps
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.run_eager()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.run_eager()
+
+    def run_eager(self):
+        for r, sn in zip(self.rings, self.snaps):
+            r.copy_(sn)
+        for i in range(self.n):
+            self.step_fn(i)
+
+    def replay(self):
+        self.graph.replay()
 
 
 class CsaPrefill:

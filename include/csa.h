@@ -29,8 +29,9 @@
  *     first: on any error nothing is launched, outputs are untouched, and
  *     csa_last_error() (thread-local) describes the problem.
  *   - Results are deterministic: the same inputs give bitwise-equal outputs,
- *     and a sequence's results do not depend on the other sequences in the
- *     batch.
+ *     and, for the same descriptor, a sequence's results do not depend on
+ *     the other sequences in the batch or on the batch size (work is split
+ *     per sequence by its own entry count only).
  */
 #ifndef CSA_H_
 #define CSA_H_
@@ -205,7 +206,11 @@ int csa_index_topk_decode(const csa_index_desc* desc, int B, const int64_t* pos,
  *   lse : device float [B][T][H] or NULL
  *   ws  : device workspace of csa_workspace_bytes(...) bytes (may be 0)
  * In all four attention calls softmax_scale must be positive and finite
- * (CSA_ERR_INVALID_ARG otherwise). */
+ * (CSA_ERR_INVALID_ARG otherwise).  With 64 BF16 heads over 512 + 64 BF16
+ * or FP8 dims (the matrix-core path) each cache buffer of one sequence must
+ * stay below 2^31 bytes: capacity <= 2^21 (BF16 non-RoPE rows) or 2^22 (FP8
+ * rows), CSA_ERR_UNSUPPORTED otherwise.  Decode workspaces hold per-sequence
+ * split partials: csa_workspace_bytes grows linearly with B. */
 int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
                             const void* q, const csa_cache* kv, const int32_t* idx, int k,
                             float softmax_scale, void* o, float* lse, void* ws,

@@ -116,3 +116,34 @@ def test_mxfp4_workspace_holds_query_operands():
         a = cb.workspace_bytes(op, mx, B, T, 4 * 8000, 1024)
         b = cb.workspace_bytes(op, bf, B, T, 4 * 8000, 1024)
         assert a - b >= B * T * (64 * 16 + 64 * 4)
+
+
+@pytest.mark.parametrize("nope", ["bf16", "fp8"])
+def test_attention_rejects_capacity_past_32bit_row_offsets(nope):
+    # the MFMA kernels gather rows by 32-bit byte offsets within a sequence:
+    # 2^21 BF16 (1 KB) or 2^22 FP8 (512 B) non-RoPE rows is the largest cache
+    # they can address; one entry more is rejected before any launch
+    L = cb.lib()
+    lim = (1 << 31) // (1024 if nope == "bf16" else 512)
+    P = fake(0x4000)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    over = cb.attn_desc(64, 512, 64, "bf16", "bf16", nope, "bf16", 4, lim + 1)
+    ws = 1 << 40
+    assert L.csa_sparse_attn_prefill(ctypes.byref(over), 1, 16, 0, P, ctypes.byref(kv), P, 1024, 0.1, P, None,
+                                     P, ws, None) == 3
+    assert b"2^31" in L.csa_last_error()
+    assert L.csa_sparse_attn_decode(ctypes.byref(over), 1, P, P, ctypes.byref(kv), P, 1024, 0.1, P, None, P, ws,
+                                    None) == 3
+    assert L.hca_dense_attn_prefill(ctypes.byref(over), 1, 16, 0, P, ctypes.byref(kv), 0.1, P, None, P, ws, None) == 3
+    assert L.hca_dense_attn_decode(ctypes.byref(over), 1, P, P, ctypes.byref(kv), 0.1, P, None, P, ws, None) == 3
+
+
+def test_decode_attention_workspace_is_per_sequence():
+    # the decode split count depends on the entry count only, never on the
+    # batch size, so the workspace grows linearly with B
+    for op, k, cap in ((cb.OP_SPARSE_ATTN_DECODE, 1024, 32776), (cb.OP_DENSE_ATTN_DECODE, 0, 8194)):
+        d = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4 if k else 128, cap)
+        one = cb.workspace_bytes(op, d, 1, 1, 0, k)
+        assert one > 0
+        for B in (4, 16, 32):
+            assert cb.workspace_bytes(op, d, B, 1, 0, k) == B * one
