@@ -1,18 +1,28 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times, on sampled outputs the oracle computes one by one:
+benchmark times, on outputs the oracle computes one by one:
 
 * CSA prefill, bf16, L = 32768, 64 heads, top-1024 (sampled query rows);
 * CSA decode, batch 32, 131072-token contexts (FP8 / BF16 split cache, FP8
-  indexer keys), four decode steps including an entry completion;
+  indexer keys): every sequence, four decode steps including an entry
+  completion;
 * HCA prefill of a 2^20-token sequence in 8192-token chunks (sampled rows of
-  the first, second and last chunk) and HCA decode at batch 16;
+  chunks 0, 1, 64 and 127) and HCA decode at batch 16 (four sequences);
 * the CSA + HCA layer pair at batch 4 with 2^20-token contexts, MXFP4
-  indexer and BF16 scores, with indexer recall against the fp32 oracle.
+  indexer and BF16 scores (every sequence), with indexer recall against the
+  fp32 oracle.
 
-Top-k sets must equal the oracle's except for swaps that the bounded input
-differences explain (a key element whose exact value lies within the GPU's
-fp32 error of a rounding boundary, fp32 score accumulation);
-outputs must match within max-rel 1e-2 on rows whose sets agree.
+Two legs per workload:
+
+A. independent: the oracle recomputes the caches in fp64 from the seeded
+   tokens.  Top-k sets must equal the oracle's except for swaps that the
+   bounded input differences explain (a key element whose exact value lies
+   within the GPU's fp32 error of a rounding boundary, fp32 accumulation);
+   attention is compared on every sampled row, against the oracle run with
+   the GPU's index list where the sets differ.
+B. GPU-written caches: the oracle decodes the caches the kernels wrote and
+   runs its indexer, top-k and attention on them.  Top-k sets must be exact
+   except for ties within 1e-6 * max(1, max|I|) (plus one BF16 step in BF16
+   score mode); attention over the GPU's index list within max-rel 1e-2.
 """
 import numpy as np
 import pytest
@@ -20,27 +30,36 @@ import torch
 
 from compressed_sparse_amd import path, synth
 from oracle import csa
-from oracle import formats as F
 from tests import fullsize_ref as R
-from tests.helpers import ascending_padded, max_rel_rows, topk_explained
+from tests import gpu_cache as G
+from tests.helpers import ascending_padded, compressor_error_bound, topk_explained
 
 pytestmark = pytest.mark.gpu
 
 
-def check_rows(name, rows, gpu_idx, ref_idx, scores, deltas, gpu_o, ref_o, eps_rel=2e-6, tol=1e-2):
-    same = []
+def leg_a_topk(name, rows, gpu_idx, ref_idx, scores, deltas, eps_rel=2e-6):
+    """Independent leg: every GPU set is the oracle's or a swap the bounded
+    input differences explain; returns the rows whose sets differ."""
+    diff = []
     for r in range(len(rows)):
         I = scores[r]
         eps = eps_rel * max(1.0, float(np.abs(I).max())) if len(I) else 0.0
         assert topk_explained(gpu_idx[r], ref_idx[r], I, deltas[r], eps), f"{name}: row {rows[r]} top-k"
-        same.append(set(gpu_idx[r][gpu_idx[r] >= 0]) == set(ref_idx[r][ref_idx[r] >= 0]))
-    same = np.array(same)
-    if len(rows) >= 20:
-        assert same.mean() > 0.9, f"{name}: only {same.mean():.3f} identical sets"
-    err = max_rel_rows(gpu_o[same].reshape(-1, gpu_o.shape[-1]), ref_o[same].reshape(-1, ref_o.shape[-1]))
-    print(f"{name}: {same.sum()}/{len(rows)} identical sets, max-rel {err:.2e}", flush=True)
-    assert err <= tol, f"{name}: max-rel {err}"
+        if set(gpu_idx[r][gpu_idx[r] >= 0]) != set(ref_idx[r][ref_idx[r] >= 0]):
+            diff.append(r)
+    print(f"{name} [A]: {len(rows) - len(diff)}/{len(rows)} identical sets", flush=True)
+    return diff
 
+
+def leg_b_topk(name, gpu_idx_row, I, n, k, score_fmt, tally):
+    ok, swaps, _ = G.topk_exact_rule(gpu_idx_row, I, n, k, score_fmt)
+    assert ok, f"{name} [B]: top-k differs beyond the tie rule"
+    tally.append(swaps)
+
+
+# ---------------------------------------------------------------------------
+# CSA prefill, L = 32768
+# ---------------------------------------------------------------------------
 
 def test_csa_prefill_32k_bf16():
     w = synth.CSA_PREFILL_BF16_32K
@@ -63,20 +82,45 @@ def test_csa_prefill_32k_bf16():
     cache = csa.finalize_kv(ent, 0, m, w.d_nope, w.rope_base, "bf16", "bf16")
     kexact = csa.compress(tok["ka"], tok["kza"], p["kBa"], m, tok["kb"], tok["kzb"], p["kBb"])
     keys = csa.finalize_keys(kexact, "bf16")
-    from tests.helpers import compressor_error_bound
     dk = R.key_flip_delta(kexact, "bf16", compressor_error_bound({"a": tok["ka"], "b": tok["kb"]}, m, True, w.idx_dim))
 
     rng = np.random.default_rng(7)
     rows = np.unique(np.concatenate([np.arange(8), np.arange(4090, 4110), rng.integers(0, T, 160), [T - 1]]))
     q, qI, wt = h(st.q)[rows], h(st.qI)[rows], h(st.wt)[rows]
+    go, gl = h(st.o)[rows], h(st.lse)[rows]
+    gi = idx[rows]
+    # leg A
     ref = csa.csa_rows(rows, rows, q, qI, wt, cache, keys, m, k, w.d_nope, w.rope_base, w.tau)
     deltas = [R.score_delta(qI[r], wt[r], dk[:len(ref["scores"][r])]) for r in range(len(rows))]
-    check_rows("csa prefill 32k", rows, idx[rows], ref["idx"], ref["scores"], deltas,
-               h(st.o)[rows], ref["o"])
+    diff = leg_a_topk("csa prefill 32k", rows, gi, ref["idx"], ref["scores"], deltas)
+    oa, la = ref["o"].copy(), ref["lse"].copy()
+    for r in diff:  # judged with the GPU's list (oracle cache)
+        oa[r], la[r] = csa.sparse_attention_row(q[r], int(rows[r]), cache, gi[r], w.d_nope, w.rope_base, w.tau)
+    ea, _ = G.check_attention("csa prefill 32k [A]", go, gl, oa, la)
+    # leg B: the GPU-written key and KV caches
+    N = T // m
+    Kk = G.decode_nope(st.keys, 0, np.arange(N))
+    Kv = G.decode_kv(st.kv, 0, np.arange(N))
+    gcache = {"k": Kv, "v": Kv[:, :w.d_nope]}
+    swaps, ob, lb = [], np.zeros_like(go), np.zeros_like(gl)
+    for r, t in enumerate(rows):
+        n = int(n_vis[t])
+        I = csa.index_scores(qI[r], wt[r], Kk, n, "f32")
+        leg_b_topk(f"csa prefill 32k row {t}", gi[r], I, n, k, "f32", swaps)
+        ob[r], lb[r] = csa.sparse_attention_row(q[r], int(t), gcache, gi[r], w.d_nope, w.rope_base, w.tau)
+    eb, _ = G.check_attention("csa prefill 32k [B]", go, gl, ob, lb)
+    print(f"csa prefill 32k: max-rel A {ea:.2e} B {eb:.2e}; tie swaps (B) {sum(swaps)} in {len(rows)} rows",
+          flush=True)
 
 
-def csa_decode_reference(w, lay, b, pos, chunk):
-    """Oracle top-k and attention of sequence b's query at `pos`."""
+# ---------------------------------------------------------------------------
+# CSA decode (batch 32, 128K) and the pair's CSA layer
+# ---------------------------------------------------------------------------
+
+def csa_decode_reference(w, b, pos, chunk, gpu_row):
+    """Independent leg for sequence b's query at `pos`: oracle keys and top-k
+    from the fp64 compressor; attention over the oracle's list, and over the
+    GPU's list when the two differ (entries compressed in fp64, stored)."""
     n = (pos + 1) // w.m
     kexact = R.chunked_entries(w, b, n * w.m, chunk, prefix="k")[:n]
     keys = csa.finalize_keys(kexact, w.key_fmt)
@@ -85,21 +129,54 @@ def csa_decode_reference(w, lay, b, pos, chunk):
     c, r = divmod(pos, chunk)
     qs = synth.query_chunk(w, b, c, chunk, 0, "cuda")
     q, qI, wt = (R.host(qs[x][r]) for x in ("q", "qI", "w"))
-    I = csa.index_scores(csa.quantize_query(qI, w.qk_fmt), wt, keys["k"], n, w.score_fmt)
-    sel = csa.topk(I, n, w.topk)
     qq = csa.quantize_query(qI, w.qk_fmt)
+    I = csa.index_scores(qq, wt, keys["k"], n, w.score_fmt)
+    sel = csa.topk(I, n, w.topk)
     delta = R.score_delta(qq, wt, dk)
     if w.score_fmt == "bf16":  # one BF16 step of the score on either side
         delta = delta + 2.0 ** -7 * np.abs(I)
-    ids = sel[sel >= 0]
-    # the selected entries only, each turned at its own position, then stored
+    gsel = np.asarray(gpu_row, dtype=np.int64)
+    ids = np.union1d(sel[sel >= 0], gsel[(gsel >= 0) & (gsel < n)])
+    # the needed entries only, each turned at its own position, then stored
     ex = csa.rope(R.csa_entries(w, b, ids, chunk), csa.entry_position(ids, w.m), w.d_nope, w.rope_base)
     nope, _ = csa.store_format(ex[:, :w.d_nope], w.nope_fmt)
     rope, _ = csa.store_format(ex[:, w.d_nope:], w.rope_fmt)
     K = np.zeros((n, w.c))
     K[ids] = np.concatenate([nope, rope], 1)
-    o, lse = csa.sparse_attention_row(q, pos, {"k": K, "v": K[:, :w.d_nope]}, sel, w.d_nope, w.rope_base, w.tau)
-    return dict(sel=sel, I=I, delta=delta, o=o, lse=lse, qI=qI, wt=wt, kexact=kexact, n=n)
+    cache = {"k": K, "v": K[:, :w.d_nope]}
+    same = set(sel[sel >= 0].tolist()) == set(gsel[gsel >= 0].tolist())
+    o, lse = csa.sparse_attention_row(q, pos, cache, sel if same else gsel, w.d_nope, w.rope_base, w.tau)
+    return dict(sel=sel, I=I, delta=delta, o=o, lse=lse, q=q, qI=qI, qq=qq, wt=wt, kexact=kexact, n=n)
+
+
+def check_csa_decode_batch(name, w, lay, out, pos, seqs, chunk):
+    """Both legs for every listed sequence of a CSA decode batch."""
+    idx = out["idx"].cpu().numpy()
+    assert ascending_padded(idx) and ((idx >= 0).sum(1) == np.minimum(w.topk, (pos + 1) // w.m)).all()
+    o = R.host(out["o"])
+    lse = R.host(out["lse"])
+    refs, rows_a, swaps_b = {}, [], []
+    oa, la, ob, lb = [], [], [], []
+    for b in seqs:
+        ref = csa_decode_reference(w, lay.seq_ids[b], pos, chunk, idx[b])
+        refs[b] = ref
+        rows_a.append(ref)
+        oa.append(ref["o"]); la.append(ref["lse"])
+        # leg B: GPU-written key cache (exact top-k rule) and KV rows
+        n = ref["n"]
+        Kk = G.decode_nope(lay.keys, b, np.arange(n))
+        I = csa.index_scores(ref["qq"], ref["wt"], Kk, n, w.score_fmt)
+        leg_b_topk(f"{name} seq {b}", idx[b], I, n, w.topk, w.score_fmt, swaps_b)
+        ob_, lb_ = G.attend_gpu_idx(ref["q"], pos, lay.kv, b, idx[b], w.d_nope, w.rope_base, w.tau)
+        ob.append(ob_); lb.append(lb_)
+    seqs = list(seqs)
+    diff = leg_a_topk(name, seqs, idx[seqs], np.array([r["sel"] for r in rows_a]), [r["I"] for r in rows_a],
+                      [r["delta"] for r in rows_a])
+    ea, _ = G.check_attention(f"{name} [A]", o[seqs], lse[seqs], np.array(oa), np.array(la))
+    eb, _ = G.check_attention(f"{name} [B]", o[seqs], lse[seqs], np.array(ob), np.array(lb))
+    print(f"{name}: {len(seqs)} sequences, sets differing (A) {len(diff)}, tie swaps (B) {sum(swaps_b)}, "
+          f"max-rel A {ea:.2e} B {eb:.2e}", flush=True)
+    return refs, idx
 
 
 def test_csa_decode_b32_128k():
@@ -114,28 +191,30 @@ def test_csa_decode_b32_128k():
         lay.decode_step(x, out)
     torch.cuda.synchronize()
     pos = ctx + steps - 1                      # this step completed entry ctx/m
-    idx = out["idx"].cpu().numpy()
-    assert ascending_padded(idx) and ((idx >= 0).sum(1) == w.topk).all()
-    o = out["o"].to("cpu", torch.float64).numpy()
-    rows, gi, ri, sc, de, go, ro = [], [], [], [], [], [], []
-    for b in (0, 17):
-        ref = csa_decode_reference(w, lay, b, pos, chunk)
-        assert ref["n"] == ctx // w.m + 1
-        rows.append(b); gi.append(idx[b]); ri.append(ref["sel"]); sc.append(ref["I"]); de.append(ref["delta"])
-        go.append(o[b]); ro.append(ref["o"])
-    check_rows("csa decode b32", rows, np.array(gi), np.array(ri), sc, de, np.array(go), np.array(ro))
+    assert (pos + 1) // w.m == ctx // w.m + 1
+    check_csa_decode_batch("csa decode b32", w, lay, out, pos, range(w.batch), chunk)
 
 
-def hca_reference_cache(w, b, T, chunk):
-    ent = R.chunked_entries(w, b, T, chunk, overlap=False)
+# ---------------------------------------------------------------------------
+# HCA prefill (2^20 tokens in chunks) and decode (batch 16)
+# ---------------------------------------------------------------------------
+
+def hca_reference_cache(w, b, T, chunk, seed=0):
+    ent = R.chunked_entries(w, b, T, chunk, overlap=False, seed=seed)
     return csa.finalize_kv(ent, 0, w.m, w.d_nope, w.rope_base, w.nope_fmt, w.rope_fmt)
+
+
+def gpu_hca_cache(lay, b, n):
+    K = G.decode_kv(lay.kv, b, np.arange(n))
+    return {"k": K, "v": K[:, :lay.w.d_nope]}
 
 
 def test_hca_prefill_1m_chunked():
     w = synth.HCA_PREFILL_1M
     T, chunk = w.tokens, w.chunk
     lay = path.HcaLayer(w, 1, T // w.m + 1)
-    checked = {0: None, 1: None, T // chunk - 1: None}
+    last = T // chunk - 1
+    checked = {0: None, 1: None, 64: None, last: None}
     rng = np.random.default_rng(3)
     for c in range(T // chunk):
         lay.compress_chunk(c, chunk)
@@ -148,15 +227,15 @@ def test_hca_prefill_1m_chunked():
             checked[c] = (rows, R.host(q[0])[rows], R.host(o[0])[rows], R.host(lse[0])[rows])
     torch.cuda.synchronize()
     cache = hca_reference_cache(w, 0, T, chunk)
+    gcache = gpu_hca_cache(lay, 0, T // w.m)
     for c, (rows, q, o, lse) in checked.items():
         pos = c * chunk + rows
-        oref, lref = csa.hca_rows(pos, q, cache, w.m, w.d_nope, w.rope_base, w.tau)
-        err = max_rel_rows(o.reshape(-1, w.d_nope), oref.reshape(-1, w.d_nope))
-        fin = np.isfinite(lref)
-        assert np.array_equal(np.isfinite(lse), fin)
-        assert err <= 1e-2 and np.abs(lse[fin] - lref[fin]).max() <= 1e-2, f"chunk {c}: {err}"
+        for leg, cc in (("A", cache), ("B", gcache)):
+            oref, lref = csa.hca_rows(pos, q, cc, w.m, w.d_nope, w.rope_base, w.tau)
+            G.check_attention(f"hca prefill chunk {c} [{leg}]", o, lse, oref, lref)
         if c == 0:
             assert (o[rows < 127] == 0).all()   # no entry visible yet
+            assert np.isneginf(lse[rows < 127]).all()
 
 
 def test_hca_decode_b16_1m():
@@ -168,13 +247,17 @@ def test_hca_decode_b16_1m():
     x = lay.decode_inputs([ctx] * w.batch)
     lay.decode_step(x, out)
     torch.cuda.synchronize()
-    for b in (9,):
-        cache = hca_reference_cache(w, b, ctx, chunk)
-        oref, lref = csa.dense_attention_row(R.host(x["q"][b]), ctx, cache, w.m, w.d_nope, w.rope_base, w.tau)
-        err = max_rel_rows(R.host(out["o"][b]), oref)
-        assert err <= 1e-2, f"seq {b}: {err}"
-        assert np.abs(R.host(out["lse"][b]) - lref).max() <= 1e-2
+    n = (ctx + 1) // w.m
+    for b in (0, 5, 9, 15):
+        q = R.host(x["q"][b])
+        for leg, cc in (("A", hca_reference_cache(w, b, ctx, chunk)), ("B", gpu_hca_cache(lay, b, n))):
+            oref, lref = csa.dense_attention_row(q, ctx, cc, w.m, w.d_nope, w.rope_base, w.tau)
+            G.check_attention(f"hca decode seq {b} [{leg}]", R.host(out["o"][b]), R.host(out["lse"][b]), oref, lref)
 
+
+# ---------------------------------------------------------------------------
+# the layer pair, batch 4 at 2^20 context (MXFP4 indexer, BF16 scores)
+# ---------------------------------------------------------------------------
 
 def test_pair_decode_b4_1m_mxfp4():
     wc, wh = synth.PAIR_CSA_DECODE_B4_1M, synth.PAIR_HCA_DECODE_B4_1M
@@ -186,23 +269,30 @@ def test_pair_decode_b4_1m_mxfp4():
     co, ho = csa_l.alloc_decode_outputs(), hca_l.alloc_decode_outputs()
     xc = csa_l.decode_inputs([ctx] * B)
     xh = hca_l.decode_inputs([ctx] * B)
-    scores = torch.zeros((B, csa_l.cap), dtype=torch.float32, device="cuda")
-    csa_l.decode_step(xc, co, scores)
+    csa_l.decode_step(xc, co)
     hca_l.decode_step(xh, ho)
     torch.cuda.synchronize()
-    idx = co["idx"].cpu().numpy()
-    assert ascending_padded(idx) and ((idx >= 0).sum(1) == wc.topk).all()
-    b = 1
-    ref = csa_decode_reference(wc, csa_l, b, ctx, chunk)
-    check_rows("pair csa mxfp4", [b], idx[b:b + 1], ref["sel"][None], [ref["I"]], [ref["delta"]],
-               R.host(co["o"][b])[None], ref["o"][None])
-    # recall of the MXFP4 / BF16-score selection against the fp32 (unquantised) indexer
-    I32 = csa.index_scores(ref["qI"], ref["wt"], ref["kexact"], ref["n"], "f32")
-    full = set(csa.topk(I32, ref["n"], wc.topk).tolist())
-    recall = len(full & set(idx[b].tolist())) / wc.topk
-    print(f"MXFP4 indexer recall vs fp32: {recall:.4f} (pages quote 0.997 for a trained model)")
-    assert recall > 0.5
-    cache = csa.finalize_kv(R.chunked_entries(wh, b, ctx, chunk, overlap=False, seed=1), 0, wh.m, wh.d_nope,
-                            wh.rope_base, wh.nope_fmt, wh.rope_fmt)
-    oref, lref = csa.dense_attention_row(R.host(xh["q"][b]), ctx, cache, wh.m, wh.d_nope, wh.rope_base, wh.tau)
-    assert max_rel_rows(R.host(ho["o"][b]), oref) <= 1e-2
+    refs, idx = check_csa_decode_batch("pair csa mxfp4", wc, csa_l, co, ctx, range(B), chunk)
+    # recall of the MXFP4 / BF16-score selection against the fp32 indexer on
+    # the exact (unquantised) keys: the GPU's and the oracle's own MXFP4 path
+    k = wc.topk
+    rec_gpu, rec_orc, moved = [], [], 0
+    for b in range(B):
+        ref = refs[b]
+        I32 = csa.index_scores(ref["qI"], ref["wt"], ref["kexact"], ref["n"], "f32")
+        full = set(csa.topk(I32, ref["n"], k).tolist())
+        g = set(idx[b].tolist())
+        o = set(ref["sel"].tolist())
+        rec_gpu.append(len(full & g) / k)
+        rec_orc.append(len(full & o) / k)
+        moved += len(g - o)
+    print(f"MXFP4 indexer recall vs fp32 over {B} sequences: GPU {np.mean(rec_gpu):.4f}, "
+          f"oracle MXFP4 path {np.mean(rec_orc):.4f} (pages quote 0.997 for a trained model)", flush=True)
+    # the GPU equals the oracle's MXFP4 path up to the swaps leg A allowed
+    assert abs(sum(rec_gpu) - sum(rec_orc)) * k <= moved
+    n = (ctx + 1) // wh.m
+    for b in range(B):
+        q = R.host(xh["q"][b])
+        for leg, cc in (("A", hca_reference_cache(wh, b, ctx, chunk, seed=1)), ("B", gpu_hca_cache(hca_l, b, n))):
+            oref, lref = csa.dense_attention_row(q, ctx, cc, wh.m, wh.d_nope, wh.rope_base, wh.tau)
+            G.check_attention(f"pair hca seq {b} [{leg}]", R.host(ho["o"][b]), R.host(ho["lse"][b]), oref, lref)

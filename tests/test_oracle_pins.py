@@ -229,6 +229,37 @@ def test_attend_single_entry_and_empty_and_permutation():
     assert np.allclose(o1, o2, atol=1e-14) and np.allclose(l1, l2, atol=1e-14)
 
 
+def test_query_rescaling_keeps_topk_and_changes_temperature():
+    """Rescaling the query by c > 0: the indexer's top-k is unchanged (ReLU
+    and the head weights are positively homogeneous), while attention sees
+    the logits scaled by c, i.e. the temperature tau -> c tau.  The two limits
+    pin where tau enters: tau -> 0 gives the plain mean of the selected values
+    with lse = log(count); a large tau gives the value of the best entry."""
+    HI, dI, H, c, dv, n, k = 4, 8, 3, 10, 6, 300, 20
+    qI, w, Ki = rnd((HI, dI), 110), rnd(HI, 111), rnd((n, dI), 112)
+    for cc in (0.25, 3.0, 1e3):
+        assert np.array_equal(csa.topk(csa.index_scores(qI, w, Ki, n), n, k),
+                              csa.topk(csa.index_scores(cc * qI, w, Ki, n), n, k))
+    q, K = rnd((H, c), 113), rnd((n, c), 114)
+    V = K[:, :dv]
+    sel = csa.topk(csa.index_scores(qI, w, Ki, n), n, k)
+    tau = 1 / math.sqrt(c)
+    o1, l1 = csa.attend(q, K, V, sel, tau)
+    o2, l2 = csa.attend(2.0 * q, K, V, sel, tau)
+    o3, l3 = csa.attend(q, K, V, sel, 2.0 * tau)
+    assert np.allclose(o2, o3, atol=1e-13) and np.allclose(l2, l3, atol=1e-12)
+    assert np.abs(o2 - o1).max() > 1e-2          # a different temperature
+    # tau -> 0: uniform weights
+    o0, l0 = csa.attend(q, K, V, sel, 1e-13)
+    assert np.allclose(o0, np.broadcast_to(V[sel].mean(0), o0.shape), atol=1e-9)
+    assert np.allclose(l0, math.log(k), atol=1e-9)
+    # large tau: the arg-max entry of each head
+    oi, li = csa.attend(q, K, V, sel, 1e4)
+    best = sel[np.argmax(q @ K[sel].T, axis=1)]
+    assert np.allclose(oi, V[best], atol=1e-9)
+    assert np.allclose(li, 1e4 * np.max(q @ K[sel].T, axis=1), rtol=1e-12)
+
+
 def test_lse_merge_of_partitions():
     """Splitting the entry set and merging (o, lse) partials by LSE gives the
     unsplit result (the identity the split-K GPU kernels rely on)."""
