@@ -42,6 +42,7 @@ from compressed_sparse_amd import path, synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
+CPU_BASELINE = True     # the oracle timings (cleared by --no-cpu-baseline)
 
 
 def log(msg):
@@ -108,9 +109,140 @@ def cpu_baseline(w, st, budget_s=15.0):
         rows_done += len(rows)
     total = t_comp + t_rows / rows_done * w.tokens
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
-    return {"value": w.tokens / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+    return {"value": w.tokens / total, "unit": "tokens/s", "cores": int(threads), "cpu": host_cpu()[0],
+            "kind": "oracle",
             "sample": f"full fp64 compression of {w.tokens} tokens ({t_comp:.1f} s) + {rows_done} random query rows "
                       f"of indexer/top-k/attention ({t_rows:.1f} s), extrapolated linearly to {w.tokens} rows"}
+
+
+def host_cpu():
+    """The host's CPU model and the threads the oracle's BLAS uses."""
+    import platform
+    import threadpoolctl
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] + [1])
+    return model, int(threads), os.cpu_count()
+
+
+def oracle_entries(w, seq, T, prefix="", seed=0, overlap=True):
+    """Exact (fp64) entries of tokens [0, T) of sequence `seq`, computed by
+    the oracle's compressor chunk by chunk (the previous chunk's last m rows
+    carry the C^b side).  CPU-baseline setup: the cache a decode step reads."""
+    from oracle import csa
+    m, chunk = w.m, w.chunk
+    names = [prefix + n for n in (("a", "za", "b", "zb") if overlap else ("a", "za"))]
+    prm = {k: v.to("cpu", torch.float64).numpy() for k, v in synth.compressor_params(w, seed, "cuda").items()}
+    outs, tail = [], None
+    for c in range((T + chunk - 1) // chunk):
+        n = min(chunk, T - c * chunk)
+        x = synth.token_chunk(w, seq, c, chunk, seed, "cuda", names=names)
+        x = {k: v[:n].to("cpu", torch.float64).numpy() for k, v in x.items()}
+        tok0 = c * chunk
+        if overlap and tail is not None:
+            x = {k: np.concatenate([tail[k], x[k]], 0) for k in x}
+            tok0 -= m
+        i0, i1 = (c * chunk + m) // m - 1, (c * chunk + n) // m
+        if i1 > i0:
+            extra = (x[names[2]], x[names[3]], prm[prefix + "Bb"]) if overlap else ()
+            outs.append(csa.compress(x[names[0]], x[names[1]], prm[prefix + "Ba"], m, *extra, i0=i0, i1=i1, tok0=tok0))
+        if overlap:
+            tail = {k: v[-m:] for k, v in x.items()}
+    return np.concatenate(outs, 0)
+
+
+def cpu_baseline_csa_decode(w, lay, x, gpu_idx, seqs, recall=False):
+    """The oracle's CSA decode step (indexer over every visible key, top-k,
+    attention over the selected entries) timed for the sampled sequences of
+    the batch and extrapolated to the whole batch; its caches are built by the
+    oracle's own compressor (untimed setup).  With recall=True also the
+    indexer recall against the fp32 indexer on the exact keys, for the
+    oracle's own selection and for the GPU's."""
+    from oracle import csa
+    pos = int(x["pos"][0])
+    n = (pos + 1) // w.m
+    t_step, rec_o, rec_g = 0.0, [], []
+    for b in seqs:
+        sid = lay.seq_ids[b]
+        kexact = oracle_entries(w, sid, n * w.m, prefix="k")[:n]
+        keys = csa.finalize_keys(kexact, w.key_fmt)
+        q, qI, wt = (x[k][b].to("cpu", torch.float64).numpy() for k in ("q", "qI", "w"))
+        t0 = time.perf_counter()
+        I = csa.index_scores(csa.quantize_query(qI, w.qk_fmt), wt, keys["k"], n, w.score_fmt)
+        sel = csa.topk(I, n, w.topk)
+        t1 = time.perf_counter()
+        ids = sel[sel >= 0]
+        ex = csa.rope(oracle_selected_entries(w, sid, ids), csa.entry_position(ids, w.m), w.d_nope, w.rope_base)
+        K = np.zeros((n, w.c))
+        K[ids] = np.concatenate([csa.store_format(ex[:, :w.d_nope], w.nope_fmt)[0],
+                                 csa.store_format(ex[:, w.d_nope:], w.rope_fmt)[0]], 1)
+        t2 = time.perf_counter()
+        csa.sparse_attention_row(q, pos, {"k": K, "v": K[:, :w.d_nope]}, sel, w.d_nope, w.rope_base, w.tau)
+        t3 = time.perf_counter()
+        t_step += (t1 - t0) + (t3 - t2)
+        if recall:
+            full = set(csa.topk(csa.index_scores(qI, wt, kexact, n, "f32"), n, w.topk).tolist())
+            rec_o.append(len(full & set(sel.tolist())) / w.topk)
+            rec_g.append(len(full & set(gpu_idx[b].tolist())) / w.topk)
+    model, threads, _ = host_cpu()
+    us = t_step / len(seqs) * w.batch * 1e6
+    out = {"value": us, "unit": "us/step", "cores": threads, "cpu": model, "kind": "oracle",
+           "sample": f"decode step at position {pos} of {len(seqs)} of {w.batch} sequences (indexer over {n} keys, "
+                     f"top-{w.topk}, attention), extrapolated to the batch; caches from the oracle's compressor"}
+    if recall:
+        out["indexer_recall"] = {"gpu_vs_fp32": float(np.mean(rec_g)), "oracle_vs_fp32": float(np.mean(rec_o)),
+                                 "sequences": len(seqs), "target_pages_trained_model": 0.997}
+    return out
+
+
+def oracle_selected_entries(w, seq, ids, seed=0):
+    """Exact pre-RoPE CSA entries `ids` of sequence `seq`, each from its own
+    2m tokens (windows i-1 and i), by the oracle's compressor."""
+    from oracle import csa
+    m, chunk = w.m, w.chunk
+    ids = np.asarray(ids, dtype=np.int64)
+    rows = np.maximum((ids[:, None] - 1) * m + np.arange(2 * m)[None, :], 0).ravel()
+    names = ("a", "za", "b", "zb")
+    got = {nm: np.zeros((len(rows), w.c)) for nm in names}
+    for c in np.unique(rows // chunk):
+        sel = np.nonzero(rows // chunk == c)[0]
+        xc = synth.token_chunk(w, seq, int(c), chunk, seed, "cuda", names=list(names))
+        r = torch.as_tensor(rows[sel] % chunk, device="cuda")
+        for nm in names:
+            got[nm][sel] = xc[nm][r].to("cpu", torch.float64).numpy()
+    prm = {k: v.to("cpu", torch.float64).numpy() for k, v in synth.compressor_params(w, seed, "cuda").items()}
+    out = np.zeros((len(ids), w.c))
+    for j, i in enumerate(ids):
+        sl = slice(j * 2 * m, (j + 1) * 2 * m)
+        out[j] = csa.compress(got["a"][sl], got["za"][sl], prm["Ba"], m, got["b"][sl], got["zb"][sl], prm["Bb"],
+                              i0=int(i), i1=int(i) + 1, tok0=(int(i) - 1) * m)[0]
+    return out
+
+
+def cpu_baseline_hca_decode(w, lay, x, seqs, seed=0):
+    """The oracle's HCA decode step (dense attention over every visible
+    entry) timed for the sampled sequences, extrapolated to the batch."""
+    from oracle import csa
+    pos = int(x["pos"][0])
+    n = (pos + 1) // w.m
+    t = 0.0
+    for b in seqs:
+        cache = csa.finalize_kv(oracle_entries(w, lay.seq_ids[b], n * w.m, seed=seed, overlap=False)[:n], 0, w.m,
+                                w.d_nope, w.rope_base, w.nope_fmt, w.rope_fmt)
+        q = x["q"][b].to("cpu", torch.float64).numpy()
+        t0 = time.perf_counter()
+        csa.dense_attention_row(q, pos, cache, w.m, w.d_nope, w.rope_base, w.tau)
+        t += time.perf_counter() - t0
+    model, threads, _ = host_cpu()
+    return {"value": t / len(seqs) * w.batch * 1e6, "unit": "us/step", "cores": threads, "cpu": model,
+            "kind": "oracle", "sample": f"dense attention of {len(seqs)} of {w.batch} sequences at position {pos} "
+                                        f"over {n} entries, extrapolated to the batch; cache from the oracle's compressor"}
 
 
 def decode_bytes_csa(w, n, B):
@@ -129,65 +261,69 @@ def decode_bytes_hca(w, n, B):
     return B * (n * ent_b + 2 * w.heads * w.c + 2 * w.heads * w.d_nope + 4 * w.heads + 2 * 2 * w.c)
 
 
-def time_graph(step_fn, n_steps, replays=20, warmup=3):
-    """Captures n_steps consecutive decode steps in one HIP graph; returns
-    the average ms per step over `replays` replays."""
-    g = torch.cuda.CUDAGraph()
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        for i in range(n_steps):  # eager run also fills caches for the positions
-            step_fn(i)
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    with torch.cuda.graph(g):
-        for i in range(n_steps):
-            step_fn(i)
+DECODE_STEPS = 128
+
+
+def time_graph(layers, step_fn, n_steps=DECODE_STEPS, replays=12, warmup=2):
+    """Captures n_steps consecutive decode steps in one HIP graph (each replay
+    restores the layers' staging rings first, so every replay computes the
+    same steps); returns (median, p10, p90) ms per step over the replays."""
+    dg = path.DecodeGraph(layers, step_fn, n_steps)
     for _ in range(warmup):
-        g.replay()
+        dg.replay()
     torch.cuda.synchronize()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(replays):
-        g.replay()
-    b.record()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(replays)]
+    for a, b in evs:
+        a.record()
+        dg.replay()
+        b.record()
     torch.cuda.synchronize()
-    return a.elapsed_time(b) / (replays * n_steps)
+    per = np.array([a.elapsed_time(b) / n_steps for a, b in evs])
+    return float(np.median(per)), float(np.percentile(per, 10)), float(np.percentile(per, 90))
 
 
-def csa_decode_line(n_steps=8):
+def decode_line(name, metric, ms3, by, B):
+    ms, p10, p90 = ms3
+    return {"workload": name, "metric": metric, "value": ms * 1e3, "unit": "us", "p10_us": p10 * 1e3,
+            "p90_us": p90 * 1e3, "steps_per_graph": DECODE_STEPS, "tokens_per_s": B / (ms * 1e-3),
+            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
+                         "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         "algorithmic_bytes_per_step": by}}
+
+
+def csa_decode_line(n_steps=DECODE_STEPS):
     w = synth.CSA_DECODE_B32_128K
     log(f"setup {w.name}")
     lay = path.CsaLayer(w, w.batch, w.tokens // w.m + n_steps)
     lay.prefill_context(w.tokens)
     o = lay.alloc_decode_outputs()
-    xs = [lay.decode_inputs([w.tokens + i] * w.batch) for i in range(n_steps)]
-    ms = time_graph(lambda i: lay.decode_step(xs[i], o), n_steps)
+    xs = lay.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
+    ms3 = time_graph([lay], lambda i: lay.decode_step(xs[i], o), n_steps)
     by = decode_bytes_csa(w, w.tokens // w.m, w.batch)
-    return {"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
-            "tokens_per_s": w.batch / (ms * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "algorithmic_bytes_per_step": by}}
+    line = decode_line(w.name, "decode us/step (whole batch)", ms3, by, w.batch)
+    if CPU_BASELINE:
+        log("cpu baseline (oracle) " + w.name)
+        line["cpu_baseline"] = cpu_baseline_csa_decode(w, lay, xs[-1], o["idx"].cpu().numpy(), seqs=[0, 17])
+    return line
 
 
-def hca_decode_line(n_steps=8):
+def hca_decode_line(n_steps=DECODE_STEPS):
     w = synth.HCA_DECODE_B16_1M
     log(f"setup {w.name}")
     lay = path.HcaLayer(w, w.batch, w.tokens // w.m + n_steps)
     lay.prefill_context(w.tokens)
     o = lay.alloc_decode_outputs()
-    xs = [lay.decode_inputs([w.tokens + i] * w.batch) for i in range(n_steps)]
-    ms = time_graph(lambda i: lay.decode_step(xs[i], o), n_steps)
+    xs = lay.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
+    ms3 = time_graph([lay], lambda i: lay.decode_step(xs[i], o), n_steps)
     by = decode_bytes_hca(w, w.tokens // w.m, w.batch)
-    return {"workload": w.name, "metric": "decode us/step (whole batch)", "value": ms * 1e3, "unit": "us",
-            "tokens_per_s": w.batch / (ms * 1e-3),
-            "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                         "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                         "algorithmic_bytes_per_step": by}}
+    line = decode_line(w.name, "decode us/step (whole batch)", ms3, by, w.batch)
+    if CPU_BASELINE:
+        log("cpu baseline (oracle) " + w.name)
+        line["cpu_baseline"] = cpu_baseline_hca_decode(w, lay, xs[-1], seqs=[9])
+    return line
 
 
-def pair_decode_lines(n_steps=8):
+def pair_decode_lines(n_steps=DECODE_STEPS):
     wc, wh = synth.PAIR_CSA_DECODE_B4_1M, synth.PAIR_HCA_DECODE_B4_1M
     log(f"setup {wc.name} + {wh.name}")
     lc = path.CsaLayer(wc, wc.batch, wc.tokens // wc.m + n_steps)
@@ -195,39 +331,164 @@ def pair_decode_lines(n_steps=8):
     lc.prefill_context(wc.tokens)
     lh.prefill_context(wh.tokens)
     oc, oh = lc.alloc_decode_outputs(), lh.alloc_decode_outputs()
-    xc = [lc.decode_inputs([wc.tokens + i] * wc.batch) for i in range(n_steps)]
-    xh = [lh.decode_inputs([wh.tokens + i] * wh.batch) for i in range(n_steps)]
-    ms_c = time_graph(lambda i: lc.decode_step(xc[i], oc), n_steps)
+    xc = lc.decode_input_steps([[wc.tokens + i] * wc.batch for i in range(n_steps)])
+    xh = lh.decode_input_steps([[wh.tokens + i] * wh.batch for i in range(n_steps)])
+    ms_c = time_graph([lc], lambda i: lc.decode_step(xc[i], oc), n_steps)
 
     def pair(i):
         lc.decode_step(xc[i], oc)
         lh.decode_step(xh[i], oh)
-    ms = time_graph(pair, n_steps)
+    ms = time_graph([lc, lh], pair, n_steps)
     by_c = decode_bytes_csa(wc, wc.tokens // wc.m, wc.batch)
     by = by_c + decode_bytes_hca(wh, wh.tokens // wh.m, wh.batch)
-    return [{"workload": wc.name, "metric": "CSA layer decode us/step (whole batch)", "value": ms_c * 1e3,
-             "unit": "us", "roofline": {"bound": "hbm", "achieved": by_c / (ms_c * 1e-3) / 1e9,
-                                        "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                                        "frac": by_c / (ms_c * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                                        "algorithmic_bytes_per_step": by_c}},
-            {"workload": wc.name + " + " + wh.name, "metric": "CSA+HCA layer pair decode us/step",
-             "value": ms * 1e3, "unit": "us",
-             "roofline": {"bound": "hbm", "achieved": by / (ms * 1e-3) / 1e9, "peak": PEAK_HBM_GBS,
-                          "unit": "GB/s", "frac": by / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
-                          "algorithmic_bytes_per_step": by}}]
+    lines = [decode_line(wc.name, "CSA layer decode us/step (whole batch)", ms_c, by_c, wc.batch),
+             decode_line(wc.name + " + " + wh.name, "CSA+HCA layer pair decode us/step", ms, by, wc.batch)]
+    if CPU_BASELINE:
+        # the oracle on every sequence of the CSA layer: its time, and the
+        # indexer recall (GPU and oracle MXFP4 / BF16-score selections against
+        # the fp32 indexer on the exact keys) at the last timed step
+        log("cpu baseline (oracle) + indexer recall " + wc.name)
+        lines[0]["cpu_baseline"] = cpu_baseline_csa_decode(wc, lc, xc[-1], oc["idx"].cpu().numpy(),
+                                                           seqs=range(wc.batch), recall=True)
+        lines[0]["indexer_recall"] = lines[0]["cpu_baseline"].pop("indexer_recall")
+    return lines
 
 
 def secondary_lines():
-    out = [csa_decode_line()]
-    torch.cuda.empty_cache()
-    out.append(hca_decode_line())
-    torch.cuda.empty_cache()
-    out.extend(pair_decode_lines())
-    torch.cuda.empty_cache()
-    out.append(secondary_hca_prefill())
-    torch.cuda.empty_cache()
-    out.append(secondary_mxfp4_prefill_indexer())
+    out = []
+    for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, secondary_hca_prefill,
+               secondary_hca_prefill_whole, secondary_mxfp4_prefill_indexer, secondary_tiny):
+        r = fn()
+        out.extend(r if isinstance(r, list) else [r])
+        torch.cuda.empty_cache()
     return out
+
+
+def measured_peaks():
+    """Microbenchmarks beside the datasheet peaks: a 4 GiB device copy (HBM
+    read + write bytes over its time) and a 8192^3 BF16 GEMM (torch.matmul,
+    the vendor BLAS) on this GPU."""
+    a = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    hbm = 5 * 2 * a.numel() / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del a, b
+    n = 8192
+    x = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    y = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    z = x @ y
+    e0.record()
+    for _ in range(10):
+        z = x @ y
+    e1.record()
+    torch.cuda.synchronize()
+    tf = 10 * 2.0 * n ** 3 / (e0.elapsed_time(e1) * 1e-3) / 1e12
+    del x, y, z
+    torch.cuda.empty_cache()
+    return {"hbm_copy_GBs": hbm, "bf16_gemm_TFLOPs": tf,
+            "note": "4 GiB device copy (2 x bytes / time); torch.matmul 8192^3 bf16"}
+
+
+def secondary_hca_prefill_whole(reps=2):
+    """The whole 2^20-token HCA prefill: all 128 chunks, each compressing its
+    8192 tokens and running dense attention for its 8192 queries over the
+    entries visible to them.  Token projections, all 128 query chunks and
+    all 128 output chunks are resident in HBM (about 150 GB)."""
+    w = synth.HCA_PREFILL_1M
+    chunk, nch = w.chunk, w.tokens // w.chunk
+    log(f"setup {w.name} (whole sequence)")
+    lay = path.HcaLayer(w, 1, w.tokens // w.m)
+    toks = [{k: v[None].contiguous() for k, v in synth.token_chunk(w, 0, c, chunk, 0, "cuda").items()}
+            for c in range(nch)]
+    qs = [synth.query_chunk(w, 0, c, chunk, 0, "cuda", with_index=False)["q"][None].contiguous() for c in range(nch)]
+    odt = synth.TORCH_DTYPE[w.out_dtype]
+    outs = [torch.empty((1, chunk, w.heads, w.d_nope), dtype=odt, device="cuda") for _ in range(nch)]
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nch)]
+
+    def whole(time_attn=False):
+        for c in range(nch):
+            cb.compress_prefill(lay.kv, c * chunk, toks[c]["a"], toks[c]["za"], lay.prm["Ba"])
+            if time_attn:
+                evs[c][0].record()
+            cb.dense_attn_prefill(lay.adesc, lay.kv, c * chunk, qs[c], w.tau, outs[c])
+            if time_attn:
+                evs[c][1].record()
+    whole()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        whole()
+    b.record()
+    torch.cuda.synchronize()
+    s_total = a.elapsed_time(b) / reps * 1e-3
+    whole(time_attn=True)
+    torch.cuda.synchronize()
+    s_attn = sum(e0.elapsed_time(e1) for e0, e1 in evs) * 1e-3
+    t = np.arange(w.tokens, dtype=np.int64)
+    flops = 2.0 * float(np.minimum((t + 1) // w.m, w.tokens // w.m).sum()) * w.heads * (w.c + w.d_nope)
+    del toks, qs, outs
+    return {"workload": w.name + " (whole sequence)", "metric": "HCA prefill tokens/s (2^20 tokens, 128 chunks)",
+            "value": w.tokens / s_total, "unit": "tokens/s", "s_per_prefill": s_total,
+            "roofline": {"bound": "mfma", "kernel": "dense attention prefill (128 launches)",
+                         "achieved": flops / s_attn / 1e12, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": flops / s_attn / 1e12 / PEAK_BF16_TFLOPS, "algorithmic_flop": flops,
+                         "attention_s": s_attn, "whole_step_frac": flops / s_total / 1e12 / PEAK_BF16_TFLOPS}}
+
+
+def secondary_tiny(reps=20):
+    """The tiny fp32 CSA prefill (2048 tokens, 8 heads, 32 + 32 dims, k = 64;
+    the parity workload) end to end on the GPU, and the oracle on the host."""
+    w = synth.TINY_CSA_PREFILL_FP32
+    pr = {k: v.to("cuda") for k, v in synth.tiny_projections(w).items()}
+    T, m, k = w.tokens, w.m, w.topk
+    N = T // m
+    kv = cb.KVCache(cb.cache_desc(m, True, w.d_nope, w.d_rope, "f32", "f32", "f32", N), 1)
+    keys = cb.KVCache(cb.cache_desc(m, True, w.idx_dim, 0, "f32", "f32", "f32", N), 1)
+    u = lambda t: t[None].contiguous()
+    x = {kk: u(v) for kk, v in pr.items() if v.dim() > 1 and v.shape[0] == T}
+    idesc = cb.index_desc(w.idx_heads, w.idx_dim, "f32", "f32", "f32", "f32", m, N)
+    adesc = cb.attn_desc(w.heads, w.d_nope, w.d_rope, "f32", "f32", "f32", "f32", m, N)
+    idx = torch.empty((1, T, k), dtype=torch.int32, device="cuda")
+    o = torch.empty((1, T, w.heads, w.d_nope), dtype=torch.float32, device="cuda")
+    iws = cb.workspace(cb.workspace_bytes(cb.OP_INDEX_TOPK_PREFILL, idesc, 1, T, 0, k))
+
+    def step():
+        cb.compress_prefill(kv, 0, x["a"], x["za"], pr["Ba"], x["b"], x["zb"], pr["Bb"])
+        cb.compress_prefill(keys, 0, x["ka"], x["kza"], pr["kBa"], x["kb"], x["kzb"], pr["kBb"])
+        cb.index_topk_prefill(idesc, keys, 0, x["qI"], x["w"], k, idx, ws=iws)
+        cb.sparse_attn_prefill(adesc, kv, 0, x["q"], idx, w.tau, o)
+    step()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        step()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    line = {"workload": w.name, "metric": "tiny fp32 CSA prefill tokens/s (parity workload, generic fp32 kernels)",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms}
+    if CPU_BASELINE:
+        from oracle import csa
+        h = {kk: v.cpu().double().numpy() for kk, v in pr.items()}
+        t0 = time.perf_counter()
+        cache = csa.finalize_kv(csa.compress(h["a"], h["za"], h["Ba"], m, h["b"], h["zb"], h["Bb"]), 0, m,
+                                w.d_nope, w.rope_base, "f32", "f32")
+        kk_ = csa.finalize_keys(csa.compress(h["ka"], h["kza"], h["kBa"], m, h["kb"], h["kzb"], h["kBb"]), "f32")
+        rows = np.arange(T)
+        csa.csa_rows(rows, rows, h["q"], h["qI"], h["w"], cache, kk_, m, k, w.d_nope, w.rope_base, w.tau)
+        dt = time.perf_counter() - t0
+        model, threads, _ = host_cpu()
+        line["cpu_baseline"] = {"value": T / dt, "unit": "tokens/s", "cores": threads, "cpu": model, "kind": "oracle",
+                                "sample": f"the whole workload ({T} tokens: compression, indexer, top-k, attention)"}
+    return line
 
 def secondary_hca_prefill(steps=5):
     """The last 8192-token chunk of a 2^20-token HCA prefill: compress the
@@ -314,9 +575,12 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=15.0)
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
-    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill", "mxfp4-indexer"],
+    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill", "hca-prefill-whole",
+                                       "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
     args = ap.parse_args()
+    global CPU_BASELINE
+    CPU_BASELINE = not args.no_cpu_baseline
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X; "
               "multi-GPU sharding is not built (run with --gpus 1)", file=sys.stderr)
@@ -328,7 +592,9 @@ def main():
         copy_calibration()
     if args.only:
         fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
-              "hca-prefill": secondary_hca_prefill, "mxfp4-indexer": secondary_mxfp4_prefill_indexer}[args.only]
+              "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
+              "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
+              "peaks": measured_peaks}[args.only]
         print(json.dumps(fn()), flush=True)
         return
     w = synth.CSA_PREFILL_BF16_32K
@@ -379,7 +645,17 @@ def main():
     if not args.no_secondary:
         del st
         torch.cuda.empty_cache()
+        log("measured peaks")
+        pk = measured_peaks()
+        out["measured_peaks"] = pk
+        out["roofline"]["frac_vs_measured_gemm"] = achieved / pk["bf16_gemm_TFLOPs"]
         out["secondary"] = secondary_lines()
+        for line in out["secondary"]:
+            r = line.get("roofline", {})
+            if r.get("unit") == "GB/s":
+                r["frac_vs_measured_copy"] = r["achieved"] / pk["hbm_copy_GBs"]
+            elif r.get("unit") == "TFLOP/s":
+                r["frac_vs_measured_gemm"] = r["achieved"] / pk["bf16_gemm_TFLOPs"]
     print(json.dumps(out), flush=True)
 
 
