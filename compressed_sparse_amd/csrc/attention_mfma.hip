@@ -84,12 +84,13 @@ size_t part_bytes(int B, int splits) {
 // Decode splits of one sequence: a function of its entry count alone (the
 // list length k, or the capacity for dense), never of the batch size, so a
 // sequence's partials, their merge and its output bits are the same in any
-// batch.  A sparse split covers one 64-entry tile (k = 1024: 16 splits); a
+// batch.  A sparse split covers two 64-entry tiles (k = 1024: 8 splits); a
 // dense split at least DENSE_TILES tiles, at most MAX_SPLITS splits.
+constexpr int SPARSE_TILES = 2;
 constexpr int DENSE_TILES = 4;
 int decode_splits(bool dense, int64_t count) {
   const int64_t ntiles = (count + TILE - 1) / TILE;
-  const int64_t per = dense ? DENSE_TILES : 1;
+  const int64_t per = dense ? DENSE_TILES : SPARSE_TILES;
   int64_t s = (ntiles + per - 1) / per;
   if (s > MAX_SPLITS) s = MAX_SPLITS;
   return s < 1 ? 1 : static_cast<int>(s);
