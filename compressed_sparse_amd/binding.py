@@ -48,9 +48,10 @@ class AttnDesc(ctypes.Structure):
 
 
 EXPORTS = ["csa_compress_prefill", "csa_compress_decode", "csa_index_topk_prefill", "csa_index_topk_decode",
-           "csa_sparse_attn_prefill", "csa_sparse_attn_decode", "hca_dense_attn_prefill",
-           "hca_dense_attn_decode", "csa_workspace_bytes", "csa_status_string", "csa_last_error",
-           "csa_version"]
+           "csa_sparse_attn_prefill", "csa_sparse_attn_decode", "csa_sparse_attn_decode_noalloc",
+           "hca_dense_attn_prefill", "hca_dense_attn_decode", "csa_workspace_bytes", "csa_status_string",
+           "csa_last_error", "csa_version"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -70,6 +71,7 @@ def lib():
             "csa_index_topk_decode": [P, I, P, P, P, P, I, P, P, P, SZ, P],
             "csa_sparse_attn_prefill": [P, I, I, I64, P, P, P, I, F, P, P, P, SZ, P],
             "csa_sparse_attn_decode": [P, I, P, P, P, P, I, F, P, P, P, SZ, P],
+            "csa_sparse_attn_decode_noalloc": [P, I, P, P, P, P, I, F, P, P, P],
             "hca_dense_attn_prefill": [P, I, I, I64, P, P, F, P, P, P, SZ, P],
             "hca_dense_attn_decode": [P, I, P, P, P, F, P, P, P, SZ, P],
             "csa_workspace_bytes": [I, P, I, I, I64, I],
@@ -218,6 +220,14 @@ def sparse_attn_decode(desc, kv: KVCache, pos, q, idx, scale, o, lse=None, ws=No
     cs = kv.struct()
     _check(lib().csa_sparse_attn_decode(ctypes.byref(desc), B, ptr(pos), ptr(q), ctypes.byref(cs), ptr(idx), k,
                                         scale, ptr(o), ptr(lse), ptr(ws), ws.numel(), stream_ptr(stream)))
+
+
+def sparse_attn_decode_noalloc(desc, kv: KVCache, pos, q, idx, scale, o, lse=None, stream=None):
+    """csa_sparse_attn_decode with the split partials in the library's own
+    device scratch (no workspace argument)."""
+    cs = kv.struct()
+    _check(lib().csa_sparse_attn_decode_noalloc(ctypes.byref(desc), q.shape[0], ptr(pos), ptr(q), ctypes.byref(cs),
+                                                ptr(idx), idx.shape[-1], scale, ptr(o), ptr(lse), stream_ptr(stream)))
 
 
 def dense_attn_prefill(desc, kv: KVCache, pos0, q, scale, o, lse=None, ws=None, stream=None):

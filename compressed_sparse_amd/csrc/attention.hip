@@ -10,6 +10,8 @@
 // fp32, one workgroup per (query, head), online softmax over chunks of 256
 // entries) and the host entry points, which route the MI355X-shaped cases
 // (64 heads, 512 + 64 dims, BF16 / FP8 caches) to the MFMA kernels.
+#include <mutex>
+
 #include "attention.hpp"
 
 namespace csa {
@@ -172,6 +174,37 @@ static int dispatch(AttnParams& P, int op, int B, void* stream) {
   return launch_generic(P, B, s);
 }
 
+// ---------------------------------------------------------------------------
+// allocation-free decode: split partials in a library-owned device array
+// ---------------------------------------------------------------------------
+// One copy of this array lives on every GPU the library runs on, for the life
+// of the process.  In host code its name is a host-side stand-in: kernels get
+// the device address looked up once per device by hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[CSA_NOALLOC_SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[MAX_DEVICES] = {};
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with it current).
+static int scratch_on_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(CSA_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= MAX_DEVICES) return fail(CSA_ERR_UNSUPPORTED, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(CSA_ERR_HIP, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return CSA_OK;
+}
+
 }  // namespace csa
 
 using namespace csa;
@@ -206,6 +239,29 @@ extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const in
     return fail(CSA_ERR_WORKSPACE, "workspace too small");
   if (B == 0) return CSA_OK;
   AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes);
+  P.T = 1; P.pos0 = 0; P.pos_dev = pos;
+  return dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
+}
+
+// The allocation-free variant of csa_sparse_attn_decode: the split partials
+// go to the library's device array instead of a caller workspace.
+extern "C" int csa_sparse_attn_decode_noalloc(const csa_attn_desc* desc, int B, const int64_t* pos,
+                                              const void* q, const csa_cache* kv, const int32_t* idx, int k,
+                                              float softmax_scale, void* o, float* lse, void* stream) {
+  int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
+  if (st != CSA_OK) return st;
+  if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
+  if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
+  if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
+  const size_t need = attn_ws_bytes(desc, CSA_OP_SPARSE_ATTN_DECODE, B, 1, 0, k);
+  if (need > CSA_NOALLOC_SCRATCH_BYTES)
+    return fail(CSA_ERR_WORKSPACE, "split partials need " + std::to_string(need) + " bytes, above the " +
+                                       std::to_string(static_cast<size_t>(CSA_NOALLOC_SCRATCH_BYTES)) +
+                                       "-byte library scratch: use csa_sparse_attn_decode with a workspace");
+  if (B == 0) return CSA_OK;
+  void* ws = nullptr;
+  if ((st = scratch_on_current_device(&ws)) != CSA_OK) return st;
+  AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, CSA_NOALLOC_SCRATCH_BYTES);
   P.T = 1; P.pos0 = 0; P.pos_dev = pos;
   return dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
 }

@@ -223,6 +223,23 @@ int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
                            float softmax_scale, void* o, float* lse, void* ws,
                            size_t ws_bytes, void* stream);
 
+/* Allocation-free variant of csa_sparse_attn_decode, for callers that cannot
+ * allocate device memory or hand the library a workspace (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same arguments and results as csa_sparse_attn_decode without ws/ws_bytes:
+ * the decode split partials go to one library-owned device array of
+ * CSA_NOALLOC_SCRATCH_BYTES per GPU, which each GPU the library runs on
+ * holds until the process ends.  CSA_ERR_WORKSPACE when the call needs more
+ * than that (csa_workspace_bytes(CSA_OP_SPARSE_ATTN_DECODE, ...) bytes: about
+ * 0.5 MiB per sequence at k = 1024, so B <= 127).  Every call on a GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  No part of the array
+ * needs to start at zero: every call writes each partial it reads. */
+#define CSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int csa_sparse_attn_decode_noalloc(const csa_attn_desc* desc, int B, const int64_t* pos,
+                                   const void* q, const csa_cache* kv, const int32_t* idx, int k,
+                                   float softmax_scale, void* o, float* lse, void* stream);
+
 int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
                            const void* q, const csa_cache* kv, float softmax_scale, void* o,
                            float* lse, void* ws, size_t ws_bytes, void* stream);

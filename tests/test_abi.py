@@ -147,3 +147,19 @@ def test_decode_attention_workspace_is_per_sequence():
         assert one > 0
         for B in (4, 16, 32):
             assert cb.workspace_bytes(op, d, B, 1, 0, k) == B * one
+
+
+def test_noalloc_decode_rejects_past_its_scratch_on_the_host():
+    # the allocation-free decode holds its split partials in a fixed device
+    # array; a batch whose partials would not fit is rejected before launch
+    L = cb.lib()
+    desc = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192)
+    per_seq = cb.workspace_bytes(cb.OP_SPARSE_ATTN_DECODE, desc, 1, 1, 0, 1024)
+    B = cb.NOALLOC_SCRATCH_BYTES // per_seq + 1
+    P = fake(0x4000)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    assert L.csa_sparse_attn_decode_noalloc(ctypes.byref(desc), B, P, P, ctypes.byref(kv), P, 1024, 0.1, P, None,
+                                            None) == 4
+    assert b"scratch" in L.csa_last_error()
+    assert L.csa_sparse_attn_decode_noalloc(ctypes.byref(desc), 1, P, P, ctypes.byref(kv), P, 0, 0.1, P, None,
+                                            None) == 1
