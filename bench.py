@@ -43,6 +43,8 @@ from compressed_sparse_amd import path, synth  # noqa: E402
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 CPU_BASELINE = True     # the oracle timings (cleared by --no-cpu-baseline)
+REPLAYS = 12            # timed replays of each decode graph (--replays)
+DECODE_EAGER = 0        # > 0: that many eager decode steps instead of graphs (--decode-eager, counter runs)
 
 
 def log(msg):
@@ -264,10 +266,20 @@ def decode_bytes_hca(w, n, B):
 DECODE_STEPS = 128
 
 
-def time_graph(layers, step_fn, n_steps=DECODE_STEPS, replays=12, warmup=2):
+def time_graph(layers, step_fn, n_steps=DECODE_STEPS, replays=None, warmup=2):
     """Captures n_steps consecutive decode steps in one HIP graph (each replay
     restores the layers' staging rings first, so every replay computes the
     same steps); returns (median, p10, p90) ms per step over the replays."""
+    replays = replays or REPLAYS
+    if DECODE_EAGER:  # counter collection: a few plain launches, no graph
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(DECODE_EAGER):
+            step_fn(i % n_steps)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / DECODE_EAGER
+        return ms, ms, ms
     dg = path.DecodeGraph(layers, step_fn, n_steps)
     for _ in range(warmup):
         dg.replay()
@@ -573,14 +585,19 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=15.0)
+    ap.add_argument("--replays", type=int, default=12, help="timed replays of each 128-step decode graph")
+    ap.add_argument("--decode-eager", type=int, default=0,
+                    help="run this many eager decode steps instead of the graphs (for counter collection)")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
     ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill", "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
     args = ap.parse_args()
-    global CPU_BASELINE
+    global CPU_BASELINE, REPLAYS, DECODE_EAGER
     CPU_BASELINE = not args.no_cpu_baseline
+    REPLAYS = args.replays
+    DECODE_EAGER = args.decode_eager
     if args.gpus != 1:
         print("bench.py measures one GPU only: the path runs on a single MI355X; "
               "multi-GPU sharding is not built (run with --gpus 1)", file=sys.stderr)

@@ -71,15 +71,18 @@ class CsaLayer:
         chunk = chunk or self.w.chunk
         per = [[None] * self.B for _ in steps]
         for b, sid in enumerate(self.seq_ids):  # one sequence's chunks alive at a time
-            drawn = {}
+            by_chunk = {}
             for i, positions in enumerate(steps):
-                c, r = divmod(int(positions[b]), chunk)
-                if c not in drawn:
-                    d = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
-                    d.update(synth.query_chunk(self.w, sid, c, chunk, self.seed, self.device))
-                    drawn[c] = d
-                per[i][b] = {k: v[r].clone() for k, v in drawn[c].items()}  # rows, not views of the chunk
-            del drawn
+                by_chunk.setdefault(int(positions[b]) // chunk, []).append(i)
+            for c, its in by_chunk.items():
+                d = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
+                d.update(synth.query_chunk(self.w, sid, c, chunk, self.seed, self.device))
+                rows = torch.tensor([int(steps[i][b]) % chunk for i in its], device=self.device)
+                # the rows gathered into new tensors (an index kernel), so the chunk is freed
+                got = {k: v.index_select(0, rows) for k, v in d.items()}
+                for j, i in enumerate(its):
+                    per[i][b] = {k: v[j] for k, v in got.items()}
+                del d
         out = []
         for i, positions in enumerate(steps):
             x = {k: _stack([p[k] for p in per[i]]) for k in per[i][0]}
@@ -152,15 +155,18 @@ class HcaLayer:
         chunk = chunk or self.w.chunk
         per = [[None] * self.B for _ in steps]
         for b, sid in enumerate(self.seq_ids):  # one sequence's chunks alive at a time
-            drawn = {}
+            by_chunk = {}
             for i, positions in enumerate(steps):
-                c, r = divmod(int(positions[b]), chunk)
-                if c not in drawn:
-                    d = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
-                    d["q"] = synth.query_chunk(self.w, sid, c, chunk, self.seed, self.device, with_index=False)["q"]
-                    drawn[c] = d
-                per[i][b] = {k: v[r].clone() for k, v in drawn[c].items()}  # rows, not views of the chunk
-            del drawn
+                by_chunk.setdefault(int(positions[b]) // chunk, []).append(i)
+            for c, its in by_chunk.items():
+                d = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
+                d["q"] = synth.query_chunk(self.w, sid, c, chunk, self.seed, self.device, with_index=False)["q"]
+                rows = torch.tensor([int(steps[i][b]) % chunk for i in its], device=self.device)
+                # the rows gathered into new tensors (an index kernel), so the chunk is freed
+                got = {k: v.index_select(0, rows) for k, v in d.items()}
+                for j, i in enumerate(its):
+                    per[i][b] = {k: v[j] for k, v in got.items()}
+                del d
         out = []
         for i, positions in enumerate(steps):
             x = {k: _stack([p[k] for p in per[i]]) for k in per[i][0]}
