@@ -47,10 +47,15 @@ class AttnDesc(ctypes.Structure):
                 ("capacity", ctypes.c_int64)]
 
 
+class DecodeInputs(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("a", "b", "za", "zb", "Ba", "Bb", "ka", "kb", "kza", "kzb", "kBa", "kBb",
+                                               "q", "qI", "w")]
+
+
 EXPORTS = ["csa_compress_prefill", "csa_compress_decode", "csa_index_topk_prefill", "csa_index_topk_decode",
            "csa_sparse_attn_prefill", "csa_sparse_attn_decode", "csa_sparse_attn_decode_noalloc",
-           "hca_dense_attn_prefill", "hca_dense_attn_decode", "csa_workspace_bytes", "csa_status_string",
-           "csa_last_error", "csa_version"]
+           "hca_dense_attn_prefill", "hca_dense_attn_decode", "csa_decode_step", "csa_decode_step_workspace_bytes",
+           "csa_workspace_bytes", "csa_status_string", "csa_last_error", "csa_version"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
@@ -75,11 +80,13 @@ def lib():
             "hca_dense_attn_prefill": [P, I, I, I64, P, P, F, P, P, P, SZ, P],
             "hca_dense_attn_decode": [P, I, P, P, P, F, P, P, P, SZ, P],
             "csa_workspace_bytes": [I, P, I, I, I64, I],
+            "csa_decode_step": [P, P, P, P, P, P, I, P, P, I, F, P, P, P, P, P, SZ, P],
+            "csa_decode_step_workspace_bytes": [P, P, I, I],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
             fn.argtypes = args
-            fn.restype = SZ if name == "csa_workspace_bytes" else I
+            fn.restype = SZ if name.endswith("workspace_bytes") else I
         L.csa_status_string.restype = ctypes.c_char_p
         L.csa_status_string.argtypes = [I]
         L.csa_last_error.restype = ctypes.c_char_p
@@ -228,6 +235,27 @@ def sparse_attn_decode_noalloc(desc, kv: KVCache, pos, q, idx, scale, o, lse=Non
     cs = kv.struct()
     _check(lib().csa_sparse_attn_decode_noalloc(ctypes.byref(desc), q.shape[0], ptr(pos), ptr(q), ctypes.byref(cs),
                                                 ptr(idx), idx.shape[-1], scale, ptr(o), ptr(lse), stream_ptr(stream)))
+
+
+def decode_step_workspace_bytes(idesc, adesc, B, k):
+    return lib().csa_decode_step_workspace_bytes(ctypes.byref(idesc), ctypes.byref(adesc), B, k)
+
+
+def decode_step(kv: KVCache, keys: KVCache, idesc, adesc, pos, x, prm, k, scale, idx, o, lse=None, scores=None,
+                ws=None, stream=None):
+    """csa_decode_step: both compressors, indexer + top-k and sparse
+    attention of one CSA decode step.  x: the step's rows (a, za, b, zb, ka,
+    kza, kb, kzb, q, qI, w); prm: Ba, Bb, kBa, kBb."""
+    B = x["q"].shape[0]
+    if ws is None:
+        ws = workspace(decode_step_workspace_bytes(idesc, adesc, B, k), x["q"].device)
+    g = lambda d, n: None if d.get(n) is None else d[n].data_ptr()
+    inp = DecodeInputs(g(x, "a"), g(x, "b"), g(x, "za"), g(x, "zb"), g(prm, "Ba"), g(prm, "Bb"), g(x, "ka"), g(x, "kb"),
+                       g(x, "kza"), g(x, "kzb"), g(prm, "kBa"), g(prm, "kBb"), g(x, "q"), g(x, "qI"), g(x, "w"))
+    kvs, ks = kv.struct(), keys.struct()
+    _check(lib().csa_decode_step(ctypes.byref(kv.desc), ctypes.byref(kvs), ctypes.byref(keys.desc), ctypes.byref(ks),
+                                 ctypes.byref(idesc), ctypes.byref(adesc), B, ptr(pos), ctypes.byref(inp), k, scale,
+                                 ptr(idx), ptr(scores), ptr(o), ptr(lse), ptr(ws), ws.numel(), stream_ptr(stream)))
 
 
 def dense_attn_prefill(desc, kv: KVCache, pos0, q, scale, o, lse=None, ws=None, stream=None):

@@ -163,7 +163,7 @@ size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0,
   return mfma_attn_ws_bytes(d, op, B, T, pos0, k);
 }
 
-static int dispatch(AttnParams& P, int op, int B, void* stream) {
+int attn_dispatch(AttnParams& P, int op, int B, void* stream) {
   hipStream_t s = as_stream(stream);
   if (mfma_attn_supported(P)) {
     if (!mfma_attn_capacity_ok(P))
@@ -223,13 +223,14 @@ extern "C" int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, 
   if (B == 0 || T == 0) return CSA_OK;
   AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes);
   P.T = T; P.pos0 = pos0; P.pos_dev = nullptr;
-  return dispatch(P, CSA_OP_SPARSE_ATTN_PREFILL, B, stream);
+  return attn_dispatch(P, CSA_OP_SPARSE_ATTN_PREFILL, B, stream);
 }
 
-extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
-                                      const void* q, const csa_cache* kv, const int32_t* idx, int k,
-                                      float softmax_scale, void* o, float* lse, void* ws,
-                                      size_t ws_bytes, void* stream) {
+namespace csa {
+
+int sparse_attn_decode_setup(const csa_attn_desc* desc, int B, const int64_t* pos, const void* q, const csa_cache* kv,
+                             const int32_t* idx, int k, float softmax_scale, void* o, float* lse, void* ws,
+                             size_t ws_bytes, AttnParams* out) {
   int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
@@ -237,10 +238,26 @@ extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const in
   if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
   if (ws_bytes < attn_ws_bytes(desc, CSA_OP_SPARSE_ATTN_DECODE, B, 1, 0, k))
     return fail(CSA_ERR_WORKSPACE, "workspace too small");
-  if (B == 0) return CSA_OK;
   AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes);
   P.T = 1; P.pos0 = 0; P.pos_dev = pos;
-  return dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
+  if (mfma_attn_supported(P) && !mfma_attn_capacity_ok(P))
+    return fail(CSA_ERR_UNSUPPORTED, "capacity too large: each cache buffer of a sequence must stay below 2^31 bytes "
+                                     "(2^21 BF16 or 2^22 FP8 entries of 512 dims)");
+  *out = P;
+  return CSA_OK;
+}
+
+}  // namespace csa
+
+extern "C" int csa_sparse_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
+                                      const void* q, const csa_cache* kv, const int32_t* idx, int k,
+                                      float softmax_scale, void* o, float* lse, void* ws,
+                                      size_t ws_bytes, void* stream) {
+  AttnParams P;
+  int st = sparse_attn_decode_setup(desc, B, pos, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes, &P);
+  if (st != CSA_OK) return st;
+  if (B == 0) return CSA_OK;
+  return attn_dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
 }
 
 // The allocation-free variant of csa_sparse_attn_decode: the split partials
@@ -263,7 +280,7 @@ extern "C" int csa_sparse_attn_decode_noalloc(const csa_attn_desc* desc, int B, 
   if ((st = scratch_on_current_device(&ws)) != CSA_OK) return st;
   AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, CSA_NOALLOC_SCRATCH_BYTES);
   P.T = 1; P.pos0 = 0; P.pos_dev = pos;
-  return dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
+  return attn_dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
 }
 
 extern "C" int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
@@ -277,7 +294,7 @@ extern "C" int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, i
   if (B == 0 || T == 0) return CSA_OK;
   AttnParams P = make_attn_params(desc, q, kv, nullptr, 0, softmax_scale, o, lse, ws, ws_bytes);
   P.T = T; P.pos0 = pos0; P.pos_dev = nullptr;
-  return dispatch(P, CSA_OP_DENSE_ATTN_PREFILL, B, stream);
+  return attn_dispatch(P, CSA_OP_DENSE_ATTN_PREFILL, B, stream);
 }
 
 extern "C" int hca_dense_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
@@ -291,5 +308,5 @@ extern "C" int hca_dense_attn_decode(const csa_attn_desc* desc, int B, const int
   if (B == 0) return CSA_OK;
   AttnParams P = make_attn_params(desc, q, kv, nullptr, 0, softmax_scale, o, lse, ws, ws_bytes);
   P.T = 1; P.pos0 = 0; P.pos_dev = pos;
-  return dispatch(P, CSA_OP_DENSE_ATTN_DECODE, B, stream);
+  return attn_dispatch(P, CSA_OP_DENSE_ATTN_DECODE, B, stream);
 }

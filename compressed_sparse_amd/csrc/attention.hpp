@@ -34,4 +34,12 @@ size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t 
 // receives the split partials).
 void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int splits, int64_t per, void* part);
 
+// host: a sparse decode call's validation and parameters, and the launch of
+// any attention op (routes to the MFMA path or the generic kernel)
+int sparse_attn_decode_setup(const csa_attn_desc* desc, int B, const int64_t* pos, const void* q, const csa_cache* kv,
+                             const int32_t* idx, int k, float softmax_scale, void* o, float* lse, void* ws,
+                             size_t ws_bytes, AttnParams* out);
+int attn_dispatch(AttnParams& P, int op, int B, void* stream);
+size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k);
+
 }  // namespace csa

@@ -9,7 +9,8 @@
 // the weighted value; the entry then sits in LDS for the RoPE turn and the
 // FP8 / MXFP4 scale reductions.  HBM traffic is the 2m rows in and one entry
 // out; the kernel is bandwidth-bound and tiny next to attention.
-#include "common.hpp"
+#include "compress.hpp"
+#include "index_prep.hpp"
 
 namespace csa {
 
@@ -18,21 +19,7 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 
-struct CompressParams {
-  int m, overlap, d_nope, d_rope, c, in_dt, nope_dt, rope_dt;
-  int R, NT;
-  double base;
-  int64_t cap;
-  // prefill: token rows [pos0, pos0 + T) of a/za/b/zb; decode: one row each
-  int T;
-  int64_t pos0;
-  const void *a, *za, *b, *zb;
-  const float *Ba, *Bb;
-  void *nope, *scale, *rope;
-  float* ring;
-};
 
-enum { RING_A = 0, RING_ZA = 1, RING_B = 2, RING_ZB = 3 };
 
 __device__ __forceinline__ float* ring_row(const CompressParams& P, int b, int64_t t, int which) {
   int64_t slot = t % P.R;
@@ -393,7 +380,7 @@ __device__ __forceinline__ float load_in(const void* p, size_t i) {
 // completes a window, runs the channel's softmax over the window with the
 // new row taken from its registers; nothing waits for the ring stores.
 template <bool IN_BF16>
-__global__ void __launch_bounds__(1024) compress_decode_kernel(CompressParams P, const int64_t* pos_dev) {
+__device__ __forceinline__ void compress_decode_body(const CompressParams& P, const int64_t* pos_dev) {
   extern __shared__ float smem[];
   float* red = smem;        // 32
   float* buf = smem + 32;   // c: the emitted entry
@@ -428,6 +415,31 @@ __global__ void __launch_bounds__(1024) compress_decode_kernel(CompressParams P,
   if (!emit) return;
   __syncthreads();
   finalize_entry(P, buf, red, b, i);
+}
+
+
+template <bool IN_BF16>
+__global__ void __launch_bounds__(1024) compress_decode_kernel(CompressParams P, const int64_t* pos_dev) {
+  compress_decode_body<IN_BF16>(P, pos_dev);
+}
+
+// The first launch of a fused CSA decode step, grid (B, 3): row y = 0
+// compresses the new token into the KV cache, y = 1 into the indexer-key
+// cache (the same code as compress_decode_kernel, so the entries are the
+// same bits), y = 2 prepares the indexer's row b (histogram and candidate
+// count cleared; the MXFP4 query operand when mx_prep).
+template <bool IN_BF16>
+__global__ void __launch_bounds__(1024) decode_step_prep_kernel(CompressParams Pkv, CompressParams Pkey, IndexParams Pi,
+                                                                const int64_t* pos_dev, int mx_prep) {
+  if (blockIdx.y == 0) {
+    compress_decode_body<IN_BF16>(Pkv, pos_dev);
+  } else if (blockIdx.y == 1) {
+    compress_decode_body<IN_BF16>(Pkey, pos_dev);
+  } else {
+    const size_t r = blockIdx.x;
+    if (mx_prep && threadIdx.x < 64) mx_prep_row(Pi, r);
+    if (Pi.ghist) clear_decode_row(Pi, r);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -539,25 +551,58 @@ extern "C" int csa_compress_prefill(const csa_cache_desc* desc, int B, int T, in
   return check_launch("ring_store_kernel");
 }
 
-extern "C" int csa_compress_decode(const csa_cache_desc* desc, int B, const int64_t* pos,
-                                   const void* a, const void* b, const void* za, const void* zb,
-                                   const float* Ba, const float* Bb, const csa_cache* cache,
-                                   void* stream) {
+namespace csa {
+
+int compress_decode_setup(const csa_cache_desc* desc, int B, const int64_t* pos, const void* a, const void* b,
+                          const void* za, const void* zb, const float* Ba, const float* Bb, const csa_cache* cache,
+                          CompressParams* out) {
   int st;
   if ((st = validate_cache_desc(desc)) != CSA_OK) return st;
   if (B < 0 || B > 65535) return fail(CSA_ERR_INVALID_ARG, "B must be in 0..65535");
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be a 16-byte aligned device pointer");
   if ((st = validate_cache(desc, cache)) != CSA_OK) return st;
   if ((st = validate_inputs(desc, a, b, za, zb, Ba, Bb)) != CSA_OK) return st;
-  if (B == 0) return CSA_OK;
-  CompressParams P = make_params(desc, cache, a, b, za, zb, Ba, Bb);
-  P.T = 1;
-  P.pos0 = 0;
+  *out = make_params(desc, cache, a, b, za, zb, Ba, Bb);
+  out->T = 1;
+  out->pos0 = 0;
+  return CSA_OK;
+}
+
+static int decode_threads(int c) { return c >= 1024 ? 1024 : ((c + 63) / 64) * 64; }
+
+int launch_compress_decode(const CompressParams& P, int B, const int64_t* pos, hipStream_t s) {
   const size_t lds = (32 + static_cast<size_t>(P.c)) * sizeof(float);
-  const int threads = P.c >= 1024 ? 1024 : ((P.c + 63) / 64) * 64;
+  const int threads = decode_threads(P.c);
   if (P.in_dt == CSA_BF16)
-    hipLaunchKernelGGL(compress_decode_kernel<true>, dim3(B), dim3(threads), lds, as_stream(stream), P, pos);
+    hipLaunchKernelGGL(compress_decode_kernel<true>, dim3(B), dim3(threads), lds, s, P, pos);
   else
-    hipLaunchKernelGGL(compress_decode_kernel<false>, dim3(B), dim3(threads), lds, as_stream(stream), P, pos);
+    hipLaunchKernelGGL(compress_decode_kernel<false>, dim3(B), dim3(threads), lds, s, P, pos);
   return check_launch("compress_decode_kernel");
+}
+
+int launch_decode_step_prep(const CompressParams& kv, const CompressParams& keys, const IndexParams& ip, bool mx_prep,
+                            int B, const int64_t* pos, hipStream_t s) {
+  const int c = kv.c > keys.c ? kv.c : keys.c;
+  const size_t lds = (32 + static_cast<size_t>(c)) * sizeof(float);
+  int threads = decode_threads(c);
+  if (threads < 256) threads = 256;  // the indexer rows clear 2048 histogram bins
+  const dim3 grid(B, 3);
+  if (kv.in_dt == CSA_BF16)
+    hipLaunchKernelGGL(decode_step_prep_kernel<true>, grid, dim3(threads), lds, s, kv, keys, ip, pos, mx_prep ? 1 : 0);
+  else
+    hipLaunchKernelGGL(decode_step_prep_kernel<false>, grid, dim3(threads), lds, s, kv, keys, ip, pos, mx_prep ? 1 : 0);
+  return check_launch("decode_step_prep_kernel");
+}
+
+}  // namespace csa
+
+extern "C" int csa_compress_decode(const csa_cache_desc* desc, int B, const int64_t* pos,
+                                   const void* a, const void* b, const void* za, const void* zb,
+                                   const float* Ba, const float* Bb, const csa_cache* cache,
+                                   void* stream) {
+  CompressParams P;
+  int st = compress_decode_setup(desc, B, pos, a, b, za, zb, Ba, Bb, cache, &P);
+  if (st != CSA_OK) return st;
+  if (B == 0) return CSA_OK;
+  return launch_compress_decode(P, B, pos, as_stream(stream));
 }

@@ -83,4 +83,15 @@ bool index_ws_select_ok(const IndexParams& P, int64_t n_max);
 int launch_index_ws_select(const IndexParams& P, int B, hipStream_t s);
 int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s);
 
+// host: a decode call's validation and parameters (workspace carved), and
+// its launches; with prep_done the per-row preparation is skipped (a fused
+// decode step has enqueued it).  index_decode_prep_mx: whether that
+// preparation forms MXFP4 query operands.
+int index_decode_setup(const csa_index_desc* desc, int B, const int64_t* pos, const void* qI, const float* w,
+                       const csa_cache* keys, int k, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                       IndexParams* out);
+bool index_decode_prep_mx(const IndexParams& P);
+int launch_index_decode(IndexParams& P, int B, void* stream, bool prep_done);
+size_t index_ws_bytes(const csa_index_desc* d, int op, int B, int T, int64_t pos0);
+
 }  // namespace csa

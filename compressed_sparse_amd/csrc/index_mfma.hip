@@ -22,6 +22,7 @@
 // All kernels reduce heads in a fixed order (4 or 8 heads inside a lane,
 // then fixed cross-lane shuffles), so scores are run-to-run deterministic.
 #include "index.hpp"
+#include "index_prep.hpp"
 
 namespace csa {
 namespace {
@@ -767,42 +768,10 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 __global__ void __launch_bounds__(256) index_mx_prep_kernel(IndexParams P, int rows) {
   // decode: one row per workgroup (its waves then clear the histogram);
   // prefill: one row per wave
-  const int tid = threadIdx.x, lane = tid & 63;
+  const int tid = threadIdx.x;
   const size_t r = P.ghist ? blockIdx.x : static_cast<size_t>(blockIdx.x) * 4 + (tid >> 6);
-  if ((P.ghist ? tid < 64 : true) && r < static_cast<size_t>(rows)) {
-    const int h = lane & 31, kb = lane >> 5;
-    u32x4 codes = {0u, 0u, 0u, 0u};
-    int e8 = 127;
-    if (h < HI) {
-      const u32x4* src =
-          reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(P.qI) + (r * HI + h) * DI + 32 * kb);
-      float x[32];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 v = src[i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[8 * i + 2 * j] = bf16_to_f32(static_cast<bf16_t>(v[j] & 0xFFFFu));
-          x[8 * i + 2 * j + 1] = bf16_to_f32(static_cast<bf16_t>(v[j] >> 16));
-        }
-      }
-      float am = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(x[i]));
-      const int ex = mx_exponent(am);
-      const float inv = exp2i(-ex);
-#pragma unroll
-      for (int i = 0; i < 32; ++i) codes[i >> 3] |= f32_to_e2m1(x[i] * inv) << (4 * (i & 7));
-      e8 = ex + 127;
-    }
-    uint8_t* dst = P.qpack + r * QPACK_ROW_BYTES;
-    reinterpret_cast<u32x4*>(dst)[lane] = codes;
-    reinterpret_cast<int*>(dst + 64 * 16)[lane] = e8;
-  }
-  if (P.ghist) {  // decode: one row per sequence
-    for (int i = tid; i < HIST_BINS; i += blockDim.x) P.ghist[r * HIST_BINS + i] = 0;
-    if (tid == 0) P.ccount[r] = 0;
-  }
+  if ((P.ghist ? tid < 64 : true) && r < static_cast<size_t>(rows)) mx_prep_row(P, r);
+  if (P.ghist) clear_decode_row(P, r);  // decode: one row per sequence
 }
 
 // Per 32-entry block one scaled MFMA: 32 (16 real) heads x 32 entries x 64

@@ -437,15 +437,18 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   ordered_take(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, out);
 }
 
-static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream) {
+// prep_done: the decode rows' preparation (cleared histogram and count,
+// MXFP4 query operands) has already been enqueued by a fused decode step.
+static int launch_index(IndexParams& P, int B, int64_t n_max, void* stream, bool prep_done = false) {
   hipStream_t s = as_stream(stream);
   if (index_mfma_supported(P)) {
     // scores stay on chip when every row fits the fused kernel's LDS rows
     if (!P.scores_out && index_fused_prefill_ok(P, n_max)) return launch_index_fused_prefill(P, B, s);
     const int bits = P.score_dt == CSA_BF16 ? 16 : 32;
     if (P.ghist) {  // decode: histogram in the scan, candidates, exact final select
-      int st;
-      if (index_scan_mx(P)) {
+      int st = CSA_OK;
+      if (prep_done) {
+      } else if (index_scan_mx(P)) {
         st = launch_index_mx_prep(P, B, s);  // clears the histograms too
       } else {
         hipLaunchKernelGGL(topk_zero_kernel, dim3(B), dim3(256), 0, s, P);
@@ -584,16 +587,16 @@ extern "C" int csa_index_topk_prefill(const csa_index_desc* desc, int B, int T, 
   return launch_index(P, B, nmax, stream);
 }
 
-extern "C" int csa_index_topk_decode(const csa_index_desc* desc, int B, const int64_t* pos,
-                                     const void* qI, const float* w, const csa_cache* keys, int k,
-                                     int32_t* idx, float* scores, void* ws, size_t ws_bytes,
-                                     void* stream) {
+namespace csa {
+
+int index_decode_setup(const csa_index_desc* desc, int B, const int64_t* pos, const void* qI, const float* w,
+                       const csa_cache* keys, int k, int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                       IndexParams* out) {
   int st = common_index_checks(desc, B, qI, w, keys, k, idx, scores, ws);
   if (st != CSA_OK) return st;
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
   if (ws_bytes < index_ws_bytes(desc, CSA_OP_INDEX_TOPK_DECODE, B, 1, 0))
     return fail(CSA_ERR_WORKSPACE, "workspace too small");
-  if (B == 0) return CSA_OK;
   IndexParams P = make_index_params(desc, qI, w, keys, k, idx, scores, ws);
   P.T = 1;
   P.pos0 = 0;
@@ -610,5 +613,26 @@ extern "C" int csa_index_topk_decode(const csa_index_desc* desc, int B, const in
     P.ccnt = P.cbase + static_cast<size_t>(B) * P.nch;
     P.csel = P.ccnt + static_cast<size_t>(B) * P.nch;
   }
-  return launch_index(P, B, desc->capacity, stream);
+  *out = P;
+  return CSA_OK;
+}
+
+bool index_decode_prep_mx(const IndexParams& P) { return P.ghist != nullptr && index_scan_mx(P); }
+
+int launch_index_decode(IndexParams& P, int B, void* stream, bool prep_done) {
+  // rows without the multi-workgroup state need no preparation
+  return launch_index(P, B, P.cap, stream, prep_done && P.ghist != nullptr);
+}
+
+}  // namespace csa
+
+extern "C" int csa_index_topk_decode(const csa_index_desc* desc, int B, const int64_t* pos,
+                                     const void* qI, const float* w, const csa_cache* keys, int k,
+                                     int32_t* idx, float* scores, void* ws, size_t ws_bytes,
+                                     void* stream) {
+  IndexParams P;
+  int st = index_decode_setup(desc, B, pos, qI, w, keys, k, idx, scores, ws, ws_bytes, &P);
+  if (st != CSA_OK) return st;
+  if (B == 0) return CSA_OK;
+  return launch_index_decode(P, B, stream, false);
 }

@@ -100,12 +100,18 @@ class CsaLayer:
                                 self.device)
         self.aws = cb.workspace(cb.workspace_bytes(cb.OP_SPARSE_ATTN_DECODE, self.adesc, self.B, 1, 0, w.topk),
                                 self.device)
+        self.sws = cb.workspace(cb.decode_step_workspace_bytes(self.idesc, self.adesc, self.B, w.topk), self.device)
         return out
 
     def decode_step(self, x, out, scores=None):
-        """One CSA decode step: the new token enters both compressors (an
-        entry completed at this position is visible to it), then indexer +
-        top-k and sparse attention."""
+        """One CSA decode step through the fused entry point: the new token
+        enters both compressors (an entry completed at this position is
+        visible to it), then indexer + top-k and sparse attention."""
+        cb.decode_step(self.kv, self.keys, self.idesc, self.adesc, x["pos"], x, self.prm, self.w.topk, self.w.tau,
+                       out["idx"], out["o"], out["lse"], scores, ws=self.sws)
+
+    def decode_step_separate(self, x, out, scores=None):
+        """The same step as the four separate entry points."""
         p, w = self.prm, self.w
         cb.compress_decode(self.kv, x["pos"], x["a"], x["za"], p["Ba"], x.get("b"), x.get("zb"), p.get("Bb"))
         cb.compress_decode(self.keys, x["pos"], x["ka"], x["kza"], p["kBa"], x.get("kb"), x.get("kzb"), p.get("kBb"))

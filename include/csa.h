@@ -248,6 +248,54 @@ int hca_dense_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
                           const void* q, const csa_cache* kv, float softmax_scale, void* o,
                           float* lse, void* ws, size_t ws_bytes, void* stream);
 
+/* ---- fused CSA decode step -------------------------------------------------
+ * One decode step of a CSA layer ([CSA/HCA 混注意力] §1.1: compress, index,
+ * select the top k, attend; §1.3: one CSA layer of the interleaved stack)
+ * in one call: exactly
+ *   csa_compress_decode(kv_desc, B, pos, a, b, za, zb, Ba, Bb, kv)
+ *   csa_compress_decode(key_desc, B, pos, ka, kb, kza, kzb, kBa, kBb, keys)
+ *   csa_index_topk_decode(idesc, B, pos, qI, w, keys, k, idx, scores, ...)
+ *   csa_sparse_attn_decode(adesc, B, pos, q, kv, idx, k, softmax_scale, o, lse, ...)
+ * with the same results bit for bit, in fewer launches (both compressors and
+ * the indexer's per-row preparation run in one; they need the same in_dtype,
+ * else they launch apart).  The descriptors must agree (m, capacities, the
+ * KV layout with the attention's, the key layout with the indexer's), else
+ * CSA_ERR_INVALID_ARG.  Every argument of the four calls is validated first;
+ * on any error nothing is launched.
+ *   in : the new token's compressor rows and queries, device pointers:
+ *        a, b, za, zb [B][c]; Ba, Bb [m][c] (b, zb, Bb NULL without
+ *        overlap); ka, kb, kza, kzb [B][d_I]; kBa, kBb [m][d_I]; q [B][H][c];
+ *        qI [B][H_I][d_I]; w float [B][H_I]
+ *   idx: device int32 [B][k] (receives the selection); scores as in
+ *        csa_index_topk_decode; o, lse as in csa_sparse_attn_decode
+ *   ws : device workspace of csa_decode_step_workspace_bytes(idesc, adesc, B, k) */
+typedef struct csa_decode_inputs {
+  const void* a;
+  const void* b;
+  const void* za;
+  const void* zb;
+  const float* Ba;
+  const float* Bb;
+  const void* ka;
+  const void* kb;
+  const void* kza;
+  const void* kzb;
+  const float* kBa;
+  const float* kBb;
+  const void* q;
+  const void* qI;
+  const float* w;
+} csa_decode_inputs;
+
+int csa_decode_step(const csa_cache_desc* kv_desc, const csa_cache* kv, const csa_cache_desc* key_desc,
+                    const csa_cache* keys, const csa_index_desc* idesc, const csa_attn_desc* adesc, int B,
+                    const int64_t* pos, const csa_decode_inputs* in, int k, float softmax_scale, int32_t* idx,
+                    float* scores, void* o, float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes of csa_decode_step for B sequences and k selected entries
+ * (pure host function; 0 for NULL descriptors). */
+size_t csa_decode_step_workspace_bytes(const csa_index_desc* idesc, const csa_attn_desc* adesc, int B, int k);
+
 /* ---- workspace and diagnostics ------------------------------------------ */
 enum {
   CSA_OP_INDEX_TOPK_PREFILL = 1,  /* desc: csa_index_desc */

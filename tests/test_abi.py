@@ -163,3 +163,32 @@ def test_noalloc_decode_rejects_past_its_scratch_on_the_host():
     assert b"scratch" in L.csa_last_error()
     assert L.csa_sparse_attn_decode_noalloc(ctypes.byref(desc), 1, P, P, ctypes.byref(kv), P, 0, 0.1, P, None,
                                             None) == 1
+
+
+def test_decode_step_validates_everything_before_launch():
+    L = cb.lib()
+    assert ctypes.sizeof(cb.DecodeInputs) == 15 * 8
+    cap = 8192
+    kvd = cb.cache_desc(4, True, 512, 64, "bf16", "fp8", "bf16", cap)
+    kd = cb.cache_desc(4, True, 64, 0, "bf16", "fp8", "f32", cap)
+    idesc = cb.index_desc(16, 64, "bf16", "bf16", "fp8", "f32", 4, cap)
+    adesc = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, cap)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    ks = cb.Cache(0x6000, 0x7000, 0, 0x8000)
+    P = 0x4000
+    inp = cb.DecodeInputs(*([P] * 15))
+    need = L.csa_decode_step_workspace_bytes(ctypes.byref(idesc), ctypes.byref(adesc), 4, 1024)
+    assert need >= cb.workspace_bytes(cb.OP_INDEX_TOPK_DECODE, idesc, 4, 1, 0, 1024) + \
+        cb.workspace_bytes(cb.OP_SPARSE_ATTN_DECODE, adesc, 4, 1, 0, 1024)
+    args = lambda d1, d2, d3, d4, i, ws_bytes: (ctypes.byref(d1), ctypes.byref(kv), ctypes.byref(d2), ctypes.byref(ks),
+                                                ctypes.byref(d3), ctypes.byref(d4), 4, fake(P), i, 1024, 0.1,
+                                                fake(P), None, fake(P), None, fake(P), ws_bytes, None)
+    assert L.csa_decode_step(*args(kvd, kd, idesc, adesc, None, need)) == 1          # no inputs
+    bad_m = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 8, cap)
+    assert L.csa_decode_step(*args(kvd, kd, idesc, bad_m, ctypes.byref(inp), need)) == 1
+    assert b"share m" in L.csa_last_error()
+    bad_key = cb.index_desc(16, 64, "bf16", "bf16", "bf16", "f32", 4, cap)       # keys stored FP8
+    assert L.csa_decode_step(*args(kvd, kd, bad_key, adesc, ctypes.byref(inp), need)) == 1
+    assert L.csa_decode_step(*args(kvd, kd, idesc, adesc, ctypes.byref(inp), need - 256)) == 4
+    no_b = cb.DecodeInputs(P, None, P, None, P, None, P, P, P, P, P, P, P, P, P)    # overlap needs b, zb, Bb
+    assert L.csa_decode_step(*args(kvd, kd, idesc, adesc, ctypes.byref(no_b), need)) == 1
