@@ -42,11 +42,14 @@ def uniform_int(shape, low, high, name, seed=0, seq=0, chunk=0, device="cpu"):
 
 
 def random_fp8_codes(shape, name, seed=0, seq=0, device="cpu"):
-    """Random OFP8 E4M3 bytes with exponent field 1..12 (no NaN code), used
-    to fill a cache directly when a kernel is tested on its own."""
-    e = uniform_int(shape, 1, 13, name + ".e", seed, seq, device=device)
+    """Random OFP8 E4M3 bytes over every exponent field 0..15 (subnormals and
+    the top binades included; the NaN code S.1111.111 is replaced by the
+    largest finite S.1111.110), used to fill a cache directly when a kernel is
+    tested on its own."""
+    e = uniform_int(shape, 0, 16, name + ".e", seed, seq, device=device)
     mnt = uniform_int(shape, 0, 8, name + ".m", seed, seq, device=device)
     s = uniform_int(shape, 0, 2, name + ".s", seed, seq, device=device)
+    mnt = torch.where((e == 15) & (mnt == 7), torch.full_like(mnt, 6), mnt)
     return ((s << 7) | (e << 3) | mnt).to(torch.uint8)
 
 
@@ -55,8 +58,8 @@ def random_e2m1_bytes(shape, name, seed=0, seq=0, device="cpu"):
     return uniform_int(shape, 0, 256, name, seed, seq, device=device).to(torch.uint8)
 
 
-def random_e8m0(shape, name, lo=120, hi=131, seed=0, seq=0, device="cpu"):
-    """Random E8M0 scale bytes in [lo, hi)."""
+def random_e8m0(shape, name, lo=104, hi=141, seed=0, seq=0, device="cpu"):
+    """Random E8M0 scale bytes in [lo, hi) (2^-23 .. 2^13 by default)."""
     return uniform_int(shape, lo, hi, name, seed, seq, device=device).to(torch.uint8)
 
 

@@ -129,3 +129,13 @@ def topk_explained(gpu_row, ref_row, I, delta, eps):
     near = np.abs(I - kth) <= 2 * float(delta.max()) + eps
     d_thr = float(delta[near].max()) if near.any() else 0.0
     return all(s < len(I) and abs(I[s] - kth) <= delta[s] + d_thr + eps for s in g ^ o)
+
+
+def fp32_score_bound(qq, w_row, K, n, gamma=2.0 ** -17):
+    """Bound on the fp32 accumulation error of the indexer scores of one
+    query: the standard summation bound (a constant times the unit roundoff
+    times the sum of the absolute terms), gamma * sum_h |w_h| * sum_d
+    |qq_hd K_sd| for s < n.  gamma = 2^-17 covers the 16 x 64 products of a
+    score (u = 2^-24) with room for the order of the sums."""
+    mag = np.abs(np.asarray(K[:n], np.float64)) @ np.abs(np.asarray(qq, np.float64)).T
+    return gamma * (mag @ np.abs(np.asarray(w_row, np.float64)))
