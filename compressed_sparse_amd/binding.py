@@ -43,8 +43,8 @@ class IndexDesc(ctypes.Structure):
 class AttnDesc(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32), ("nope_dtype", ctypes.c_int32),
-                ("rope_dtype", ctypes.c_int32), ("m", ctypes.c_int32), ("rope_base", ctypes.c_double),
-                ("capacity", ctypes.c_int64)]
+                ("rope_dtype", ctypes.c_int32), ("m", ctypes.c_int32), ("window", ctypes.c_int32),
+                ("qk_mode", ctypes.c_int32), ("rope_base", ctypes.c_double), ("capacity", ctypes.c_int64)]
 
 
 class DecodeInputs(ctypes.Structure):
@@ -54,7 +54,7 @@ class DecodeInputs(ctypes.Structure):
 
 EXPORTS = ["csa_compress_prefill", "csa_compress_decode", "csa_index_topk_prefill", "csa_index_topk_decode",
            "csa_sparse_attn_prefill", "csa_sparse_attn_decode", "csa_sparse_attn_decode_noalloc",
-           "hca_dense_attn_prefill", "hca_dense_attn_decode", "csa_decode_step", "csa_decode_step_workspace_bytes",
+           "hca_dense_attn_prefill", "hca_dense_attn_decode", "csa_decode_step", "csa_decode_step_workspace_bytes", "csa_lse_merge",
            "csa_workspace_bytes", "csa_status_string", "csa_last_error", "csa_version"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -82,6 +82,7 @@ def lib():
             "csa_workspace_bytes": [I, P, I, I, I64, I],
             "csa_decode_step": [P, P, P, P, P, P, I, P, P, I, F, P, P, P, P, P, SZ, P],
             "csa_decode_step_workspace_bytes": [P, P, I, I],
+            "csa_lse_merge": [I, I, I, I, P, P, P, P, P, P, P],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -199,9 +200,9 @@ def index_topk_decode(desc, keys: KVCache, pos, qI, w, k, idx, scores=None, ws=N
                                        ptr(idx), ptr(scores), ptr(ws), ws.numel(), stream_ptr(stream)))
 
 
-def attn_desc(n_heads, d_nope, d_rope, q_fmt, o_fmt, nope_fmt, rope_fmt, m, capacity, base=10000.0):
+def attn_desc(n_heads, d_nope, d_rope, q_fmt, o_fmt, nope_fmt, rope_fmt, m, capacity, base=10000.0, window=0):
     return AttnDesc(n_heads, d_nope, d_rope, FMT[q_fmt], FMT[o_fmt], FMT[nope_fmt], FMT.get(rope_fmt, F32),
-                    m, base, capacity)
+                    m, window, 0, base, capacity)
 
 
 def _ws(op, desc, B, T, pos0, k, ws, device):
@@ -256,6 +257,16 @@ def decode_step(kv: KVCache, keys: KVCache, idesc, adesc, pos, x, prm, k, scale,
     _check(lib().csa_decode_step(ctypes.byref(kv.desc), ctypes.byref(kvs), ctypes.byref(keys.desc), ctypes.byref(ks),
                                  ctypes.byref(idesc), ctypes.byref(adesc), B, ptr(pos), ctypes.byref(inp), k, scale,
                                  ptr(idx), ptr(scores), ptr(o), ptr(lse), ptr(ws), ws.numel(), stream_ptr(stream)))
+
+
+def lse_merge(o1, lse1, o2, lse2, o, lse=None, stream=None):
+    """csa_lse_merge: one softmax over the union of two attention results'
+    keys from their (o, lse) pairs; o [..., H, d_v] (may alias o1 or o2)."""
+    H, dv = o1.shape[-2], o1.shape[-1]
+    rows = o1.numel() // (H * dv)
+    fmt = F32 if o1.dtype == torch.float32 else BF16
+    _check(lib().csa_lse_merge(rows, H, dv, fmt, ptr(o1), ptr(lse1), ptr(o2), ptr(lse2), ptr(o), ptr(lse),
+                               stream_ptr(stream)))
 
 
 def dense_attn_prefill(desc, kv: KVCache, pos0, q, scale, o, lse=None, ws=None, stream=None):

@@ -60,13 +60,15 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnParams P) {
   }
   for (int d = tid; d < P.d_nope; d += nt) o[d] = 0.0f;
   __syncthreads();
-  const int64_t count = P.idx ? P.k : n;
+  // dense: the visible entries [lo, n), lo > 0 under a sliding window
+  const int64_t lo = (!P.idx && P.window > 0 && n > P.window) ? n - P.window : 0;
+  const int64_t count = P.idx ? P.k : n - lo;
   const int32_t* list = P.idx ? P.idx + (static_cast<size_t>(b) * P.T + t) * P.k : nullptr;
   float mx = -INFINITY, sum = 0.0f;
   for (int64_t base = 0; base < count; base += nt) {
     const int64_t j = base + tid;
     int64_t s = -1;
-    if (j < count) s = list ? static_cast<int64_t>(list[j]) : j;
+    if (j < count) s = list ? static_cast<int64_t>(list[j]) : lo + j;
     if (s >= n) s = -1;
     float l = -INFINITY;
     if (s >= 0) {
@@ -134,6 +136,8 @@ static int validate_attn(const csa_attn_desc* d, int B, const void* q, const csa
     return fail(CSA_ERR_UNSUPPORTED, "rope_dtype must be F32 or BF16");
   if (d->m < 1 || d->m > 256) return fail(CSA_ERR_INVALID_ARG, "m must be in 1..256");
   if (d->capacity < 1 || d->capacity > (int64_t(1) << 31) - 1) return fail(CSA_ERR_INVALID_ARG, "capacity must be in 1..2^31-1");
+  if (d->window < 0) return fail(CSA_ERR_INVALID_ARG, "window must be >= 0");
+  if (d->qk_mode != 0) return fail(CSA_ERR_UNSUPPORTED, "qk_mode must be 0");
   if (!(d->rope_base > 0.0)) return fail(CSA_ERR_INVALID_ARG, "rope_base must be > 0");
   if (B < 0 || B > 65535) return fail(CSA_ERR_INVALID_ARG, "B must be in 0..65535");
   if (!q || !kv || !kv->nope || !o) return fail(CSA_ERR_INVALID_ARG, "NULL argument");
@@ -151,7 +155,7 @@ static AttnParams make_attn_params(const csa_attn_desc* d, const void* q, const 
   AttnParams P{};
   P.H = d->n_heads; P.d_nope = d->d_nope; P.d_rope = d->d_rope;
   P.q_dt = d->q_dtype; P.o_dt = d->o_dtype; P.nope_dt = d->nope_dtype; P.rope_dt = d->rope_dtype;
-  P.m = d->m; P.base = d->rope_base; P.cap = d->capacity;
+  P.m = d->m; P.base = d->rope_base; P.cap = d->capacity; P.window = d->window;
   P.q = q; P.nope = kv->nope; P.scale = kv->scale; P.rope = kv->rope;
   P.idx = idx; P.k = k; P.scale_qk = scale; P.o = o; P.lse = lse;
   P.ws = ws; P.ws_bytes = ws_bytes;
@@ -172,6 +176,42 @@ int attn_dispatch(AttnParams& P, int op, int B, void* stream) {
     return launch_mfma_attn(P, op, B, s);
   }
   return launch_generic(P, B, s);
+}
+
+// ---------------------------------------------------------------------------
+// log-sum-exp merge of two attention results (sliding-window branch + the
+// compressed branch): one softmax over the union of their keys
+// ---------------------------------------------------------------------------
+// grid (rows, H); each thread 4 consecutive value dims.
+__global__ void __launch_bounds__(256) lse_merge_kernel(int H, int dv, int o_dt, const void* o1, const float* l1,
+                                                        const void* o2, const float* l2, void* o, float* lse) {
+  const size_t rh = static_cast<size_t>(blockIdx.x) * H + blockIdx.y;
+  const float a = l1[rh], b = l2[rh];
+  const float mx = fmaxf(a, b);
+  float fa = 0.0f, fb = 0.0f, L = -INFINITY;
+  if (mx != -INFINITY) {
+    const float wa = expf(a - mx), wb = expf(b - mx);  // exp(-inf) = 0 for an empty side
+    const float sw = wa + wb;
+    fa = wa / sw;
+    fb = wb / sw;
+    L = mx + logf(sw);
+  }
+  for (int d = 4 * threadIdx.x; d < dv; d += 4 * blockDim.x) {
+    const size_t e = rh * dv + d;
+    float x[4], y[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = load_elem(o1, e + u, o_dt);
+      y[u] = load_elem(o2, e + u, o_dt);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float v = fa * x[u] + fb * y[u];
+      if (o_dt == CSA_F32) static_cast<float*>(o)[e + u] = v;
+      else static_cast<bf16_t*>(o)[e + u] = f32_to_bf16(v);
+    }
+  }
+  if (lse && threadIdx.x == 0) lse[rh] = L;
 }
 
 // ---------------------------------------------------------------------------
@@ -215,6 +255,7 @@ extern "C" int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, 
                                        size_t ws_bytes, void* stream) {
   int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
+  if (desc->window != 0) return fail(CSA_ERR_INVALID_ARG, "window must be 0 for sparse attention");
   if (T < 0 || T > 65535 || pos0 < 0) return fail(CSA_ERR_INVALID_ARG, "T must be in 0..65535, pos0 >= 0");
   if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
   if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
@@ -233,6 +274,7 @@ int sparse_attn_decode_setup(const csa_attn_desc* desc, int B, const int64_t* po
                              size_t ws_bytes, AttnParams* out) {
   int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
+  if (desc->window != 0) return fail(CSA_ERR_INVALID_ARG, "window must be 0 for sparse attention");
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
   if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
   if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
@@ -267,6 +309,7 @@ extern "C" int csa_sparse_attn_decode_noalloc(const csa_attn_desc* desc, int B, 
                                               float softmax_scale, void* o, float* lse, void* stream) {
   int st = validate_attn(desc, B, q, kv, o, lse, softmax_scale);
   if (st != CSA_OK) return st;
+  if (desc->window != 0) return fail(CSA_ERR_INVALID_ARG, "window must be 0 for sparse attention");
   if (!pos || !aligned16(pos)) return fail(pos ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "pos must be an aligned device pointer");
   if (!idx || !aligned16(idx)) return fail(idx ? CSA_ERR_ALIGNMENT : CSA_ERR_INVALID_ARG, "idx must be an aligned device pointer");
   if (k < 1 || k > 2048) return fail(CSA_ERR_INVALID_ARG, "k must be in 1..2048");
@@ -281,6 +324,22 @@ extern "C" int csa_sparse_attn_decode_noalloc(const csa_attn_desc* desc, int B, 
   AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, CSA_NOALLOC_SCRATCH_BYTES);
   P.T = 1; P.pos0 = 0; P.pos_dev = pos;
   return attn_dispatch(P, CSA_OP_SPARSE_ATTN_DECODE, B, stream);
+}
+
+extern "C" int csa_lse_merge(int rows, int H, int d_v, int o_dtype, const void* o1, const float* lse1,
+                             const void* o2, const float* lse2, void* o, float* lse, void* stream) {
+  if (rows < 0 || rows > 0x7FFFFFFF / 2) return fail(CSA_ERR_INVALID_ARG, "rows out of range");
+  if (H < 1 || H > 65535) return fail(CSA_ERR_INVALID_ARG, "H must be in 1..65535");
+  if (d_v < 4 || d_v > 4096 || d_v % 4) return fail(CSA_ERR_INVALID_ARG, "d_v must be a multiple of 4 in 4..4096");
+  if (o_dtype != CSA_F32 && o_dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "o_dtype must be F32 or BF16");
+  if (!o1 || !lse1 || !o2 || !lse2 || !o) return fail(CSA_ERR_INVALID_ARG, "NULL argument");
+  if (!aligned16(o1) || !aligned16(o2) || !aligned16(o) || !aligned16(lse1) || !aligned16(lse2) || !aligned16(lse))
+    return fail(CSA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  if (rows == 0) return CSA_OK;
+  const int threads = d_v / 4 >= 256 ? 256 : ((d_v / 4 + 63) / 64) * 64;
+  hipLaunchKernelGGL(lse_merge_kernel, dim3(rows, H), dim3(threads), 0, as_stream(stream), H, d_v, o_dtype, o1, lse1,
+                     o2, lse2, o, lse);
+  return check_launch("lse_merge_kernel");
 }
 
 extern "C" int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,

@@ -9,6 +9,7 @@ struct AttnParams {
   int H, d_nope, d_rope, q_dt, o_dt, nope_dt, rope_dt, m;
   double base;
   int64_t cap;
+  int64_t window;          // dense: attend the last `window` visible entries (0: all)
   int T;
   int64_t pos0;
   const int64_t* pos_dev;  // decode: per-sequence positions (T == 1)

@@ -251,9 +251,12 @@ __device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int s
   }
   int64_t n = I.pos < 0 ? 0 : (I.pos + 1) / P.m;
   I.n = n > P.cap ? P.cap : n;
-  const int64_t count = DENSE ? I.n : P.k;
-  I.r0 = static_cast<int64_t>(I.split) * per_split;
-  I.r1 = I.r0 + per_split < count ? I.r0 + per_split : count;
+  // dense: the visible entries [lo, n), lo > 0 under a sliding window; the
+  // splits of a decode sequence cover them from lo on
+  const int64_t lo = (DENSE && P.window > 0 && I.n > P.window) ? I.n - P.window : 0;
+  const int64_t end = DENSE ? I.n : P.k;
+  I.r0 = lo + static_cast<int64_t>(I.split) * per_split;
+  I.r1 = I.r0 + per_split < end ? I.r0 + per_split : end;
   I.qrow = (static_cast<size_t>(I.b) * P.T + I.t) * NH;
   I.seq = static_cast<size_t>(I.b) * P.cap;
   return I;

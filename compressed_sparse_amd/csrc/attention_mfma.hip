@@ -96,6 +96,9 @@ int decode_splits(bool dense, int64_t count) {
   return s < 1 ? 1 : static_cast<int>(s);
 }
 
+// Entries a dense decode sequence can attend: the capacity, or the window.
+int64_t dense_span(int64_t cap, int64_t window) { return window > 0 && window < cap ? window : cap; }
+
 // Gather offsets of the MFMA kernel are 32-bit byte offsets within one
 // sequence's rows (row id times row bytes): every cache buffer of a
 // sequence must stay below 2^31 bytes.
@@ -125,7 +128,7 @@ size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, i
   if (op != CSA_OP_SPARSE_ATTN_DECODE && op != CSA_OP_DENSE_ATTN_DECODE) return 0;
   if (!mfma_shape(d->n_heads, d->d_nope, d->d_rope, d->q_dtype, d->o_dtype, d->nope_dtype, d->rope_dtype)) return 0;
   const bool dense = op == CSA_OP_DENSE_ATTN_DECODE;
-  return part_bytes(B, decode_splits(dense, dense ? d->capacity : k));
+  return part_bytes(B, decode_splits(dense, dense ? dense_span(d->capacity, d->window) : k));
 }
 
 int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
@@ -136,7 +139,7 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
     launch_attn_bf16(P, dense, B, s, 1, per, nullptr);
     return check_launch("attn_bf16_kernel");
   }
-  const int64_t count = dense ? P.cap : P.k;
+  const int64_t count = dense ? dense_span(P.cap, P.window) : P.k;
   const int64_t ntiles = (count + TILE - 1) / TILE;
   const int splits = decode_splits(dense, count);
   const int64_t tiles_per = (ntiles + splits - 1) / splits;

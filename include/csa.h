@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 1
+#define CSA_ABI_VERSION 2
 
 /* Status codes. */
 enum {
@@ -124,6 +124,11 @@ typedef struct csa_attn_desc {
   int32_t nope_dtype; /* cache: CSA_F32, CSA_BF16, CSA_FP8E4M3 */
   int32_t rope_dtype; /* cache: CSA_F32, CSA_BF16 */
   int32_t m;          /* tokens per entry (visibility) */
+  int32_t window;     /* dense attention only: attend the last `window` visible entries
+                         (a sliding window; with m = 1 over per-token entries, the
+                         sliding-window branch); 0 = every visible entry.  Must be 0
+                         for sparse attention. */
+  int32_t qk_mode;    /* must be 0: QK in the query's own format */
   double rope_base;
   int64_t capacity;   /* entries per sequence */
 } csa_attn_desc;
@@ -198,8 +203,9 @@ int csa_index_topk_decode(const csa_index_desc* desc, int B, const int64_t* pos,
  *   l_s = softmax_scale * q~ . K_s      (K_s: the whole decoded entry)
  *   o[h] = sum_s softmax(l)_s * V_s     (V_s: the d_nope part of the entry)
  *   lse[h] = log sum_s exp(l_s)
- * over S = the listed entries (CSA) or all s < n(p) (HCA).  Listed indices
- * outside [0, n(p)) are skipped.  An empty S gives o = 0 and lse = -inf.
+ * over S = the listed entries (CSA) or all s < n(p) (HCA; with window w > 0
+ * only max(0, n(p) - w) <= s < n(p)).  Listed indices outside [0, n(p)) are
+ * skipped.  An empty S gives o = 0 and lse = -inf.
  *   q   : device [B][T][H][d_nope + d_rope] of q_dtype
  *   idx : device int32 [B][T][k] (CSA only)
  *   o   : device [B][T][H][d_nope] of o_dtype
@@ -247,6 +253,21 @@ int hca_dense_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0
 int hca_dense_attn_decode(const csa_attn_desc* desc, int B, const int64_t* pos,
                           const void* q, const csa_cache* kv, float softmax_scale, void* o,
                           float* lse, void* ws, size_t ws_bytes, void* stream);
+
+/* ---- log-sum-exp merge of two attention results --------------------------
+ * The sliding-window branch of a CSA / HCA layer ([CSA/HCA 混注意力] §1.3:
+ * V4-Flash's sliding-window layers; the uncompressed SWA KV of the prefix-cache
+ * paragraph) attends the most recent uncompressed tokens; its result and the
+ * compressed branch's are one softmax over the union of their keys, formed
+ * from the two partial results: per (row, head)
+ *   l = log(exp(lse1) + exp(lse2)),  o = exp(lse1 - l) o1 + exp(lse2 - l) o2
+ * (both -inf: o = 0, lse = -inf).
+ *   o1, o2, o : device [rows][H][d_v] of o_dtype (CSA_F32 or CSA_BF16); o may
+ *               alias o1 or o2
+ *   lse1, lse2: device float [rows][H]; lse: device float [rows][H] or NULL
+ * rows = B*T (prefill) or B (decode).  d_v a multiple of 4, at most 4096. */
+int csa_lse_merge(int rows, int H, int d_v, int o_dtype, const void* o1, const float* lse1, const void* o2,
+                  const float* lse2, void* o, float* lse, void* stream);
 
 /* ---- fused CSA decode step -------------------------------------------------
  * One decode step of a CSA layer ([CSA/HCA 混注意力] §1.1: compress, index,

@@ -256,12 +256,37 @@ def sparse_attention_row(q, pos, cache, sel, d_nope, base, tau):
     return attend(rope_query(q, pos, d_nope, base), cache["k"], cache["v"], sel, tau)
 
 
-def dense_attention_row(q, pos, cache, m, d_nope, base, tau):
+def dense_attention_row(q, pos, cache, m, d_nope, base, tau, window=0):
     """HCA attention for one query: every visible entry, s < n(pos)
     ([CSA/HCA 混注意力] §1.2: dense attention over the 128x shorter
-    sequence)."""
+    sequence).  With window w > 0 only the last w visible entries,
+    max(0, n - w) <= s < n: with m = 1 over per-token entries this is the
+    sliding-window branch over the most recent uncompressed tokens
+    ([CSA/HCA 混注意力] §1.3: V4-Flash's sliding-window layers; the
+    uncompressed SWA KV of the prefix-cache paragraph)."""
     n = min(int(n_visible(pos, m)), cache["k"].shape[0])
-    return attend(rope_query(q, pos, d_nope, base), cache["k"], cache["v"], np.arange(n), tau)
+    lo = n - window if 0 < window < n else 0
+    return attend(rope_query(q, pos, d_nope, base), cache["k"], cache["v"], np.arange(lo, n), tau)
+
+
+def lse_merge(o1, lse1, o2, lse2):
+    """One softmax over the union of two disjoint key sets, from the two
+    partial results: o = (e^lse1 o1 + e^lse2 o2) / (e^lse1 + e^lse2) and
+    lse = log(e^lse1 + e^lse2) per head; both empty gives o = 0, lse = -inf.
+    Reading: the sliding-window branch and the compressed branch of a layer
+    are joined this way (the pages name both branches, not how they join).
+    o: [..., H, d_v], lse: [..., H]."""
+    lse1 = np.asarray(lse1, np.float64)
+    lse2 = np.asarray(lse2, np.float64)
+    mx = np.maximum(lse1, lse2)
+    safe = np.where(np.isneginf(mx), 0.0, mx)
+    w1 = np.exp(lse1 - safe)
+    w2 = np.exp(lse2 - safe)
+    tot = w1 + w2
+    den = np.where(tot > 0, tot, 1.0)
+    o = (w1[..., None] * np.asarray(o1, np.float64) + w2[..., None] * np.asarray(o2, np.float64)) / den[..., None]
+    lse = np.where(tot > 0, safe + np.log(den), -np.inf)
+    return o, lse
 
 
 # ---------------------------------------------------------------------------

@@ -30,7 +30,7 @@ def test_library_exports_every_declared_symbol():
     L = cb.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.csa_version() == 1
+    assert L.csa_version() == 2
     assert L.csa_status_string(0) == b"CSA_OK"
     assert L.csa_status_string(5) == b"CSA_ERR_CAPACITY"
 
@@ -39,7 +39,7 @@ def test_struct_sizes_match_header_layout():
     assert ctypes.sizeof(cb.CacheDesc) == 48
     assert ctypes.sizeof(cb.Cache) == 32
     assert ctypes.sizeof(cb.IndexDesc) == 40
-    assert ctypes.sizeof(cb.AttnDesc) == 48
+    assert ctypes.sizeof(cb.AttnDesc) == 56
 
 
 def fake(addr):
@@ -192,3 +192,27 @@ def test_decode_step_validates_everything_before_launch():
     assert L.csa_decode_step(*args(kvd, kd, idesc, adesc, ctypes.byref(inp), need - 256)) == 4
     no_b = cb.DecodeInputs(P, None, P, None, P, None, P, P, P, P, P, P, P, P, P)    # overlap needs b, zb, Bb
     assert L.csa_decode_step(*args(kvd, kd, idesc, adesc, ctypes.byref(no_b), need)) == 1
+
+
+def test_window_and_merge_validation():
+    L = cb.lib()
+    P = fake(0x4000)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    # a window is for dense attention only
+    win = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192, window=128)
+    assert L.csa_sparse_attn_prefill(ctypes.byref(win), 1, 16, 0, P, ctypes.byref(kv), P, 1024, 0.1, P, None, P,
+                                     1 << 30, None) == 1
+    assert b"window" in L.csa_last_error()
+    neg = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192, window=-1)
+    assert L.hca_dense_attn_prefill(ctypes.byref(neg), 1, 16, 0, P, ctypes.byref(kv), 0.1, P, None, P, 1 << 30,
+                                    None) == 1
+    # the dense decode workspace covers the window's splits only
+    full = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 1, 1 << 20)
+    w128 = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 1, 1 << 20, window=128)
+    assert cb.workspace_bytes(cb.OP_DENSE_ATTN_DECODE, w128, 1, 1, 0, 0) < \
+        cb.workspace_bytes(cb.OP_DENSE_ATTN_DECODE, full, 1, 1, 0, 0)
+    # merge: shapes and formats
+    assert L.csa_lse_merge(4, 64, 510, 1, P, P, P, P, P, None, None) == 1
+    assert L.csa_lse_merge(4, 64, 512, 2, P, P, P, P, P, None, None) == 3
+    assert L.csa_lse_merge(4, 64, 512, 1, fake(0x4004), P, P, P, P, None, None) == 2
+    assert L.csa_lse_merge(0, 64, 512, 1, P, P, P, P, P, None, None) == 0

@@ -401,3 +401,59 @@ def test_page_values():
     ratio = split_bytes / (576 * 2)
     assert abs(ratio - g["split_kv_vs_bf16_approx"]["value"]) < 0.1
     assert k == 1024 and m == 4 and mh == 128
+
+
+# ---------------------------------------------------------------- sliding-window branch
+
+def test_sliding_window_is_banded_causal_attention_sdpa():
+    """m = 1 per-token entries (the compressor with one row per window passes
+    the token row through), window w: each query attends tokens
+    t - w < s <= t; torch's attention with that band as the mask agrees."""
+    T, H, dn, dr, w, base, tau = 40, 3, 6, 4, 7, 1e4, 0.3
+    c = dn + dr
+    a, za = rnd((T, c), 120), rnd((T, c), 121)
+    Ba = rnd((1, c), 122, 0.1)
+    ent = csa.compress(a, za, Ba, 1)                 # m = 1: the token rows themselves
+    assert np.allclose(ent, a, atol=1e-15)
+    cache = csa.finalize_kv(ent, 0, 1, dn, base, "f32", "f32")
+    q = rnd((T, H, c), 123)
+    o = np.zeros((T, H, dn))
+    lse = np.zeros((T, H))
+    for t in range(T):
+        o[t], lse[t] = csa.dense_attention_row(q[t], t, cache, 1, dn, base, tau, window=w)
+    qr = np.stack([csa.rope_query(q[t], t, dn, base) for t in range(T)])      # [T, H, c]
+    K = torch.as_tensor(cache["k"])[None, None]                                # [1, 1, T, c]
+    V = torch.as_tensor(cache["v"])[None, None]
+    i, j = np.arange(T)[:, None], np.arange(T)[None, :]
+    band = torch.as_tensor((j <= i) & (j > i - w))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.as_tensor(qr).permute(1, 0, 2)[None], K.expand(1, H, T, c), V.expand(1, H, T, dn),
+        attn_mask=band, scale=tau)[0].permute(1, 0, 2).numpy()
+    assert np.allclose(o, ref, atol=1e-12)
+    # a window at least as long as the prefix is plain dense attention
+    for t in (0, 5, T - 1):
+        od, ld = csa.dense_attention_row(q[t], t, cache, 1, dn, base, tau)
+        ow, lw = csa.dense_attention_row(q[t], t, cache, 1, dn, base, tau, window=T)
+        assert np.allclose(od, ow, atol=1e-15) and np.allclose(ld, lw, atol=1e-15)
+
+
+def test_lse_merge_is_one_softmax_over_the_union():
+    """The merge of a compressed branch (selected entries) and a window branch
+    (recent tokens) equals attention over both key sets at once (written out
+    by brute force over the concatenated keys)."""
+    H, c, dv, tau = 4, 9, 5, 0.35
+    q = rnd((H, c), 130)
+    K1, K2 = rnd((20, c), 131), rnd((11, c), 132)
+    sel1, sel2 = np.array([0, 3, 4, 9, 15, 19]), np.arange(11)
+    o1, l1 = csa.attend(q, K1, K1[:, :dv], sel1, tau)
+    o2, l2 = csa.attend(q, K2, K2[:, :dv], sel2, tau)
+    om, lm = csa.lse_merge(o1, l1, o2, l2)
+    Ku = np.concatenate([K1[sel1], K2[sel2]], 0)
+    ob, lb = brute.attend(q.tolist(), Ku.tolist(), Ku[:, :dv].tolist(), list(range(len(Ku))), tau)
+    assert np.allclose(om, ob, atol=1e-13) and np.allclose(lm, lb, atol=1e-13)
+    # one branch empty (no visible entry yet): the other branch unchanged
+    oe, le = csa.attend(q, K1, K1[:, :dv], [-1], tau)
+    o, lse = csa.lse_merge(oe, le, o2, l2)
+    assert np.array_equal(o, o2) and np.allclose(lse, l2, atol=0)
+    o, lse = csa.lse_merge(oe, le, oe, le)
+    assert not o.any() and np.isneginf(lse).all()
