@@ -238,9 +238,9 @@ __device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int s
   const int64_t bt = SPLIT ? it / splits : it;
   I.t = SPLIT ? 0 : static_cast<int>(bt % P.T);
   I.b = static_cast<int>(SPLIT ? bt : bt / P.T);
-  // decode (split) items take the sequence's position, prefill ones pos0 + t;
-  // kept in scalar registers
-  if (SPLIT) {
+  // decode items take the sequence's position, prefill ones pos0 + t; kept
+  // in scalar registers
+  if (SPLIT || P.pos_dev) {
     // a scalar load (constant address space, uniform index): a vector load
     // here would make its wait drain every load and gather in flight
     typedef const __attribute__((address_space(4))) int64_t cpos_t;

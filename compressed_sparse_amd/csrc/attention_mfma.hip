@@ -144,6 +144,10 @@ int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
   const int splits = decode_splits(dense, count);
   const int64_t tiles_per = (ntiles + splits - 1) / splits;
   const int64_t per = tiles_per * TILE;
+  if (splits == 1) {  // one item per sequence writes o and lse itself (the same bits a one-split merge gives)
+    launch_attn_bf16(P, dense, B, s, 1, per, nullptr);
+    return check_launch("attn_bf16_kernel");
+  }
   const size_t need = part_bytes(B, splits);
   if (!P.ws || P.ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace too small for the split partials");
   void* part = P.ws;
