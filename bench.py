@@ -366,9 +366,34 @@ def pair_decode_lines(n_steps=DECODE_STEPS):
     return lines
 
 
+def swa_decode_lines(n_steps=DECODE_STEPS, window=128):
+    """The 2^20-context CSA layer of the pair (B = 4, MXFP4 indexer) with its
+    sliding-window branch over the last 128 tokens: per step the CSA decode,
+    then the new token into the per-token cache, window attention and the
+    log-sum-exp merge into the layer's output."""
+    w = synth.PAIR_CSA_DECODE_B4_1M
+    log(f"setup {w.name} + sliding window {window}")
+    lc = path.CsaLayer(w, w.batch, w.tokens // w.m + n_steps)
+    sw = path.SwaBranch(w, w.batch, w.tokens + n_steps, window)
+    lc.prefill_context(w.tokens)
+    sw.prefill_context(w.tokens)
+    oc, osw = lc.alloc_decode_outputs(), sw.alloc_decode_outputs()
+    xs = lc.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
+
+    def step(i):
+        lc.decode_step(xs[i], oc)
+        sw.decode_step(xs[i], osw, oc)
+    ms3 = time_graph([lc, sw], step, n_steps)
+    ent_b = w.d_nope + 4 + 2 * w.d_rope
+    by = decode_bytes_csa(w, w.tokens // w.m, w.batch) + w.batch * (window * ent_b + 2 * 2 * w.c + 2 * 2 * w.heads *
+                                                                     w.d_nope)
+    return decode_line(w.name + f" + sliding window {window}", "CSA layer + sliding-window branch decode us/step",
+                       ms3, by, w.batch)
+
+
 def secondary_lines():
     out = []
-    for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, secondary_hca_prefill,
+    for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, swa_decode_lines, secondary_hca_prefill,
                secondary_hca_prefill_whole, secondary_mxfp4_prefill_indexer, secondary_tiny):
         r = fn()
         out.extend(r if isinstance(r, list) else [r])
@@ -590,7 +615,8 @@ def main():
                     help="run this many eager decode steps instead of the graphs (for counter collection)")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
-    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "hca-prefill", "hca-prefill-whole",
+    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "hca-prefill",
+                                       "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
     args = ap.parse_args()
@@ -609,6 +635,7 @@ def main():
         copy_calibration()
     if args.only:
         fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
+              "swa-decode": swa_decode_lines,
               "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
               "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
               "peaks": measured_peaks}[args.only]

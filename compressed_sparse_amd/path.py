@@ -192,6 +192,51 @@ class HcaLayer:
         cb.dense_attn_decode(self.adesc, self.kv, x["pos"], x["q"], self.w.tau, out["o"], out["lse"], ws=self.aws)
 
 
+class SwaBranch:
+    """The sliding-window branch of a layer: per-token entries of the layer's
+    C^a rows (the compressor with m = 1: a window of one token passes its row
+    through, turned by RoPE at the token's position and stored like the
+    layer's entries) and dense attention over the last `window` of them,
+    joined to the layer's (o, lse) by csa_lse_merge: one softmax over the
+    union of the layer's keys and the window's tokens."""
+
+    def __init__(self, w: synth.Workload, B, capacity, window, device="cuda", seed=0, seq_ids=None):
+        self.w, self.B, self.cap, self.window, self.device, self.seed = w, B, capacity, window, device, seed
+        self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
+        act = w.act_dtype
+        self.kv = cb.KVCache(cb.cache_desc(1, False, w.d_nope, w.d_rope, act, w.nope_fmt, w.rope_fmt, capacity,
+                                           w.rope_base), B, device)
+        self.adesc = cb.attn_desc(w.heads, w.d_nope, w.d_rope, act, w.out_dtype, w.nope_fmt, w.rope_fmt, 1, capacity,
+                                  w.rope_base, window=window)
+        self.Ba = torch.zeros((1, w.c), dtype=torch.float32, device=device)  # one row: weight 1 whatever the bias
+        self.aws = None
+
+    def caches(self):
+        return [self.kv]
+
+    def prefill_context(self, T, chunk=None):
+        chunk = chunk or self.w.chunk or T
+        for c in range(math.ceil(T / chunk)):
+            n = min(chunk, T - c * chunk)
+            toks = [synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device, names=["a", "za"])
+                    for sid in self.seq_ids]
+            x = {k: _stack([t[k][:n] for t in toks]) for k in toks[0]}
+            cb.compress_prefill(self.kv, c * chunk, x["a"], x["za"], self.Ba)
+
+    def alloc_decode_outputs(self):
+        w = self.w
+        self.aws = cb.workspace(cb.workspace_bytes(cb.OP_DENSE_ATTN_DECODE, self.adesc, self.B, 1, 0, 0), self.device)
+        return {"o": torch.empty((self.B, w.heads, w.d_nope), dtype=synth.TORCH_DTYPE[w.out_dtype], device=self.device),
+                "lse": torch.empty((self.B, w.heads), dtype=torch.float32, device=self.device)}
+
+    def decode_step(self, x, own, layer_out):
+        """The new token enters the window; window attention into `own`, then
+        merged into the layer's outputs in place."""
+        cb.compress_decode(self.kv, x["pos"], x["a"], x["za"], self.Ba)
+        cb.dense_attn_decode(self.adesc, self.kv, x["pos"], x["q"], self.w.tau, own["o"], own["lse"], ws=self.aws)
+        cb.lse_merge(layer_out["o"], layer_out["lse"], own["o"], own["lse"], layer_out["o"], layer_out["lse"])
+
+
 class DecodeGraph:
     """n consecutive decode steps of one or more layers captured in one HIP
     graph.  Every run starts from the same state: the graph first restores

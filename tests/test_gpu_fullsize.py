@@ -9,7 +9,8 @@ benchmark times, on outputs the oracle computes one by one:
   chunks 0, 1, 64 and 127) and HCA decode at batch 16 (four sequences);
 * the CSA + HCA layer pair at batch 4 with 2^20-token contexts, MXFP4
   indexer and BF16 scores (every sequence), with indexer recall against the
-  fp32 oracle.
+  fp32 oracle, and that CSA layer with its sliding-window branch (last 128
+  tokens) merged.
 
 Two legs per workload:
 
@@ -32,7 +33,8 @@ from compressed_sparse_amd import path, synth
 from oracle import csa
 from tests import fullsize_ref as R
 from tests import gpu_cache as G
-from tests.helpers import ascending_padded, compressor_error_bound, topk_explained
+from oracle import formats as F
+from tests.helpers import ascending_padded, compressor_error_bound, near_boundary, topk_explained
 
 pytestmark = pytest.mark.gpu
 
@@ -296,3 +298,73 @@ def test_pair_decode_b4_1m_mxfp4():
         for leg, cc in (("A", hca_reference_cache(wh, b, ctx, chunk, seed=1)), ("B", gpu_hca_cache(hca_l, b, n))):
             oref, lref = csa.dense_attention_row(q, ctx, cc, wh.m, wh.d_nope, wh.rope_base, wh.tau)
             G.check_attention(f"pair hca seq {b} [{leg}]", R.host(ho["o"][b]), R.host(ho["lse"][b]), oref, lref)
+
+
+def window_rows_checked(w, exact, gpu, name):
+    """The oracle's stored window rows (per-token entries: the token's row
+    turned by RoPE, then FP8 + scale / BF16), with the GPU's value taken where
+    the two differ only because the exact value lies within the GPU's fp32
+    error of a rounding boundary (a token's BF16 row over its scale can land
+    exactly on an FP8 midpoint, where the fp32 and the fp64 quotient round
+    apart); any other difference fails."""
+    dn = w.d_nope
+    ref = np.concatenate([csa.store_format(exact[:, :dn], w.nope_fmt)[0],
+                          csa.store_format(exact[:, dn:], w.rope_fmt)[0]], 1)
+    s = F.to_f32(np.where(np.abs(exact[:, :dn]).max(1) > 0, np.abs(exact[:, :dn]).max(1) / 448, 1.0))[:, None]
+    y = exact[:, :dn] / s
+    near_n = near_boundary(y, F.fp8_round, 2.0 ** -20 * np.abs(y) + 2.0 ** -20)
+    near_r = near_boundary(exact[:, dn:], F.to_bf16, 2.0 ** -21 * np.abs(exact[:, dn:]))
+    near = np.concatenate([near_n, near_r], 1)
+    diff = ref != gpu
+    assert not (diff & ~near).any(), f"{name}: window rows differ away from rounding boundaries"
+    print(f"{name}: {int(diff.sum())} window elements at rounding boundaries", flush=True)
+    return np.where(diff, gpu, ref)
+
+
+def test_csa_layer_with_window_branch_b4_1m():
+    """The pair's CSA layer (B = 4, 2^20-token contexts, MXFP4 indexer) with
+    its sliding-window branch over the last 128 tokens, merged: every
+    sequence's CSA part (over the GPU's selection), window part and merged
+    output against the oracle (one softmax over the selected compressed
+    entries and the window's tokens for the merge), with both legs' entries
+    (the oracle's fp64 compressor and rows, and the GPU-written caches)."""
+    w, win = synth.PAIR_CSA_DECODE_B4_1M, 128
+    ctx, chunk, B = w.tokens, w.chunk, w.batch
+    lay = path.CsaLayer(w, B, ctx // w.m + 2)
+    sw = path.SwaBranch(w, B, ctx + 2, win)
+    lay.prefill_context(ctx)
+    sw.prefill_context(ctx)
+    out, own = lay.alloc_decode_outputs(), sw.alloc_decode_outputs()
+    x = lay.decode_inputs([ctx] * B)
+    lay.decode_step(x, out)
+    torch.cuda.synchronize()
+    o_csa, l_csa = R.host(out["o"]), R.host(out["lse"])
+    sw.decode_step(x, own, out)
+    torch.cuda.synchronize()
+    idx = out["idx"].cpu().numpy()
+    o, lse = R.host(out["o"]), R.host(out["lse"])
+    o_w, l_w = R.host(own["o"]), R.host(own["lse"])
+    pos = ctx
+    store = lambda e: np.concatenate([csa.store_format(e[:, :w.d_nope], w.nope_fmt)[0],
+                                      csa.store_format(e[:, w.d_nope:], w.rope_fmt)[0]], 1)
+    ref = {leg: {"csa": ([], []), "win": ([], []), "all": ([], [])} for leg in "AB"}
+    for b in range(B):
+        qr = csa.rope_query(R.host(x["q"][b]), pos, w.d_nope, w.rope_base)
+        ids = idx[b][idx[b] >= 0]
+        tpos = np.arange(pos - win + 1, pos + 1)
+        ex = csa.rope(R.csa_entries(w, b, ids, chunk), csa.entry_position(ids, w.m), w.d_nope, w.rope_base)
+        tr = csa.rope(R.token_rows(w, b, chunk, tpos, ["a"])["a"], tpos, w.d_nope, w.rope_base)
+        gw = G.decode_kv(sw.kv, b, tpos)
+        aw = window_rows_checked(w, tr, gw, f"seq {b}")
+        parts = {"A": (store(ex), aw),                                                # oracle entries
+                 "B": (G.decode_kv(lay.kv, b, ids), gw)}                              # GPU-written caches
+        for leg, (Kc, Kw) in parts.items():
+            for name, K in (("csa", Kc), ("win", Kw), ("all", np.concatenate([Kc, Kw], 0))):
+                r = csa.attend(qr, K, K[:, :w.d_nope], np.arange(len(K)), w.tau)
+                ref[leg][name][0].append(r[0])
+                ref[leg][name][1].append(r[1])
+    for leg in "AB":
+        for name, (og, lg) in (("csa", (o_csa, l_csa)), ("win", (o_w, l_w)), ("all", (o, lse))):
+            e, _ = G.check_attention(f"window branch {name} [{leg}]", og, lg, np.array(ref[leg][name][0]),
+                                     np.array(ref[leg][name][1]))
+            print(f"csa + window 1M, {name} [{leg}]: max-rel {e:.2e}", flush=True)
