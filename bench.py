@@ -391,9 +391,41 @@ def swa_decode_lines(n_steps=DECODE_STEPS, window=128):
                        ms3, by, w.batch)
 
 
+def paged_decode_lines(n_steps=DECODE_STEPS, page=64):
+    """Paged, variable-length CSA decode: 32 sequences with context lengths
+    log-uniform over 8K..256K tokens, KV and indexer-key caches in 64-entry
+    pages of one pool handed out in a seeded random order; the same batch in
+    contiguous per-sequence caches (capacity of the longest) beside it."""
+    w = synth.PAGED_CSA_DECODE_B32_MIXED
+    lengths = synth.mixed_lengths(w.batch, 13, 18)
+    need = [(L + n_steps) // w.m + 1 for L in lengths]
+    cap = -(-max(need) // page) * page
+    table, pool = path.block_tables(need, page, cap)
+    by = sum(decode_bytes_csa(w, L // w.m, 1) for L in lengths)
+    lines = []
+    for paged in (True, False):
+        log(f"setup {w.name} ({'paged' if paged else 'contiguous'})")
+        kw = dict(page_size=page, block_table=table, pool_pages=pool) if paged else {}
+        lay = path.CsaLayer(w, w.batch, cap, **kw)
+        lay.prefill_contexts(lengths)
+        o = lay.alloc_decode_outputs()
+        xs = lay.decode_input_steps([[L + i for L in lengths] for i in range(n_steps)])
+        ms3 = time_graph([lay], lambda i: lay.decode_step(xs[i], o), n_steps)
+        name = w.name if paged else w.name.replace("paged", "contiguous").replace("_page64", "")
+        line = decode_line(name, "decode us/step (whole batch, mixed contexts)", ms3, by, w.batch)
+        line["contexts"] = {"min": min(lengths), "max": max(lengths), "mean": float(np.mean(lengths))}
+        if paged:
+            line["pages"] = {"entries_per_page": page, "pool_pages": pool, "capacity_per_seq": cap}
+        lines.append(line)
+        del lay, o, xs
+        torch.cuda.empty_cache()
+    return lines
+
+
 def secondary_lines():
     out = []
-    for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, swa_decode_lines, secondary_hca_prefill,
+    for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, swa_decode_lines, paged_decode_lines,
+               secondary_hca_prefill,
                secondary_hca_prefill_whole, secondary_mxfp4_prefill_indexer, secondary_tiny):
         r = fn()
         out.extend(r if isinstance(r, list) else [r])
@@ -615,7 +647,8 @@ def main():
                     help="run this many eager decode steps instead of the graphs (for counter collection)")
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
-    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "hca-prefill",
+    ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "paged-decode",
+                                       "hca-prefill",
                                        "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
@@ -635,7 +668,7 @@ def main():
         copy_calibration()
     if args.only:
         fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
-              "swa-decode": swa_decode_lines,
+              "swa-decode": swa_decode_lines, "paged-decode": paged_decode_lines,
               "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
               "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
               "peaks": measured_peaks}[args.only]

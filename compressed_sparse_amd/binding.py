@@ -25,26 +25,28 @@ OP_DENSE_ATTN_PREFILL, OP_DENSE_ATTN_DECODE = 5, 6
 class CacheDesc(ctypes.Structure):
     _fields_ = [("m", ctypes.c_int32), ("overlap", ctypes.c_int32), ("d_nope", ctypes.c_int32),
                 ("d_rope", ctypes.c_int32), ("in_dtype", ctypes.c_int32), ("nope_dtype", ctypes.c_int32),
-                ("rope_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32), ("rope_base", ctypes.c_double),
-                ("capacity", ctypes.c_int64)]
+                ("rope_dtype", ctypes.c_int32), ("page_size", ctypes.c_int32), ("rope_base", ctypes.c_double),
+                ("capacity", ctypes.c_int64), ("pool_pages", ctypes.c_int64)]
 
 
 class Cache(ctypes.Structure):
     _fields_ = [("nope", ctypes.c_void_p), ("scale", ctypes.c_void_p), ("rope", ctypes.c_void_p),
-                ("ring", ctypes.c_void_p)]
+                ("ring", ctypes.c_void_p), ("block_table", ctypes.c_void_p)]
 
 
 class IndexDesc(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("dim", ctypes.c_int32), ("q_dtype", ctypes.c_int32),
                 ("qk_dtype", ctypes.c_int32), ("key_dtype", ctypes.c_int32), ("score_dtype", ctypes.c_int32),
-                ("m", ctypes.c_int32), ("reserved", ctypes.c_int32), ("capacity", ctypes.c_int64)]
+                ("m", ctypes.c_int32), ("page_size", ctypes.c_int32), ("capacity", ctypes.c_int64),
+                ("pool_pages", ctypes.c_int64)]
 
 
 class AttnDesc(ctypes.Structure):
     _fields_ = [("n_heads", ctypes.c_int32), ("d_nope", ctypes.c_int32), ("d_rope", ctypes.c_int32),
                 ("q_dtype", ctypes.c_int32), ("o_dtype", ctypes.c_int32), ("nope_dtype", ctypes.c_int32),
                 ("rope_dtype", ctypes.c_int32), ("m", ctypes.c_int32), ("window", ctypes.c_int32),
-                ("qk_mode", ctypes.c_int32), ("rope_base", ctypes.c_double), ("capacity", ctypes.c_int64)]
+                ("qk_mode", ctypes.c_int32), ("rope_base", ctypes.c_double), ("capacity", ctypes.c_int64),
+                ("page_size", ctypes.c_int32), ("reserved", ctypes.c_int32), ("pool_pages", ctypes.c_int64)]
 
 
 class DecodeInputs(ctypes.Structure):
@@ -120,35 +122,75 @@ def stream_ptr(stream=None):
 # descriptors and caches
 # ---------------------------------------------------------------------------
 
-def cache_desc(m, overlap, d_nope, d_rope, in_fmt, nope_fmt, rope_fmt, capacity, base=10000.0):
+def cache_desc(m, overlap, d_nope, d_rope, in_fmt, nope_fmt, rope_fmt, capacity, base=10000.0, page_size=0,
+               pool_pages=0):
     return CacheDesc(m, int(overlap), d_nope, d_rope, FMT[in_fmt], FMT[nope_fmt],
-                     FMT.get(rope_fmt, F32), 0, base, capacity)
+                     FMT.get(rope_fmt, F32), page_size, base, capacity, pool_pages)
 
 
 class KVCache:
-    """Device buffers of a compressed cache for B sequences (torch tensors)."""
+    """Device buffers of a compressed cache for B sequences (torch tensors).
 
-    def __init__(self, desc: CacheDesc, B, device="cuda"):
+    Contiguous (desc.page_size == 0): nope [B][cap][..], scale [B][cap](..),
+    rope [B][cap][d_rope].  Paged: the same per row of a pool, [pool_pages]
+    [page_size][..], and block_table int32 [B][cap / page_size] (the caller's
+    mapping; identity-free: any page order)."""
+
+    def __init__(self, desc: CacheDesc, B, device="cuda", block_table=None):
         self.desc, self.B = desc, B
         cap, dn, dr = desc.capacity, desc.d_nope, desc.d_rope
         c = dn + dr
         nf = desc.nope_dtype
+        paged = desc.page_size > 0
+        lead = (desc.pool_pages, desc.page_size) if paged else (B, cap)
+        if paged:
+            if block_table is None or tuple(block_table.shape) != (B, cap // desc.page_size) \
+                    or block_table.dtype != torch.int32:
+                raise ValueError("a paged cache needs an int32 block_table [B][capacity / page_size]")
+        elif block_table is not None:
+            raise ValueError("block_table given for a contiguous cache")
+        self.block_table = block_table
         if nf == MXFP4:
-            self.nope = torch.zeros((B, cap, dn // 2), dtype=torch.uint8, device=device)
-            self.scale = torch.zeros((B, cap, dn // 32), dtype=torch.uint8, device=device)
+            self.nope = torch.zeros(lead + (dn // 2,), dtype=torch.uint8, device=device)
+            self.scale = torch.zeros(lead + (dn // 32,), dtype=torch.uint8, device=device)
         else:
             dt = {F32: torch.float32, BF16: torch.bfloat16, FP8E4M3: torch.uint8}[nf]
-            self.nope = torch.zeros((B, cap, dn), dtype=dt, device=device)
-            self.scale = torch.zeros((B, cap), dtype=torch.float32, device=device) if nf == FP8E4M3 else None
+            self.nope = torch.zeros(lead + (dn,), dtype=dt, device=device)
+            self.scale = torch.zeros(lead, dtype=torch.float32, device=device) if nf == FP8E4M3 else None
         rdt = torch.float32 if desc.rope_dtype == F32 else torch.bfloat16
-        self.rope = torch.zeros((B, cap, dr), dtype=rdt, device=device) if dr else None
+        self.rope = torch.zeros(lead + (dr,), dtype=rdt, device=device) if dr else None
         R = 2 * desc.m if desc.overlap else desc.m
         NT = 4 if desc.overlap else 2
         self.ring = torch.zeros((B, R, NT, c), dtype=torch.float32, device=device)
 
     def struct(self):
         return Cache(self.nope.data_ptr(), None if self.scale is None else self.scale.data_ptr(),
-                     None if self.rope is None else self.rope.data_ptr(), self.ring.data_ptr())
+                     None if self.rope is None else self.rope.data_ptr(), self.ring.data_ptr(),
+                     None if self.block_table is None else self.block_table.data_ptr())
+
+    def seq_view(self, b):
+        """Sequence b alone, as a one-sequence cache over the same memory (its
+        ring and block-table row; for a contiguous cache its rows)."""
+        v = object.__new__(KVCache)
+        v.desc, v.B = self.desc, 1
+        v.ring = self.ring[b:b + 1]
+        if self.desc.page_size:
+            v.nope, v.scale, v.rope = self.nope, self.scale, self.rope
+            v.block_table = self.block_table[b:b + 1]
+        else:
+            v.nope = self.nope[b:b + 1]
+            v.scale = None if self.scale is None else self.scale[b:b + 1]
+            v.rope = None if self.rope is None else self.rope[b:b + 1]
+            v.block_table = None
+        return v
+
+    def logical(self, t):
+        """One of nope / scale / rope in sequence order, [B][cap][..] (a gather of
+        the pages for a paged cache; the tensor itself when contiguous)."""
+        if self.desc.page_size == 0 or t is None:
+            return t
+        pages = t[self.block_table.long()]  # [B][cap / page][page][..]
+        return pages.reshape((self.B, self.desc.capacity) + tuple(t.shape[2:]))
 
 
 # ---------------------------------------------------------------------------
@@ -168,8 +210,9 @@ def compress_decode(cache: KVCache, pos, a, za, Ba, b=None, zb=None, Bb=None, st
                                      ptr(zb), ptr(Ba), ptr(Bb), ctypes.byref(cs), stream_ptr(stream)))
 
 
-def index_desc(n_heads, dim, q_fmt, qk_fmt, key_fmt, score_fmt, m, capacity):
-    return IndexDesc(n_heads, dim, FMT[q_fmt], FMT[qk_fmt], FMT[key_fmt], FMT[score_fmt], m, 0, capacity)
+def index_desc(n_heads, dim, q_fmt, qk_fmt, key_fmt, score_fmt, m, capacity, page_size=0, pool_pages=0):
+    return IndexDesc(n_heads, dim, FMT[q_fmt], FMT[qk_fmt], FMT[key_fmt], FMT[score_fmt], m, page_size, capacity,
+                     pool_pages)
 
 
 def workspace_bytes(op, desc, B, T, pos0=0, k=0):
@@ -200,9 +243,10 @@ def index_topk_decode(desc, keys: KVCache, pos, qI, w, k, idx, scores=None, ws=N
                                        ptr(idx), ptr(scores), ptr(ws), ws.numel(), stream_ptr(stream)))
 
 
-def attn_desc(n_heads, d_nope, d_rope, q_fmt, o_fmt, nope_fmt, rope_fmt, m, capacity, base=10000.0, window=0):
+def attn_desc(n_heads, d_nope, d_rope, q_fmt, o_fmt, nope_fmt, rope_fmt, m, capacity, base=10000.0, window=0,
+              page_size=0, pool_pages=0):
     return AttnDesc(n_heads, d_nope, d_rope, FMT[q_fmt], FMT[o_fmt], FMT[nope_fmt], FMT.get(rope_fmt, F32),
-                    m, window, 0, base, capacity)
+                    m, window, 0, base, capacity, page_size, 0, pool_pages)
 
 
 def _ws(op, desc, B, T, pos0, k, ws, device):

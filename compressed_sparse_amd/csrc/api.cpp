@@ -3,7 +3,7 @@
 
 #include <string>
 
-#include "csa.h"
+#include "common.hpp"
 
 namespace csa {
 
@@ -19,6 +19,38 @@ int fail(int status, const std::string& msg) {
 int check_launch(const char* what) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(CSA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+  return CSA_OK;
+}
+
+int check_paging(int32_t page_size, int64_t pool_pages, int64_t capacity) {
+  if (page_size == 0) {
+    if (pool_pages != 0) return fail(CSA_ERR_INVALID_ARG, "pool_pages must be 0 for a contiguous cache");
+    return CSA_OK;
+  }
+  if (page_size < 64 || page_size > 65536 || (page_size & (page_size - 1)))
+    return fail(CSA_ERR_INVALID_ARG, "page_size must be 0 or a power of two in 64..65536");
+  if (capacity % page_size) return fail(CSA_ERR_INVALID_ARG, "capacity must be a multiple of page_size");
+  if (pool_pages < 1 || pool_pages > (int64_t(1) << 31) / page_size)
+    return fail(CSA_ERR_INVALID_ARG, "pool_pages must be in 1..2^31/page_size");
+  return CSA_OK;
+}
+
+int make_pages(int32_t page_size, int64_t pool_pages, int64_t capacity, const int32_t* table, Pages* out) {
+  int st;
+  if ((st = check_paging(page_size, pool_pages, capacity)) != CSA_OK) return st;
+  *out = Pages{};
+  if (page_size == 0) {
+    if (table) return fail(CSA_ERR_INVALID_ARG, "block_table must be NULL for a contiguous cache");
+    return CSA_OK;
+  }
+  if (!table) return fail(CSA_ERR_INVALID_ARG, "a paged cache needs a block_table");
+  if (reinterpret_cast<uintptr_t>(table) & 3u) return fail(CSA_ERR_ALIGNMENT, "block_table must be 4-byte aligned");
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  out->table = table;
+  out->shift = shift;
+  out->tps = capacity >> shift;
+  out->pool = pool_pages;
   return CSA_OK;
 }
 

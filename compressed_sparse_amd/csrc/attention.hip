@@ -36,13 +36,13 @@ __device__ __forceinline__ float kv_rope(const AttnParams& P, size_t e, int d) {
 
 // grid (H, T, B), 256 threads.
 __global__ void __launch_bounds__(256) attn_generic_kernel(AttnParams P) {
-  extern __shared__ float smem[];
+  extern __shared__ int64_t smem64[];
   const int c = P.d_nope + P.d_rope;
-  float* red = smem;             // 32
-  float* q = smem + 32;          // c
-  float* p = q + c;              // 256 probabilities of the current chunk
-  int* ent = reinterpret_cast<int*>(p + 256);  // 256 entry ids
-  float* o = reinterpret_cast<float*>(ent + 256);  // d_nope accumulators
+  int64_t* ent = smem64;                               // 256 cache rows (-1: none)
+  float* red = reinterpret_cast<float*>(ent + 256);    // 32
+  float* q = red + 32;                                 // c
+  float* p = q + c;                                    // 256 probabilities of the current chunk
+  float* o = p + 256;                                  // d_nope accumulators
   const int h = blockIdx.x, t = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, nt = blockDim.x;
   const int64_t pos = attn_pos(P, b, t);
@@ -70,9 +70,10 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnParams P) {
     int64_t s = -1;
     if (j < count) s = list ? static_cast<int64_t>(list[j]) : lo + j;
     if (s >= n) s = -1;
+    const int64_t er = s >= 0 ? entry_row(P.pg, P.cap, b, s) : -1;  // -1: page outside the pool
     float l = -INFINITY;
-    if (s >= 0) {
-      const size_t e = static_cast<size_t>(b) * P.cap + s;
+    if (er >= 0) {
+      const size_t e = static_cast<size_t>(er);
       float dot = 0.0f;
       for (int d = 0; d < P.d_nope; ++d) dot = fmaf(q[d], kv_nope(P, e, d), dot);
       for (int d = 0; d < P.d_rope; ++d) dot = fmaf(q[P.d_nope + d], kv_rope(P, e, d), dot);
@@ -80,19 +81,19 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnParams P) {
     }
     const float cmax = block_max(l, red);
     const float nmx = fmaxf(mx, cmax);
-    float pe = (s >= 0) ? expf(l - nmx) : 0.0f;
+    float pe = (er >= 0) ? expf(l - nmx) : 0.0f;
     const float csum = block_sum(pe, red);
     const float corr = (nmx == -INFINITY) ? 1.0f : expf(mx - nmx);
     p[tid] = pe;
-    ent[tid] = static_cast<int>(s);
+    ent[tid] = er;
     __syncthreads();
     if (nmx != -INFINITY) {
       const int lim = static_cast<int>((count - base) < nt ? (count - base) : nt);
       for (int d = tid; d < P.d_nope; d += nt) {
         float acc = o[d] * corr;
         for (int i = 0; i < lim; ++i) {
-          int ss = ent[i];
-          if (ss >= 0) acc = fmaf(p[i], kv_nope(P, static_cast<size_t>(b) * P.cap + ss, d), acc);
+          const int64_t e = ent[i];
+          if (e >= 0) acc = fmaf(p[i], kv_nope(P, static_cast<size_t>(e), d), acc);
         }
         o[d] = acc;
       }
@@ -112,7 +113,7 @@ __global__ void __launch_bounds__(256) attn_generic_kernel(AttnParams P) {
 
 static int launch_generic(const AttnParams& P, int B, hipStream_t s) {
   const int c = P.d_nope + P.d_rope;
-  const size_t lds = (32 + c + 256 + 256 + P.d_nope) * sizeof(float);
+  const size_t lds = (32 + c + 256 + P.d_nope) * sizeof(float) + 256 * sizeof(int64_t);
   hipLaunchKernelGGL(attn_generic_kernel, dim3(P.H, P.T, B), dim3(256), lds, s, P);
   return check_launch("attn_generic_kernel");
 }
@@ -138,6 +139,7 @@ static int validate_attn(const csa_attn_desc* d, int B, const void* q, const csa
   if (d->capacity < 1 || d->capacity > (int64_t(1) << 31) - 1) return fail(CSA_ERR_INVALID_ARG, "capacity must be in 1..2^31-1");
   if (d->window < 0) return fail(CSA_ERR_INVALID_ARG, "window must be >= 0");
   if (d->qk_mode != 0) return fail(CSA_ERR_UNSUPPORTED, "qk_mode must be 0");
+  if (d->reserved != 0) return fail(CSA_ERR_INVALID_ARG, "reserved field must be 0");
   if (!(d->rope_base > 0.0)) return fail(CSA_ERR_INVALID_ARG, "rope_base must be > 0");
   if (B < 0 || B > 65535) return fail(CSA_ERR_INVALID_ARG, "B must be in 0..65535");
   if (!q || !kv || !kv->nope || !o) return fail(CSA_ERR_INVALID_ARG, "NULL argument");
@@ -146,7 +148,8 @@ static int validate_attn(const csa_attn_desc* d, int B, const void* q, const csa
   if (!aligned16(q) || !aligned16(kv->nope) || !aligned16(kv->scale) || !aligned16(kv->rope) ||
       !aligned16(o) || !aligned16(lse))
     return fail(CSA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  return CSA_OK;
+  Pages pg;
+  return make_pages(d->page_size, d->pool_pages, d->capacity, kv->block_table, &pg);
 }
 
 static AttnParams make_attn_params(const csa_attn_desc* d, const void* q, const csa_cache* kv,
@@ -159,20 +162,24 @@ static AttnParams make_attn_params(const csa_attn_desc* d, const void* q, const 
   P.q = q; P.nope = kv->nope; P.scale = kv->scale; P.rope = kv->rope;
   P.idx = idx; P.k = k; P.scale_qk = scale; P.o = o; P.lse = lse;
   P.ws = ws; P.ws_bytes = ws_bytes;
+  make_pages(d->page_size, d->pool_pages, d->capacity, kv->block_table, &P.pg);  // validated before
+  P.span_rows = P.pg.table ? (P.pg.pool << P.pg.shift) : P.cap;
+  P.list_rows = false;
   return P;
 }
 
 size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k) {
   if (!d || B < 0 || T < 0) return 0;
-  return mfma_attn_ws_bytes(d, op, B, T, pos0, k);
+  if (check_paging(d->page_size, d->pool_pages, d->capacity) != CSA_OK) return 0;
+  return mfma_attn_ws_bytes(d, op, B, T, pos0, k) + page_list_bytes(d, op, B, T, k);
 }
 
 int attn_dispatch(AttnParams& P, int op, int B, void* stream) {
   hipStream_t s = as_stream(stream);
   if (mfma_attn_supported(P)) {
     if (!mfma_attn_capacity_ok(P))
-      return fail(CSA_ERR_UNSUPPORTED, "capacity too large: each cache buffer of a sequence must stay below 2^31 bytes "
-                                       "(2^21 BF16 or 2^22 FP8 entries of 512 dims)");
+      return fail(CSA_ERR_UNSUPPORTED, "capacity too large: each cache buffer of a sequence (of the pool, when "
+                                       "paged) must stay below 2^31 bytes (2^21 BF16 or 2^22 FP8 entries of 512 dims)");
     return launch_mfma_attn(P, op, B, s);
   }
   return launch_generic(P, B, s);
@@ -283,8 +290,8 @@ int sparse_attn_decode_setup(const csa_attn_desc* desc, int B, const int64_t* po
   AttnParams P = make_attn_params(desc, q, kv, idx, k, softmax_scale, o, lse, ws, ws_bytes);
   P.T = 1; P.pos0 = 0; P.pos_dev = pos;
   if (mfma_attn_supported(P) && !mfma_attn_capacity_ok(P))
-    return fail(CSA_ERR_UNSUPPORTED, "capacity too large: each cache buffer of a sequence must stay below 2^31 bytes "
-                                     "(2^21 BF16 or 2^22 FP8 entries of 512 dims)");
+    return fail(CSA_ERR_UNSUPPORTED, "capacity too large: each cache buffer of a sequence (of the pool, when "
+                                     "paged) must stay below 2^31 bytes (2^21 BF16 or 2^22 FP8 entries of 512 dims)");
   *out = P;
   return CSA_OK;
 }

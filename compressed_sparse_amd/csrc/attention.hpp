@@ -22,6 +22,9 @@ struct AttnParams {
   float* lse;
   void* ws;
   size_t ws_bytes;
+  Pages pg;           // KV placement (contiguous or paged)
+  int64_t span_rows;  // rows one gather descriptor covers: cap from the sequence's first row, or the whole pool
+  bool list_rows;     // sparse lists already hold pool rows (paged: turned by page_rows_kernel)
 };
 
 // MFMA path (64 heads, 512 + 64 dims, BF16 q, BF16 / FP8 cache).
@@ -42,5 +45,7 @@ int sparse_attn_decode_setup(const csa_attn_desc* desc, int B, const int64_t* po
                              size_t ws_bytes, AttnParams* out);
 int attn_dispatch(AttnParams& P, int op, int B, void* stream);
 size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k);
+// paged sparse attention on the MFMA path: bytes of the list turned into pool rows
+size_t page_list_bytes(const csa_attn_desc* d, int op, int B, int T, int k);
 
 }  // namespace csa

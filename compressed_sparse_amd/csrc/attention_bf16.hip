@@ -142,10 +142,29 @@ __device__ __forceinline__ int slot_id(const int* s_list, int64_t r, int64_t r0,
 // instruction, lane L fetching the chunk that belongs at slot L); loads 16
 // and 17 are RoPE rows 16w .. 16w+7 and 16w+8 .. 16w+15 (8 rows x 8 chunks
 // each).  my_id: lane i < 16 holds the entry id of row 16w + i.
+// Dense attention over a paged cache: the rows are consecutive entries of
+// sequence b (slots past the valid ones repeat the last valid entry), so the
+// 16 rows of a wave lie in at most two pages (a page holds at least 64
+// entries), whose table entries arrive by two scalar loads; the lane's id
+// becomes its pool row.  A page outside the pool reads as page 0.
+__device__ __forceinline__ int64_t page_base(const AttnParams& P, int b, int id) {
+  typedef const __attribute__((address_space(4))) int32_t ctab_t;
+  const int64_t ix = static_cast<int64_t>(b) * P.pg.tps + (id >> P.pg.shift);
+  const int64_t pg = reinterpret_cast<ctab_t*>(reinterpret_cast<uintptr_t>(P.pg.table))[ix];
+  return (pg >= 0 && pg < P.pg.pool ? pg : 0) << P.pg.shift;
+}
+
 template <bool DENSE>
-__device__ __forceinline__ int tile_ids(const int* s_list, int64_t rl, int64_t r0, int64_t nvalid) {
+__device__ __forceinline__ int tile_ids(const AttnParams& P, int b, const int* s_list, int64_t rl, int64_t r0,
+                                        int64_t nvalid) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  return slot_id<DENSE>(s_list, rl + 16 * w + (lane & 15), r0, nvalid);
+  const int64_t r = rl + 16 * w + (lane & 15);
+  if (!DENSE || !P.pg.table) return slot_id<DENSE>(s_list, r, r0, nvalid);
+  const int id = static_cast<int>(r0 + (r < nvalid ? r : nvalid - 1));
+  const int f = __builtin_amdgcn_readlane(id, 0), l = __builtin_amdgcn_readlane(id, 15);
+  const int64_t bf = page_base(P, b, f), bl = page_base(P, b, l);
+  const int mask = (1 << P.pg.shift) - 1;
+  return static_cast<int>(((id >> P.pg.shift) == (f >> P.pg.shift) ? bf : bl) + (id & mask));
 }
 
 // Buffer descriptor (raw, byte-addressed, 32-bit data format) over
@@ -167,7 +186,7 @@ __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, in
   typedef __attribute__((address_space(3))) void lds_void;
   typedef Lay<FP8> L;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // rows, LDS addresses: scalar
-  const uint64_t cap = static_cast<uint64_t>(P.cap);
+  const uint64_t cap = static_cast<uint64_t>(P.span_rows);  // rows the descriptors cover
   if (!FP8 && it < 16) {
     const int id = __builtin_amdgcn_readlane(my_id, it);
     const int r = 16 * w + it;
@@ -217,8 +236,8 @@ __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, in
 // All loads of the tile at list slot rl, back to back.
 template <bool FP8, bool DENSE>
 __device__ __forceinline__ void issue_tile(uint8_t* buf, const AttnParams& P, const int* s_list, int64_t rl,
-                                           int64_t r0, int64_t nvalid, size_t seq) {
-  const int my_id = tile_ids<DENSE>(s_list, rl, r0, nvalid);
+                                           int64_t r0, int64_t nvalid, size_t seq, int b) {
+  const int my_id = tile_ids<DENSE>(P, b, s_list, rl, r0, nvalid);
 #pragma unroll
   for (int it = 0; it < Lay<FP8>::NLOAD; ++it) issue_load<FP8>(buf, P, my_id, seq, it);
 }
@@ -258,7 +277,7 @@ __device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int s
   I.r0 = lo + static_cast<int64_t>(I.split) * per_split;
   I.r1 = I.r0 + per_split < end ? I.r0 + per_split : end;
   I.qrow = (static_cast<size_t>(I.b) * P.T + I.t) * NH;
-  I.seq = static_cast<size_t>(I.b) * P.cap;
+  I.seq = P.pg.table ? 0 : static_cast<size_t>(I.b) * P.cap;  // paged: rows are pool rows
   return I;
 }
 
@@ -378,11 +397,11 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   } else {
     int32_t lr[4];
     load_list(P, I, tid, lr);
-    nvalid = compact_list(lr, I.n, s_list, s_cnt);
+    nvalid = compact_list(lr, P.list_rows ? P.span_rows : I.n, s_list, s_cnt);
   }
   int ntiles = (nvalid + TILE - 1) / TILE;
   int par = 0;  // buffer of the next tile: kb0 / kb1
-  if (ntiles > 0) issue_tile<FP8, DENSE>(kb0, P, s_list, 0, I.r0, nvalid, I.seq);
+  if (ntiles > 0) issue_tile<FP8, DENSE>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
   bf16x8 qf[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
@@ -458,7 +477,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
 
     rope_q(th, I.pos, qf);
     // entry ids of the tile whose loads the current tile issues (read ahead)
-    int my_id_pf = ntiles > 1 ? tile_ids<DENSE>(s_list, TILE, I.r0, nvalid) : 0;
+    int my_id_pf = ntiles > 1 ? tile_ids<DENSE>(P, I.b, s_list, TILE, I.r0, nvalid) : 0;
     f32x16 oacc[4][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -468,8 +487,8 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
 
     // next item's list compacted into s_list, its first tile issued into buf
     auto start_next = [&](uint8_t* buf) {
-      nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, In.n, s_list, s_cnt);
-      if (nvalid_n > 0) issue_tile<FP8, DENSE>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq);
+      nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, P.list_rows ? P.span_rows : In.n, s_list, s_cnt);
+      if (nvalid_n > 0) issue_tile<FP8, DENSE>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq, In.b);
       next_started = true;
     };
 
@@ -515,10 +534,10 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       if (!last) {
         my_id = my_id_pf;
       } else if (has_next) {
-        nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, In.n, s_list, s_cnt);
+        nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, P.list_rows ? P.span_rows : In.n, s_list, s_cnt);
         next_started = true;
         if (nvalid_n > 0) {
-          my_id = tile_ids<DENSE>(s_list, 0, In.r0, nvalid_n);
+          my_id = tile_ids<DENSE>(P, In.b, s_list, 0, In.r0, nvalid_n);
           lseq = In.seq;
         }
       }
@@ -709,7 +728,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     };
     for (int j = 0; j < ntiles; ++j) {
       tile(par ? kb1 : kb0, par ? kb0 : kb1, pbuf, j);
-      if (j + 2 < ntiles) my_id_pf = tile_ids<DENSE>(s_list, static_cast<int64_t>(j + 2) * TILE, I.r0, nvalid);
+      if (j + 2 < ntiles) my_id_pf = tile_ids<DENSE>(P, I.b, s_list, static_cast<int64_t>(j + 2) * TILE, I.r0, nvalid);
       par ^= 1;
     }
 

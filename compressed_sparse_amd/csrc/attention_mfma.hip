@@ -100,12 +100,31 @@ int decode_splits(bool dense, int64_t count) {
 int64_t dense_span(int64_t cap, int64_t window) { return window > 0 && window < cap ? window : cap; }
 
 // Gather offsets of the MFMA kernel are 32-bit byte offsets within one
-// sequence's rows (row id times row bytes): every cache buffer of a
-// sequence must stay below 2^31 bytes.
+// sequence's rows, or within the pool of a paged cache (row id times row
+// bytes): every cache buffer of a sequence (of the pool) must stay below
+// 2^31 bytes.
 bool offsets_fit(const AttnParams& P) {
   const int64_t nope_row = P.nope_dt == CSA_FP8E4M3 ? DN : DN * 2;
   const int64_t lim = int64_t(1) << 31;
-  return P.cap <= lim / nope_row && P.cap <= lim / (DRP * 2);
+  return P.span_rows <= lim / nope_row && P.span_rows <= lim / (DRP * 2);
+}
+
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+// Paged sparse attention: each listed id turned into its pool row before the
+// gather kernel runs, -1 for an id outside [0, n(p)) or on a page outside
+// the pool, so that the kernel's tile loop keeps reading rows straight from
+// its list.  One thread per list entry.
+__global__ void __launch_bounds__(256) page_rows_kernel(AttnParams P, int32_t* rows, int64_t total) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= total) return;
+  const int64_t bt = i / P.k;
+  const int b = static_cast<int>(bt / P.T), t = static_cast<int>(bt % P.T);
+  const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
+  int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
+  if (n > P.cap) n = P.cap;
+  const int64_t id = P.idx[i];
+  rows[i] = static_cast<int32_t>(id >= 0 && id < n ? entry_row(P.pg, P.cap, b, id) : -1);
 }
 
 bool mfma_shape(int H, int d_nope, int d_rope, int q_dt, int o_dt, int nope_dt, int rope_dt) {
@@ -128,12 +147,39 @@ size_t mfma_attn_ws_bytes(const csa_attn_desc* d, int op, int B, int, int64_t, i
   if (op != CSA_OP_SPARSE_ATTN_DECODE && op != CSA_OP_DENSE_ATTN_DECODE) return 0;
   if (!mfma_shape(d->n_heads, d->d_nope, d->d_rope, d->q_dtype, d->o_dtype, d->nope_dtype, d->rope_dtype)) return 0;
   const bool dense = op == CSA_OP_DENSE_ATTN_DECODE;
-  return part_bytes(B, decode_splits(dense, dense ? dense_span(d->capacity, d->window) : k));
+  return round256(part_bytes(B, decode_splits(dense, dense ? dense_span(d->capacity, d->window) : k)));
 }
 
-int launch_mfma_attn(const AttnParams& P, int op, int B, hipStream_t s) {
+size_t page_list_bytes(const csa_attn_desc* d, int op, int B, int T, int k) {
+  if (d->page_size == 0 || (op != CSA_OP_SPARSE_ATTN_PREFILL && op != CSA_OP_SPARSE_ATTN_DECODE)) return 0;
+  if (!mfma_shape(d->n_heads, d->d_nope, d->d_rope, d->q_dtype, d->o_dtype, d->nope_dtype, d->rope_dtype)) return 0;
+  const int rows = op == CSA_OP_SPARSE_ATTN_DECODE ? 1 : T;
+  return round256(static_cast<size_t>(B) * rows * k * sizeof(int32_t));
+}
+
+int launch_mfma_attn(const AttnParams& P0, int op, int B, hipStream_t s) {
   const bool dense = op == CSA_OP_DENSE_ATTN_PREFILL || op == CSA_OP_DENSE_ATTN_DECODE;
   const bool decode = op == CSA_OP_SPARSE_ATTN_DECODE || op == CSA_OP_DENSE_ATTN_DECODE;
+  AttnParams P = P0;
+  size_t part_room = 0;  // workspace bytes ahead of the page list: the decode split partials
+  if (decode) {
+    const int64_t count = dense ? dense_span(P.cap, P.window) : P.k;
+    const int splits = decode_splits(dense, count);
+    part_room = splits > 1 ? round256(part_bytes(B, splits)) : 0;
+  }
+  if (!dense && P.pg.table && !P.list_rows) {
+    // paged sparse: the list turned into pool rows in the workspace, after the partials
+    const int64_t total = static_cast<int64_t>(B) * P.T * P.k;
+    const size_t need = part_room + static_cast<size_t>(total) * sizeof(int32_t);
+    if (!P.ws || P.ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace too small for the paged list");
+    int32_t* rows = reinterpret_cast<int32_t*>(static_cast<char*>(P.ws) + part_room);
+    hipLaunchKernelGGL(page_rows_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, P, rows,
+                       total);
+    int st = check_launch("page_rows_kernel");
+    if (st != CSA_OK) return st;
+    P.idx = rows;
+    P.list_rows = true;
+  }
   if (!decode) {
     const int64_t per = dense ? P.cap : P.k;
     launch_attn_bf16(P, dense, B, s, 1, per, nullptr);

@@ -170,4 +170,37 @@ __device__ __forceinline__ float block_sum(float v, float* red) {
   return r;
 }
 
+
+// ---------------------------------------------------------------------------
+// entry placement: contiguous or paged caches
+// ---------------------------------------------------------------------------
+// Where entry s of sequence b lives.  Contiguous caches keep sequence b at
+// rows [b*cap, (b+1)*cap).  Paged caches keep it at row pg*2^shift + s mod
+// 2^shift of a pool of `pool` pages, pg = table[b][s >> shift]; a table
+// entry outside [0, pool) maps to row -1 (not written; readers clamp it).
+struct Pages {
+  const int32_t* table;  // [B][tps] when paged, NULL when contiguous
+  int shift;             // log2 entries per page
+  int64_t tps;           // table entries per sequence (cap >> shift)
+  int64_t pool;          // pages in the pool
+};
+
+__device__ __forceinline__ int64_t entry_row(const Pages& pg, int64_t cap, int b, int64_t s) {
+  if (!pg.table) return static_cast<int64_t>(b) * cap + s;
+  const int64_t p = pg.table[static_cast<int64_t>(b) * pg.tps + (s >> pg.shift)];
+  if (p < 0 || p >= pg.pool) return -1;
+  return (p << pg.shift) | (s & ((int64_t(1) << pg.shift) - 1));
+}
+
+// Rows a cache's buffers hold: B*cap contiguous, pool*2^shift paged.
+inline int64_t cache_rows(const Pages& pg, int B, int64_t cap) {
+  return pg.table ? (pg.pool << pg.shift) : static_cast<int64_t>(B) * cap;
+}
+
+// host: checks the paging fields of a descriptor against the cache's block
+// table and fills `out`.  page_size 0: contiguous (table must be NULL).
+int make_pages(int32_t page_size, int64_t pool_pages, int64_t capacity, const int32_t* table, Pages* out);
+// host: the paging fields alone (workspace queries, which see no buffers)
+int check_paging(int32_t page_size, int64_t pool_pages, int64_t capacity);
+
 }  // namespace csa

@@ -89,7 +89,9 @@ __device__ void finalize_entry(const CompressParams& P, float* buf, float* red, 
     buf[P.d_nope + 2 * p + 1] = static_cast<float>(x0 * s + x1 * co);
   }
   __syncthreads();
-  const size_t e = static_cast<size_t>(b) * P.cap + i;
+  const int64_t er = entry_row(P.pg, P.cap, b, i);  // uniform over the workgroup
+  if (er < 0) return;                                // page outside the pool: not stored
+  const size_t e = static_cast<size_t>(er);
   switch (P.nope_dt) {
     case CSA_F32: {
       float* dst = static_cast<float*>(P.nope) + e * P.d_nope;
@@ -283,17 +285,20 @@ __global__ void __launch_bounds__(256, 2) compress_prefill_wave_kernel(CompressP
     x[8] = static_cast<float>(x0 * co - x1 * sn);
     x[9] = static_cast<float>(x0 * sn + x1 * co);
   }
-  const size_t e = static_cast<size_t>(b) * P.cap + i;
+  // the entry's row; lanes of an entry whose page lies outside the pool store nothing
+  const int64_t er = ok ? entry_row(P.pg, P.cap, b, i) : -1;
+  const bool sg = hg && er >= 0, sp = hp && er >= 0, so = ok && er >= 0;
+  const size_t e = er >= 0 ? static_cast<size_t>(er) : 0;
   switch (P.nope_dt) {
     case CSA_F32:
-      if (hg) {
+      if (sg) {
         float* dst = static_cast<float*>(P.nope) + e * P.d_nope + jg;
         *reinterpret_cast<f32x4*>(dst) = f32x4{x[0], x[1], x[2], x[3]};
         *reinterpret_cast<f32x4*>(dst + 4) = f32x4{x[4], x[5], x[6], x[7]};
       }
       break;
     case CSA_BF16:
-      if (hg) {
+      if (sg) {
         u32x4 o;
 #pragma unroll
         for (int c = 0; c < 4; ++c)
@@ -308,7 +313,7 @@ __global__ void __launch_bounds__(256, 2) compress_prefill_wave_kernel(CompressP
         for (int c = 0; c < 8; ++c) am = fmaxf(am, fabsf(x[c]));
       for (int o = 1; o < lpe; o <<= 1) am = fmaxf(am, __shfl_xor(am, o));  // over the entry's lanes
       const float s = am > 0.0f ? am / 448.0f : 1.0f;
-      if (hg) {
+      if (sg) {
         uint32_t w0 = 0u, w1 = 0u;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -317,7 +322,7 @@ __global__ void __launch_bounds__(256, 2) compress_prefill_wave_kernel(CompressP
         }
         *reinterpret_cast<u32x2*>(static_cast<uint8_t*>(P.nope) + e * P.d_nope + jg) = u32x2{w0, w1};
       }
-      if (ok && ll == 0) static_cast<float*>(P.scale)[e] = s;
+      if (so && ll == 0) static_cast<float*>(P.scale)[e] = s;
       break;
     }
     case CSA_MXFP4: {
@@ -330,7 +335,7 @@ __global__ void __launch_bounds__(256, 2) compress_prefill_wave_kernel(CompressP
       am = fmaxf(am, __shfl_xor(am, 2));
       const int ex = mx_exponent(am);
       const float inv = exp2i(-ex);
-      if (hg) {
+      if (sg) {
         uint32_t wd = 0u;
 #pragma unroll
         for (int c = 0; c < 8; ++c) wd |= f32_to_e2m1(x[c] * inv) << (4 * c);
@@ -340,7 +345,7 @@ __global__ void __launch_bounds__(256, 2) compress_prefill_wave_kernel(CompressP
       break;
     }
   }
-  if (hp) {
+  if (sp) {
     if (P.rope_dt == CSA_F32) {
       *reinterpret_cast<f32x2*>(static_cast<float*>(P.rope) + e * P.d_rope + 2 * ll) = f32x2{x[8], x[9]};
     } else {
@@ -458,8 +463,9 @@ static int validate_cache_desc(const csa_cache_desc* d) {
   if (d->nope_dtype == CSA_FP8E4M3 && d->d_nope < 1) return fail(CSA_ERR_INVALID_ARG, "FP8 entries need d_nope >= 1");
   if (d->d_rope > 0 && d->rope_dtype != CSA_F32 && d->rope_dtype != CSA_BF16)
     return fail(CSA_ERR_UNSUPPORTED, "rope_dtype must be F32 or BF16");
-  if (d->reserved != 0) return fail(CSA_ERR_INVALID_ARG, "reserved field must be 0");
   if (d->capacity < 1) return fail(CSA_ERR_INVALID_ARG, "capacity must be >= 1");
+  int st;
+  if ((st = check_paging(d->page_size, d->pool_pages, d->capacity)) != CSA_OK) return st;
   if (!(d->rope_base > 0.0)) return fail(CSA_ERR_INVALID_ARG, "rope_base must be > 0");
   return CSA_OK;
 }
@@ -472,7 +478,8 @@ static int validate_cache(const csa_cache_desc* d, const csa_cache* c) {
   if (d->d_rope > 0 && !c->rope) return fail(CSA_ERR_INVALID_ARG, "cache rope is NULL");
   if (!aligned16(c->nope) || !aligned16(c->ring) || !aligned16(c->scale) || !aligned16(c->rope))
     return fail(CSA_ERR_ALIGNMENT, "cache buffers must be 16-byte aligned");
-  return CSA_OK;
+  Pages pg;
+  return make_pages(d->page_size, d->pool_pages, d->capacity, c->block_table, &pg);
 }
 
 static CompressParams make_params(const csa_cache_desc* d, const csa_cache* c, const void* a,
@@ -493,6 +500,7 @@ static CompressParams make_params(const csa_cache_desc* d, const csa_cache* c, c
   P.cap = d->capacity;
   P.a = a; P.b = b; P.za = za; P.zb = zb; P.Ba = Ba; P.Bb = Bb;
   P.nope = c->nope; P.scale = c->scale; P.rope = c->rope; P.ring = c->ring;
+  make_pages(d->page_size, d->pool_pages, d->capacity, c->block_table, &P.pg);  // validated before
   return P;
 }
 

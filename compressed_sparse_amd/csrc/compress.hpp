@@ -19,6 +19,7 @@ struct CompressParams {
   const float *Ba, *Bb;
   void *nope, *scale, *rope;
   float* ring;
+  Pages pg;  // entry placement (contiguous or paged)
 };
 
 enum { RING_A = 0, RING_ZA = 1, RING_B = 2, RING_ZB = 3 };

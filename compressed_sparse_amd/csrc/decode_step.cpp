@@ -27,6 +27,9 @@ int check_consistent(const csa_cache_desc* kvd, const csa_cache_desc* kd, const 
     return fail(CSA_ERR_INVALID_ARG, "KV cache and attention descriptors disagree");
   if (kd->d_nope != id->dim || kd->d_rope != 0 || kd->nope_dtype != id->key_dtype)
     return fail(CSA_ERR_INVALID_ARG, "indexer-key cache and indexer descriptors disagree");
+  if (kvd->page_size != ad->page_size || kvd->pool_pages != ad->pool_pages || kd->page_size != id->page_size ||
+      kd->pool_pages != id->pool_pages)
+    return fail(CSA_ERR_INVALID_ARG, "cache and reader paging (page_size, pool_pages) differ");
   return CSA_OK;
 }
 

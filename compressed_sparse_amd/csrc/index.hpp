@@ -35,6 +35,7 @@ struct IndexParams {
   // MXFP4 scan: per query row the A operand of the scaled MFMA, 64 lanes x
   // 16 bytes of E2M1 codes, then 64 int32 E8M0 scales (QPACK_ROW_BYTES)
   uint8_t* qpack;
+  Pages pg;  // key placement (contiguous or paged)
 };
 
 constexpr int HIST_BITS = 11;
@@ -42,6 +43,18 @@ constexpr int HIST_BINS = 1 << HIST_BITS;
 constexpr int CAND_CAP = 8192;    // candidates one row may keep in LDS
 constexpr int CAND_CHUNK = 4096;  // entries per candidate workgroup
 constexpr int NCH_MAX = 4096;     // chunks per row the final pass can order (cap <= 16M entries)
+
+// First row of a key block that starts at entry s (wave-uniform) of
+// sequence b and lies inside one page: contiguous keys are rows b*cap + s;
+// paged ones take the page from one scalar table load (a page outside the
+// pool reads as page 0).
+__device__ __forceinline__ int64_t key_block_row(const IndexParams& P, int b, int64_t s) {
+  if (!P.pg.table) return static_cast<int64_t>(b) * P.cap + s;
+  typedef const __attribute__((address_space(4))) int32_t ctab_t;
+  const int64_t ix = static_cast<int64_t>(b) * P.pg.tps + (s >> P.pg.shift);
+  const int64_t pg = reinterpret_cast<ctab_t*>(reinterpret_cast<uintptr_t>(P.pg.table))[ix];
+  return ((pg >= 0 && pg < P.pg.pool ? pg : 0) << P.pg.shift) | (s & ((int64_t(1) << P.pg.shift) - 1));
+}
 
 // Order-preserving key of a score: larger score -> larger key; -0 == +0.
 __device__ __forceinline__ uint32_t score_key(float x) {

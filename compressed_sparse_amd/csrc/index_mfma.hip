@@ -640,7 +640,7 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   // this chunk's top-11-bit key histogram (decode top-k), one per wave so
   // that no barrier separates the clearing from the counting
   __shared__ int lhist_w[4][HIST_BINS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z, t = blockIdx.y;
   const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
   int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
@@ -660,13 +660,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   float wv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) wv[v] = P.w[row * HI + g * 4 + v];
-  const size_t seq = static_cast<size_t>(b) * P.cap;
   const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);  // entries of this chunk
-  // wave-uniform bases of this chunk; per-lane offsets are 32-bit
+  // wave-uniform bases of this chunk (of each key block); per-lane offsets are 32-bit
   float* wsb = P.ws + row * P.n_stride + c0;
   float* sob = P.scores_out ? P.scores_out + row * P.cap + c0 : nullptr;
-  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + (seq + c0) * (KFMT == CSA_BF16 ? 2 * DI : DI);
-  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * 4;
+  constexpr int KROW = KFMT == CSA_BF16 ? 2 * DI : DI;  // bytes per key row
+  const uint8_t* knope = static_cast<const uint8_t*>(P.knope);
+  const uint8_t* kscale = static_cast<const uint8_t*>(P.kscale);
   int* lhist = lhist_w[w];
   if (P.ghist) clear_hist(lhist, lane);
   // each wave: 16-entry column blocks w, w+4, ...  A batch of NB blocks is
@@ -674,16 +674,22 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   // batch is widened, multiplied and reduced over heads (two register sets,
   // used in turn).
   constexpr int NB = 4;
+  // Block j of a batch: the 16 entries from e0 + 64 j, clamped into the
+  // chunk (a block past its end re-reads the chunk's last block; those
+  // scores are dropped).  A block never crosses a page.
   auto load = [&](int e0, u32x4 (&ra)[NB], u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int s = min(e0 + 64 * j + (lane & 15), cn - 1);
+      const int blk = min(e0 + 64 * j, (cn - 1) & ~15);
+      const int64_t r0 = key_block_row(P, b, c0 + blk);
+      const uint8_t* kb = knope + r0 * KROW;
+      const int s = min(blk + (lane & 15), cn - 1) - blk;
       if constexpr (KFMT == CSA_BF16) {
         ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32));
         rb[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32 + 16));
       } else {
         ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * DI + g * 16));
-        rs[j] = *reinterpret_cast<const uint32_t*>(sb + static_cast<uint32_t>(s * 4));
+        rs[j] = *reinterpret_cast<const uint32_t*>(kscale + r0 * 4 + static_cast<uint32_t>(s * 4));
       }
     }
   };
@@ -786,7 +792,7 @@ constexpr int MX_PAIRS = SCAN_CHUNK / 256;  // block pairs per wave
 
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) index_scan_mx_kernel(IndexParams P) {
   __shared__ int lhist_w[4][HIST_BINS];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.z, t = blockIdx.y;
   const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
   int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
@@ -795,20 +801,24 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   if (c0 >= n) return;
   const size_t row = static_cast<size_t>(b) * P.T + t;
   const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);
-  const size_t seq = static_cast<size_t>(b) * P.cap;
-  const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + (seq + c0) * (DI / 2);
-  const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * (DI / 32);
-  // every key load first (clamped to the last entry: branch-free)
+  // every key load first (a 64-entry block pair past the chunk's end
+  // re-reads its last pair, branch-free; those scores are dropped).  A pair
+  // never crosses a page.
   u32x4 kc[MX_PAIRS][2];
   uint32_t ks[MX_PAIRS][2];
 #pragma unroll
-  for (int p = 0; p < MX_PAIRS; ++p)
+  for (int p = 0; p < MX_PAIRS; ++p) {
+    const int blk = min(64 * (w + 4 * p), (cn - 1) & ~63);
+    const int64_t r0 = key_block_row(P, b, c0 + blk);
+    const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + r0 * (DI / 2);
+    const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + r0 * (DI / 32);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int s = min(64 * (w + 4 * p) + 32 * j + (lane & 31), cn - 1);
+      const int s = min(blk + 32 * j + (lane & 31), cn - 1) - blk;
       kc[p][j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * (DI / 2) + 16 * (lane >> 5)));
       ks[p][j] = sb[static_cast<uint32_t>(s * (DI / 32) + (lane >> 5))];
     }
+  }
   const uint8_t* qp = P.qpack + row * QPACK_ROW_BYTES;
   const u32x4 qc = reinterpret_cast<const u32x4*>(qp)[lane];
   const int qs = reinterpret_cast<const int*>(qp + 64 * 16)[lane];

@@ -77,7 +77,8 @@ __global__ void __launch_bounds__(256) index_scores_generic(IndexParams P) {
   load_index_query(P, b, t, q, w);
   const int64_t s = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (s >= n) return;
-  const size_t e = static_cast<size_t>(b) * P.cap + s;
+  const int64_t er = entry_row(P.pg, P.cap, b, s);
+  const size_t e = er >= 0 ? static_cast<size_t>(er) : 0;  // a page outside the pool reads as row 0
   const float ksc = P.key_dt == CSA_FP8E4M3 ? static_cast<const float*>(P.kscale)[e] : 1.0f;
   float acc = 0.0f;
   for (int h = 0; h < P.H; ++h) {
@@ -495,8 +496,7 @@ static int validate_index_desc(const csa_index_desc* d) {
   if (d->score_dtype != CSA_F32 && d->score_dtype != CSA_BF16) return fail(CSA_ERR_UNSUPPORTED, "score_dtype must be F32 or BF16");
   if (d->m < 1 || d->m > 256) return fail(CSA_ERR_INVALID_ARG, "m must be in 1..256");
   if (d->capacity < 1 || d->capacity > (int64_t(1) << 31) - 1) return fail(CSA_ERR_INVALID_ARG, "capacity must be in 1..2^31-1");
-  if (d->reserved != 0) return fail(CSA_ERR_INVALID_ARG, "reserved field must be 0");
-  return CSA_OK;
+  return check_paging(d->page_size, d->pool_pages, d->capacity);
 }
 
 static int64_t stride_for(int64_t n) { return ((n + 63) / 64) * 64; }
@@ -548,7 +548,8 @@ static int common_index_checks(const csa_index_desc* d, int B, const void* qI, c
   if (!aligned16(qI) || !aligned16(w) || !aligned16(keys->nope) || !aligned16(keys->scale) ||
       !aligned16(idx) || !aligned16(scores) || !aligned16(ws))
     return fail(CSA_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
-  return CSA_OK;
+  Pages pg;
+  return make_pages(d->page_size, d->pool_pages, d->capacity, keys->block_table, &pg);
 }
 
 static IndexParams make_index_params(const csa_index_desc* d, const void* qI, const float* w,
@@ -559,6 +560,7 @@ static IndexParams make_index_params(const csa_index_desc* d, const void* qI, co
   P.qI = qI; P.w = w; P.knope = keys->nope; P.kscale = keys->scale;
   P.k = k; P.idx = idx; P.scores_out = scores;
   P.ws = static_cast<float*>(ws);
+  make_pages(d->page_size, d->pool_pages, d->capacity, keys->block_table, &P.pg);  // validated before
   return P;
 }
 
@@ -574,6 +576,7 @@ extern "C" int csa_index_topk_prefill(const csa_index_desc* desc, int B, int T, 
   if (st != CSA_OK) return st;
   if (T < 0 || T > 65535 * 16 || pos0 < 0) return fail(CSA_ERR_INVALID_ARG, "T must be in 0..1048560, pos0 >= 0");
   if (T > 65535) return fail(CSA_ERR_UNSUPPORTED, "T > 65535 per call: split the prefill");
+  if (desc->page_size != 0) return fail(CSA_ERR_UNSUPPORTED, "paged key caches are read by the decode indexer only");
   if (ws_bytes < index_ws_bytes(desc, CSA_OP_INDEX_TOPK_PREFILL, B, T, pos0))
     return fail(CSA_ERR_WORKSPACE, "workspace too small");
   if (B == 0 || T == 0) return CSA_OK;

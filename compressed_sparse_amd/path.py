@@ -25,21 +25,65 @@ def _stack(tensors):
     return torch.stack(tensors, 0).contiguous()
 
 
-class CsaLayer:
-    """seq_ids: the seeded sequence held in each batch slot (default 0..B-1)."""
+def block_tables(entries, page_size, capacity, seed=0, device="cuda", share=None):
+    """Block tables of B sequences over one page pool: sequence b gets
+    ceil(entries[b] / page_size) pages, in a seeded random order of the pool;
+    its other logical pages are -1.  share = (b0, b1, n): sequence b1's first
+    n pages are sequence b0's (a shared prefix).  Returns (int32 table
+    [B][capacity / page_size], pool_pages)."""
+    assert capacity % page_size == 0
+    tps = capacity // page_size
+    need = [min(tps, -(-int(e) // page_size)) for e in entries]
+    own = list(need)
+    if share is not None:
+        b0, b1, n = share
+        assert n <= min(need[b0], need[b1])
+        own[b1] -= n
+    pool = max(1, sum(own))
+    g = torch.Generator().manual_seed(1000 + seed)
+    perm = torch.randperm(pool, generator=g).to(torch.int32)
+    table = torch.full((len(entries), tps), -1, dtype=torch.int32)
+    at = 0
+    for b, nb in enumerate(need):
+        if share is not None and b == share[1]:
+            n = share[2]
+            table[b, :n] = table[share[0], :n]
+            table[b, n:nb] = perm[at:at + nb - n]
+            at += nb - n
+        else:
+            table[b, :nb] = perm[at:at + nb]
+            at += nb
+    return table.to(device), pool
 
-    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None):
+
+def _caches(desc_fn, B, device, page_size, block_table, pool_pages, capacity):
+    """cache_desc arguments -> KVCache, contiguous or paged."""
+    if page_size:
+        return cb.KVCache(desc_fn(page_size=page_size, pool_pages=pool_pages), B, device, block_table)
+    return cb.KVCache(desc_fn(), B, device)
+
+
+class CsaLayer:
+    """seq_ids: the seeded sequence held in each batch slot (default 0..B-1).
+    page_size > 0: paged KV and indexer-key caches over pools of pool_pages
+    pages, both addressed by block_table (the same logical entries)."""
+
+    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None, page_size=0,
+                 block_table=None, pool_pages=0):
         self.w, self.B, self.cap, self.device, self.seed = w, B, capacity, device, seed
         self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
         assert len(self.seq_ids) == B
         act = w.act_dtype
-        self.kv = cb.KVCache(cb.cache_desc(w.m, w.overlap, w.d_nope, w.d_rope, act, w.nope_fmt, w.rope_fmt,
-                                           capacity, w.rope_base), B, device)
-        self.keys = cb.KVCache(cb.cache_desc(w.m, w.overlap, w.idx_dim, 0, act, w.key_fmt, "f32", capacity), B,
-                               device)
-        self.idesc = cb.index_desc(w.idx_heads, w.idx_dim, act, w.qk_fmt, w.key_fmt, w.score_fmt, w.m, capacity)
+        pg = dict(page_size=page_size, pool_pages=pool_pages) if page_size else {}
+        self.kv = _caches(lambda **k: cb.cache_desc(w.m, w.overlap, w.d_nope, w.d_rope, act, w.nope_fmt, w.rope_fmt,
+                                                    capacity, w.rope_base, **k),
+                          B, device, page_size, block_table, pool_pages, capacity)
+        self.keys = _caches(lambda **k: cb.cache_desc(w.m, w.overlap, w.idx_dim, 0, act, w.key_fmt, "f32", capacity,
+                                                      **k),
+                            B, device, page_size, block_table, pool_pages, capacity)
+        self.idesc = cb.index_desc(w.idx_heads, w.idx_dim, act, w.qk_fmt, w.key_fmt, w.score_fmt, w.m, capacity, **pg)
         self.adesc = cb.attn_desc(w.heads, w.d_nope, w.d_rope, act, w.out_dtype, w.nope_fmt, w.rope_fmt, w.m,
-                                  capacity, w.rope_base)
+                                  capacity, w.rope_base, **pg)
         self.prm = synth.compressor_params(w, seed, device)
         self.iws = None
         self.aws = None
@@ -59,6 +103,21 @@ class CsaLayer:
             cb.compress_prefill(self.kv, c * chunk, x["a"], x["za"], p["Ba"], x.get("b"), x.get("zb"), p.get("Bb"))
             cb.compress_prefill(self.keys, c * chunk, x["ka"], x["kza"], p["kBa"], x.get("kb"), x.get("kzb"),
                                 p.get("kBb"))
+
+    def prefill_contexts(self, lengths, chunk=None):
+        """Mixed contexts: tokens [0, lengths[b]) of sequence b, one sequence
+        per call (its ring and block-table row)."""
+        chunk = chunk or self.w.chunk
+        p = self.prm
+        for b, (sid, T) in enumerate(zip(self.seq_ids, lengths)):
+            kv, keys = self.kv.seq_view(b), self.keys.seq_view(b)
+            for c in range(math.ceil(T / chunk)):
+                n = min(chunk, T - c * chunk)
+                t = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
+                x = {k: v[:n][None].contiguous() for k, v in t.items()}
+                cb.compress_prefill(kv, c * chunk, x["a"], x["za"], p["Ba"], x.get("b"), x.get("zb"), p.get("Bb"))
+                cb.compress_prefill(keys, c * chunk, x["ka"], x["kza"], p["kBa"], x.get("kb"), x.get("kzb"),
+                                    p.get("kBb"))
 
     # -- decode -----------------------------------------------------------
     def decode_inputs(self, positions, chunk=None):
@@ -124,14 +183,17 @@ class CsaLayer:
 class HcaLayer:
     """seq_ids: the seeded sequence held in each batch slot (default 0..B-1)."""
 
-    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None):
+    def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None, page_size=0,
+                 block_table=None, pool_pages=0):
         self.w, self.B, self.cap, self.device, self.seed = w, B, capacity, device, seed
         self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
         assert len(self.seq_ids) == B
-        self.kv = cb.KVCache(cb.cache_desc(w.m, False, w.d_nope, w.d_rope, w.act_dtype, w.nope_fmt, w.rope_fmt,
-                                           capacity, w.rope_base), B, device)
+        pg = dict(page_size=page_size, pool_pages=pool_pages) if page_size else {}
+        self.kv = _caches(lambda **k: cb.cache_desc(w.m, False, w.d_nope, w.d_rope, w.act_dtype, w.nope_fmt,
+                                                    w.rope_fmt, capacity, w.rope_base, **k),
+                          B, device, page_size, block_table, pool_pages, capacity)
         self.adesc = cb.attn_desc(w.heads, w.d_nope, w.d_rope, w.act_dtype, w.out_dtype, w.nope_fmt, w.rope_fmt,
-                                  w.m, capacity, w.rope_base)
+                                  w.m, capacity, w.rope_base, **pg)
         self.prm = synth.compressor_params(w, seed, device)
         self.aws = None
 
@@ -148,6 +210,17 @@ class HcaLayer:
         chunk = chunk or self.w.chunk or T
         for c in range(math.ceil(T / chunk)):
             self.compress_chunk(c, chunk, min(chunk, T - c * chunk))
+
+    def prefill_contexts(self, lengths, chunk=None):
+        """Mixed contexts: tokens [0, lengths[b]) of sequence b, one sequence per call."""
+        chunk = chunk or self.w.chunk
+        for b, (sid, T) in enumerate(zip(self.seq_ids, lengths)):
+            kv = self.kv.seq_view(b)
+            for c in range(math.ceil(T / chunk)):
+                n = min(chunk, T - c * chunk)
+                t = synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device)
+                cb.compress_prefill(kv, c * chunk, t["a"][:n][None].contiguous(), t["za"][:n][None].contiguous(),
+                                    self.prm["Ba"])
 
     def prefill_chunk_attention(self, c, chunk, q, o, lse=None):
         """Dense attention of the queries at positions [c*chunk, c*chunk + T)."""

@@ -153,9 +153,22 @@ PAIR_CSA_DECODE_B4_1M = Workload(
 PAIR_HCA_DECODE_B4_1M = dataclasses.replace(
     HCA_DECODE_B16_1M, name="pair_hca_decode_b4_ctx1M", batch=4)
 
+# Paged, variable-length CSA decode (the serving shape): the B = 32 FP8
+# workload's formats, each sequence with its own context length (mixed_lengths:
+# log-uniform over 8K..256K tokens), caches in 64-entry pages of one pool.
+PAGED_CSA_DECODE_B32_MIXED = dataclasses.replace(
+    CSA_DECODE_B32_128K, name="paged_csa_decode_b32_ctx8K-256K_page64")
+
 WORKLOADS = {w.name: w for w in (TINY_CSA_PREFILL_FP32, CSA_PREFILL_BF16_32K, CSA_DECODE_B32_128K,
                                  HCA_PREFILL_1M, HCA_DECODE_B16_1M, PAIR_CSA_DECODE_B4_1M,
-                                 PAIR_HCA_DECODE_B4_1M)}
+                                 PAIR_HCA_DECODE_B4_1M, PAGED_CSA_DECODE_B32_MIXED)}
+
+
+def mixed_lengths(B, lo_log2, hi_log2, seed=0):
+    """B context lengths log-uniform over [2^lo_log2, 2^hi_log2) tokens, seeded."""
+    g = torch.Generator().manual_seed(stream_key(seed, "ctx.len"))
+    u = torch.rand(B, generator=g, dtype=torch.float64)
+    return [int(2.0 ** (lo_log2 + (hi_log2 - lo_log2) * float(x))) for x in u]
 
 TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
 

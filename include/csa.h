@@ -43,7 +43,7 @@
 extern "C" {
 #endif
 
-#define CSA_ABI_VERSION 2
+#define CSA_ABI_VERSION 3
 
 /* Status codes. */
 enum {
@@ -76,26 +76,43 @@ typedef struct csa_cache_desc {
   int32_t in_dtype;   /* a, b, za, zb element type: CSA_F32 or CSA_BF16 */
   int32_t nope_dtype; /* CSA_F32, CSA_BF16, CSA_FP8E4M3, or CSA_MXFP4 (indexer keys only) */
   int32_t rope_dtype; /* CSA_F32 or CSA_BF16 */
-  int32_t reserved;   /* must be 0 */
+  int32_t page_size;  /* 0: contiguous caches (sequence b owns rows [b*capacity, (b+1)*capacity));
+                         else entries per page, a power of two in 64..65536, and the cache is
+                         paged (csa_cache.block_table) */
   double rope_base;   /* RoPE base (10000) */
-  int64_t capacity;   /* entries per sequence */
+  int64_t capacity;   /* entries per sequence (logical; a multiple of page_size when paged) */
+  int64_t pool_pages; /* paged: physical pages in the pool; 0 when contiguous */
 } csa_cache_desc;
 
-/* Device buffers of a compressed cache for B sequences (sequence stride =
- * capacity entries).  c = d_nope + d_rope.
- *   nope : [B][capacity][d_nope] elements; MXFP4: [B][capacity][d_nope/2] bytes
- *   scale: FP8E4M3: float [B][capacity]; MXFP4: uint8 [B][capacity][d_nope/32];
+/* Device buffers of a compressed cache for B sequences.  c = d_nope + d_rope.
+ * Rows: contiguous caches hold entry s of sequence b in row b*capacity + s
+ * (ROWS = B*capacity); paged caches hold it in row
+ * block_table[b][s / page_size] * page_size + s % page_size of a pool shared
+ * by the batch (ROWS = pool_pages*page_size).  [百万令牌的智慧觉醒] §🏗️
+ * (heterogeneous KV cache of the serving framework), [CSA/HCA 混注意力]
+ * 共享前缀场景的理复用 (compressed entries reused on a shared prefix: two
+ * sequences' tables may name the same pages for a common, complete prefix).
+ *   nope : [ROWS][d_nope] elements; MXFP4: [ROWS][d_nope/2] bytes
+ *   scale: FP8E4M3: float [ROWS]; MXFP4: uint8 [ROWS][d_nope/32];
  *          otherwise unused (may be NULL)
- *   rope : [B][capacity][d_rope] elements of rope_dtype (NULL when d_rope = 0)
+ *   rope : [ROWS][d_rope] elements of rope_dtype (NULL when d_rope = 0)
  *   ring : float [B][R][NT][c] staging rows of the most recent tokens,
  *          R = overlap ? 2m : m, NT = overlap ? 4 (a, za, b, zb) : 2 (a, za);
  *          token p lives in slot p mod R.  The compressor reads it for entries
- *          that need tokens before the current call and refreshes it. */
+ *          that need tokens before the current call and refreshes it.  Never
+ *          paged.
+ *   block_table: device int32 [B][capacity/page_size] when paged, NULL when
+ *          contiguous.  Entries must lie in [0, pool_pages); the kernels
+ *          never touch memory outside the pool: an entry whose page is out of
+ *          range is not written and reads as some row of the pool (its
+ *          results are then unspecified).  Pages written in one call (the
+ *          compressor's) must not be shared with another sequence of it. */
 typedef struct csa_cache {
   void* nope;
   void* scale;
   void* rope;
   float* ring;
+  const int32_t* block_table;
 } csa_cache;
 
 /* Lightning-indexer configuration.  [CSA/HCA 混注意力] §1.4 LIGHTNING INDEXER
@@ -110,8 +127,9 @@ typedef struct csa_index_desc {
   int32_t key_dtype;   /* key cache format: CSA_F32, CSA_BF16, CSA_FP8E4M3, CSA_MXFP4 */
   int32_t score_dtype; /* CSA_F32, or CSA_BF16 (scores rounded FP32 -> BF16 before selection) */
   int32_t m;           /* tokens per key entry (visibility) */
-  int32_t reserved;    /* must be 0 */
+  int32_t page_size;   /* key cache paging, as csa_cache_desc.page_size (decode only) */
   int64_t capacity;    /* key entries per sequence */
+  int64_t pool_pages;  /* paged: pages in the key pool; 0 when contiguous */
 } csa_index_desc;
 
 /* Attention configuration (CSA sparse and HCA dense). */
@@ -131,6 +149,9 @@ typedef struct csa_attn_desc {
   int32_t qk_mode;    /* must be 0: QK in the query's own format */
   double rope_base;
   int64_t capacity;   /* entries per sequence */
+  int32_t page_size;  /* KV cache paging, as csa_cache_desc.page_size */
+  int32_t reserved;   /* must be 0 */
+  int64_t pool_pages; /* paged: pages in the KV pool; 0 when contiguous */
 } csa_attn_desc;
 
 /* ---- compressor ---------------------------------------------------------
@@ -181,7 +202,10 @@ int csa_compress_decode(const csa_cache_desc* desc, int B, const int64_t* pos,
  *   idx   : device int32 [B][T][k]
  *   scores: device float [B][T][capacity] or NULL; when given, receives I
  *           (as used for selection) for s < n, the rest untouched
- *   ws    : device workspace of csa_workspace_bytes(CSA_OP_INDEX_TOPK_*) bytes */
+ *   ws    : device workspace of csa_workspace_bytes(CSA_OP_INDEX_TOPK_*) bytes
+ * Paged key caches (desc->page_size > 0) are read by csa_index_topk_decode;
+ * csa_index_topk_prefill returns CSA_ERR_UNSUPPORTED for them.  A key block
+ * of the scan (16 entries, 64 for MXFP4) never crosses a page. */
 int csa_index_topk_prefill(const csa_index_desc* desc, int B, int T, int64_t pos0,
                            const void* qI, const float* w, const csa_cache* keys, int k,
                            int32_t* idx, float* scores, void* ws, size_t ws_bytes,
@@ -216,7 +240,12 @@ int csa_index_topk_decode(const csa_index_desc* desc, int B, const int64_t* pos,
  * or FP8 dims (the matrix-core path) each cache buffer of one sequence must
  * stay below 2^31 bytes: capacity <= 2^21 (BF16 non-RoPE rows) or 2^22 (FP8
  * rows), CSA_ERR_UNSUPPORTED otherwise.  Decode workspaces hold per-sequence
- * split partials: csa_workspace_bytes grows linearly with B. */
+ * split partials: csa_workspace_bytes grows linearly with B.
+ * Paged KV caches (desc->page_size > 0, kv->block_table): the same results
+ * as the contiguous layout holding the same entries.  The 2^31-byte limit
+ * then applies to the pool (pool_pages*page_size rows), and the sparse calls
+ * first turn their lists into pool rows inside the workspace
+ * (csa_workspace_bytes includes B*T*k int32 for it). */
 int csa_sparse_attn_prefill(const csa_attn_desc* desc, int B, int T, int64_t pos0,
                             const void* q, const csa_cache* kv, const int32_t* idx, int k,
                             float softmax_scale, void* o, float* lse, void* ws,

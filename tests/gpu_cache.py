@@ -15,23 +15,32 @@ from oracle import formats as F
 from tests.helpers import lse_err, max_rel_rows
 
 
-def _rows(t, b, ids):
-    ids_t = torch.as_tensor(np.asarray(ids, dtype=np.int64), device=t.device)
-    return t[b].index_select(0, ids_t)
+def _rows(kv, t, b, ids):
+    """Rows `ids` of sequence b of one cache tensor: rows b*cap + id of a
+    contiguous cache; for a paged one the pool rows its block table names
+    (table[b][id / page] * page + id mod page)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    if kv.desc.page_size:
+        P = kv.desc.page_size
+        tab = kv.block_table[b].cpu().numpy().astype(np.int64)
+        phys = tab[ids // P] * P + ids % P
+        flat = t.reshape((-1,) + tuple(t.shape[2:]))
+        return flat.index_select(0, torch.as_tensor(phys, device=t.device))
+    return t[b].index_select(0, torch.as_tensor(ids, device=t.device))
 
 
 def decode_nope(kv, b, ids):
     """Decoded non-RoPE (or indexer-key) rows `ids` of sequence b, fp64."""
     fmt = kv.desc.nope_dtype
     if fmt == 2:  # FP8 E4M3 + per-entry scale
-        codes = _rows(kv.nope, b, ids).cpu().numpy()
-        sc = _rows(kv.scale, b, ids).cpu().double().numpy()
+        codes = _rows(kv, kv.nope, b, ids).cpu().numpy()
+        sc = _rows(kv, kv.scale, b, ids).cpu().double().numpy()
         return F.fp8_decode(codes) * sc[:, None]
     if fmt == 3:  # MXFP4
-        packed = _rows(kv.nope, b, ids).cpu().numpy().astype(np.int64)
+        packed = _rows(kv, kv.nope, b, ids).cpu().numpy().astype(np.int64)
         codes = np.stack([packed & 0xF, packed >> 4], -1).reshape(packed.shape[0], -1)
-        return F.mxfp4_decode(codes, _rows(kv.scale, b, ids).cpu().numpy())
-    return _rows(kv.nope, b, ids).to("cpu", torch.float64).numpy()
+        return F.mxfp4_decode(codes, _rows(kv, kv.scale, b, ids).cpu().numpy())
+    return _rows(kv, kv.nope, b, ids).to("cpu", torch.float64).numpy()
 
 
 def decode_kv(kv, b, ids):
@@ -39,7 +48,7 @@ def decode_kv(kv, b, ids):
     V = decode_nope(kv, b, ids)
     if kv.rope is None:
         return V
-    R = _rows(kv.rope, b, ids).to("cpu", torch.float64).numpy()
+    R = _rows(kv, kv.rope, b, ids).to("cpu", torch.float64).numpy()
     return np.concatenate([V, R], 1)
 
 

@@ -30,16 +30,16 @@ def test_library_exports_every_declared_symbol():
     L = cb.lib()
     for name in declared_functions():
         assert hasattr(L, name), name
-    assert L.csa_version() == 2
+    assert L.csa_version() == 3
     assert L.csa_status_string(0) == b"CSA_OK"
     assert L.csa_status_string(5) == b"CSA_ERR_CAPACITY"
 
 
 def test_struct_sizes_match_header_layout():
-    assert ctypes.sizeof(cb.CacheDesc) == 48
-    assert ctypes.sizeof(cb.Cache) == 32
-    assert ctypes.sizeof(cb.IndexDesc) == 40
-    assert ctypes.sizeof(cb.AttnDesc) == 56
+    assert ctypes.sizeof(cb.CacheDesc) == 56
+    assert ctypes.sizeof(cb.Cache) == 40
+    assert ctypes.sizeof(cb.IndexDesc) == 48
+    assert ctypes.sizeof(cb.AttnDesc) == 72
 
 
 def fake(addr):
@@ -216,3 +216,75 @@ def test_window_and_merge_validation():
     assert L.csa_lse_merge(4, 64, 512, 2, P, P, P, P, P, None, None) == 3
     assert L.csa_lse_merge(4, 64, 512, 1, fake(0x4004), P, P, P, P, None, None) == 2
     assert L.csa_lse_merge(0, 64, 512, 1, P, P, P, P, P, None, None) == 0
+
+
+def test_paging_fields_are_validated_before_launch():
+    # paged caches: page_size a power of two in 64..65536, capacity a multiple
+    # of it, pool_pages >= 1, a block table exactly when paged (4-byte aligned)
+    L = cb.lib()
+    P = fake(0x4000)
+    T = 0x9000
+    cases = [(48, 640, 10, T, 1), (64, 100, 10, T, 1), (64, 640, 0, T, 1), (64, 640, 10, None, 1),
+             (0, 640, 0, T, 1), (0, 640, 5, None, 1), (64, 640, 10, 0x9002, 2), (1 << 17, 1 << 17, 1, T, 1)]
+    for ps, cap, pool, table, want in cases:
+        d = cb.cache_desc(4, True, 32, 32, "f32", "f32", "f32", cap, page_size=ps, pool_pages=pool)
+        c = cb.Cache(0x1000, 0, 0x2000, 0x3000, table)
+        assert L.csa_compress_prefill(ctypes.byref(d), 1, 4, 0, P, P, P, P, P, P, ctypes.byref(c), None) == want, \
+            (ps, cap, pool, table)
+        a = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, cap, page_size=ps, pool_pages=pool)
+        kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000, table)
+        assert L.hca_dense_attn_decode(ctypes.byref(a), 1, P, P, ctypes.byref(kv), 0.1, P, None, P, 1 << 30,
+                                       None) == want
+        i = cb.index_desc(16, 64, "bf16", "bf16", "fp8", "f32", 4, cap, page_size=ps, pool_pages=pool)
+        ks = cb.Cache(0x1000, 0x5000, 0, 0x3000, table)
+        assert L.csa_index_topk_decode(ctypes.byref(i), 1, P, P, P, ctypes.byref(ks), 16, P, None, P, 1 << 30,
+                                       None) == want
+    # the attention descriptor's reserved field
+    bad = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 640)
+    bad.reserved = 1
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    assert L.hca_dense_attn_decode(ctypes.byref(bad), 1, P, P, ctypes.byref(kv), 0.1, P, None, P, 1 << 30, None) == 1
+    # the prefill indexer reads contiguous keys only
+    i = cb.index_desc(16, 64, "bf16", "bf16", "fp8", "f32", 4, 640, page_size=64, pool_pages=10)
+    ks = cb.Cache(0x1000, 0x5000, 0, 0x3000, T)
+    assert L.csa_index_topk_prefill(ctypes.byref(i), 1, 16, 0, P, P, ctypes.byref(ks), 16, P, None, P, 1 << 30,
+                                    None) == 3
+    assert b"paged" in L.csa_last_error()
+    # the pool's rows must be addressable by the attention's 32-bit offsets
+    big = cb.attn_desc(64, 512, 64, "bf16", "bf16", "bf16", "bf16", 4, 1024, page_size=1024, pool_pages=2049)
+    kvp = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000, T)
+    assert L.hca_dense_attn_decode(ctypes.byref(big), 1, P, P, ctypes.byref(kvp), 0.1, P, None, P, 1 << 40,
+                                   None) == 3
+
+
+def test_paged_workspaces():
+    # paged sparse attention turns its lists into pool rows in the workspace
+    # (B*T*k int32 after the split partials); dense attention and the
+    # indexer need nothing more
+    for op, T in ((cb.OP_SPARSE_ATTN_DECODE, 1), (cb.OP_SPARSE_ATTN_PREFILL, 64)):
+        flat = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192)
+        paged = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192, page_size=64, pool_pages=512)
+        for B in (1, 4):
+            extra = cb.workspace_bytes(op, paged, B, T, 0, 1024) - cb.workspace_bytes(op, flat, B, T, 0, 1024)
+            assert extra == -(-B * T * 1024 * 4 // 256) * 256
+    flat = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 128, 8192)
+    paged = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 128, 8192, page_size=64, pool_pages=512)
+    assert cb.workspace_bytes(cb.OP_DENSE_ATTN_DECODE, paged, 4, 1, 0, 0) == \
+        cb.workspace_bytes(cb.OP_DENSE_ATTN_DECODE, flat, 4, 1, 0, 0)
+
+
+def test_decode_step_rejects_mixed_paging():
+    L = cb.lib()
+    cap = 8192
+    kvd = cb.cache_desc(4, True, 512, 64, "bf16", "fp8", "bf16", cap, page_size=64, pool_pages=256)
+    kd = cb.cache_desc(4, True, 64, 0, "bf16", "fp8", "f32", cap, page_size=64, pool_pages=256)
+    idesc = cb.index_desc(16, 64, "bf16", "bf16", "fp8", "f32", 4, cap, page_size=64, pool_pages=256)
+    adesc = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, cap)   # not paged
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000, 0x9000)
+    ks = cb.Cache(0x6000, 0x7000, 0, 0x8000, 0x9000)
+    inp = cb.DecodeInputs(*([0x4000] * 15))
+    P = fake(0x4000)
+    assert L.csa_decode_step(ctypes.byref(kvd), ctypes.byref(kv), ctypes.byref(kd), ctypes.byref(ks),
+                             ctypes.byref(idesc), ctypes.byref(adesc), 4, P, ctypes.byref(inp), 1024, 0.1, P, None,
+                             P, None, P, 1 << 30, None) == 1
+    assert b"paging" in L.csa_last_error()
