@@ -391,7 +391,7 @@ def swa_decode_lines(n_steps=DECODE_STEPS, window=128):
                        ms3, by, w.batch)
 
 
-def paged_decode_lines(n_steps=DECODE_STEPS, page=64):
+def paged_decode_lines(n_steps=DECODE_STEPS, page=64, layouts=("paged", "contiguous")):
     """Paged, variable-length CSA decode: 32 sequences with context lengths
     log-uniform over 8K..256K tokens, KV and indexer-key caches in 64-entry
     pages of one pool handed out in a seeded random order; the same batch in
@@ -403,7 +403,7 @@ def paged_decode_lines(n_steps=DECODE_STEPS, page=64):
     table, pool = path.block_tables(need, page, cap)
     by = sum(decode_bytes_csa(w, L // w.m, 1) for L in lengths)
     lines = []
-    for paged in (True, False):
+    for paged in [lt == "paged" for lt in layouts]:
         log(f"setup {w.name} ({'paged' if paged else 'contiguous'})")
         kw = dict(page_size=page, block_table=table, pool_pages=pool) if paged else {}
         lay = path.CsaLayer(w, w.batch, cap, **kw)

@@ -164,6 +164,7 @@ static AttnParams make_attn_params(const csa_attn_desc* d, const void* q, const 
   P.ws = ws; P.ws_bytes = ws_bytes;
   make_pages(d->page_size, d->pool_pages, d->capacity, kv->block_table, &P.pg);  // validated before
   P.span_rows = P.pg.table ? (P.pg.pool << P.pg.shift) : P.cap;
+  P.seq_stride = P.pg.table ? 0 : P.cap;
   P.list_rows = false;
   return P;
 }

@@ -24,6 +24,7 @@ struct AttnParams {
   size_t ws_bytes;
   Pages pg;           // KV placement (contiguous or paged)
   int64_t span_rows;  // rows one gather descriptor covers: cap from the sequence's first row, or the whole pool
+  int64_t seq_stride; // rows from one sequence's first row to the next's: cap, or 0 when paged
   bool list_rows;     // sparse lists already hold pool rows (paged: turned by page_rows_kernel)
 };
 
@@ -45,7 +46,10 @@ int sparse_attn_decode_setup(const csa_attn_desc* desc, int B, const int64_t* po
                              size_t ws_bytes, AttnParams* out);
 int attn_dispatch(AttnParams& P, int op, int B, void* stream);
 size_t attn_ws_bytes(const csa_attn_desc* d, int op, int B, int T, int64_t pos0, int k);
-// paged sparse attention on the MFMA path: bytes of the list turned into pool rows
+// paged sparse attention on the MFMA path: bytes of the list turned into pool
+// rows, and where in P.ws that list goes (NULL when the call needs none or
+// the workspace lacks room)
 size_t page_list_bytes(const csa_attn_desc* d, int op, int B, int T, int k);
+int32_t* page_list_slot(const AttnParams& P, int op, int B);
 
 }  // namespace csa

@@ -154,12 +154,12 @@ __device__ __forceinline__ int64_t page_base(const AttnParams& P, int b, int id)
   return (pg >= 0 && pg < P.pg.pool ? pg : 0) << P.pg.shift;
 }
 
-template <bool DENSE>
+template <bool DENSE, bool PAGED>
 __device__ __forceinline__ int tile_ids(const AttnParams& P, int b, const int* s_list, int64_t rl, int64_t r0,
                                         int64_t nvalid) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t r = rl + 16 * w + (lane & 15);
-  if (!DENSE || !P.pg.table) return slot_id<DENSE>(s_list, r, r0, nvalid);
+  if constexpr (!DENSE || !PAGED) return slot_id<DENSE>(s_list, r, r0, nvalid);
   const int id = static_cast<int>(r0 + (r < nvalid ? r : nvalid - 1));
   const int f = __builtin_amdgcn_readlane(id, 0), l = __builtin_amdgcn_readlane(id, 15);
   const int64_t bf = page_base(P, b, f), bl = page_base(P, b, l);
@@ -234,10 +234,10 @@ __device__ __forceinline__ void issue_load(uint8_t* buf, const AttnParams& P, in
 }
 
 // All loads of the tile at list slot rl, back to back.
-template <bool FP8, bool DENSE>
+template <bool FP8, bool DENSE, bool PAGED>
 __device__ __forceinline__ void issue_tile(uint8_t* buf, const AttnParams& P, const int* s_list, int64_t rl,
                                            int64_t r0, int64_t nvalid, size_t seq, int b) {
-  const int my_id = tile_ids<DENSE>(P, b, s_list, rl, r0, nvalid);
+  const int my_id = tile_ids<DENSE, PAGED>(P, b, s_list, rl, r0, nvalid);
 #pragma unroll
   for (int it = 0; it < Lay<FP8>::NLOAD; ++it) issue_load<FP8>(buf, P, my_id, seq, it);
 }
@@ -277,7 +277,7 @@ __device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int s
   I.r0 = lo + static_cast<int64_t>(I.split) * per_split;
   I.r1 = I.r0 + per_split < end ? I.r0 + per_split : end;
   I.qrow = (static_cast<size_t>(I.b) * P.T + I.t) * NH;
-  I.seq = P.pg.table ? 0 : static_cast<size_t>(I.b) * P.cap;  // paged: rows are pool rows
+  I.seq = static_cast<size_t>(I.b) * P.seq_stride;  // paged: 0 (rows are pool rows)
   return I;
 }
 
@@ -367,7 +367,7 @@ __device__ __forceinline__ void rope_q(const Theta& th, int64_t pos, bf16x8 (&qf
   }
 }
 
-template <bool FP8, bool DENSE, bool SPLIT>
+template <bool FP8, bool DENSE, bool SPLIT, bool PAGED>
 __global__ void __launch_bounds__(NT, 1)
 attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* part, int64_t nitems, int nbatch) {
   typedef Lay<FP8> L;
@@ -401,7 +401,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   }
   int ntiles = (nvalid + TILE - 1) / TILE;
   int par = 0;  // buffer of the next tile: kb0 / kb1
-  if (ntiles > 0) issue_tile<FP8, DENSE>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
+  if (ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
   bf16x8 qf[QS];
 #pragma unroll
   for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
@@ -477,7 +477,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
 
     rope_q(th, I.pos, qf);
     // entry ids of the tile whose loads the current tile issues (read ahead)
-    int my_id_pf = ntiles > 1 ? tile_ids<DENSE>(P, I.b, s_list, TILE, I.r0, nvalid) : 0;
+    int my_id_pf = ntiles > 1 ? tile_ids<DENSE, PAGED>(P, I.b, s_list, TILE, I.r0, nvalid) : 0;
     f32x16 oacc[4][2];
 #pragma unroll
     for (int mb = 0; mb < 4; ++mb)
@@ -488,7 +488,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     // next item's list compacted into s_list, its first tile issued into buf
     auto start_next = [&](uint8_t* buf) {
       nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, P.list_rows ? P.span_rows : In.n, s_list, s_cnt);
-      if (nvalid_n > 0) issue_tile<FP8, DENSE>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq, In.b);
+      if (nvalid_n > 0) issue_tile<FP8, DENSE, PAGED>(buf, P, s_list, 0, In.r0, nvalid_n, In.seq, In.b);
       next_started = true;
     };
 
@@ -537,7 +537,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
         nvalid_n = DENSE ? static_cast<int>(In.r1 > In.r0 ? In.r1 - In.r0 : 0) : compact_list(lrn, P.list_rows ? P.span_rows : In.n, s_list, s_cnt);
         next_started = true;
         if (nvalid_n > 0) {
-          my_id = tile_ids<DENSE>(P, In.b, s_list, 0, In.r0, nvalid_n);
+          my_id = tile_ids<DENSE, PAGED>(P, In.b, s_list, 0, In.r0, nvalid_n);
           lseq = In.seq;
         }
       }
@@ -728,7 +728,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     };
     for (int j = 0; j < ntiles; ++j) {
       tile(par ? kb1 : kb0, par ? kb0 : kb1, pbuf, j);
-      if (j + 2 < ntiles) my_id_pf = tile_ids<DENSE>(P, I.b, s_list, static_cast<int64_t>(j + 2) * TILE, I.r0, nvalid);
+      if (j + 2 < ntiles) my_id_pf = tile_ids<DENSE, PAGED>(P, I.b, s_list, static_cast<int64_t>(j + 2) * TILE, I.r0, nvalid);
       par ^= 1;
     }
 
@@ -822,23 +822,36 @@ void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int
   if (nitems <= 0) return;
   const dim3 grid(static_cast<unsigned>(nitems < cu ? nitems : cu));
   const bool fp8 = P.nope_dt == CSA_FP8E4M3;
-#define CSA_ATTN_LAUNCH(F, D, S) \
-  hipLaunchKernelGGL((attn_bf16_kernel<F, D, S>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B)
+  // paged caches need a kernel of their own only for dense attention (sparse
+  // lists arrive as pool rows)
+  const bool paged = dense && P.pg.table != nullptr;
+#define CSA_ATTN_LAUNCH(F, D, S, G) \
+  hipLaunchKernelGGL((attn_bf16_kernel<F, D, S, G>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B)
   if (fp8) {
     if (dense) {
-      if (split) CSA_ATTN_LAUNCH(true, true, true);
-      else CSA_ATTN_LAUNCH(true, true, false);
+      if (paged) {
+        if (split) CSA_ATTN_LAUNCH(true, true, true, true);
+        else CSA_ATTN_LAUNCH(true, true, false, true);
+      } else {
+        if (split) CSA_ATTN_LAUNCH(true, true, true, false);
+        else CSA_ATTN_LAUNCH(true, true, false, false);
+      }
     } else {
-      if (split) CSA_ATTN_LAUNCH(true, false, true);
-      else CSA_ATTN_LAUNCH(true, false, false);
+      if (split) CSA_ATTN_LAUNCH(true, false, true, false);
+      else CSA_ATTN_LAUNCH(true, false, false, false);
     }
   } else {
     if (dense) {
-      if (split) CSA_ATTN_LAUNCH(false, true, true);
-      else CSA_ATTN_LAUNCH(false, true, false);
+      if (paged) {
+        if (split) CSA_ATTN_LAUNCH(false, true, true, true);
+        else CSA_ATTN_LAUNCH(false, true, false, true);
+      } else {
+        if (split) CSA_ATTN_LAUNCH(false, true, true, false);
+        else CSA_ATTN_LAUNCH(false, true, false, false);
+      }
     } else {
-      if (split) CSA_ATTN_LAUNCH(false, false, true);
-      else CSA_ATTN_LAUNCH(false, false, false);
+      if (split) CSA_ATTN_LAUNCH(false, false, true, false);
+      else CSA_ATTN_LAUNCH(false, false, false, false);
     }
   }
 #undef CSA_ATTN_LAUNCH

@@ -157,22 +157,28 @@ size_t page_list_bytes(const csa_attn_desc* d, int op, int B, int T, int k) {
   return round256(static_cast<size_t>(B) * rows * k * sizeof(int32_t));
 }
 
+int32_t* page_list_slot(const AttnParams& P, int op, int B) {
+  const bool dense = op == CSA_OP_DENSE_ATTN_PREFILL || op == CSA_OP_DENSE_ATTN_DECODE;
+  if (dense || !P.pg.table || !mfma_attn_supported(P)) return nullptr;
+  size_t part_room = 0;  // workspace bytes ahead of the list: the decode split partials
+  if (op == CSA_OP_SPARSE_ATTN_DECODE) {
+    const int splits = decode_splits(false, P.k);
+    part_room = splits > 1 ? round256(part_bytes(B, splits)) : 0;
+  }
+  const size_t need = part_room + static_cast<size_t>(B) * P.T * P.k * sizeof(int32_t);
+  if (!P.ws || P.ws_bytes < need) return nullptr;
+  return reinterpret_cast<int32_t*>(static_cast<char*>(P.ws) + part_room);
+}
+
 int launch_mfma_attn(const AttnParams& P0, int op, int B, hipStream_t s) {
   const bool dense = op == CSA_OP_DENSE_ATTN_PREFILL || op == CSA_OP_DENSE_ATTN_DECODE;
   const bool decode = op == CSA_OP_SPARSE_ATTN_DECODE || op == CSA_OP_DENSE_ATTN_DECODE;
   AttnParams P = P0;
-  size_t part_room = 0;  // workspace bytes ahead of the page list: the decode split partials
-  if (decode) {
-    const int64_t count = dense ? dense_span(P.cap, P.window) : P.k;
-    const int splits = decode_splits(dense, count);
-    part_room = splits > 1 ? round256(part_bytes(B, splits)) : 0;
-  }
   if (!dense && P.pg.table && !P.list_rows) {
     // paged sparse: the list turned into pool rows in the workspace, after the partials
     const int64_t total = static_cast<int64_t>(B) * P.T * P.k;
-    const size_t need = part_room + static_cast<size_t>(total) * sizeof(int32_t);
-    if (!P.ws || P.ws_bytes < need) return fail(CSA_ERR_WORKSPACE, "workspace too small for the paged list");
-    int32_t* rows = reinterpret_cast<int32_t*>(static_cast<char*>(P.ws) + part_room);
+    int32_t* rows = page_list_slot(P, op, B);
+    if (!rows) return fail(CSA_ERR_WORKSPACE, "workspace too small for the paged list");
     hipLaunchKernelGGL(page_rows_kernel, dim3(static_cast<unsigned>((total + 255) / 256)), dim3(256), 0, s, P, rows,
                        total);
     int st = check_launch("page_rows_kernel");

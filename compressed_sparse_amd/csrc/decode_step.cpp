@@ -74,6 +74,17 @@ extern "C" int csa_decode_step(const csa_cache_desc* kv_desc, const csa_cache* k
                                      &Pa)) != CSA_OK)
     return st;
   if (B == 0) return CSA_OK;
+  // paged KV cache: the final top-k pass writes the selected entries' pool
+  // rows where the attention reads its list (no separate translation launch)
+  if (Pi.ghist) {
+    if (int32_t* rows = page_list_slot(Pa, CSA_OP_SPARSE_ATTN_DECODE, B)) {
+      Pi.rows_out = rows;
+      Pi.row_pg = Pa.pg;
+      Pi.row_cap = Pa.cap;
+      Pa.idx = rows;
+      Pa.list_rows = true;
+    }
+  }
   hipStream_t s = as_stream(stream);
   const bool fused = Pkv.in_dt == Pkey.in_dt;
   if (fused) {

@@ -36,6 +36,11 @@ struct IndexParams {
   // 16 bytes of E2M1 codes, then 64 int32 E8M0 scales (QPACK_ROW_BYTES)
   uint8_t* qpack;
   Pages pg;  // key placement (contiguous or paged)
+  // fused decode step over a paged KV cache (NULL otherwise): the final
+  // top-k pass also writes each selected entry's row of that cache
+  int32_t* rows_out;  // [B][k]
+  Pages row_pg;
+  int64_t row_cap;
 };
 
 constexpr int HIST_BITS = 11;

@@ -635,12 +635,13 @@ __device__ __forceinline__ void flush_hist(const int (*lhist_w)[HIST_BINS], int*
   }
 }
 
-template <int KFMT>
+template <int KFMT, bool PAGED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT == CSA_FP8E4M3 ? 3 : 4))) index_scan_kernel(IndexParams P) {
   // this chunk's top-11-bit key histogram (decode top-k), one per wave so
   // that no barrier separates the clearing from the counting
   __shared__ int lhist_w[4][HIST_BINS];
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the wave index as a scalar where paged key blocks need it for their table loads
+  const int tid = threadIdx.x, lane = tid & 63, w = PAGED ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int b = blockIdx.z, t = blockIdx.y;
   const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
   int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
@@ -648,6 +649,13 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * SCAN_CHUNK;
   if (c0 >= n) return;
   const size_t row = static_cast<size_t>(b) * P.T + t;
+  const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);  // entries of this chunk
+  int page_of_block = 0;  // paged: lane l holds the page of the wave's block l
+  if constexpr (PAGED) {
+    const int64_t blk = min(16 * w + 64 * lane, (cn - 1) & ~15);
+    const int64_t pg = P.pg.table[static_cast<int64_t>(b) * P.pg.tps + ((c0 + blk) >> P.pg.shift)];
+    page_of_block = pg >= 0 && pg < P.pg.pool ? static_cast<int>(pg) : 0;  // outside the pool: page 0
+  }
   // A operand (16x16x32): head = lane & 15, g = lane >> 4; k-step ks covers
   // dims g*16 + ks*8 .. +8
   const int g = lane >> 4, h = lane & 15;
@@ -660,13 +668,16 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   float wv[4];
 #pragma unroll
   for (int v = 0; v < 4; ++v) wv[v] = P.w[row * HI + g * 4 + v];
-  const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);  // entries of this chunk
   // wave-uniform bases of this chunk (of each key block); per-lane offsets are 32-bit
   float* wsb = P.ws + row * P.n_stride + c0;
   float* sob = P.scores_out ? P.scores_out + row * P.cap + c0 : nullptr;
   constexpr int KROW = KFMT == CSA_BF16 ? 2 * DI : DI;  // bytes per key row
   const uint8_t* knope = static_cast<const uint8_t*>(P.knope);
   const uint8_t* kscale = static_cast<const uint8_t*>(P.kscale);
+  // contiguous keys: the chunk's rows from one base
+  const size_t seq = static_cast<size_t>(b) * P.cap;
+  const uint8_t* kbc = knope + (seq + c0) * KROW;
+  const uint8_t* sbc = kscale + (seq + c0) * 4;
   int* lhist = lhist_w[w];
   if (P.ghist) clear_hist(lhist, lane);
   // each wave: 16-entry column blocks w, w+4, ...  A batch of NB blocks is
@@ -674,22 +685,35 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
   // batch is widened, multiplied and reduced over heads (two register sets,
   // used in turn).
   constexpr int NB = 4;
-  // Block j of a batch: the 16 entries from e0 + 64 j, clamped into the
-  // chunk (a block past its end re-reads the chunk's last block; those
-  // scores are dropped).  A block never crosses a page.
+  // Block j of a batch: the 16 entries from e0 + 64 j (entries past the
+  // chunk's end re-read its last entry; those scores are dropped).  Paged:
+  // the block's rows from its page (a block never crosses one; a block past
+  // the end re-reads the chunk's last block).
+  // Paged: the wave's blocks are 16w + 64 l (l = 0, 1, ..; past the chunk's
+  // end its last block); lane l fetched block l's page once, at the start,
+  // and a block takes it with a lane read, so no key load waits on the table.
   auto load = [&](int e0, u32x4 (&ra)[NB], u32x4 (&rb)[NB], uint32_t (&rs)[NB]) {
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int blk = min(e0 + 64 * j, (cn - 1) & ~15);
-      const int64_t r0 = key_block_row(P, b, c0 + blk);
-      const uint8_t* kb = knope + r0 * KROW;
-      const int s = min(blk + (lane & 15), cn - 1) - blk;
+      const uint8_t* kb = kbc;
+      const uint8_t* sb = sbc;
+      int s;
+      if constexpr (PAGED) {
+        const int blk = min(e0 + 64 * j, (cn - 1) & ~15);
+        const int64_t pg = __builtin_amdgcn_readlane(page_of_block, (e0 - 16 * w) / 64 + j);
+        const int64_t r0 = (pg << P.pg.shift) | ((c0 + blk) & ((int64_t(1) << P.pg.shift) - 1));
+        kb = knope + r0 * KROW;
+        sb = kscale + r0 * 4;
+        s = min(blk + (lane & 15), cn - 1) - blk;
+      } else {
+        s = min(e0 + 64 * j + (lane & 15), cn - 1);
+      }
       if constexpr (KFMT == CSA_BF16) {
         ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32));
         rb[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * 2 * DI + g * 32 + 16));
       } else {
         ra[j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * DI + g * 16));
-        rs[j] = *reinterpret_cast<const uint32_t*>(kscale + r0 * 4 + static_cast<uint32_t>(s * 4));
+        rs[j] = *reinterpret_cast<const uint32_t*>(sb + static_cast<uint32_t>(s * 4));
       }
     }
   };
@@ -790,9 +814,11 @@ __global__ void __launch_bounds__(256) index_mx_prep_kernel(IndexParams P, int r
 // are issued before the first MFMA.
 constexpr int MX_PAIRS = SCAN_CHUNK / 256;  // block pairs per wave
 
+template <bool PAGED>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) index_scan_mx_kernel(IndexParams P) {
   __shared__ int lhist_w[4][HIST_BINS];
-  const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // the wave index as a scalar where paged key blocks need it for their table loads
+  const int tid = threadIdx.x, lane = tid & 63, w = PAGED ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int b = blockIdx.z, t = blockIdx.y;
   const int64_t pos = P.pos_dev ? P.pos_dev[b] : P.pos0 + t;
   int64_t n = pos < 0 ? 0 : (pos + 1) / P.m;
@@ -801,20 +827,30 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) i
   if (c0 >= n) return;
   const size_t row = static_cast<size_t>(b) * P.T + t;
   const int cn = static_cast<int>(n - c0 < SCAN_CHUNK ? n - c0 : SCAN_CHUNK);
-  // every key load first (a 64-entry block pair past the chunk's end
-  // re-reads its last pair, branch-free; those scores are dropped).  A pair
-  // never crosses a page.
+  // every key load first (entries past the chunk's end re-read its last
+  // entry, branch-free; those scores are dropped).  Paged: each 64-entry
+  // block pair from its page (a pair never crosses one; a pair past the end
+  // re-reads the chunk's last pair).
+  const size_t seq = static_cast<size_t>(b) * P.cap;
+  const uint8_t* kbc = static_cast<const uint8_t*>(P.knope) + (seq + c0) * (DI / 2);
+  const uint8_t* sbc = static_cast<const uint8_t*>(P.kscale) + (seq + c0) * (DI / 32);
   u32x4 kc[MX_PAIRS][2];
   uint32_t ks[MX_PAIRS][2];
 #pragma unroll
   for (int p = 0; p < MX_PAIRS; ++p) {
-    const int blk = min(64 * (w + 4 * p), (cn - 1) & ~63);
-    const int64_t r0 = key_block_row(P, b, c0 + blk);
-    const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + r0 * (DI / 2);
-    const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + r0 * (DI / 32);
+    int blk = 64 * (w + 4 * p), s0 = 0;  // entry s of the chunk at kb + (s - s0) rows
+    const uint8_t* kb = kbc;
+    const uint8_t* sb = sbc;
+    if constexpr (PAGED) {
+      blk = min(blk, (cn - 1) & ~63);
+      const int64_t r0 = key_block_row(P, b, c0 + blk);
+      kb = static_cast<const uint8_t*>(P.knope) + r0 * (DI / 2);
+      sb = static_cast<const uint8_t*>(P.kscale) + r0 * (DI / 32);
+      s0 = blk;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const int s = min(blk + 32 * j + (lane & 31), cn - 1) - blk;
+      const int s = min(blk + 32 * j + (lane & 31), cn - 1) - s0;
       kc[p][j] = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(s * (DI / 2) + 16 * (lane >> 5)));
       ks[p][j] = sb[static_cast<uint32_t>(s * (DI / 32) + (lane >> 5))];
     }
@@ -989,9 +1025,17 @@ int launch_index_scan(const IndexParams& P, int B, int64_t n_max, hipStream_t s)
     hipLaunchKernelGGL(index_scan_mx2_kernel, dim3(grid.x, (P.T + 1) / 2, B), dim3(256), 0, s, P);
     return check_launch("index_scan_mx2_kernel");
   }
-  if (P.qk_dt == CSA_MXFP4) hipLaunchKernelGGL(index_scan_mx_kernel, grid, dim3(256), 0, s, P);
-  else if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL(index_scan_kernel<CSA_FP8E4M3>, grid, dim3(256), 0, s, P);
-  else hipLaunchKernelGGL(index_scan_kernel<CSA_BF16>, grid, dim3(256), 0, s, P);
+  const bool paged = P.pg.table != nullptr;
+  if (P.qk_dt == CSA_MXFP4) {
+    if (paged) hipLaunchKernelGGL(index_scan_mx_kernel<true>, grid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL(index_scan_mx_kernel<false>, grid, dim3(256), 0, s, P);
+  } else if (P.key_dt == CSA_FP8E4M3) {
+    if (paged) hipLaunchKernelGGL((index_scan_kernel<CSA_FP8E4M3, true>), grid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((index_scan_kernel<CSA_FP8E4M3, false>), grid, dim3(256), 0, s, P);
+  } else {
+    if (paged) hipLaunchKernelGGL((index_scan_kernel<CSA_BF16, true>), grid, dim3(256), 0, s, P);
+    else hipLaunchKernelGGL((index_scan_kernel<CSA_BF16, false>), grid, dim3(256), 0, s, P);
+  }
   return check_launch("index_scan_kernel");
 }
 

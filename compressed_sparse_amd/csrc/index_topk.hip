@@ -203,11 +203,11 @@ __device__ __forceinline__ void radix_threshold(KeyOf key_of, int64_t cnt, int k
 
 // Ordered compaction after radix_threshold: the elements whose key is above
 // the threshold, and the first `remaining` equal to it, in element order,
-// their idx_of(i) written to out[0..).  Each thread takes E consecutive
-// elements per tile; one workgroup scan per tile.
-template <typename KeyOf, typename IdxOf>
+// put(j, idx_of(i)) for output slots j = 0, 1, ..  Each thread takes E
+// consecutive elements per tile; one workgroup scan per tile.
+template <typename KeyOf, typename IdxOf, typename Put>
 __device__ __forceinline__ void ordered_take(KeyOf key_of, IdxOf idx_of, int64_t cnt, uint32_t prefix, uint32_t pmask,
-                             int remaining, int* s_part, int32_t* out) {
+                             int remaining, int* s_part, Put put) {
   constexpr int E = 8;
   const int tid = threadIdx.x, nt = blockDim.x;
   int gt_done = 0, eq_done = 0;
@@ -231,9 +231,9 @@ __device__ __forceinline__ void ordered_take(KeyOf key_of, IdxOf idx_of, int64_t
     for (int u = 0; u < E; ++u) {
       if (i0 + u >= cnt) break;
       if (key[u] > prefix) {
-        out[pos++] = idx_of(i0 + u);
+        put(pos++, idx_of(i0 + u));
       } else if (key[u] == prefix) {
-        if (eq_before < remaining) out[pos++] = idx_of(i0 + u);
+        if (eq_before < remaining) put(pos++, idx_of(i0 + u));
         ++eq_before;
       }
     }
@@ -243,8 +243,9 @@ __device__ __forceinline__ void ordered_take(KeyOf key_of, IdxOf idx_of, int64_t
 }
 
 // Top-k of sc[0..n) (n > k) by one workgroup, ascending indices, ties to the
-// lower index.
-__device__ __forceinline__ void row_radix_select(const float* sc, int64_t n, int k, int key_bits, int32_t* out) {
+// lower index; put(j, index) for slots j < k.
+template <typename Put>
+__device__ __forceinline__ void row_radix_select(const float* sc, int64_t n, int k, int key_bits, Put put) {
   __shared__ int hist[256];
   __shared__ int s_sel[2];
   __shared__ int s_part[34];
@@ -252,8 +253,7 @@ __device__ __forceinline__ void row_radix_select(const float* sc, int64_t n, int
   int remaining;
   auto key_of = [sc](int64_t i) { return score_key(sc[i]); };
   radix_threshold(key_of, n, k, key_bits, hist, s_sel, &prefix, &pmask, &remaining);
-  ordered_take(key_of, [](int64_t i) { return static_cast<int32_t>(i); }, n, prefix, pmask, remaining, s_part,
-               out);
+  ordered_take(key_of, [](int64_t i) { return static_cast<int32_t>(i); }, n, prefix, pmask, remaining, s_part, put);
 }
 
 // One workgroup (1024 threads) selects the top-k of one query row.
@@ -266,7 +266,7 @@ __global__ void __launch_bounds__(1024) topk_radix_kernel(IndexParams P, int key
     for (int64_t j = threadIdx.x; j < P.k; j += blockDim.x) out[j] = j < n ? static_cast<int32_t>(j) : -1;
     return;
   }
-  row_radix_select(P.ws + row * P.n_stride, n, P.k, key_bits, out);
+  row_radix_select(P.ws + row * P.n_stride, n, P.k, key_bits, [out](int64_t j, int32_t id) { out[j] = id; });
 }
 
 // ---------------------------------------------------------------------------
@@ -376,8 +376,11 @@ __global__ void __launch_bounds__(256) topk_cand_kernel(IndexParams P) {
   }
 }
 
+constexpr int ROW_TAB_LDS = 4096;  // block-table entries the final pass stages in LDS
+
 __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key_bits) {
   constexpr int CPT = NCH_MAX / 1024;  // chunks per thread
+  __shared__ int32_t s_tab[ROW_TAB_LDS];
   __shared__ uint32_t s_key[CAND_CAP];
   __shared__ int32_t s_idx[CAND_CAP];
   __shared__ int s_pre[NCH_MAX];
@@ -388,8 +391,41 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int64_t n = visible(query_pos(P, b, 0), P.m, P.cap);
   int32_t* out = P.idx + static_cast<size_t>(b) * P.k;
+  // a fused decode step over a paged KV cache: each selected entry's pool
+  // row as well, the list its sparse attention reads (-1 on a page outside
+  // the pool, like the padding).  The sequence's block-table row is staged
+  // in LDS first (when it fits), so that no output waits on a table load.
+  int32_t* rows = P.rows_out ? P.rows_out + static_cast<size_t>(b) * P.k : nullptr;
+  const bool tab_lds = rows && P.row_pg.table && P.row_pg.tps <= ROW_TAB_LDS;
+  // the table row's loads are issued now and land in LDS just before the
+  // first output (stage_tab; a barrier follows before any put)
+  int32_t tr[ROW_TAB_LDS / 1024];
+  if (tab_lds) {
+#pragma unroll
+    for (int u = 0; u < ROW_TAB_LDS / 1024; ++u) {
+      const int64_t j = tid + 1024 * u;
+      tr[u] = j < P.row_pg.tps ? P.row_pg.table[b * P.row_pg.tps + j] : 0;
+    }
+  }
+  auto stage_tab = [&]() {
+    if (tab_lds)
+#pragma unroll
+      for (int u = 0; u < ROW_TAB_LDS / 1024; ++u) s_tab[tid + 1024 * u] = tr[u];
+  };
+  auto row_of = [&](int32_t id) -> int32_t {
+    if (!tab_lds) return static_cast<int32_t>(entry_row(P.row_pg, P.row_cap, b, id));
+    const int64_t pg = s_tab[id >> P.row_pg.shift];
+    if (pg < 0 || pg >= P.row_pg.pool) return -1;
+    return static_cast<int32_t>((pg << P.row_pg.shift) | (id & ((1 << P.row_pg.shift) - 1)));
+  };
+  auto put = [&](int64_t j, int32_t id) {
+    out[j] = id;
+    if (rows) rows[j] = id >= 0 ? row_of(id) : -1;
+  };
   if (n <= P.k) {
-    for (int64_t j = tid; j < P.k; j += nt) out[j] = j < n ? static_cast<int32_t>(j) : -1;
+    stage_tab();
+    __syncthreads();
+    for (int64_t j = tid; j < P.k; j += nt) put(j, j < n ? static_cast<int32_t>(j) : -1);
     return;
   }
   // where each chunk's candidates go in index order: prefix of the chunk
@@ -407,7 +443,8 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   int pre, unused, c, unused_tot;
   block_scan2(loc, 0, s_part, &pre, &unused, &c, &unused_tot);
   if (c > CAND_CAP) {  // too many candidates: exact select over the whole row
-    row_radix_select(P.ws + static_cast<size_t>(b) * P.n_stride, n, P.k, key_bits, out);
+    stage_tab();          // (the select's barriers precede its first output)
+    row_radix_select(P.ws + static_cast<size_t>(b) * P.n_stride, n, P.k, key_bits, put);
     return;
   }
 #pragma unroll
@@ -435,7 +472,8 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   const int above = P.csel[2 * b + 1];
   radix_threshold(key_of, c, P.k - above, key_bits, hist, s_sel, &prefix, &pmask, &remaining,
                   bstar << (32 - HIST_BITS), ~0u << (32 - HIST_BITS), 32 - HIST_BITS - 8);
-  ordered_take(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, out);
+  stage_tab();  // ordered_take's workgroup scan (barriers) precedes its first output
+  ordered_take(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, put);
 }
 
 // prep_done: the decode rows' preparation (cleared histogram and count,
