@@ -36,6 +36,20 @@ def compress(a, za, Ba, m, b=None, zb=None, Bb=None):
     return out
 
 
+def matvec_rows(X, W):
+    """Rows of X (lists) times W (d_model x c, lists): explicit dot products."""
+    d, c = len(W), len(W[0])
+    return [[sum(x[k] * W[k][j] for k in range(d)) for j in range(c)] for x in X]
+
+
+def compress_from_hidden(X, W, Ba, m, Bb=None):
+    """The four projections as explicit dot products, then compress()."""
+    a, za = matvec_rows(X, W["aKV"]), matvec_rows(X, W["aZ"])
+    if "bKV" in W:
+        return compress(a, za, Ba, m, matvec_rows(X, W["bKV"]), matvec_rows(X, W["bZ"]), Bb)
+    return compress(a, za, Ba, m)
+
+
 def rotate(vec, pos, d_nope, base):
     c = len(vec)
     d_rope = c - d_nope

@@ -75,6 +75,26 @@ def compress(a, za, Ba, m, b=None, zb=None, Bb=None, i0=0, i1=None, tok0=0):
     return np.sum(wts * vals, axis=1)
 
 
+def project(X, W):
+    """One of the compressor's input projections from hidden states, fp64:
+    X [n_tok, d_model] times W [d_model, c].  [读完这篇] §三 压缩机制 names the
+    compressor's learnable parameters: four projection matrices W^{aKV},
+    W^{bKV}, W^{aZ}, W^{bZ} (C^a = H W^{aKV}, C^b = H W^{bKV}, Z^a = H W^{aZ},
+    Z^b = H W^{bZ}) and the two biases B^a, B^b."""
+    return np.asarray(X, np.float64) @ np.asarray(W, np.float64)
+
+
+def compress_from_hidden(X, W, Ba, m, Bb=None, i0=0, i1=None, tok0=0):
+    """Entries from hidden states: the four projections (W: dict with keys
+    aKV, aZ and, overlapped, bKV, bZ; each [d_model, c]) in fp64, then
+    compress() on them.  The projections are not rounded to any storage
+    format between the two steps (reading: they never leave the kernel)."""
+    a, za = project(X, W["aKV"]), project(X, W["aZ"])
+    b = project(X, W["bKV"]) if "bKV" in W else None
+    zb = project(X, W["bZ"]) if "bZ" in W else None
+    return compress(a, za, Ba, m, b, zb, Bb, i0=i0, i1=i1, tok0=tok0)
+
+
 def compress_weights(za, Ba, m, zb=None, Bb=None, i=0, tok0=0):
     """The per-channel softmax weights of entry i, shape [rows, c] (rows = m,
     or 2m for an overlapped entry with i >= 1); exposed for the row-sum pin."""

@@ -51,6 +51,42 @@ def test_compress_matches_bruteforce_single_window(m):
     assert np.allclose(got, ref, rtol=0, atol=1e-13)
 
 
+@pytest.mark.parametrize("m,overlap", [(4, True), (8, False)])
+def test_compress_from_hidden_matches_bruteforce(m, overlap):
+    """Projections from hidden states then compression, against explicit
+    Python dot products and the brute-force compressor."""
+    T, d, c = 16, 7, 3
+    X = rnd((T, d), 60)
+    names = ("aKV", "aZ", "bKV", "bZ") if overlap else ("aKV", "aZ")
+    W = {n: rnd((d, c), 61 + i, 0.5) for i, n in enumerate(names)}
+    Ba, Bb = rnd((m, c), 70), (rnd((m, c), 71) if overlap else None)
+    got = csa.compress_from_hidden(X, W, Ba, m, Bb)
+    ref = np.array(brute.compress_from_hidden(X.tolist(), {k: v.tolist() for k, v in W.items()}, Ba.tolist(), m,
+                                              None if Bb is None else Bb.tolist()))
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_compress_from_hidden_closed_forms():
+    """(1) Z-projections and biases zero: every overlapped entry i >= 1 is
+    the mean of its 2m hidden rows times the value projections, (mean of
+    window i) W^{aKV} / 2 + (mean of window i-1) W^{bKV} / 2 (entry 0: the mean
+    of its window times W^{aKV}).  (2) d_model = c and identity projections:
+    the entries are those of compress() on X itself."""
+    T, d, c, m = 24, 5, 4, 4
+    X = rnd((T, d), 80)
+    W = {"aKV": rnd((d, c), 81), "bKV": rnd((d, c), 82), "aZ": np.zeros((d, c)), "bZ": np.zeros((d, c))}
+    zero = np.zeros((m, c))
+    got = csa.compress_from_hidden(X, W, zero, m, zero)
+    win = X.reshape(T // m, m, d).mean(1)
+    ref = np.concatenate([win[:1] @ W["aKV"], 0.5 * (win[1:] @ W["aKV"]) + 0.5 * (win[:-1] @ W["bKV"])], 0)
+    assert np.allclose(got, ref, rtol=0, atol=1e-12)
+    Xc = rnd((T, c), 83)
+    eye = {"aKV": np.eye(c), "aZ": np.eye(c), "bKV": np.eye(c), "bZ": np.eye(c)}
+    Ba, Bb = rnd((m, c), 84), rnd((m, c), 85)
+    assert np.allclose(csa.compress_from_hidden(Xc, eye, Ba, m, Bb), csa.compress(Xc, Xc, Ba, m, Xc, Xc, Bb),
+                       rtol=0, atol=1e-14)
+
+
 def test_compress_zero_logits_is_mean():
     """Z = B = 0: an overlapped entry is the plain mean of its 2m rows (of m
     rows for entry 0); an HCA entry is the mean of its m' rows."""
