@@ -422,10 +422,48 @@ def paged_decode_lines(n_steps=DECODE_STEPS, page=64, layouts=("paged", "contigu
     return lines
 
 
+def secondary_project_prefill(steps=5):
+    """The 32K prefill's two compressors fed from hidden states (d_model =
+    4096): projections fused with the compression (csa_compress_project_prefill)
+    for the KV entries (4 x 576 projected columns) and the indexer keys (4 x 64).
+    Priced as the GEMM it is: 2 * T * d_model * 2560 flop per step."""
+    w, d = synth.PROJECT_PREFILL_32K, synth.PROJECT_D_MODEL
+    T, m = w.tokens, w.m
+    log(f"setup {w.name}")
+    X = synth.hidden_chunk(0, 0, T, d, 0, "cuda")[None].contiguous()
+    Wkv = cb.pack_projection_weights(synth.projection_weights(w.c, d, True, "", 0, "cuda"))
+    Wk = cb.pack_projection_weights(synth.projection_weights(w.idx_dim, d, True, "k", 0, "cuda"))
+    prm = synth.compressor_params(w, 0, "cuda")
+    kv = cb.KVCache(cb.cache_desc(m, True, w.d_nope, w.d_rope, "bf16", w.nope_fmt, w.rope_fmt, T // m), 1)
+    keys = cb.KVCache(cb.cache_desc(m, True, w.idx_dim, 0, "bf16", w.key_fmt, "f32", T // m), 1)
+    ws = cb.workspace(max(cb.project_workspace_bytes(kv.desc, 1, T), cb.project_workspace_bytes(keys.desc, 1, T)))
+
+    def step():
+        cb.compress_project_prefill(kv, 0, X, Wkv, prm["Ba"], prm["Bb"], ws=ws)
+        cb.compress_project_prefill(keys, 0, X, Wk, prm["kBa"], prm["kBb"], ws=ws)
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flops = 2.0 * T * d * 4 * (w.c + w.idx_dim)
+    ach = flops / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "metric": "compressor prefill from hidden states tokens/s (L=32768, d_model=4096)",
+            "value": T / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "roofline": {"bound": "mfma", "kernel": "project_gemm_kernel (projection GEMM + compressor epilogue)",
+                         "achieved": ach, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                         "algorithmic_flop_per_step": flops}}
+
+
 def secondary_lines():
     out = []
     for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, swa_decode_lines, paged_decode_lines,
-               secondary_hca_prefill,
+               secondary_project_prefill, secondary_hca_prefill,
                secondary_hca_prefill_whole, secondary_mxfp4_prefill_indexer, secondary_tiny):
         r = fn()
         out.extend(r if isinstance(r, list) else [r])
@@ -648,7 +686,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
     ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "paged-decode",
-                                       "hca-prefill",
+                                       "project-prefill", "hca-prefill",
                                        "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
@@ -669,6 +707,7 @@ def main():
     if args.only:
         fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
               "swa-decode": swa_decode_lines, "paged-decode": paged_decode_lines,
+              "project-prefill": secondary_project_prefill,
               "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
               "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
               "peaks": measured_peaks}[args.only]

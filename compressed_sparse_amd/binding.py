@@ -57,6 +57,7 @@ class DecodeInputs(ctypes.Structure):
 EXPORTS = ["csa_compress_prefill", "csa_compress_decode", "csa_index_topk_prefill", "csa_index_topk_decode",
            "csa_sparse_attn_prefill", "csa_sparse_attn_decode", "csa_sparse_attn_decode_noalloc",
            "hca_dense_attn_prefill", "hca_dense_attn_decode", "csa_decode_step", "csa_decode_step_workspace_bytes", "csa_lse_merge",
+           "csa_compress_project_prefill", "csa_compress_project_workspace_bytes",
            "csa_workspace_bytes", "csa_status_string", "csa_last_error", "csa_version"]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 
@@ -85,6 +86,8 @@ def lib():
             "csa_decode_step": [P, P, P, P, P, P, I, P, P, I, F, P, P, P, P, P, SZ, P],
             "csa_decode_step_workspace_bytes": [P, P, I, I],
             "csa_lse_merge": [I, I, I, I, P, P, P, P, P, P, P],
+            "csa_compress_project_prefill": [P, I, I, I64, P, I, P, P, P, P, P, SZ, P],
+            "csa_compress_project_workspace_bytes": [P, I, I, I64],
         }
         for name, args in sig.items():
             fn = getattr(L, name)
@@ -208,6 +211,29 @@ def compress_decode(cache: KVCache, pos, a, za, Ba, b=None, zb=None, Bb=None, st
     cs = cache.struct()
     _check(lib().csa_compress_decode(ctypes.byref(cache.desc), a.shape[0], ptr(pos), ptr(a), ptr(b), ptr(za),
                                      ptr(zb), ptr(Ba), ptr(Bb), ctypes.byref(cs), stream_ptr(stream)))
+
+
+def pack_projection_weights(W):
+    """The library's weight layout for compress_project_prefill: W is a dict of
+    [d_model, c] matrices aKV, aZ (and bKV, bZ); row j*NT + u of the result
+    is column j of matrix u in the order aKV, aZ, bKV, bZ."""
+    names = [n for n in ("aKV", "aZ", "bKV", "bZ") if n in W]
+    return torch.stack([W[n].t() for n in names], 1).reshape(-1, W[names[0]].shape[0]).contiguous()
+
+
+def project_workspace_bytes(desc, B, T, pos0=0):
+    return lib().csa_compress_project_workspace_bytes(ctypes.byref(desc), B, T, pos0)
+
+
+def compress_project_prefill(cache: KVCache, pos0, X, W, Ba, Bb=None, ws=None, stream=None):
+    """X [B][T][d_model] BF16 hidden states, W [NT * c][d_model] BF16 packed
+    projection rows (row j*NT + u: column j of W^{aKV}, W^{aZ}, W^{bKV}, W^{bZ})."""
+    B, T, d = X.shape
+    if ws is None:
+        ws = workspace(project_workspace_bytes(cache.desc, B, T, pos0), X.device)
+    cs = cache.struct()
+    _check(lib().csa_compress_project_prefill(ctypes.byref(cache.desc), B, T, pos0, ptr(X), d, ptr(W), ptr(Ba),
+                                              ptr(Bb), ctypes.byref(cs), ptr(ws), ws.numel(), stream_ptr(stream)))
 
 
 def index_desc(n_heads, dim, q_fmt, qk_fmt, key_fmt, score_fmt, m, capacity, page_size=0, pool_pages=0):

@@ -24,6 +24,11 @@ struct CompressParams {
 
 enum { RING_A = 0, RING_ZA = 1, RING_B = 2, RING_ZB = 3 };
 
+// host: a cache descriptor and its buffers checked; the compressor
+// parameters of a cache (no token inputs; biases Ba, Bb)
+int compress_validate_cache(const csa_cache_desc* d, const csa_cache* c);
+CompressParams compress_make_params(const csa_cache_desc* d, const csa_cache* c, const float* Ba, const float* Bb);
+
 // host: validation of a decode call's arguments and its parameters
 int compress_decode_setup(const csa_cache_desc* d, int B, const int64_t* pos, const void* a, const void* b,
                           const void* za, const void* zb, const float* Ba, const float* Bb, const csa_cache* cache,

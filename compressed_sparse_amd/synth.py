@@ -159,6 +159,11 @@ PAIR_HCA_DECODE_B4_1M = dataclasses.replace(
 PAGED_CSA_DECODE_B32_MIXED = dataclasses.replace(
     CSA_DECODE_B32_128K, name="paged_csa_decode_b32_ctx8K-256K_page64")
 
+# Compressor inputs projected from hidden states for the 32K prefill: the
+# pages give no model width; d_model = 4096 is this workload's reading.
+PROJECT_PREFILL_32K = dataclasses.replace(CSA_PREFILL_BF16_32K, name="csa_compress_from_hidden_L32768_d4096")
+PROJECT_D_MODEL = 4096
+
 WORKLOADS = {w.name: w for w in (TINY_CSA_PREFILL_FP32, CSA_PREFILL_BF16_32K, CSA_DECODE_B32_128K,
                                  HCA_PREFILL_1M, HCA_DECODE_B16_1M, PAIR_CSA_DECODE_B4_1M,
                                  PAIR_HCA_DECODE_B4_1M, PAGED_CSA_DECODE_B32_MIXED)}
@@ -236,3 +241,22 @@ def query_chunk(w: Workload, seq, chunk, n_tok, seed=0, device="cpu", with_index
         out["qI"] = normal((n_tok, w.idx_heads, w.idx_dim), "qI", seed, seq, chunk, device=device, dtype=dt)
         out["w"] = normal((n_tok, w.idx_heads), "w", seed, seq, chunk, device=device, dtype=torch.float32)
     return out
+
+
+# ---------------------------------------------------------------------------
+# hidden states and the compressor's projection weights (prefill from hidden
+# states): X ~ N(0, 1) and each projection W ~ N(0, 1 / d_model) in BF16, so
+# the projected rows are again about N(0, 1) like the other workloads'
+# ---------------------------------------------------------------------------
+
+def hidden_chunk(seq, chunk, n_tok, d_model, seed=0, device="cpu"):
+    """Hidden states [n_tok, d_model] BF16 of tokens [chunk*n_tok, +n_tok) of `seq`."""
+    return normal((n_tok, d_model), "hid.x", seed, seq, chunk, device=device, dtype=torch.bfloat16)
+
+
+def projection_weights(c, d_model, overlap, prefix="", seed=0, device="cpu"):
+    """The compressor's projections W^{aKV}, W^{aZ} (and W^{bKV}, W^{bZ}), each
+    [d_model, c] BF16, std 1/sqrt(d_model)."""
+    names = ("aKV", "aZ", "bKV", "bZ") if overlap else ("aKV", "aZ")
+    return {n: normal((d_model, c), "W." + prefix + n, seed, device=device, dtype=torch.bfloat16,
+                      std=d_model ** -0.5) for n in names}

@@ -186,6 +186,30 @@ int csa_compress_decode(const csa_cache_desc* desc, int B, const int64_t* pos,
                         const float* Ba, const float* Bb, const csa_cache* cache,
                         void* stream);
 
+/* Prefill from hidden states: the compressor's four input projections
+ * ([读完这篇] §三 压缩机制: learnable W^{aKV}, W^{bKV}, W^{aZ}, W^{bZ} and the
+ * biases B^a, B^b) fused with the compression, so that a, za, b, zb never
+ * reach memory:
+ *   a = X W^{aKV}, za = X W^{aZ}, b = X W^{bKV}, zb = X W^{bZ}
+ * (fp32 accumulation, not rounded), then exactly the entries, RoPE, storage
+ * and ring update of csa_compress_prefill on those rows.
+ *   X  : device BF16 [B][T][d_model] hidden states of tokens [pos0, pos0 + T)
+ *   W  : device BF16 [NT * c][d_model]: row j*NT + u is column j of projection
+ *        u, u = 0: W^{aKV}, 1: W^{aZ}, 2: W^{bKV}, 3: W^{bZ} (NT = 4 when
+ *        overlapped, else NT = 2: W^{aKV}, W^{aZ}); c = d_nope + d_rope
+ *   Ba, Bb : device float [m][c] (Bb NULL iff !overlap)
+ *   ws : device workspace of csa_compress_project_workspace_bytes() bytes
+ * desc->in_dtype must be CSA_BF16 (the type of X and W).  Supported shapes
+ * (CSA_ERR_UNSUPPORTED otherwise): m divides 128 (at most 64 when
+ * overlapped), pos0 a multiple of m, NT * c a multiple of 128, d_nope a
+ * multiple of 8 up to 512, d_rope up to 128, d_model a multiple of 64, and
+ * T * d_model * 2 and NT * c * d_model * 2 below 2^31 bytes.
+ * CSA_ERR_CAPACITY if an entry index reaches capacity. */
+int csa_compress_project_prefill(const csa_cache_desc* desc, int B, int T, int64_t pos0, const void* X,
+                                 int d_model, const void* W, const float* Ba, const float* Bb,
+                                 const csa_cache* cache, void* ws, size_t ws_bytes, void* stream);
+size_t csa_compress_project_workspace_bytes(const csa_cache_desc* desc, int B, int T, int64_t pos0);
+
 /* ---- lightning indexer + top-k ------------------------------------------
  * For the query at absolute position p, n(p) = floor((p + 1) / m) entries are
  * visible (an entry becomes visible once its window is complete), capped at

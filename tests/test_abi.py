@@ -288,3 +288,24 @@ def test_decode_step_rejects_mixed_paging():
                              ctypes.byref(idesc), ctypes.byref(adesc), 4, P, ctypes.byref(inp), 1024, 0.1, P, None,
                              P, None, P, 1 << 30, None) == 1
     assert b"paging" in L.csa_last_error()
+
+
+def test_project_prefill_validation():
+    # the compressor fed from hidden states: shapes it does not take are
+    # rejected before any launch
+    L = cb.lib()
+    desc = cb.cache_desc(4, True, 512, 64, "bf16", "fp8", "bf16", 1000)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    P = fake(0x4000)
+    args = lambda d, T, pos0, dm: (ctypes.byref(d), 1, T, pos0, P, dm, P, P, P, ctypes.byref(kv), P, 1 << 30, None)
+    assert L.csa_compress_project_prefill(*args(desc, 16, 2, 256)) == 3      # pos0 not a multiple of m
+    assert L.csa_compress_project_prefill(*args(desc, 16, 0, 100)) == 1      # d_model not a multiple of 64
+    f32 = cb.cache_desc(4, True, 512, 64, "f32", "fp8", "bf16", 1000)
+    assert L.csa_compress_project_prefill(*args(f32, 16, 0, 256)) == 3       # hidden states must be BF16
+    m3 = cb.cache_desc(3, True, 512, 64, "bf16", "fp8", "bf16", 1000)
+    assert L.csa_compress_project_prefill(*args(m3, 16, 0, 256)) == 3        # m must divide 128
+    assert L.csa_compress_project_prefill(*args(desc, 4004, 0, 256)) == 5    # capacity
+    assert b"capacity" in L.csa_last_error()
+    assert L.csa_compress_project_prefill(*args(desc, 16, 0, 256)[:10], P, 16, None) == 4   # workspace
+    assert L.csa_compress_project_prefill(ctypes.byref(desc), 1, 0, 0, P, 256, P, P, P, ctypes.byref(kv), P, 0,
+                                          None) == 0                      # T == 0: nothing to do
