@@ -460,10 +460,66 @@ def secondary_project_prefill(steps=5):
                          "algorithmic_flop_per_step": flops}}
 
 
+def planted_recall_line(rhos=(0.5, 0.6, 0.7, 0.8)):
+    """planted_recall at several separations rho (the value reported is the
+    recall at rho = 0.6, where the planted and the other keys still overlap
+    near the k-th score)."""
+    by = {rho: planted_recall(rho) for rho in rhos}
+    main = by[0.6] if 0.6 in by else by[rhos[0]]
+    out = dict(main)
+    out["by_rho"] = {str(r): {"gpu": v["value"], "oracle_mxfp4": v["oracle_mxfp4_recall"],
+                              "planted_share_of_fp32_top": v["planted_share_of_fp32_top"]} for r, v in by.items()}
+    return out
+
+
+def planted_recall(rho):
+    """MXFP4 indexer recall on the labelled "planted" variant of the pair's
+    CSA layer (B = 4 at 2^20 context: 262144 keys, 1024 of them planted along
+    the query direction; synth.planted_index_inputs).  The keys reach the
+    MXFP4 key cache through the library's own compressor (one-token windows
+    with zero logits store each row as it is); the decode indexer (MXFP4 QK,
+    BF16 scores) selects 1024; recall = overlap with the fp32 top-1024 on the
+    exact keys, for the GPU and for the oracle's MXFP4 path."""
+    from oracle import csa
+    w = synth.PAIR_CSA_DECODE_B4_1M
+    n, d, H, k, B = w.tokens // w.m, w.idx_dim, w.idx_heads, w.topk, w.batch
+    log(f"setup planted recall ({B} x {n} keys, rho {rho})")
+    desc = cb.cache_desc(1, False, d, 0, "f32", "mxfp4", "f32", n)
+    keys = cb.KVCache(desc, B)
+    zero = torch.zeros((1, d), dtype=torch.float32, device="cuda")
+    inp = [synth.planted_index_inputs(n, d, H, k, rho, b) for b in range(B)]
+    for b, (kk, _, _, _) in enumerate(inp):
+        x = kk[None].cuda().contiguous()
+        cb.compress_prefill(keys.seq_view(b), 0, x, torch.zeros_like(x), zero)
+    idesc = cb.index_desc(H, d, "bf16", "mxfp4", "mxfp4", "bf16", w.m, n)
+    qI = torch.stack([q for _, q, _, _ in inp]).to(torch.bfloat16).cuda().contiguous()
+    wt = torch.stack([ww for _, _, ww, _ in inp]).cuda().contiguous()
+    pos = torch.full((B,), w.tokens, dtype=torch.int64, device="cuda")
+    idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
+    cb.index_topk_decode(idesc, keys, pos, qI, wt, k, idx)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    rec_g, rec_o, planted_in = [], [], []
+    for b, (kk, q, ww, pl) in enumerate(inp):
+        kx = kk.double().numpy()
+        qb = qI[b].float().cpu().double().numpy()
+        full = set(csa.topk(csa.index_scores(qb, ww.double().numpy(), kx, n, "f32"), n, k).tolist())
+        Kq = csa.finalize_keys(kx, "mxfp4")["k"]
+        sel = csa.topk(csa.index_scores(csa.quantize_query(qb, "mxfp4"), ww.double().numpy(), Kq, n, "bf16"), n, k)
+        rec_g.append(len(full & set(gidx[b].tolist())) / k)
+        rec_o.append(len(full & set(sel.tolist())) / k)
+        planted_in.append(len(full & set(pl.tolist())) / k)
+    return {"workload": w.name + " (planted keys, labelled variant)",
+            "metric": "MXFP4 indexer recall vs fp32 top-1024 (planted keys)",
+            "value": float(np.mean(rec_g)), "unit": "fraction",
+            "oracle_mxfp4_recall": float(np.mean(rec_o)), "planted_share_of_fp32_top": float(np.mean(planted_in)),
+            "rho": rho, "sequences": B, "pages_value": 0.997}
+
+
 def secondary_lines():
     out = []
     for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, swa_decode_lines, paged_decode_lines,
-               secondary_project_prefill, secondary_hca_prefill,
+               planted_recall_line, secondary_project_prefill, secondary_hca_prefill,
                secondary_hca_prefill_whole, secondary_mxfp4_prefill_indexer, secondary_tiny):
         r = fn()
         out.extend(r if isinstance(r, list) else [r])
@@ -686,7 +742,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
     ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "paged-decode",
-                                       "project-prefill", "hca-prefill",
+                                       "project-prefill", "planted-recall", "hca-prefill",
                                        "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
@@ -707,7 +763,7 @@ def main():
     if args.only:
         fn = {"csa-decode": csa_decode_line, "hca-decode": hca_decode_line, "pair-decode": pair_decode_lines,
               "swa-decode": swa_decode_lines, "paged-decode": paged_decode_lines,
-              "project-prefill": secondary_project_prefill,
+              "project-prefill": secondary_project_prefill, "planted-recall": planted_recall_line,
               "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
               "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
               "peaks": measured_peaks}[args.only]

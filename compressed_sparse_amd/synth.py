@@ -260,3 +260,26 @@ def projection_weights(c, d_model, overlap, prefix="", seed=0, device="cpu"):
     names = ("aKV", "aZ", "bKV", "bZ") if overlap else ("aKV", "aZ")
     return {n: normal((d_model, c), "W." + prefix + n, seed, device=device, dtype=torch.bfloat16,
                       std=d_model ** -0.5) for n in names}
+
+
+# ---------------------------------------------------------------------------
+# "planted" indexer inputs (a labelled variant for the MXFP4 recall, never a
+# headline): the isotropic workloads give near-uniform scores, so MXFP4
+# rounding reorders the many keys near the k-th score.  Here a sequence's
+# query heads share a unit direction u and `n_plant` keys are drawn as
+# rho * sqrt(d) * u + sqrt(1 - rho^2) * eps (the other keys eps ~ N(0, I)), so
+# the top set stands apart as it does for a trained model's peaked scores.
+# ---------------------------------------------------------------------------
+
+def planted_index_inputs(n, d, heads, n_plant, rho, seq, seed=0):
+    """fp32 keys [n, d], query heads [heads, d], positive head weights
+    [heads] and the planted key indices, for one sequence (CPU tensors)."""
+    u = normal((d,), "pl.u", seed, seq, dtype=torch.float64)
+    u = u / u.norm()
+    keys = normal((n, d), "pl.k", seed, seq, dtype=torch.float64)
+    g = torch.Generator().manual_seed(stream_key(seed, "pl.idx", seq))
+    idx = torch.randperm(n, generator=g)[:n_plant].sort().values
+    keys[idx] = rho * d ** 0.5 * u + (1.0 - rho * rho) ** 0.5 * keys[idx]
+    q = d ** 0.5 * u + 0.3 * normal((heads, d), "pl.q", seed, seq, dtype=torch.float64)
+    w = normal((heads,), "pl.w", seed, seq, dtype=torch.float64).abs() + 0.1
+    return keys.float(), q.float(), w.float(), idx
