@@ -270,13 +270,33 @@ def rope_query(q, pos, d_nope, base):
     return rope(q, pos, d_nope, base)
 
 
-def sparse_attention_row(q, pos, cache, sel, d_nope, base, tau):
+def quantize_attn_query(q, d_nope, qk_fmt="bf16"):
+    """The attention query in the format of the QK product.
+
+    "bf16": the query as given.  "mxfp8": each head's d_nope non-RoPE dims
+    become MXFP8 (blocks of 32 consecutive dims, E4M3 elements, one E8M0
+    scale each), so that they meet the FP8 cache codes in FP8; the RoPE dims
+    stay as given, like the cache's BF16 RoPE dims.  Reading of
+    [CSA/HCA 混注意力] §1.4 存储格式混 (non-RoPE dims in FP8, RoPE dims in
+    BF16 for precision): the pages name no query format; MXFP8 is the block
+    form that keeps a 32-dim block's dynamic range.  q: [..., H, c]."""
+    q = np.asarray(q, np.float64)
+    if qk_fmt == "bf16":
+        return q
+    assert qk_fmt == "mxfp8"
+    out = q.copy()
+    out[..., :d_nope] = F.mxfp8_quantize(q[..., :d_nope])[0]
+    return out
+
+
+def sparse_attention_row(q, pos, cache, sel, d_nope, base, tau, qk_fmt="bf16"):
     """CSA attention for one query at absolute position `pos` over the
     selected entries (indices outside [0, n) are not used)."""
+    q = quantize_attn_query(q, d_nope, qk_fmt)
     return attend(rope_query(q, pos, d_nope, base), cache["k"], cache["v"], sel, tau)
 
 
-def dense_attention_row(q, pos, cache, m, d_nope, base, tau, window=0):
+def dense_attention_row(q, pos, cache, m, d_nope, base, tau, window=0, qk_fmt="bf16"):
     """HCA attention for one query: every visible entry, s < n(pos)
     ([CSA/HCA 混注意力] §1.2: dense attention over the 128x shorter
     sequence).  With window w > 0 only the last w visible entries,
@@ -286,6 +306,7 @@ def dense_attention_row(q, pos, cache, m, d_nope, base, tau, window=0):
     uncompressed SWA KV of the prefix-cache paragraph)."""
     n = min(int(n_visible(pos, m)), cache["k"].shape[0])
     lo = n - window if 0 < window < n else 0
+    q = quantize_attn_query(q, d_nope, qk_fmt)
     return attend(rope_query(q, pos, d_nope, base), cache["k"], cache["v"], np.arange(lo, n), tau)
 
 
@@ -337,12 +358,12 @@ def csa_rows(rows, pos_of_row, q, qI, w, cache, keys, m, k, d_nope, base, tau,
     return dict(idx=idx, o=o, lse=lse, scores=scores)
 
 
-def hca_rows(pos_of_row, q, cache, m, d_nope, base, tau):
+def hca_rows(pos_of_row, q, cache, m, d_nope, base, tau, window=0, qk_fmt="bf16"):
     """Dense HCA attention for a list of query rows."""
     R, H = q.shape[0], q.shape[1]
     dv = cache["v"].shape[1]
     o = np.zeros((R, H, dv))
     lse = np.zeros((R, H))
     for r in range(R):
-        o[r], lse[r] = dense_attention_row(q[r], int(pos_of_row[r]), cache, m, d_nope, base, tau)
+        o[r], lse[r] = dense_attention_row(q[r], int(pos_of_row[r]), cache, m, d_nope, base, tau, window, qk_fmt)
     return o, lse

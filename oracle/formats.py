@@ -15,11 +15,16 @@ Written from the public format definitions, not from any GPU code:
   their negatives) sharing one E8M0 scale 2^(e-127).  The shared exponent is
   floor(log2(amax)) - emax_elem with emax_elem = 2 for E2M1; elements are
   rounded RNE and clamped to +-6.
+* MXFP8 (same specification): blocks of 32 E4M3 elements sharing one E8M0
+  scale; shared exponent floor(log2(amax)) - 8, elements RNE saturating to
+  +-448.
 
 The pages fix only the format names: the KV cache keeps the RoPE dims in BF16
 and the rest in FP8, and the indexer runs its QK product in FP4 with scores
 cast from FP32 to BF16 ("逐层剖析 CSA / HCA 混注意力" page, §1.4 精度优化叠加,
-sub-sections 存储格式混 and LIGHTNING INDEXER 的 FP4 计).
+sub-sections 存储格式混 and LIGHTNING INDEXER 的 FP4 计).  MXFP8 serves the
+attention's optional FP8 QK product (the query's non-RoPE dims against the
+FP8 cache), a reading of the same sub-section.
 """
 import numpy as np
 
@@ -128,14 +133,16 @@ def e2m1_encode(v):
     return (idx | (sign.astype(np.int64) << 3)).astype(np.uint8)
 
 
-def mx_scale_exponent(block_amax):
-    """OCP MX v1.0 shared exponent for E2M1 elements: floor(log2 amax) - 2,
-    clamped to the E8M0 range [-127, 127].  A block of zeros gets -127."""
+def mx_scale_exponent(block_amax, emax_elem=2):
+    """OCP MX v1.0 shared exponent: floor(log2 amax) - emax_elem, where
+    emax_elem is the exponent of the element format's largest normal (2 for
+    E2M1: 6 = 1.5 * 2^2; 8 for E4M3: 448 = 1.75 * 2^8), clamped to the E8M0
+    range [-127, 127].  A block of zeros gets -127."""
     a = np.asarray(block_amax, dtype=np.float64)
     out = np.full(a.shape, -127, dtype=np.int64)
     nz = a > 0
     _, e = np.frexp(a[nz])
-    out[nz] = np.clip(e.astype(np.int64) - 1 - 2, -127, 127)
+    out[nz] = np.clip(e.astype(np.int64) - 1 - emax_elem, -127, 127)
     return out
 
 
@@ -154,6 +161,27 @@ def mxfp4_quantize(x):
     elems = e2m1_round(xb / X)
     vals = (elems * X).reshape(x.shape)
     codes = e2m1_encode(elems).reshape(x.shape)
+    return vals, codes, (ex + 127).astype(np.uint8)
+
+
+def mxfp8_quantize(x):
+    """Quantise the last axis (a multiple of 32) to MXFP8 (OCP MX v1.0):
+    blocks of 32 E4M3 elements sharing one E8M0 scale 2^e with
+    e = floor(log2 amax) - 8; each element becomes RNE(x / 2^e) on the E4M3
+    grid, saturating to +-448 (the block maximum lands in [256, 512) before
+    rounding, so only it can saturate).
+
+    Returns (values, element_codes, scale_codes): decoded fp64 values, E4M3
+    bytes with the shape of x, E8M0 bytes (e + 127) of shape [..., d/32]."""
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    assert d % MX_BLOCK == 0
+    xb = x.reshape(x.shape[:-1] + (d // MX_BLOCK, MX_BLOCK))
+    ex = mx_scale_exponent(np.max(np.abs(xb), axis=-1), emax_elem=8)
+    X = np.ldexp(1.0, ex)[..., None]
+    elems = fp8_round(xb / X)
+    vals = (elems * X).reshape(x.shape)
+    codes = fp8_encode(elems).reshape(x.shape)
     return vals, codes, (ex + 127).astype(np.uint8)
 
 

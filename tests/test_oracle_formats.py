@@ -2,9 +2,9 @@
 
 BF16 and FP8 E4M3 rounding are pinned to torch's own casts (library
 routines); the FP8 decode table to torch's float8_e4m3fn view and to values
-fixed by the OFP8 specification; E2M1 and the MX scale rule to the OCP MX
-v1.0 definitions checked by exhaustive enumeration / brute-force nearest
-search."""
+fixed by the OFP8 specification; E2M1 and the MX scale rule (MXFP4 and
+MXFP8) to the OCP MX v1.0 definitions checked by exhaustive enumeration /
+brute-force nearest search."""
 import numpy as np
 import pytest
 import torch
@@ -86,6 +86,65 @@ def test_mx_scale_rule():
     # a zero block gets the smallest scale and all-zero codes
     v0, c0, s0 = F.mxfp4_quantize(np.zeros((1, 32)))
     assert s0[0, 0] == 0 and not c0.any() and not v0.any()
+
+
+def _e4m3_nearest_brute(v):
+    """Nearest E4M3 value to v by scanning all 127 finite magnitudes (ties to
+    the even code), saturating at 448; independent of round_rne."""
+    mags = F.fp8_decode(np.arange(0x7F))
+    d = np.abs(mags - min(abs(v), 448.0))
+    best = np.nonzero(d == d.min())[0]
+    pick = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+    return np.copysign(mags[pick], v), pick
+
+
+def test_mxfp8_brute_force():
+    """MXFP8 (OCP MX v1.0, E4M3 elements): shared exponent by a plain search
+    (the e with 2^(e+8) <= amax < 2^(e+9)), then each element the nearest E4M3
+    value of x / 2^e by enumeration."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, 64)) * np.exp(rng.uniform(-6, 6, (40, 1)))
+    x[3, :32] = 0.0                                          # a zero block
+    x[5, 7] = 1.9375 * 2.0 ** 3                              # scales to 496: saturates
+    x[5, :7] = x[5, 8:32] = 0.01
+    vals, codes, sc = F.mxfp8_quantize(x)
+    for r in range(x.shape[0]):
+        for blk in range(2):
+            xb = x[r, 32 * blk:32 * blk + 32]
+            amax = np.abs(xb).max()
+            if amax == 0:
+                assert sc[r, blk] == 0 and not codes[r, 32 * blk:32 * blk + 32].any()
+                continue
+            e = -130
+            while 2.0 ** (e + 1 + 8) <= amax:
+                e += 1
+            assert sc[r, blk] == e + 127
+            for i, v in enumerate(xb):
+                q, c = _e4m3_nearest_brute(v / 2.0 ** e)
+                assert vals[r, 32 * blk + i] == q * 2.0 ** e
+                assert codes[r, 32 * blk + i] & 0x7F == c
+    assert codes[5, 7] == 0x7E and vals[5, 7] == 448.0 * 2.0 ** (3 - 8)
+
+
+def test_mxfp8_closed_forms():
+    # a block of 2^k: every element scales to 256 = 2^8 (code 0x78), exact
+    for k in (-20, 0, 7):
+        v, c, s = F.mxfp8_quantize(np.full((1, 32), 2.0 ** k))
+        assert (c == 0x78).all() and s[0, 0] == k - 8 + 127 and (v == 2.0 ** k).all()
+    # scaling a block by 2^j shifts the scale byte by j and keeps the codes
+    x = np.random.default_rng(12).standard_normal((8, 96))
+    v0, c0, s0 = F.mxfp8_quantize(x)
+    v1, c1, s1 = F.mxfp8_quantize(x * 2.0 ** 9)
+    assert np.array_equal(c0, c1) and np.array_equal(s1.astype(int), s0.astype(int) + 9)
+    assert np.array_equal(v1, v0 * 2.0 ** 9)
+    # error: half an E4M3 ulp (relative 2^-4) in the normal range, the
+    # subnormal quantum 2^(e-10) below it; a saturated element at most 1/8
+    Xs = np.ldexp(1.0, np.repeat(s0.astype(int) - 127, 32, axis=1))
+    sat = np.abs(x / Xs) > 448.0
+    err = np.abs(v0 - x)
+    assert np.all(err[~sat] <= np.maximum(np.abs(x) * 2.0 ** -4, Xs * 2.0 ** -10)[~sat] * (1 + 1e-12))
+    assert sat.any() and np.all(err[sat] <= np.abs(x[sat]) / 8) and np.all(np.abs(v0[sat]) == 448.0 * Xs[sat])
+    assert np.array_equal(F.fp8_decode(c0) * Xs, v0)
 
 
 def test_fp8_entry_scale():

@@ -296,6 +296,68 @@ def test_query_rescaling_keeps_topk_and_changes_temperature():
     assert np.allclose(li, 1e4 * np.max(q @ K[sel].T, axis=1), rtol=1e-12)
 
 
+def _mxfp8_brute(x):
+    """MXFP8 of one 32-element block by plain search: the e with
+    2^(e+8) <= amax < 2^(e+9), then each element the nearest of the 127 E4M3
+    magnitudes times 2^e (ties to the even code, saturating)."""
+    amax = max(abs(v) for v in x)
+    if amax == 0:
+        return [0.0] * len(x)
+    e = -130
+    while 2.0 ** (e + 9) <= amax:
+        e += 1
+    mags = F.fp8_decode(np.arange(0x7F))
+    out = []
+    for v in x:
+        d = np.abs(mags - min(abs(v) / 2.0 ** e, 448.0))
+        best = np.nonzero(d == d.min())[0]
+        pick = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+        out.append(math.copysign(mags[pick] * 2.0 ** e, v))
+    return out
+
+
+def test_fp8_qk_attention_matches_bruteforce():
+    """FP8 QK product: each head's non-RoPE query dims rounded to MXFP8 in
+    32-dim blocks, RoPE dims untouched, then the plain attention (brute
+    force end to end)."""
+    H, d_nope, d_rope, n, m, pos = 2, 64, 4, 7, 4, 29
+    c = d_nope + d_rope
+    q = rnd((H, c), 120) * np.array([0.3] * 32 + [3.0] * 32 + [1.0] * d_rope)
+    K = rnd((n, c), 121)
+    cache = {"k": K, "v": K[:, :d_nope]}
+    o, lse = csa.dense_attention_row(q, pos, cache, m, d_nope, 100.0, 0.3, qk_fmt="mxfp8")
+    qq = [_mxfp8_brute(q[h, :32].tolist()) + _mxfp8_brute(q[h, 32:64].tolist()) + q[h, d_nope:].tolist()
+          for h in range(H)]
+    qr = complex_rope(np.array(qq), pos, d_nope, 100.0)
+    ob, lb = brute.attend(qr.tolist(), K.tolist(), K[:, :d_nope].tolist(), list(range(n)), 0.3)
+    assert np.allclose(o, ob, atol=1e-12) and np.allclose(lse, lb, atol=1e-12)
+    # quantisation changes the result (the two formats are told apart)
+    o16, _ = csa.dense_attention_row(q, pos, cache, m, d_nope, 100.0, 0.3)
+    assert np.abs(o16 - o).max() > 1e-4
+
+
+def test_fp8_qk_special_cases():
+    H, d_nope, d_rope, n, m, pos = 3, 64, 8, 9, 1, 8
+    c = d_nope + d_rope
+    K = rnd((n, c), 122)
+    cache = {"k": K, "v": K[:, :d_nope]}
+    # a query already on the MXFP8 grid: both QK formats give the same bits
+    codes = np.random.default_rng(123).integers(0, 0x7F, (H, d_nope)) | (np.random.default_rng(124).integers(0, 2, (H, d_nope)) << 7)
+    codes[:, ::32] = 0x78                        # each block's maximum is 256 * 2^e
+    codes = codes.astype(np.uint8)
+    onm = (F.fp8_decode(codes) * 2.0 ** -9).clip(-0.5, 0.5)
+    onm[:, ::32] = 0.5
+    q = np.concatenate([F.mxfp8_quantize(onm)[0], rnd((H, d_rope), 125)], 1)
+    a = csa.dense_attention_row(q, pos, cache, m, d_nope, 1e4, 0.2, qk_fmt="mxfp8")
+    b = csa.dense_attention_row(q, pos, cache, m, d_nope, 1e4, 0.2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    # zero non-RoPE dims: the RoPE dims alone, untouched by the FP8 mode
+    q0 = np.concatenate([np.zeros((H, d_nope)), rnd((H, d_rope), 126)], 1)
+    a = csa.sparse_attention_row(q0, pos, cache, [0, 3, 5], d_nope, 1e4, 0.2, qk_fmt="mxfp8")
+    b = csa.sparse_attention_row(q0, pos, cache, [0, 3, 5], d_nope, 1e4, 0.2)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_lse_merge_of_partitions():
     """Splitting the entry set and merging (o, lse) partials by LSE gives the
     unsplit result (the identity the split-K GPU kernels rely on)."""
