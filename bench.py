@@ -41,6 +41,7 @@ from compressed_sparse_amd import binding as cb  # noqa: E402
 from compressed_sparse_amd import path, synth  # noqa: E402
 
 PEAK_BF16_TFLOPS = 2500.0
+PEAK_FP8_TFLOPS = 5000.0
 PEAK_HBM_GBS = 8000.0
 CPU_BASELINE = True     # the oracle timings (cleared by --no-cpu-baseline)
 REPLAYS = 12            # timed replays of each decode graph (--replays)
@@ -520,6 +521,7 @@ def secondary_lines():
     out = []
     for fn in (csa_decode_line, hca_decode_line, pair_decode_lines, swa_decode_lines, paged_decode_lines,
                planted_recall_line, secondary_project_prefill, secondary_hca_prefill,
+               lambda: secondary_hca_prefill(qk="fp8"),
                secondary_hca_prefill_whole, secondary_mxfp4_prefill_indexer, secondary_tiny):
         r = fn()
         out.extend(r if isinstance(r, list) else [r])
@@ -653,10 +655,13 @@ def secondary_tiny(reps=20):
                                 "sample": f"the whole workload ({T} tokens: compression, indexer, top-k, attention)"}
     return line
 
-def secondary_hca_prefill(steps=5):
+def secondary_hca_prefill(steps=5, qk="bf16"):
     """The last 8192-token chunk of a 2^20-token HCA prefill: compress the
     chunk's tokens and run dense attention for its 8192 queries over the
-    8192 entries of the whole context (inputs resident in HBM)."""
+    8192 entries of the whole context (inputs resident in HBM).  qk="fp8":
+    the attention's non-RoPE QK product in FP8 (MXFP8 query against the FP8
+    codes); its roofline peak is the time-weighted mix of the FP8 (QK
+    non-RoPE) and BF16 (QK RoPE, PV) MFMA peaks."""
     w = synth.HCA_PREFILL_1M
     chunk = w.chunk
     c = w.tokens // chunk - 1
@@ -668,12 +673,14 @@ def secondary_hca_prefill(steps=5):
     q = synth.query_chunk(w, 0, c, chunk, 0, "cuda", with_index=False)["q"][None].contiguous()
     o = torch.empty((1, chunk, w.heads, w.d_nope), dtype=synth.TORCH_DTYPE[w.out_dtype], device="cuda")
     pos0 = c * chunk
+    adesc = type(lay.adesc).from_buffer_copy(lay.adesc)
+    adesc.qk_mode = cb.FP8E4M3 if qk == "fp8" else 0
 
     def step(ev=None):
         cb.compress_prefill(lay.kv, pos0, x["a"], x["za"], lay.prm["Ba"])
         if ev is not None:
             ev[0].record()
-        cb.dense_attn_prefill(lay.adesc, lay.kv, pos0, q, w.tau, o)
+        cb.dense_attn_prefill(adesc, lay.kv, pos0, q, w.tau, o)
         if ev is not None:
             ev[1].record()
     for _ in range(2):
@@ -691,10 +698,15 @@ def secondary_hca_prefill(steps=5):
     pairs = int(np.minimum((np.arange(pos0, pos0 + chunk) + 1) // w.m, w.tokens // w.m).sum())
     flops = 2.0 * pairs * w.heads * (w.c + w.d_nope)
     ach = flops / (attn_ms * 1e-3) / 1e12
-    return {"workload": w.name + " (last chunk)", "metric": "HCA prefill tokens/s (chunk of 8192 at 2^20 context)",
+    peak = PEAK_BF16_TFLOPS
+    if qk == "fp8":  # FP8 share: 2 * 64 * d_nope flop per pair of the 2 * 64 * (c + d_nope)
+        f8 = w.d_nope / (w.c + w.d_nope)
+        peak = 1.0 / (f8 / PEAK_FP8_TFLOPS + (1.0 - f8) / PEAK_BF16_TFLOPS)
+    return {"workload": w.name + " (last chunk)" + (", FP8 QK" if qk == "fp8" else ""),
+            "metric": "HCA prefill tokens/s (chunk of 8192 at 2^20 context)",
             "value": chunk / (ms * 1e-3), "unit": "tokens/s", "ms_per_chunk": ms,
             "roofline": {"bound": "mfma", "kernel": "dense attention prefill", "achieved": ach,
-                         "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                         "peak": peak, "unit": "TFLOP/s", "frac": ach / peak,
                          "algorithmic_flop_per_launch": flops, "avg_launch_ms": attn_ms}}
 
 
@@ -742,7 +754,7 @@ def main():
     ap.add_argument("--no-secondary", action="store_true", help="skip the decode workloads")
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
     ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "paged-decode",
-                                       "project-prefill", "planted-recall", "hca-prefill",
+                                       "project-prefill", "planted-recall", "hca-prefill", "hca-prefill-fp8qk",
                                        "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
@@ -765,6 +777,7 @@ def main():
               "swa-decode": swa_decode_lines, "paged-decode": paged_decode_lines,
               "project-prefill": secondary_project_prefill, "planted-recall": planted_recall_line,
               "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
+              "hca-prefill-fp8qk": lambda: secondary_hca_prefill(qk="fp8"),
               "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
               "peaks": measured_peaks}[args.only]
         print(json.dumps(fn()), flush=True)

@@ -270,9 +270,12 @@ def index_topk_decode(desc, keys: KVCache, pos, qI, w, k, idx, scores=None, ws=N
 
 
 def attn_desc(n_heads, d_nope, d_rope, q_fmt, o_fmt, nope_fmt, rope_fmt, m, capacity, base=10000.0, window=0,
-              page_size=0, pool_pages=0):
+              page_size=0, pool_pages=0, qk="bf16"):
+    """qk: "bf16" (the query's own format) or "fp8" (the non-RoPE query dims
+    rounded to MXFP8 and multiplied with the FP8 cache codes in FP8)."""
+    qk_mode = {"bf16": 0, "fp8": FP8E4M3}[qk]
     return AttnDesc(n_heads, d_nope, d_rope, FMT[q_fmt], FMT[o_fmt], FMT[nope_fmt], FMT.get(rope_fmt, F32),
-                    m, window, 0, base, capacity, page_size, 0, pool_pages)
+                    m, window, qk_mode, base, capacity, page_size, 0, pool_pages)
 
 
 def _ws(op, desc, B, T, pos0, k, ws, device):

@@ -138,7 +138,11 @@ static int validate_attn(const csa_attn_desc* d, int B, const void* q, const csa
   if (d->m < 1 || d->m > 256) return fail(CSA_ERR_INVALID_ARG, "m must be in 1..256");
   if (d->capacity < 1 || d->capacity > (int64_t(1) << 31) - 1) return fail(CSA_ERR_INVALID_ARG, "capacity must be in 1..2^31-1");
   if (d->window < 0) return fail(CSA_ERR_INVALID_ARG, "window must be >= 0");
-  if (d->qk_mode != 0) return fail(CSA_ERR_UNSUPPORTED, "qk_mode must be 0");
+  if (d->qk_mode != 0 && d->qk_mode != CSA_FP8E4M3) return fail(CSA_ERR_INVALID_ARG, "qk_mode must be 0 or FP8E4M3");
+  if (d->qk_mode == CSA_FP8E4M3 &&
+      (d->nope_dtype != CSA_FP8E4M3 || d->n_heads != 64 || d->d_nope != 512 || d->d_rope != 64 ||
+       d->q_dtype != CSA_BF16 || d->o_dtype != CSA_BF16 || d->rope_dtype != CSA_BF16))
+    return fail(CSA_ERR_UNSUPPORTED, "qk_mode FP8E4M3 needs 64 BF16 heads over 512 FP8 + 64 BF16 dims, BF16 output");
   if (d->reserved != 0) return fail(CSA_ERR_INVALID_ARG, "reserved field must be 0");
   if (!(d->rope_base > 0.0)) return fail(CSA_ERR_INVALID_ARG, "rope_base must be > 0");
   if (B < 0 || B > 65535) return fail(CSA_ERR_INVALID_ARG, "B must be in 0..65535");
@@ -158,7 +162,7 @@ static AttnParams make_attn_params(const csa_attn_desc* d, const void* q, const 
   AttnParams P{};
   P.H = d->n_heads; P.d_nope = d->d_nope; P.d_rope = d->d_rope;
   P.q_dt = d->q_dtype; P.o_dt = d->o_dtype; P.nope_dt = d->nope_dtype; P.rope_dt = d->rope_dtype;
-  P.m = d->m; P.base = d->rope_base; P.cap = d->capacity; P.window = d->window;
+  P.m = d->m; P.base = d->rope_base; P.cap = d->capacity; P.window = d->window; P.qk_mode = d->qk_mode;
   P.q = q; P.nope = kv->nope; P.scale = kv->scale; P.rope = kv->rope;
   P.idx = idx; P.k = k; P.scale_qk = scale; P.o = o; P.lse = lse;
   P.ws = ws; P.ws_bytes = ws_bytes;
@@ -183,6 +187,7 @@ int attn_dispatch(AttnParams& P, int op, int B, void* stream) {
                                        "paged) must stay below 2^31 bytes (2^21 BF16 or 2^22 FP8 entries of 512 dims)");
     return launch_mfma_attn(P, op, B, s);
   }
+  if (P.qk_mode != 0) return fail(CSA_ERR_UNSUPPORTED, "qk_mode FP8E4M3: sparse prefill lists of at most 1024");
   return launch_generic(P, B, s);
 }
 

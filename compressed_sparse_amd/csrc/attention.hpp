@@ -10,6 +10,7 @@ struct AttnParams {
   double base;
   int64_t cap;
   int64_t window;          // dense: attend the last `window` visible entries (0: all)
+  int qk_mode;             // 0, or CSA_FP8E4M3: the query's non-RoPE dims as MXFP8 against the FP8 codes
   int T;
   int64_t pos0;
   const int64_t* pos_dev;  // decode: per-sequence positions (T == 1)

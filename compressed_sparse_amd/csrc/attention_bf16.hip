@@ -49,6 +49,8 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef short v4s __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int NH = 64;
 constexpr int DN = 512;
@@ -171,9 +173,17 @@ __device__ __forceinline__ int tile_ids(const AttnParams& P, int b, const int* s
 // [base, base + bytes).  The loads go through the buffer path so that the
 // compiler keeps counting LDS reads in order around them.
 __device__ __forceinline__ uint32_t span(uint64_t b) { return b < 0xFFFFFFFFull ? static_cast<uint32_t>(b) : 0xFFFFFFFFu; }
+// Base and size are wave-uniform; they are read back from lane 0 so that the
+// descriptor is built in scalar registers even where the compiler has moved
+// their arithmetic to vector registers (a descriptor it takes for divergent
+// gets a loop over its distinct values around every load).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0), static_cast<int>(bytes),
-                                           0x00020000);
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  const int nb = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0), nb, 0x00020000);
 }
 
 // Load `it` of this wave's share of one tile.  BF16: it < 16 is non-RoPE row
@@ -242,6 +252,15 @@ __device__ __forceinline__ void issue_tile(uint8_t* buf, const AttnParams& P, co
   for (int it = 0; it < Lay<FP8>::NLOAD; ++it) issue_load<FP8>(buf, P, my_id, seq, it);
 }
 
+// A wave-uniform 64-bit value read back from lane 0: keeps it (and what is
+// computed from it) in scalar registers where its arithmetic went through
+// vector registers (the 64-bit division by m has no scalar form).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
 // One work item: query t of sequence b, entries [r0, r1) of its list (or of
 // the cache, dense) among the n visible ones.
 struct Item {
@@ -269,13 +288,13 @@ __device__ __forceinline__ Item make_item(const AttnParams& P, int64_t it, int s
     I.pos = P.pos0 + I.t;
   }
   int64_t n = I.pos < 0 ? 0 : (I.pos + 1) / P.m;
-  I.n = n > P.cap ? P.cap : n;
+  I.n = uniform64(n > P.cap ? P.cap : n);
   // dense: the visible entries [lo, n), lo > 0 under a sliding window; the
   // splits of a decode sequence cover them from lo on
   const int64_t lo = (DENSE && P.window > 0 && I.n > P.window) ? I.n - P.window : 0;
   const int64_t end = DENSE ? I.n : P.k;
-  I.r0 = lo + static_cast<int64_t>(I.split) * per_split;
-  I.r1 = I.r0 + per_split < end ? I.r0 + per_split : end;
+  I.r0 = uniform64(lo + static_cast<int64_t>(I.split) * per_split);
+  I.r1 = uniform64(I.r0 + per_split < end ? I.r0 + per_split : end);
   I.qrow = (static_cast<size_t>(I.b) * P.T + I.t) * NH;
   I.seq = static_cast<size_t>(I.b) * P.seq_stride;  // paged: 0 (rows are pool rows)
   return I;
@@ -342,6 +361,86 @@ __device__ __forceinline__ bf16x8 load_qs(const AttnParams& P, size_t qrow, int 
   return *reinterpret_cast<const bf16x8*>(qh + d);
 }
 
+// FP8 QK product: the query's non-RoPE dims as B operands of
+// v_mfma_scale_f32_32x32x64_f8f6f4.  With 8-bit operands that MFMA's k-block
+// b (b < 2, 32 k values, one E8M0 scale from lane 32b + column) is held as
+// bytes 16b .. 16b+15 of both lane halves: half h holds its elements
+// 16h .. 16h+15.  MFMA u (u < 8) covers dims 64u .. 64u+63 of head
+// 32hh + lane%32, k-block b being MX block 2u + b.  Lane half h first rounds
+// the whole MX block 2u + h to MXFP8 (OCP MX: shared exponent
+// e = floor(log2 amax) - 8, elements RNE(x / 2^e) on the E4M3 grid
+// saturating to +-448), then trades 16 codes with lane l ^ 32 (one
+// v_permlane32_swap per dword pair): q8[u] ends as the MFMA operand, qsc[u]
+// the lane's own block's E8M0 byte sb = e + 127.  amax comes from the BF16 bit patterns (|x| as
+// 16-bit integers orders like the values); its exponent field E gives
+// sb = E - 8, at least 0 (smaller block maxima, zero included, all take
+// 2^-127).  The hardware conversion divides the BF16 pair by the fp32 scale
+// 2^e exactly and rounds RNE on the OCP E4M3 grid, giving the NaN code above
+// 464; NaN bytes become +-448 (0x7E / 0xFE), the saturated value.  A wave
+// with a block of sb = 0 (2^-127 is not a normal fp32) takes the general
+// form for that block instead: each lane multiplies by its 2^-e, clamps to
+// +-448 and converts unscaled (the branch is uniform over the wave).
+__device__ __forceinline__ uint32_t fp8x4_scaled(uint32_t d0, uint32_t d1, float s) {
+  typedef short v2s __attribute__((ext_vector_type(2)));
+  v2s r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(v2s{0, 0}, __builtin_bit_cast(bf16x2, d0), s, false);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, __builtin_bit_cast(bf16x2, d1), s, true);
+  const uint32_t w = __builtin_bit_cast(uint32_t, r);
+  // bytes 0x7F / 0xFF (NaN) lose one: (w & 0x7F..) + 0x01.. sets bit 7 of
+  // exactly those bytes, with no carry between bytes
+  return w - ((((w & 0x7F7F7F7Fu) + 0x01010101u) & 0x80808080u) >> 7);
+}
+__device__ __forceinline__ uint32_t fp8x4_general(uint32_t d0, uint32_t d1, float f) {
+  const float y0 = __builtin_amdgcn_fmed3f(__uint_as_float(d0 << 16) * f, -448.0f, 448.0f);
+  const float y1 = __builtin_amdgcn_fmed3f(__uint_as_float(d0 & 0xFFFF0000u) * f, -448.0f, 448.0f);
+  const float y2 = __builtin_amdgcn_fmed3f(__uint_as_float(d1 << 16) * f, -448.0f, 448.0f);
+  const float y3 = __builtin_amdgcn_fmed3f(__uint_as_float(d1 & 0xFFFF0000u) * f, -448.0f, 448.0f);
+  const int w = __builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false);
+  return static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y2, y3, w, true));
+}
+__device__ __forceinline__ void load_q8(const AttnParams& P, size_t qrow, int hh, i32x8 (&q8)[8], int (&qsc)[8]) {
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  // 16-byte chunk 8u + 4h + c (c < 4) of the row holds block 2u + h
+  const u32x4* qh =
+      reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(P.q) + (qrow + 32 * hh + (lane & 31)) * CW) + 4 * half;
+  u32x4 raw[8][4];
+#pragma unroll
+  for (int u = 0; u < 8; ++u)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) raw[u][c] = qh[8 * u + c];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    u16x2 mx = u16x2{0, 0};
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        mx = __builtin_elementwise_max(mx, __builtin_bit_cast(u16x2, raw[u][c][i] & 0x7FFF7FFFu));
+    const int E = static_cast<int>((mx[0] > mx[1] ? mx[0] : mx[1]) >> 7);
+    const int sb = E > 8 ? E - 8 : 0;
+    qsc[u] = sb;
+    uint32_t c[8];  // codes of dims 4j .. 4j+3 of the lane's block: input dwords 2j, 2j + 1
+    if (__builtin_amdgcn_ballot_w64(sb == 0) == 0) {
+      const float sc = __uint_as_float(static_cast<uint32_t>(sb) << 23);  // 2^e
+#pragma unroll
+      for (int j = 0; j < 8; ++j) c[j] = fp8x4_scaled(raw[u][j >> 1][2 * (j & 1)], raw[u][j >> 1][2 * (j & 1) + 1], sc);
+    } else {
+      const float f = __uint_as_float(static_cast<uint32_t>(254 - sb) << 23);  // 2^-e
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        c[j] = fp8x4_general(raw[u][j >> 1][2 * (j & 1)], raw[u][j >> 1][2 * (j & 1) + 1], f);
+    }
+    // lanes < 32 (block 2u) keep codes 0..15 and take block 2u + 1's codes
+    // 0..15 from lane l + 32, which keeps its codes 16..31 and takes block
+    // 2u's codes 16..31
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const auto sw = __builtin_amdgcn_permlane32_swap(c[j], c[4 + j], false, false);
+      q8[u][j] = static_cast<int>(sw[0]);
+      q8[u][4 + j] = static_cast<int>(sw[1]);
+    }
+  }
+}
+
 // Turns the RoPE k-steps (dims 512..575, pairs (2p, 2p+1)) by position pos.
 // Lane pair p = 8(s - DN/16) + 4 half + i: theta_p = r^(4 half) r^(8(s -
 // DN/16)) r^i, a few fp64 products (relative error ~1e-15).
@@ -367,7 +466,7 @@ __device__ __forceinline__ void rope_q(const Theta& th, int64_t pos, bf16x8 (&qf
   }
 }
 
-template <bool FP8, bool DENSE, bool SPLIT, bool PAGED>
+template <bool FP8, bool DENSE, bool SPLIT, bool PAGED, bool QK8>
 __global__ void __launch_bounds__(NT, 1)
 attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* part, int64_t nitems, int nbatch) {
   typedef Lay<FP8> L;
@@ -399,12 +498,19 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     load_list(P, I, tid, lr);
     nvalid = compact_list(lr, P.list_rows ? P.span_rows : I.n, s_list, s_cnt);
   }
-  int ntiles = (nvalid + TILE - 1) / TILE;
+  // the tile count is wave-uniform; read back from lane 0 so that the tile
+  // loop's exit (and what it carries: buffer parity, prefetch ids) stays
+  // scalar control flow
+  int ntiles = __builtin_amdgcn_readfirstlane((nvalid + TILE - 1) / TILE);
   int par = 0;  // buffer of the next tile: kb0 / kb1
   if (ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
+  // BF16 query fragments (QK8: the RoPE k-steps only)
+  constexpr int Q0 = QK8 ? DN / 16 : 0;
   bf16x8 qf[QS];
 #pragma unroll
-  for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
+  for (int s = Q0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
+  i32x8 q8[8];  // QK8: the non-RoPE dims as MXFP8 codes and scales (else unused)
+  int qsc[8];
 
   // LDS byte offsets of the S^T A operand (32x32x16): row 32eh + lane%32,
   // chunk 2i + lane/32 of the non-RoPE row (BF16: k-step i, FP8: k-steps 2i
@@ -414,7 +520,13 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   {
     const int r = 32 * eh + (lane & 31);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) offA[i] = r * L::NROWB + 16 * ((2 * i + half) ^ (FP8 ? swzf(r) : swz(r)));
+    for (int i = 0; i < 8; ++i) {
+      // QK8: reads 2i' and 2i' + 1 of scaled MFMA i' take chunks
+      // 4i' + half and 4i' + 2 + half (dims 64i' + 16half .. +16 and
+      // 64i' + 32 + 16half .. +16, the lane's share of both k-blocks)
+      const int c = QK8 ? 4 * (i >> 1) + half + 2 * (i & 1) : 2 * i + half;
+      offA[i] = r * L::NROWB + 16 * (c ^ (FP8 ? swzf(r) : swz(r)));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) offR[i] = L::ROPE_OFF + r * RROW + 16 * ((2 * i + half) ^ swz_rope(r));
   }
@@ -475,6 +587,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     int nvalid_n = 0;
     bool next_started = false;
 
+    if (QK8) load_q8(P, I.qrow, hh, q8, qsc);
     rope_q(th, I.pos, qf);
     // entry ids of the tile whose loads the current tile issues (read ahead)
     int my_id_pf = ntiles > 1 ? tile_ids<DENSE, PAGED>(P, I.b, s_list, TILE, I.r0, nvalid) : 0;
@@ -558,13 +671,27 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       f32x16 sacr = f32x16{};  // FP8: the RoPE part, unscaled
       {
         u32x4 ring[SPF];
+        u32x4 a_lo = u32x4{};  // QK8: the first half of a scaled MFMA's A operand
 #pragma unroll
         for (int u = 0; u < SPF; ++u) ring[u] = aop(u);
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
           const u32x4 a = ring[u % SPF];
           if (u + SPF < NU) ring[u % SPF] = aop(u + SPF);
-          if (FP8 && u < NUN) {
+          if (QK8 && u < NUN) {
+            // codes in as stored (scale 2^0), the query's block scale from
+            // its E8M0 byte; the entry's fp32 scale follows on the sum
+            if (u & 1) {
+              const i32x8 a8 = __builtin_bit_cast(i32x8, __builtin_shufflevector(a_lo, a, 0, 1, 2, 3, 4, 5, 6, 7));
+              sacc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a8, q8[u >> 1], sacc, 0, 0, 0, 127, 0,
+                                                                     qsc[u >> 1]);
+              // keeps the compiler from sinking the scaled MFMAs to the
+              // end of the loop, away from the loads they hide
+              asm volatile("" : "+v"(sacc));
+            } else {
+              a_lo = a;
+            }
+          } else if (FP8 && u < NUN) {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_bf16(a[0], a[1]), qf[2 * u], sacc, 0, 0, 0);
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fp8x8_bf16(a[2], a[3]), qf[2 * u + 1], sacc, 0, 0, 0);
           } else if (FP8) {
@@ -579,7 +706,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       }
       if (last && has_next) {
 #pragma unroll
-        for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, In.qrow, hh, s);
+        for (int s = Q0; s < QS; ++s) qf[s] = load_qs<FP8>(P, In.qrow, hh, s);
       }
       // FP8: S = scale_e (q . codes_e) + (q_rope . k_rope_e); P^T carries the
       // scale into O (the V rows in LDS are unscaled codes)
@@ -782,13 +909,13 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       if (par == 0) start_next(kb0);
       else start_next(kb1);
 #pragma unroll
-      for (int s = 0; s < QS; ++s) qf[s] = load_qs<FP8>(P, In.qrow, hh, s);
+      for (int s = Q0; s < QS; ++s) qf[s] = load_qs<FP8>(P, In.qrow, hh, s);
     }
     staged = defer;
     I = In;
     it = itn;
-    nvalid = nvalid_n;
-    ntiles = (nvalid + TILE - 1) / TILE;
+    nvalid = __builtin_amdgcn_readfirstlane(nvalid_n);
+    ntiles = __builtin_amdgcn_readfirstlane((nvalid + TILE - 1) / TILE);
     ++round;
   }
   wait_vmem();  // no load into this workgroup's LDS outlives it
@@ -826,8 +953,23 @@ void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int
   // lists arrive as pool rows)
   const bool paged = dense && P.pg.table != nullptr;
 #define CSA_ATTN_LAUNCH(F, D, S, G) \
-  hipLaunchKernelGGL((attn_bf16_kernel<F, D, S, G>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B)
-  if (fp8) {
+  hipLaunchKernelGGL((attn_bf16_kernel<F, D, S, G, false>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B)
+#define CSA_ATTN_LAUNCH8(D, S, G) \
+  hipLaunchKernelGGL((attn_bf16_kernel<true, D, S, G, true>), grid, dim3(NT), 0, s, P, th, splits, per, part, nitems, B)
+  if (fp8 && P.qk_mode == CSA_FP8E4M3) {
+    if (dense) {
+      if (paged) {
+        if (split) CSA_ATTN_LAUNCH8(true, true, true);
+        else CSA_ATTN_LAUNCH8(true, false, true);
+      } else {
+        if (split) CSA_ATTN_LAUNCH8(true, true, false);
+        else CSA_ATTN_LAUNCH8(true, false, false);
+      }
+    } else {
+      if (split) CSA_ATTN_LAUNCH8(false, true, false);
+      else CSA_ATTN_LAUNCH8(false, false, false);
+    }
+  } else if (fp8) {
     if (dense) {
       if (paged) {
         if (split) CSA_ATTN_LAUNCH(true, true, true, true);
@@ -855,6 +997,7 @@ void launch_attn_bf16(const AttnParams& P, bool dense, int B, hipStream_t s, int
     }
   }
 #undef CSA_ATTN_LAUNCH
+#undef CSA_ATTN_LAUNCH8
 }
 
 }  // namespace csa

@@ -146,7 +146,16 @@ typedef struct csa_attn_desc {
                          (a sliding window; with m = 1 over per-token entries, the
                          sliding-window branch); 0 = every visible entry.  Must be 0
                          for sparse attention. */
-  int32_t qk_mode;    /* must be 0: QK in the query's own format */
+  int32_t qk_mode;    /* 0: QK in the query's own format.  CSA_FP8E4M3 (FP8 cache,
+                         64 BF16 heads over 512 + 64 dims, BF16 output): each head's
+                         512 non-RoPE query dims are rounded to MXFP8 inside the call
+                         (OCP MX: blocks of 32 dims, E4M3 elements RNE saturating at
+                         448, one E8M0 scale 2^(floor(log2 amax) - 8)) and multiplied
+                         with the cache's FP8 codes in FP8 (exact products, fp32 sums,
+                         the entry scale applied to the sum); the RoPE dims stay BF16.
+                         A reading of [CSA/HCA 混注意力] §1.4 存储格式混 (non-RoPE dims
+                         in FP8, RoPE dims in BF16).  CSA_ERR_UNSUPPORTED for other
+                         shapes, and for sparse prefill lists longer than 1024. */
   double rope_base;
   int64_t capacity;   /* entries per sequence */
   int32_t page_size;  /* KV cache paging, as csa_cache_desc.page_size */

@@ -218,6 +218,28 @@ def test_window_and_merge_validation():
     assert L.csa_lse_merge(0, 64, 512, 1, P, P, P, P, P, None, None) == 0
 
 
+def test_fp8_qk_mode_validation():
+    """qk_mode: 0 or FP8E4M3; the FP8 QK product needs an FP8 cache and the
+    64-head 512 + 64 shape (rejected on the host, before any launch)."""
+    L = cb.lib()
+    P = fake(0x4000)
+    kv = cb.Cache(0x1000, 0x5000, 0x2000, 0x3000)
+    bad = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 128, 8192)
+    bad.qk_mode = 3
+    assert L.hca_dense_attn_prefill(ctypes.byref(bad), 1, 16, 0, P, ctypes.byref(kv), 0.1, P, None, P, 1 << 30,
+                                    None) == 1
+    for d in (cb.attn_desc(64, 512, 64, "bf16", "bf16", "bf16", "bf16", 128, 8192, qk="fp8"),
+              cb.attn_desc(32, 512, 64, "bf16", "bf16", "fp8", "bf16", 128, 8192, qk="fp8"),
+              cb.attn_desc(64, 512, 64, "f32", "bf16", "fp8", "bf16", 128, 8192, qk="fp8")):
+        assert L.hca_dense_attn_prefill(ctypes.byref(d), 1, 16, 0, P, ctypes.byref(kv), 0.1, P, None, P, 1 << 30,
+                                        None) == 3
+        assert b"qk_mode" in L.csa_last_error()
+    # sparse prefill lists beyond 1024 entries have no FP8 QK kernel
+    d = cb.attn_desc(64, 512, 64, "bf16", "bf16", "fp8", "bf16", 4, 8192, qk="fp8")
+    assert L.csa_sparse_attn_prefill(ctypes.byref(d), 1, 16, 0, P, ctypes.byref(kv), P, 2048, 0.1, P, None, P,
+                                     1 << 30, None) == 3
+
+
 def test_paging_fields_are_validated_before_launch():
     # paged caches: page_size a power of two in 64..65536, capacity a multiple
     # of it, pool_pages >= 1, a block table exactly when paged (4-byte aligned)
