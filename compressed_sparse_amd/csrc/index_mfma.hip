@@ -33,6 +33,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr int HI = 16;
 constexpr int DI = 64;
@@ -183,8 +184,15 @@ __device__ __forceinline__ void wave_radix_select(const float* row, int n, int k
 // threshold bin of more than SEL_CBH entries in a half (heavy ties), takes
 // the radix select.
 // FROM_WS: no scoring; the 4 rows' scores come from the workspace rows a
-// scan kernel wrote (MXFP4 prefill), then the same select.
-template <bool KFP8, bool FROM_WS>
+// scan kernel wrote (rows the LDS does not hold, or scores requested), then
+// the same select.
+// MX: MXFP4 keys and query (operands formed by index_mx_prep_kernel): waves
+// take 32-entry key blocks in turn; per block two scaled FP4 MFMAs, the A
+// rows of the first carrying queries 0 and 1 (16 heads each), of the second
+// queries 2 and 3, as in the two-query scan; after the ReLU-weighted head
+// sums and one cross-half swap per MFMA, lanes 0..31 hold queries 0 and 2,
+// lanes 32..63 queries 1 and 3.
+template <bool KFP8, bool FROM_WS, bool MX = false>
 __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexParams P) {
   __shared__ __align__(16) float srow[QG][FUSED_NMAX];
   // select state (histograms, bin-B candidates, ranks); while scoring, the
@@ -259,6 +267,97 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
       if (lane == 0) {
         s_mm[w][qq][0] = mnv;
         s_mm[w][qq][1] = mxv;
+      }
+    }
+   } else if constexpr (MX) {
+    const int qsel = (lane >> 4) & 1, mine = lane >> 5;
+    i32x8 qa[2];
+    int qs[2];
+    float wv[2][2][8];  // pair p, query 2p + i, head of accumulator v
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const bool lq = t0 + 2 * p + qsel < P.T;
+      u32x4 qc = {0u, 0u, 0u, 0u};
+      qs[p] = 127;
+      if (lq) {
+        const uint8_t* qp = P.qpack + (row0 + 2 * p + qsel) * QPACK_ROW_BYTES;
+        const int ql = (lane & 15) + 32 * (lane >> 5);
+        qc = reinterpret_cast<const u32x4*>(qp)[ql];
+        qs[p] = reinterpret_cast<const int*>(qp + 64 * 16)[ql];
+      }
+      qa[p] = i32x8{static_cast<int>(qc[0]), static_cast<int>(qc[1]), static_cast<int>(qc[2]),
+                    static_cast<int>(qc[3]), 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int v = 0; v < 8; ++v) {
+          const int h = (v & 4 ? 8 : 0) + 4 * (lane >> 5) + (v & 3);
+          wv[p][i][v] = t0 + 2 * p + i < P.T ? P.w[(row0 + 2 * p + i) * HI + h] : 0.0f;
+        }
+    }
+    // this lane's rows: queries mine (pair 0) and 2 + mine (pair 1)
+    const int nvr[2] = {nvis(mine), nvis(2 + mine)};
+    float mnr[2] = {INFINITY, INFINITY}, mxr[2] = {-INFINITY, -INFINITY};
+    const size_t seq = static_cast<size_t>(b) * P.cap;
+    const uint8_t* kb = static_cast<const uint8_t*>(P.knope) + seq * (DI / 2);
+    const uint8_t* sb = static_cast<const uint8_t*>(P.kscale) + seq * (DI / 32);
+    const int nb32 = (nmax + 31) / 32;
+    // lane l loads entry 32 c + l % 32, half l / 32 (a block past the end
+    // re-reads the last entry); MXD blocks in flight per wave
+    constexpr int MXD = 8;
+    auto loadk = [&](int c, u32x4& kc, uint32_t& ks) {
+      const int e = min(32 * c + (lane & 31), nmax - 1);
+      kc = *reinterpret_cast<const u32x4*>(kb + static_cast<uint32_t>(e * (DI / 2) + 16 * (lane >> 5)));
+      ks = sb[static_cast<uint32_t>(e * (DI / 32) + (lane >> 5))];
+    };
+    u32x4 kr[MXD];
+    uint32_t kss[MXD];
+#pragma unroll
+    for (int i = 0; i < MXD; ++i) loadk(min(w + FW * i, nb32 - 1), kr[i], kss[i]);
+    for (int cb = w; cb < nb32; cb += FW * MXD) {
+#pragma unroll
+      for (int i = 0; i < MXD; ++i) {
+        const int c = cb + FW * i;
+        const i32x8 kv = {static_cast<int>(kr[i][0]), static_cast<int>(kr[i][1]), static_cast<int>(kr[i][2]),
+                          static_cast<int>(kr[i][3]), 0, 0, 0, 0};
+        const int ksc = static_cast<int>(kss[i]);
+        loadk(min(c + FW * MXD, nb32 - 1), kr[i], kss[i]);
+        if (c < nb32) {
+#pragma unroll
+          for (int p = 0; p < 2; ++p) {
+            // formats 4, 4: E2M1 A and B; scale bytes in bits 0..7
+            const f32x16 acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(qa[p], kv, f32x16{}, 4, 4, 0, qs[p], 0,
+                                                                               ksc);
+            float p0 = 0.0f, p1 = 0.0f;
+#pragma unroll
+            for (int v = 0; v < 8; ++v) {
+              p0 = fmaf(wv[p][0][v], relu(acc[v]), p0);
+              p1 = fmaf(wv[p][1][v], relu(acc[v + 8]), p1);
+            }
+            const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+            float tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+            if (P.score_dt == CSA_BF16) tot = round_bf16(tot);
+            const int e = 32 * c + (lane & 31);
+            if (e < nvr[p]) {
+              srow[2 * p + mine][e] = tot;
+              mnr[p] = fminf(mnr[p], tot);
+              mxr[p] = fmaxf(mxr[p], tot);
+            }
+          }
+        }
+      }
+    }
+    // per-row extremes of this wave's scores (the 32 lanes of each row)
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+#pragma unroll
+      for (int o = 1; o < 32; o <<= 1) {
+        mnr[p] = fminf(mnr[p], __shfl_xor(mnr[p], o));
+        mxr[p] = fmaxf(mxr[p], __shfl_xor(mxr[p], o));
+      }
+      if ((lane & 31) == 0) {
+        s_mm[w][2 * p + mine][0] = mnr[p];
+        s_mm[w][2 * p + mine][1] = mxr[p];
       }
     }
    } else {
@@ -785,7 +884,6 @@ __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(KFMT =
 // ---------------------------------------------------------------------------
 // MXFP4 keys and query
 // ---------------------------------------------------------------------------
-typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 // One wave per query row (decode: one row per workgroup, whose other waves
 // clear the row's histogram).  The wave rounds the row's query to MXFP4 (per
@@ -999,13 +1097,21 @@ int launch_index_mx_prep(const IndexParams& P, int rows, hipStream_t s) {
 }
 
 bool index_fused_prefill_ok(const IndexParams& P, int64_t n_max) {
-  return index_mfma_supported(P) && P.qk_dt == CSA_BF16 && P.pos_dev == nullptr && n_max <= FUSED_NMAX;
+  return index_mfma_supported(P) && P.pos_dev == nullptr && P.pg.table == nullptr && n_max <= FUSED_NMAX;
 }
 
+// MXFP4: the query operands are formed first (index_mx_prep_kernel)
 int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
   dim3 grid((P.T + QG - 1) / QG, B);
-  if (P.key_dt == CSA_FP8E4M3) hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * FW), 0, s, P);
-  else hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * FW), 0, s, P);
+  if (P.qk_dt == CSA_MXFP4) {
+    const int st = launch_index_mx_prep(P, B * P.T, s);
+    if (st != CSA_OK) return st;
+    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false, true>), grid, dim3(64 * FW), 0, s, P);
+  } else if (P.key_dt == CSA_FP8E4M3) {
+    hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * FW), 0, s, P);
+  } else {
+    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * FW), 0, s, P);
+  }
   return check_launch("index_prefill_fused_kernel");
 }
 

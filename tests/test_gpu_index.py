@@ -259,6 +259,36 @@ def test_prefill_mxfp4_bf16_scores(T):
             assert (gs == rs[t]).mean() > 0.99
 
 
+@pytest.mark.parametrize("T,pos0", [(203, 4 * 8000 + 1), (6, 4 * 1030), (37, 4 * 200)])
+def test_prefill_mxfp4_fused_equals_scan(T, pos0):
+    """MXFP4 prefill with no scores requested runs the fused kernel (scores
+    scored by the scaled FP4 MFMA straight into LDS, then the select); it
+    must give the bits of the scan + select path (the same MFMA, head sum
+    and select), and the oracle's sets within the BF16-score allowance.  Rows
+    near n = k and an odd T (a partial last workgroup) included."""
+    B, H, d, m, k = 2, 16, 64, 4, 1024
+    cap = (pos0 + T) // m + 4
+    kc, K = key_cache("mxfp4", B, cap, d, m, seed=28)
+    qI = synth.normal((B, T, H, d), "qI", 28, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((B, T, H), "w", 28, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "mxfp4", "mxfp4", "bf16", m, cap)
+    fused = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    scan = torch.empty((B, T, k), dtype=torch.int32, device=DEV)
+    scores = torch.zeros((B, T, cap), dtype=torch.float32, device=DEV)
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, fused)
+    cb.index_topk_prefill(desc, kc, pos0, qI, w, k, scan, scores)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, scan)
+    got = fused.cpu().numpy()
+    for b in range(B):
+        assert ascending_padded(got[b])
+        ri, rs = oracle_rows(np64(qI[b]), np64(w[b]), K[b], pos0 + np.arange(T), m, k, "mxfp4", "bf16")
+        for t in range(0, T, 5):
+            qq = csa.quantize_query(np64(qI[b, t]), "mxfp4")
+            delta = 2.0 ** -7 * np.abs(rs[t]) + fp32_score_bound(qq, np64(w[b, t]), K[b], len(rs[t]))
+            assert topk_explained(got[b, t], ri[t], rs[t], delta, 0.0), f"sequence {b}: row {t}"
+
+
 def test_prefill_rows_longer_than_fused_limit():
     """Rows with more than 8192 visible entries: streaming scan, then the
     one-workgroup-per-row radix select."""
