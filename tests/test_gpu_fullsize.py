@@ -29,6 +29,7 @@ import numpy as np
 import pytest
 import torch
 
+from compressed_sparse_amd import binding as cb
 from compressed_sparse_amd import path, synth
 from oracle import csa
 from tests import fullsize_ref as R
@@ -217,6 +218,9 @@ def test_hca_prefill_1m_chunked():
     lay = path.HcaLayer(w, 1, T // w.m + 1)
     last = T // chunk - 1
     checked = {0: None, 1: None, 64: None, last: None}
+    checked8 = {64: None, last: None}   # the FP8 QK product, as bench.py times it on the last chunk
+    d8 = type(lay.adesc).from_buffer_copy(lay.adesc)
+    d8.qk_mode = cb.FP8E4M3
     rng = np.random.default_rng(3)
     for c in range(T // chunk):
         lay.compress_chunk(c, chunk)
@@ -227,6 +231,10 @@ def test_hca_prefill_1m_chunked():
         if c in checked:
             rows = np.unique(np.concatenate([[0, 126, 127, 128, chunk - 1], rng.integers(0, chunk, 11)]))
             checked[c] = (rows, R.host(q[0])[rows], R.host(o[0])[rows], R.host(lse[0])[rows])
+        if c in checked8:
+            cb.dense_attn_prefill(d8, lay.kv, c * chunk, q, w.tau, o, lse)
+            rows = checked[c][0]
+            checked8[c] = (rows, R.host(o[0])[rows], R.host(lse[0])[rows])
     torch.cuda.synchronize()
     cache = hca_reference_cache(w, 0, T, chunk)
     gcache = gpu_hca_cache(lay, 0, T // w.m)
@@ -235,6 +243,10 @@ def test_hca_prefill_1m_chunked():
         for leg, cc in (("A", cache), ("B", gcache)):
             oref, lref = csa.hca_rows(pos, q, cc, w.m, w.d_nope, w.rope_base, w.tau)
             G.check_attention(f"hca prefill chunk {c} [{leg}]", o, lse, oref, lref)
+            if c in checked8:
+                _, o8, l8 = checked8[c]
+                oref8, lref8 = csa.hca_rows(pos, q, cc, w.m, w.d_nope, w.rope_base, w.tau, qk_fmt="mxfp8")
+                G.check_attention(f"hca prefill chunk {c} FP8 QK [{leg}]", o8, l8, oref8, lref8)
         if c == 0:
             assert (o[rows < 127] == 0).all()   # no entry visible yet
             assert np.isneginf(lse[rows < 127]).all()
