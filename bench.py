@@ -321,16 +321,20 @@ def csa_decode_line(n_steps=DECODE_STEPS):
     return line
 
 
-def hca_decode_line(n_steps=DECODE_STEPS):
+def hca_decode_line(n_steps=DECODE_STEPS, qk="bf16"):
+    """qk="fp8": the FP8 QK product (MXFP8 query against the FP8 codes)."""
     w = synth.HCA_DECODE_B16_1M
     log(f"setup {w.name}")
-    lay = path.HcaLayer(w, w.batch, w.tokens // w.m + n_steps)
+    lay = path.HcaLayer(w, w.batch, w.tokens // w.m + n_steps, qk=qk)
     lay.prefill_context(w.tokens)
     o = lay.alloc_decode_outputs()
     xs = lay.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
     ms3 = time_graph([lay], lambda i: lay.decode_step(xs[i], o), n_steps)
     by = decode_bytes_hca(w, w.tokens // w.m, w.batch)
-    line = decode_line(w.name, "decode us/step (whole batch)", ms3, by, w.batch)
+    line = decode_line(w.name + (", FP8 QK" if qk == "fp8" else ""), "decode us/step (whole batch)", ms3, by,
+                       w.batch)
+    if qk == "fp8":
+        return line
     if CPU_BASELINE:
         log("cpu baseline (oracle) " + w.name)
         line["cpu_baseline"] = cpu_baseline_hca_decode(w, lay, xs[-1], seqs=[9])
@@ -760,6 +764,7 @@ def main():
     ap.add_argument("--copy-calib", action="store_true", help="run a 1 GiB copy first (counter calibration)")
     ap.add_argument("--only", choices=["csa-decode", "hca-decode", "pair-decode", "swa-decode", "paged-decode",
                                        "project-prefill", "planted-recall", "hca-prefill", "hca-prefill-fp8qk",
+                                       "hca-decode-fp8qk",
                                        "hca-prefill-whole",
                                        "mxfp4-indexer", "tiny", "peaks"],
                     help="run just this secondary workload and print its line(s) (for profiling)")
@@ -783,6 +788,7 @@ def main():
               "project-prefill": secondary_project_prefill, "planted-recall": planted_recall_line,
               "hca-prefill": secondary_hca_prefill, "hca-prefill-whole": secondary_hca_prefill_whole,
               "hca-prefill-fp8qk": lambda: secondary_hca_prefill(qk="fp8"),
+              "hca-decode-fp8qk": lambda: hca_decode_line(qk="fp8"),
               "mxfp4-indexer": secondary_mxfp4_prefill_indexer, "tiny": secondary_tiny,
               "peaks": measured_peaks}[args.only]
         print(json.dumps(fn()), flush=True)

@@ -184,7 +184,9 @@ class HcaLayer:
     """seq_ids: the seeded sequence held in each batch slot (default 0..B-1)."""
 
     def __init__(self, w: synth.Workload, B, capacity, device="cuda", seed=0, seq_ids=None, page_size=0,
-                 block_table=None, pool_pages=0):
+                 block_table=None, pool_pages=0, qk="bf16"):
+        """qk: "bf16", or "fp8" for the FP8 QK product (MXFP8 query against the
+        FP8 cache codes)."""
         self.w, self.B, self.cap, self.device, self.seed = w, B, capacity, device, seed
         self.seq_ids = list(seq_ids) if seq_ids is not None else list(range(B))
         assert len(self.seq_ids) == B
@@ -193,7 +195,7 @@ class HcaLayer:
                                                     w.rope_fmt, capacity, w.rope_base, **k),
                           B, device, page_size, block_table, pool_pages, capacity)
         self.adesc = cb.attn_desc(w.heads, w.d_nope, w.d_rope, w.act_dtype, w.out_dtype, w.nope_fmt, w.rope_fmt,
-                                  w.m, capacity, w.rope_base, **pg)
+                                  w.m, capacity, w.rope_base, qk=qk, **pg)
         self.prm = synth.compressor_params(w, seed, device)
         self.aws = None
 
