@@ -130,6 +130,18 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// x of lanes l and l ^ 32 combined in both (v_permlane32_swap: lanes 0..31
+// receive the upper half's values and give theirs, no LDS round trip as a
+// ds_bpermute shuffle takes).
+__device__ __forceinline__ float max_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+}
+__device__ __forceinline__ float sum_xor32(float x) {
+  const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+}
+
 // Row of a 32x32 MFMA result held in register v of this lane.
 __device__ __forceinline__ int acc_row(int v, int lane) { return (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3); }
 
@@ -638,10 +650,13 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
         staged = false;
       }
       // The next tile's loads (this item's tile j+1, or the next item's first
-      // tile) are spread over this tile's MFMAs: a wave that issues them back
-      // to back stalls until the memory pipeline takes them.  Every tile
-      // issues all of them, without branches in the MFMA loops; with no next
-      // tile they re-read the current item's first entry into the free buffer.
+      // tile) are spread over this tile's MFMAs (a wave that issues them back
+      // to back stalls until the memory pipeline takes them), none in the
+      // softmax, whose VALU work would wait behind them: most in the S^T
+      // MFMAs, the rest early in PV (the split measured best per format).
+      // Every tile issues all of them, without branches in the MFMA loops;
+      // with no next tile they re-read the current item's first entry into
+      // the free buffer.
       int my_id = 0;
       size_t lseq = I.seq;
       if (!last) {
@@ -700,7 +715,9 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
           } else {
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), qf[u], sacc, 0, 0, 0);
           }
-          if (FP8 ? u % 5 == 2 : u % 7 == 3) issue_load<FP8>(nxt, P, my_id, lseq, FP8 ? u / 5 : u / 7);  // loads 0..3 / 0..4
+          // loads 0..11 (BF16), 0..9 (FP8), 0..6 (QK8)
+          if (QK8 ? u % 3 == 1 : FP8 ? u % 2 == 1 : u % 3 == 1)
+            issue_load<FP8>(nxt, P, my_id, lseq, QK8 ? u / 3 : FP8 ? u / 2 : u / 3);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -745,7 +762,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       float mx = -INFINITY;
 #pragma unroll
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[v]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32)) * lscale;
+      mx = max_xor32(mx) * lscale;
       if (lane < 32) s_xchg[eh][head] = mx;
       const bool bad = m_run == -INFINITY || !(mx <= m_run + 8.0f);
       const bool wave_bad = __ballot(bad) != 0ull;
@@ -768,10 +785,6 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
       };
       float psum = 0.0f;
       if (!wave_bad) psum = write_p();
-      // loads 5..12 (FP8: 4..7 and the scales) stall the wave where it waits anyway
-#pragma unroll
-      for (int q = FP8 ? 4 : 5; q < (FP8 ? 8 : 13); ++q) issue_load<FP8>(nxt, P, my_id, lseq, q);
-      if (FP8) issue_load<FP8>(nxt, P, my_id, lseq, 10);
       lds_sync();
       if (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) {
         const float mall = fmaxf(mx, s_xchg[eh ^ 1][head]);
@@ -847,8 +860,9 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
 #pragma unroll
           for (int nb = 0; nb < 2; ++nb)
             oacc[t & 3][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbr[ks & 1][nb], oacc[t & 3][nb], 0, 0, 0);
-          // loads 13..17 (FP8: 8, 9)
-          if (FP8 ? t % 8 == 3 : t % 3 == 1) issue_load<FP8>(nxt, P, my_id, lseq, FP8 ? 8 + t / 8 : 13 + t / 3);
+          // loads 12..17 (BF16), 10 (FP8), 7..10 (QK8)
+          if (QK8 ? t % 4 == 1 : FP8 ? t == 1 : t % 2 == 1 && t < 12)
+            issue_load<FP8>(nxt, P, my_id, lseq, QK8 ? 7 + t / 4 : FP8 ? 10 : 12 + t / 2);
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -860,7 +874,7 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     }
 
     // --- finish: denominators and maxima to LDS, then each wave its O^T ----
-    l_part += __shfl_xor(l_part, 32);
+    l_part = sum_xor32(l_part);
     lds_sync();  // every wave done with the last tile: its buffer is free
     if (lane < 32) s_xchg[eh][head] = l_part;
     if (eh == 0 && lane < 32) s_m[head] = m_run;
