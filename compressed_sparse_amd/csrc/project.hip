@@ -21,6 +21,8 @@
 // the rows of the call's last tokens; project_finalize_kernel turns and
 // stores the entries like the compressor, project_ring_kernel refreshes the
 // ring.  The GEMM dominates: 2 * d_model flop per token and column.
+#include <type_traits>
+
 #include "compress_store.hpp"
 
 namespace csa {
@@ -154,9 +156,33 @@ __device__ __forceinline__ void project_gemm_body(const ProjParams& P) {
   swrite(0);
   if (S > 1) gload(1);
   lds_sync();
-  for (int ks = 0; ks < S; ++ks) {
+  // per stage: LA + LB pieces, each the LDS write of one register of the
+  // next stage's rows (loaded during the previous stage) followed by that
+  // register's load for the stage after next, spread evenly over the stage's
+  // MFMAs so that neither the writes nor the load issue hold up the MFMA
+  // stream; the other buffer is free, every wave having finished its
+  // previous stage before the last barrier
+  constexpr int NPC = LA + LB;                      // pieces per stage
+  constexpr int NMF = (PK / 16) * MB * NB;          // MFMAs per stage
+  constexpr int EVERY = NMF / NPC;                  // MFMAs between pieces
+  static_assert(EVERY >= 1, "a piece per MFMA at most");
+  // one stage; WR: write the next stage's rows, LD: load the stage after
+  // next (compile-time, so that no branch splits the MFMA stream)
+  auto stage = [&](int ks, auto wr_tag, auto ld_tag) {
+    constexpr bool WR = decltype(wr_tag)::value, LD = decltype(ld_tag)::value;
     const uint8_t* a = sA0 + (ks & 1) * STA + rowA * 128;
     const uint8_t* bb = sB0 + (ks & 1) * STB + rowB * 128;
+    const int pw = (ks + 1) & 1, soff2 = (ks + 2) * PK * 2;
+    auto piece = [&](int q) {
+      if (q < LA) {
+        *reinterpret_cast<u32x4v*>(sA0 + pw * STA + (64 * w + 8 * q + (lane >> 3)) * 128 + slotw(q)) = ra[q];
+        if (LD) ra[q] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rx, voA[q], soff2, 0));
+      } else {
+        const int i = q - LA;
+        *reinterpret_cast<u32x4v*>(sB0 + pw * STB + ((TN / 4) * w + 8 * i + (lane >> 3)) * 128 + slotw(i)) = rb[i];
+        if (LD) rb[i] = __builtin_bit_cast(u32x4v, __builtin_amdgcn_raw_buffer_load_b128(rw, voB[i], soff2, 0));
+      }
+    };
     // k step s + 1's operands are read before k step s's MFMAs (scheduling
     // barriers keep that order), hiding the reads behind MFMAs
     bf16x8 fa[2][MB], fb[2][NB];
@@ -175,19 +201,23 @@ __device__ __forceinline__ void project_gemm_body(const ProjParams& P) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NB; ++j)
+        for (int j = 0; j < NB; ++j) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s & 1][i], fb[s & 1][j], acc[i][j], 0, 0, 0);
+          const int f = (s * MB + i) * NB + j;  // MFMA index within the stage
+          if (WR && f % EVERY == EVERY - 1 && f / EVERY < NPC) {
+            piece(f / EVERY);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (ks + 1 < S) {
-      // the next stage's rows (loaded during this stage) into the other
-      // buffer, whose previous stage every wave finished before the last
-      // barrier; then the stage after next into the registers
-      swrite((ks + 1) & 1);
-      if (ks + 2 < S) gload(ks + 2);
-      lds_sync();  // the writes are visible and every wave is done with stage ks
-    }
-  }
+    if (WR) lds_sync();  // the writes are visible and every wave is done with stage ks
+  };
+  typedef std::integral_constant<bool, true> yes;
+  typedef std::integral_constant<bool, false> no;
+  for (int ks = 0; ks + 2 < S; ++ks) stage(ks, yes(), yes());
+  if (S >= 2) stage(S - 2, yes(), no());
+  stage(S - 1, no(), no());
   __syncthreads();  // every wave done with the stage buffers
 
   // ---- epilogue, in passes of 64 columns (16 or 32 channels) ------------
