@@ -188,6 +188,36 @@ def test_decode_all_ties_lowest_indices(n_entries):
     assert list(got[1]) == list(range(k))
 
 
+def test_decode_topk_many_chunks_repeatable():
+    """Rows of up to 64 candidate chunks (4096 entries each) and of different
+    lengths, the same call made several times: each row's last chunk
+    workgroup to finish selects among the candidates its row's other chunk
+    workgroups stored in the same launch, so every call must return the same
+    sets, and those are the oracle's (exact except ties within 1e-6)."""
+    B, H, d, m, k, cap = 6, 16, 64, 4, 1024, 262144
+    kc, K = key_cache("fp8", B, cap, d, m, seed=27)
+    positions = [4 * cap - 1, 4 * cap - 5, 600000, 131071, 20000, 4 * 4097]
+    pos = torch.tensor(positions, dtype=torch.int64, device=DEV)
+    qI = synth.normal((B, H, d), "qI", 27, device=DEV, dtype=torch.bfloat16)
+    w = synth.normal((B, H), "w", 27, device=DEV)
+    desc = cb.index_desc(H, d, "bf16", "bf16", "fp8", "f32", m, cap)
+    ws = cb.workspace(cb.workspace_bytes(cb.OP_INDEX_TOPK_DECODE, desc, B, 1, 0, k))  # reused: state cleared per call
+    runs = []
+    for _ in range(6):
+        idx = torch.full((B, k), -7, dtype=torch.int32, device=DEV)
+        cb.index_topk_decode(desc, kc, pos, qI, w, k, idx, ws=ws)
+        runs.append(idx)
+    torch.cuda.synchronize()
+    got = runs[0].cpu().numpy()
+    for r in runs[1:]:
+        assert np.array_equal(r.cpu().numpy(), got)
+    assert ascending_padded(got)
+    for b in range(B):
+        ri, rs = oracle_rows(np64(qI[b])[None], np64(w[b])[None], K[b], [positions[b]], m, k, "bf16", "f32")
+        differing, bad = compare_topk(got[b:b + 1], ri, rs, 1e-6)
+        assert not bad, f"sequence {b}"
+
+
 @pytest.mark.parametrize("pattern", ["all_equal", "three_values", "bf16_ties"])
 def test_prefill_fused_ties(pattern):
     """Fused prefill select under ties, against the oracle (ties to the
