@@ -373,6 +373,43 @@ __device__ __forceinline__ bf16x8 load_qs(const AttnParams& P, size_t qrow, int 
   return *reinterpret_cast<const bf16x8*>(qh + d);
 }
 
+// The first item's query (64 heads x 576 BF16 dims, one contiguous 72 KB
+// block) is staged in LDS by 72 direct loads of 1 KB, 18 per wave, each
+// covering 8 head rows x 128 contiguous bytes.  Chunk group cg (dims 64cg ..
+// 64cg + 63) of head row h sits at byte 8192 cg + 128 h of the free tile
+// buffer (cg < 8) or at byte 128 h of the P^T buffer (cg = 8, the RoPE dims),
+// its 16-byte chunk b at slot b ^ ((h >> 1) & 7): the 16 lanes of one pass
+// of a fragment read (16 head rows, one chunk) then hit distinct banks.
+// Loading the fragments straight from global memory instead reads 32 bytes
+// of each of 32 rows per instruction, and moved four times the bytes used
+// from L2 at the start of a decode item.
+__device__ __forceinline__ void stage_query(const AttnParams& P, size_t qrow, uint8_t* qb, uint8_t* qr) {
+  typedef __attribute__((address_space(3))) void lds_void;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const uint8_t* base = static_cast<const uint8_t*>(P.q) + qrow * (CW * 2);
+  const auto rs = rsrc(base, NH * CW * 2);
+#pragma unroll
+  for (int j = 0; j < NH * CW * 2 / 1024 / NW; ++j) {
+    const int blk = (NH * CW * 2 / 1024 / NW) * w + j;  // chunk group blk / 8, rows 8 (blk % 8) ..
+    const int cg = blk >> 3, h = 8 * (blk & 7) + (lane >> 3);
+    uint8_t* dst = cg < 8 ? qb + 8192 * cg + 1024 * (blk & 7) : qr + 1024 * (blk & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)dst, 16,
+                                             h * (CW * 2) + 16 * (8 * cg + ((lane & 7) ^ ((h >> 1) & 7))), 0, 0, 0);
+  }
+}
+
+// B fragment k-step s (as load_qs) read from the staged query.
+template <bool FP8>
+__device__ __forceinline__ bf16x8 read_qs(const uint8_t* qb, const uint8_t* qr, int hh, int s) {
+  const int lane = threadIdx.x & 63, half = lane >> 5;
+  const int h = 32 * hh + (lane & 31);
+  const int c = (FP8 && s < DN / 16 ? 32 * (s >> 1) + 16 * half + 8 * (s & 1) : 16 * s + 8 * half) >> 3;
+  const int cg = c >> 3;  // the same for both lane halves
+  const uint8_t* p = (cg < 8 ? qb + 8192 * cg : qr) + 128 * h + 16 * ((c & 7) ^ ((h >> 1) & 7));
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
 // FP8 QK product: the query's non-RoPE dims as B operands of
 // v_mfma_scale_f32_32x32x64_f8f6f4.  With 8-bit operands that MFMA's k-block
 // b (b < 2, 32 k values, one E8M0 scale from lane 32b + column) is held as
@@ -502,6 +539,14 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   int64_t it = item_of(g, 0, nwg);
   if (it >= nitems) return;
   Item I = make_item<DENSE, SPLIT>(P, it, splits, per_split);
+  static_assert(L::KBUF >= 8 * 8192 && sizeof(pbuf) >= NH * 128, "query staging: 64 KB + 8 KB");
+  uint8_t* const qst = reinterpret_cast<uint8_t*>(pbuf);
+  // split decode: the first item's query staged in LDS (kb1 and pbuf are
+  // free until its first tile; sparse: its loads overlap the list's).  A
+  // workgroup runs one or two such items, and this start is a large part of
+  // each; prefill workgroups run many items and keep the direct loads.
+  constexpr bool STAGE_Q = SPLIT && !QK8;
+  if constexpr (STAGE_Q && !DENSE) stage_query(P, I.qrow, kb1, qst);
   int nvalid;
   if (DENSE) {
     nvalid = static_cast<int>(I.r1 > I.r0 ? I.r1 - I.r0 : 0);
@@ -515,12 +560,25 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   // scalar control flow
   int ntiles = __builtin_amdgcn_readfirstlane((nvalid + TILE - 1) / TILE);
   int par = 0;  // buffer of the next tile: kb0 / kb1
-  if (ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
-  // BF16 query fragments (QK8: the RoPE k-steps only)
+  // BF16 query fragments (QK8: the RoPE k-steps only, loaded directly).
+  // Staged, dense: the first tile's loads go first, then the query's;
+  // sparse: the query has landed with the list, and its reads precede the
+  // first tile's loads
   constexpr int Q0 = QK8 ? DN / 16 : 0;
   bf16x8 qf[QS];
+  if (DENSE || !STAGE_Q)
+    if (ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
+  if constexpr (!STAGE_Q) {
 #pragma unroll
-  for (int s = Q0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
+    for (int s = Q0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
+  } else {
+    if constexpr (DENSE) stage_query(P, I.qrow, kb1, qst);
+    wait_vmem();  // this wave's query blocks have landed
+    lds_sync();   // and every wave's
+#pragma unroll
+    for (int s = 0; s < QS; ++s) qf[s] = read_qs<FP8>(kb1, qst, hh, s);
+    if (!DENSE && ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
+  }
   i32x8 q8[8];  // QK8: the non-RoPE dims as MXFP8 codes and scales (else unused)
   int qsc[8];
 
