@@ -68,6 +68,18 @@ __device__ __forceinline__ uint32_t score_key(float x) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Inclusive prefix sum over the wave's lanes (row shifts within 16 lanes,
+// then the row broadcasts): DPP moves, no LDS round trips
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
+
 // LDS histogram increment, aggregated over the lanes of a wave that hit the
 // same bin (scores concentrate in a few high-bit bins); after a few rounds
 // the remaining lanes (spread bins, little contention) add one by one.

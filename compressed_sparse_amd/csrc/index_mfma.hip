@@ -85,18 +85,6 @@ constexpr int SEL_CBH = 128;    // threshold-bin entries ranked directly, per ha
 constexpr int KD = 8;           // key blocks in flight per wave (scoring)
 constexpr int HSTEPS = FUSED_NMAX / 512;  // 256-entry steps in half a row, at most
 
-// Inclusive prefix sum over the wave's lanes (row shifts within 16 lanes,
-// then the row broadcasts)
-__device__ __forceinline__ int wave_incl_scan(int x) {
-  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
-  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
-  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
-  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
-  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
-  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
-  return x;
-}
-
 __device__ __forceinline__ int mbcnt(unsigned long long m) {
   return static_cast<int>(__builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(m >> 32),
                                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(m), 0u)));
@@ -121,12 +109,7 @@ __device__ __forceinline__ void wave_radix_select(const float* row, int n, int k
     int c[4], tot = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; tot += c[j]; }
-    int incl = tot;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int y = __shfl_up(incl, o);
-      if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(tot);
     const int excl = incl - tot;  // count in bins above this lane's bins
     int bin = -1, above = 0;
     if (excl < remaining && incl >= remaining) {
@@ -139,8 +122,8 @@ __device__ __forceinline__ void wave_radix_select(const float* row, int n, int k
     }
     const unsigned long long who = __ballot(bin >= 0);
     const int src = __ffsll(static_cast<long long>(who)) - 1;
-    bin = __shfl(bin, src);
-    above = __shfl(above, src);
+    bin = __builtin_amdgcn_readlane(bin, src);
+    above = __builtin_amdgcn_readlane(above, src);
     prefix |= static_cast<uint32_t>(bin) << shift;
     pmask |= 255u << shift;
     remaining -= above;

@@ -99,12 +99,7 @@ __global__ void __launch_bounds__(256) index_scores_generic(IndexParams P) {
 // Every thread of the workgroup calls it: two barriers inside.
 __device__ __forceinline__ void block_scan2(int a, int b, int* s_part, int* pa, int* pb, int* ta, int* tb) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int ia = a, ib = b;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int ya = __shfl_up(ia, o), yb = __shfl_up(ib, o);
-    if (lane >= o) { ia += ya; ib += yb; }
-  }
+  const int ia = wave_incl_scan(a), ib = wave_incl_scan(b);
   __syncthreads();  // earlier readers of s_part are done
   if (lane == 63) { s_part[wv] = ia; s_part[17 + wv] = ib; }
   __syncthreads();
@@ -130,12 +125,7 @@ __device__ __forceinline__ void find_digit(const int* hist, int remaining, int* 
   int c[4], tot = 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) { c[j] = hist[255 - 4 * lane - j]; tot += c[j]; }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  const int incl = wave_incl_scan(tot);
   const int excl = incl - tot;
   if (excl < remaining && incl >= remaining) {
     int cum = excl;
@@ -290,12 +280,7 @@ __device__ int threshold_bin(const int* gh, int k, int* s_part) {
   int c[PER], tot = 0;
 #pragma unroll
   for (int j = 0; j < PER; ++j) { c[j] = gh[HIST_BINS - 1 - (tid * PER + j)]; tot += c[j]; }
-  int incl = tot;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(incl, o);
-    if (lane >= o) incl += y;
-  }
+  int incl = wave_incl_scan(tot);
   if (lane == 63) s_part[w] = incl;
   __syncthreads();
   int before = 0;
