@@ -194,11 +194,11 @@ __device__ __forceinline__ void radix_threshold(KeyOf key_of, int64_t cnt, int k
 // Ordered compaction after radix_threshold: the elements whose key is above
 // the threshold, and the first `remaining` equal to it, in element order,
 // put(j, idx_of(i)) for output slots j = 0, 1, ..  Each thread takes E
-// consecutive elements per tile; one workgroup scan per tile.
-template <typename KeyOf, typename IdxOf, typename Put>
+// consecutive elements per tile; one workgroup scan per tile (fewer
+// elements per thread keep LDS key reads from piling onto the same banks).
+template <int E = 8, typename KeyOf, typename IdxOf, typename Put>
 __device__ __forceinline__ void ordered_take(KeyOf key_of, IdxOf idx_of, int64_t cnt, uint32_t prefix, uint32_t pmask,
                              int remaining, int* s_part, Put put) {
-  constexpr int E = 8;
   const int tid = threadIdx.x, nt = blockDim.x;
   int gt_done = 0, eq_done = 0;
   for (int64_t base = 0; base < cnt; base += static_cast<int64_t>(E) * nt) {
@@ -417,14 +417,26 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   // counts (their sum is the row's candidate count)
   const int nch = static_cast<int>((n + CAND_CHUNK - 1) / CAND_CHUNK);
   const size_t rb = static_cast<size_t>(b) * P.nch;
+  // (the whole candidate list is read at once, beside the counts: slots past
+  // the row's count hold older values and are not used)
+  const size_t cb0 = static_cast<size_t>(b) * CAND_CAP;
+  constexpr int CL = CAND_CAP / 1024;
+  int32_t cid[CL];
+  uint32_t ckv[CL];
   int cc[CPT], loc = 0;
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int j = tid * CPT + u;
     cc[u] = j < nch ? P.ccnt[rb + j] : 0;
     if (j < nch) s_cb[j] = P.cbase[rb + j];
-    loc += cc[u];
   }
+#pragma unroll
+  for (int u = 0; u < CL; ++u) {
+    cid[u] = P.cidx[cb0 + tid + 1024 * u];
+    ckv[u] = P.ckey[cb0 + tid + 1024 * u];
+  }
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) loc += cc[u];
   int pre, unused, c, unused_tot;
   block_scan2(loc, 0, s_part, &pre, &unused, &c, &unused_tot);
   if (c > CAND_CAP) {  // too many candidates: exact select over the whole row
@@ -439,13 +451,15 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
     pre += cc[u];
   }
   __syncthreads();
-  const size_t cb0 = static_cast<size_t>(b) * CAND_CAP;
-  for (int i = tid; i < c; i += nt) {
-    const int32_t s = P.cidx[cb0 + i];
-    const int j = s / CAND_CHUNK;
-    const int d = s_pre[j] + (i - s_cb[j]);
-    s_key[d] = P.ckey[cb0 + i];
-    s_idx[d] = s;
+#pragma unroll
+  for (int u = 0; u < CL; ++u) {
+    const int i = tid + 1024 * u;
+    if (i < c) {
+      const int j = cid[u] / CAND_CHUNK;
+      const int d = s_pre[j] + (i - s_cb[j]);
+      s_key[d] = ckv[u];
+      s_idx[d] = cid[u];
+    }
   }
   __syncthreads();
   // the k-th key lies in the histogram's bin (its top HIST_BITS bits), with
@@ -458,7 +472,7 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   radix_threshold(key_of, c, P.k - above, key_bits, hist, s_sel, &prefix, &pmask, &remaining,
                   bstar << (32 - HIST_BITS), ~0u << (32 - HIST_BITS), 32 - HIST_BITS - 8);
   stage_tab();  // ordered_take's workgroup scan (barriers) precedes its first output
-  ordered_take(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, put);
+  ordered_take<4>(key_of, [](int64_t i) { return s_idx[i]; }, c, prefix, pmask, remaining, s_part, put);
 }
 
 // prep_done: the decode rows' preparation (cleared histogram and count,
