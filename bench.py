@@ -53,6 +53,10 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
+def context_progress(done, total):
+    log(f"  context chunks {done}/{total}")
+
+
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_bf16_csa_prefill_L32768_traffic.txt")
 ATTN_SRC = os.path.join(ROOT, "compressed_sparse_amd", "csrc", "attention_bf16.hip")
 
@@ -309,7 +313,7 @@ def csa_decode_line(n_steps=DECODE_STEPS):
     w = synth.CSA_DECODE_B32_128K
     log(f"setup {w.name}")
     lay = path.CsaLayer(w, w.batch, w.tokens // w.m + n_steps)
-    lay.prefill_context(w.tokens)
+    lay.prefill_context(w.tokens, progress=context_progress)
     o = lay.alloc_decode_outputs()
     xs = lay.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
     ms3 = time_graph([lay], lambda i: lay.decode_step(xs[i], o), n_steps)
@@ -326,7 +330,7 @@ def hca_decode_line(n_steps=DECODE_STEPS, qk="bf16"):
     w = synth.HCA_DECODE_B16_1M
     log(f"setup {w.name}")
     lay = path.HcaLayer(w, w.batch, w.tokens // w.m + n_steps, qk=qk)
-    lay.prefill_context(w.tokens)
+    lay.prefill_context(w.tokens, progress=context_progress)
     o = lay.alloc_decode_outputs()
     xs = lay.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
     ms3 = time_graph([lay], lambda i: lay.decode_step(xs[i], o), n_steps)
@@ -346,8 +350,8 @@ def pair_decode_lines(n_steps=DECODE_STEPS):
     log(f"setup {wc.name} + {wh.name}")
     lc = path.CsaLayer(wc, wc.batch, wc.tokens // wc.m + n_steps)
     lh = path.HcaLayer(wh, wh.batch, wh.tokens // wh.m + n_steps, seed=1)
-    lc.prefill_context(wc.tokens)
-    lh.prefill_context(wh.tokens)
+    lc.prefill_context(wc.tokens, progress=context_progress)
+    lh.prefill_context(wh.tokens, progress=context_progress)
     oc, oh = lc.alloc_decode_outputs(), lh.alloc_decode_outputs()
     xc = lc.decode_input_steps([[wc.tokens + i] * wc.batch for i in range(n_steps)])
     xh = lh.decode_input_steps([[wh.tokens + i] * wh.batch for i in range(n_steps)])
@@ -381,8 +385,8 @@ def swa_decode_lines(n_steps=DECODE_STEPS, window=128):
     log(f"setup {w.name} + sliding window {window}")
     lc = path.CsaLayer(w, w.batch, w.tokens // w.m + n_steps)
     sw = path.SwaBranch(w, w.batch, w.tokens + n_steps, window)
-    lc.prefill_context(w.tokens)
-    sw.prefill_context(w.tokens)
+    lc.prefill_context(w.tokens, progress=context_progress)
+    sw.prefill_context(w.tokens, progress=context_progress)
     oc, osw = lc.alloc_decode_outputs(), sw.alloc_decode_outputs()
     xs = lc.decode_input_steps([[w.tokens + i] * w.batch for i in range(n_steps)])
 
@@ -672,7 +676,7 @@ def secondary_hca_prefill(steps=5, qk="bf16"):
     c = w.tokens // chunk - 1
     log(f"setup {w.name}")
     lay = path.HcaLayer(w, 1, w.tokens // w.m)
-    lay.prefill_context(w.tokens)
+    lay.prefill_context(w.tokens, progress=context_progress)
     tok = synth.token_chunk(w, 0, c, chunk, 0, "cuda")
     x = {k: v[None].contiguous() for k, v in tok.items()}
     q = synth.query_chunk(w, 0, c, chunk, 0, "cuda", with_index=False)["q"][None].contiguous()

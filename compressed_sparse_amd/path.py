@@ -92,11 +92,15 @@ class CsaLayer:
         return [self.kv, self.keys]
 
     # -- context ----------------------------------------------------------
-    def prefill_context(self, T, chunk=None):
-        """Compresses tokens [0, T) of every sequence into the caches."""
+    def prefill_context(self, T, chunk=None, progress=None):
+        """Compresses tokens [0, T) of every sequence into the caches
+        (progress(done, total) after every 16 chunks, when given)."""
         chunk = chunk or self.w.chunk or T
         p = self.prm
-        for c in range(math.ceil(T / chunk)):
+        nc = math.ceil(T / chunk)
+        for c in range(nc):
+            if progress and c % 16 == 15:
+                progress(c + 1, nc)
             n = min(chunk, T - c * chunk)
             toks = [synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device) for sid in self.seq_ids]
             x = {k: _stack([t[k][:n] for t in toks]) for k in toks[0]}
@@ -208,9 +212,12 @@ class HcaLayer:
         x = {k: _stack([t[k][:n] for t in toks]) for k in toks[0]}
         cb.compress_prefill(self.kv, c * chunk, x["a"], x["za"], self.prm["Ba"])
 
-    def prefill_context(self, T, chunk=None):
+    def prefill_context(self, T, chunk=None, progress=None):
         chunk = chunk or self.w.chunk or T
-        for c in range(math.ceil(T / chunk)):
+        nc = math.ceil(T / chunk)
+        for c in range(nc):
+            if progress and c % 16 == 15:
+                progress(c + 1, nc)
             self.compress_chunk(c, chunk, min(chunk, T - c * chunk))
 
     def prefill_contexts(self, lengths, chunk=None):
@@ -289,9 +296,12 @@ class SwaBranch:
     def caches(self):
         return [self.kv]
 
-    def prefill_context(self, T, chunk=None):
+    def prefill_context(self, T, chunk=None, progress=None):
         chunk = chunk or self.w.chunk or T
-        for c in range(math.ceil(T / chunk)):
+        nc = math.ceil(T / chunk)
+        for c in range(nc):
+            if progress and c % 16 == 15:
+                progress(c + 1, nc)
             n = min(chunk, T - c * chunk)
             toks = [synth.token_chunk(self.w, sid, c, chunk, self.seed, self.device, names=["a", "za"])
                     for sid in self.seq_ids]
