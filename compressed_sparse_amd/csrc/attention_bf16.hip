@@ -942,9 +942,15 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     // 128w + 32mb + acc_row(v)
     // partials of a decode split: normalised BF16 rows [B][splits][NH][DN],
     // then the log2-sum-exp per head, fp32 [B][splits][NH]
+    // partials of a split sequence go straight from registers in
+    // their own layout: piece (w, mb, nb, jq) of 64 lanes x 8 bytes at
+    // 512 ((((w * 4 + mb) * 2 + nb) * 4 + jq)) + 8 lane, lane holding head
+    // 32nb + lane % 32, dims 128w + 32mb + 8jq + 4 (lane / 32) .. +4; the merge
+    // reads them in that order.  No LDS staging, no barrier before the stores.
     const size_t slot = static_cast<size_t>(I.b) * splits + I.split;
     bf16_t* part_o = static_cast<bf16_t*>(part);
     float* part_lse = reinterpret_cast<float*>(part_o + static_cast<size_t>(nbatch) * splits * (NH * DN));
+    constexpr bool native = SPLIT;  // a split launch always has splits > 1
 #pragma unroll
     for (int nb = 0; nb < 2; ++nb) {
       const int h = 32 * nb + (lane & 31);
@@ -957,9 +963,14 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
           const f32x16& o = oacc[mb][nb];
           const uint32_t lo = pack2_bf16(o[4 * jq] * inv, o[4 * jq + 1] * inv);
           const uint32_t hi2 = pack2_bf16(o[4 * jq + 2] * inv, o[4 * jq + 3] * inv);
-          // dims 128w + 32mb + 8jq + 4half: chunk 16w + 4mb + jq, byte 8half
-          const int c = 16 * w + 4 * mb + jq;
-          *reinterpret_cast<uint2*>(stage + h * NROW + 16 * (c ^ (h & 15)) + 8 * half) = make_uint2(lo, hi2);
+          if constexpr (native) {
+            *reinterpret_cast<uint2*>(part_o + slot * (NH * DN) + 4 * ((((w * 4 + mb) * 2 + nb) * 4 + jq) * 64 + lane)) =
+                make_uint2(lo, hi2);
+          } else {
+            // dims 128w + 32mb + 8jq + 4half: chunk 16w + 4mb + jq, byte 8half
+            const int c = 16 * w + 4 * mb + jq;
+            *reinterpret_cast<uint2*>(stage + h * NROW + 16 * (c ^ (h & 15)) + 8 * half) = make_uint2(lo, hi2);
+          }
         }
       if (w == 0 && lane < 32) {
         const float l2 = ltot > 0.0f ? s_m[h] + log2f(ltot) : -INFINITY;
@@ -971,9 +982,9 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
     // when there is one; else (and for split partials) it is stored now
     const bool defer = !SPLIT && has_next && next_started && nvalid_n > 0;
     staged_qrow = I.qrow;
-    if (!defer) {
+    if (!defer && !native) {
       lds_sync();  // every wave's part of the rows written
-      store_staged(stage, SPLIT ? part_o + slot * (NH * DN) : static_cast<bf16_t*>(P.o) + staged_qrow * DN);
+      store_staged(stage, static_cast<bf16_t*>(P.o) + staged_qrow * DN);
     }
     if (!has_next) break;
     if (!next_started) {  // this item had no tile: start the next one now

@@ -31,49 +31,67 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 }
 
 // Combines split partials by log-sum-exp: O = sum_s 2^(l_s - M) O_s / sum_s
-// 2^(l_s - M), l_s the split's log2 weight sum and M their maximum; grid
-// (NH, B), one thread per 4 value dims (128 threads), the head's split
-// weights computed once in LDS.  S >= splits is a power of two: every
-// thread's S partial loads (clamped to the last split) are issued before
-// the weights are known.
+// 2^(l_s - M), l_s the split's log2 weight sum and M their maximum.  A
+// split's partial O is stored in the attention kernel's register order:
+// piece (w, mb, nb, jq) of 64 lanes x 8 bytes at 512 ((((w * 4 + mb) * 2 +
+// nb) * 4 + jq)) + 8 lane, lane holding head 32nb + lane % 32 and value dims
+// 128w + 32mb + 8jq + 4 (lane / 32) .. +4.  Grid (32 blocks (w, mb, nb), B),
+// 256 threads: thread (jq, lane) reads one 8-byte piece of every split (2 KB
+// contiguous per split and workgroup), the weights of the block's 32 heads
+// are formed once in LDS.  S >= splits is a power of two: every thread's S
+// loads (clamped to the last split) are issued before the weights are known.
 template <int S>
-__global__ void __launch_bounds__(128) attn_merge_kernel(AttnParams P, int splits, const void* part, int B) {
-  __shared__ float s_f[S];
-  __shared__ float s_L, s_M;
-  const int h = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+__global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams P, int splits, const void* part, int B) {
+  __shared__ float s_f[32][S + 1];
+  __shared__ float s_L[32], s_M[32];
+  const int blk = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
+  const int w = blk >> 3, mb = (blk >> 1) & 3, nb = blk & 1;
+  const int jq = tid >> 6, lane = tid & 63;
+  const int hl = lane & 31, h = 32 * nb + hl;
   const bf16_t* po = static_cast<const bf16_t*>(part) + static_cast<size_t>(b) * splits * (NH * DN) +
-                     static_cast<size_t>(h) * DN + 4 * tid;
+                     4 * ((blk * 4 + jq) * 64 + lane);
   uint2 v[S];
 #pragma unroll
   for (int sp = 0; sp < S; ++sp)
     v[sp] = *reinterpret_cast<const uint2*>(po + static_cast<size_t>(min(sp, splits - 1)) * NH * DN);
   const float* pl = reinterpret_cast<const float*>(static_cast<const bf16_t*>(part) + static_cast<size_t>(B) * splits * (NH * DN)) +
                     static_cast<size_t>(b) * splits * NH;
-  if (tid < 64) {
-    const float ls = tid < splits ? pl[tid * NH + h] : -INFINITY;
-    float M = ls;
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-    const float f = ls != -INFINITY ? exp2f(ls - M) : 0.0f;
-    float L = f;
-    for (int o = 32; o > 0; o >>= 1) L += __shfl_xor(L, o);
-    if (tid < S) s_f[tid] = f;
-    if (tid == 0) { s_L = L; s_M = M; }
+  // the log2 weight sums of the block's 32 heads for every split, then each
+  // head's weights (thread = head)
+  for (int i = tid; i < 32 * S; i += 256) {
+    const int hh = i & 31, sp = i >> 5;
+    s_f[hh][sp] = sp < splits ? pl[sp * NH + 32 * nb + hh] : -INFINITY;
   }
   __syncthreads();
-  const float L = s_L;
+  if (tid < 32) {
+    float M = -INFINITY;
+    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_f[tid][sp]);
+    float L = 0.0f;
+    for (int sp = 0; sp < S; ++sp) {
+      const float ls = s_f[tid][sp];
+      const float f = ls != -INFINITY ? exp2f(ls - M) : 0.0f;  // 0 past the last split and for empty splits
+      s_f[tid][sp] = f;
+      L += f;
+    }
+    s_L[tid] = L;
+    s_M[tid] = M;
+  }
+  __syncthreads();
+  const float L = s_L[hl];
   const float inv = L > 0.0f ? 1.0f / L : 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
   for (int sp = 0; sp < S; ++sp) {
-    const float f = s_f[sp];  // 0 past the last split and for empty splits
+    const float f = s_f[hl][sp];
     acc.x = fmaf(__uint_as_float(v[sp].x << 16), f, acc.x);
     acc.y = fmaf(__uint_as_float(v[sp].x & 0xFFFF0000u), f, acc.y);
     acc.z = fmaf(__uint_as_float(v[sp].y << 16), f, acc.z);
     acc.w = fmaf(__uint_as_float(v[sp].y & 0xFFFF0000u), f, acc.w);
   }
-  bf16_t* out = static_cast<bf16_t*>(P.o) + (static_cast<size_t>(b) * NH + h) * DN + 4 * tid;
+  const int d = 128 * w + 32 * mb + 8 * jq + 4 * (lane >> 5);
+  bf16_t* out = static_cast<bf16_t*>(P.o) + (static_cast<size_t>(b) * NH + h) * DN + d;
   *reinterpret_cast<uint2*>(out) = make_uint2(pack2_bf16(acc.x * inv, acc.y * inv), pack2_bf16(acc.z * inv, acc.w * inv));
-  if (P.lse && tid == 0) P.lse[static_cast<size_t>(b) * NH + h] = L > 0.0f ? (s_M + log2f(L)) * LN2 : -INFINITY;
+  if (P.lse && w == 0 && mb == 0 && tid < 32) P.lse[static_cast<size_t>(b) * NH + h] = L > 0.0f ? (s_M[hl] + log2f(L)) * LN2 : -INFINITY;
 }
 
 // bytes of the split partials of B sequences
@@ -206,13 +224,12 @@ int launch_mfma_attn(const AttnParams& P0, int op, int B, hipStream_t s) {
   launch_attn_bf16(P, dense, B, s, splits, per, part);
   int st = check_launch("attn_bf16_kernel");
   if (st != CSA_OK) return st;
-  const dim3 mg(NH, B);
-  if (splits <= 1) hipLaunchKernelGGL(attn_merge_kernel<1>, mg, dim3(128), 0, s, P, splits, part, B);
-  else if (splits <= 2) hipLaunchKernelGGL(attn_merge_kernel<2>, mg, dim3(128), 0, s, P, splits, part, B);
-  else if (splits <= 4) hipLaunchKernelGGL(attn_merge_kernel<4>, mg, dim3(128), 0, s, P, splits, part, B);
-  else if (splits <= 8) hipLaunchKernelGGL(attn_merge_kernel<8>, mg, dim3(128), 0, s, P, splits, part, B);
-  else if (splits <= 16) hipLaunchKernelGGL(attn_merge_kernel<16>, mg, dim3(128), 0, s, P, splits, part, B);
-  else hipLaunchKernelGGL(attn_merge_kernel<MAX_SPLITS>, mg, dim3(128), 0, s, P, splits, part, B);
+  const dim3 mg(32, B);  // blocks (w, mb, nb) of the partial layout
+  if (splits <= 2) hipLaunchKernelGGL(attn_merge_kernel<2>, mg, dim3(256), 0, s, P, splits, part, B);
+  else if (splits <= 4) hipLaunchKernelGGL(attn_merge_kernel<4>, mg, dim3(256), 0, s, P, splits, part, B);
+  else if (splits <= 8) hipLaunchKernelGGL(attn_merge_kernel<8>, mg, dim3(256), 0, s, P, splits, part, B);
+  else if (splits <= 16) hipLaunchKernelGGL(attn_merge_kernel<16>, mg, dim3(256), 0, s, P, splits, part, B);
+  else hipLaunchKernelGGL(attn_merge_kernel<MAX_SPLITS>, mg, dim3(256), 0, s, P, splits, part, B);
   return check_launch("attn_merge_kernel");
 }
 
