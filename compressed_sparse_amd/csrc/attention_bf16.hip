@@ -122,6 +122,13 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 // Waits until all of this wave's vector memory operations have completed
 // (its direct-to-LDS tile loads, query loads and earlier stores).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+// Waits until at most N of this wave's vector memory operations are in flight
+// (the N issued last may still be; vmcnt counts them in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmem_but() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
 
 __device__ __forceinline__ bf16x8 lds_b128(const uint8_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
@@ -546,13 +553,16 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   // workgroup runs one or two such items, and this start is a large part of
   // each; prefill workgroups run many items and keep the direct loads.
   constexpr bool STAGE_Q = SPLIT && !QK8;
-  if constexpr (STAGE_Q && !DENSE) stage_query(P, I.qrow, kb1, qst);
   int nvalid;
   if (DENSE) {
+    if constexpr (STAGE_Q) stage_query(P, I.qrow, kb1, qst);
     nvalid = static_cast<int>(I.r1 > I.r0 ? I.r1 - I.r0 : 0);
   } else {
     int32_t lr[4];
     load_list(P, I, tid, lr);
+    // the list's loads first: its compaction waits for them only, while the
+    // query's loads (issued after them) are still landing
+    if constexpr (STAGE_Q) stage_query(P, I.qrow, kb1, qst);
     nvalid = compact_list(lr, P.list_rows ? P.span_rows : I.n, s_list, s_cnt);
   }
   // the tile count is wave-uniform; read back from lane 0 so that the tile
@@ -561,23 +571,23 @@ attn_bf16_kernel(AttnParams P, Theta th, int splits, int64_t per_split, void* pa
   int ntiles = __builtin_amdgcn_readfirstlane((nvalid + TILE - 1) / TILE);
   int par = 0;  // buffer of the next tile: kb0 / kb1
   // BF16 query fragments (QK8: the RoPE k-steps only, loaded directly).
-  // Staged, dense: the first tile's loads go first, then the query's;
-  // sparse: the query has landed with the list, and its reads precede the
-  // first tile's loads
+  // Staged: the first tile's loads follow the query's, and the wait covers
+  // the query's only (loads complete in issue order), so the tile's latency
+  // runs on under the fragment reads and the RoPE turn
   constexpr int Q0 = QK8 ? DN / 16 : 0;
   bf16x8 qf[QS];
-  if (DENSE || !STAGE_Q)
-    if (ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
+  if constexpr (STAGE_Q) __builtin_amdgcn_sched_barrier(0);
+  if (ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
+  if constexpr (STAGE_Q) __builtin_amdgcn_sched_barrier(0);
   if constexpr (!STAGE_Q) {
 #pragma unroll
     for (int s = Q0; s < QS; ++s) qf[s] = load_qs<FP8>(P, I.qrow, hh, s);
   } else {
-    if constexpr (DENSE) stage_query(P, I.qrow, kb1, qst);
-    wait_vmem();  // this wave's query blocks have landed
-    lds_sync();   // and every wave's
+    if (ntiles > 0) wait_vmem_but<L::NLOAD>();  // this wave's query blocks have landed
+    else wait_vmem();
+    lds_sync();  // and every wave's
 #pragma unroll
     for (int s = 0; s < QS; ++s) qf[s] = read_qs<FP8>(kb1, qst, hh, s);
-    if (!DENSE && ntiles > 0) issue_tile<FP8, DENSE, PAGED>(kb0, P, s_list, 0, I.r0, nvalid, I.seq, I.b);
   }
   i32x8 q8[8];  // QK8: the non-RoPE dims as MXFP8 codes and scales (else unused)
   int qsc[8];
