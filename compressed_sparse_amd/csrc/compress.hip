@@ -274,19 +274,35 @@ __device__ __forceinline__ void compress_decode_body(const CompressParams& P, co
   float* red = smem;        // 32
   float* buf = smem + 32;   // c: the emitted entry
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const size_t row = static_cast<size_t>(b) * P.c;
+  // the token's projections for this thread's first channel are read beside
+  // the position (their addresses do not depend on it), without branches: a
+  // compressor without C^b reads a's row in their place and drops it
+  const bool has_b = P.NT == 4;
+  const void* pb = has_b ? P.b : P.a;
+  const void* pzb = has_b ? P.zb : P.za;
+  auto load_cur = [&](int j, float (&cur)[4]) {
+    cur[RING_A] = load_in<IN_BF16>(P.a, row + j);
+    cur[RING_ZA] = load_in<IN_BF16>(P.za, row + j);
+    const float vb = load_in<IN_BF16>(pb, row + j), vzb = load_in<IN_BF16>(pzb, row + j);
+    cur[RING_B] = has_b ? vb : 0.0f;
+    cur[RING_ZB] = has_b ? vzb : 0.0f;
+  };
   const int64_t pos = pos_dev[b];
+  float cur0[4];
+  load_cur(min(tid, P.c - 1), cur0);
+#pragma unroll
+  for (int x = 0; x < 4; ++x) asm volatile("" : "+v"(cur0[x]));  // loaded here, not sunk past the test below
   if (pos < 0) return;
   const int64_t i = (pos + 1) / P.m - 1;
   const bool emit = (pos + 1) % P.m == 0 && i < P.cap;
-  const size_t row = static_cast<size_t>(b) * P.c;
   for (int j = tid; j < P.c; j += nt) {
     float cur[4];
-    cur[RING_A] = load_in<IN_BF16>(P.a, row + j);
-    cur[RING_ZA] = load_in<IN_BF16>(P.za, row + j);
-    cur[RING_B] = cur[RING_ZB] = 0.0f;
-    if (P.NT == 4) {
-      cur[RING_B] = load_in<IN_BF16>(P.b, row + j);
-      cur[RING_ZB] = load_in<IN_BF16>(P.zb, row + j);
+    if (j == tid) {
+#pragma unroll
+      for (int x = 0; x < 4; ++x) cur[x] = cur0[x];
+    } else {
+      load_cur(j, cur);
     }
 #pragma unroll
     for (int wch = 0; wch < 4; ++wch)
