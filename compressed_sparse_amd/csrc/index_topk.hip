@@ -272,14 +272,22 @@ __global__ void __launch_bounds__(256) topk_zero_kernel(IndexParams P) {
   if (threadIdx.x == 0) P.ccount[b] = 0;
 }
 
-// The bin of the k-th largest key of row b (all 256 threads get it); the
-// number of keys in higher bins is left in s_part[5].
-__device__ int threshold_bin(const int* gh, int k, int* s_part) {
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  constexpr int PER = HIST_BINS / 256;  // bins per thread, thread 0 owns the top bins
-  int c[PER], tot = 0;
+// A 256-thread workgroup's share of row b's histogram: thread t holds the
+// counts of bins HIST_BINS-1-(PER t + j) (thread 0 the top bins).
+constexpr int HIST_PER = HIST_BINS / 256;
+__device__ __forceinline__ void load_hist(const int* gh, int (&c)[HIST_PER]) {
 #pragma unroll
-  for (int j = 0; j < PER; ++j) { c[j] = gh[HIST_BINS - 1 - (tid * PER + j)]; tot += c[j]; }
+  for (int j = 0; j < HIST_PER; ++j) c[j] = gh[HIST_BINS - 1 - (threadIdx.x * HIST_PER + j)];
+}
+
+// The bin of the k-th largest key of row b from the loaded histogram (all
+// 256 threads get it); the number of keys in higher bins is left in s_part[5].
+__device__ int threshold_bin(const int (&c)[HIST_PER], int k, int* s_part) {
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  constexpr int PER = HIST_PER;
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < PER; ++j) tot += c[j];
   int incl = wave_incl_scan(tot);
   if (lane == 63) s_part[w] = incl;
   __syncthreads();
@@ -308,16 +316,26 @@ __global__ void __launch_bounds__(256) topk_cand_kernel(IndexParams P) {
   __shared__ int s_wc[4];
   __shared__ int s_base;
   const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int64_t n = visible(query_pos(P, b, 0), P.m, P.cap);
+  const int64_t pos = P.pos_dev[b];  // decode: positions on the device
   const int64_t c0 = static_cast<int64_t>(blockIdx.x) * CAND_CHUNK;
-  if (n <= P.k || c0 >= n) return;
-  const int64_t c1 = c0 + CAND_CHUNK < n ? c0 + CAND_CHUNK : n;
   const float* sc = P.ws + static_cast<size_t>(b) * P.n_stride;
   const int64_t e0 = c0 + wv * PERW + lane;
+  // the chunk's scores (indices kept inside the row's stride; those past the
+  // visible entries are not taken) and the row's histogram are read beside
+  // the position, not after it
   float v[IT];
 #pragma unroll
-  for (int it = 0; it < IT; ++it) v[it] = e0 + it * 64 < c1 ? sc[e0 + it * 64] : 0.0f;
-  const int bstar = threshold_bin(P.ghist + static_cast<size_t>(b) * HIST_BINS, P.k, s_part);
+  for (int it = 0; it < IT; ++it) v[it] = sc[min(e0 + it * 64, P.n_stride - 1)];
+  int hc[HIST_PER];
+  load_hist(P.ghist + static_cast<size_t>(b) * HIST_BINS, hc);
+#pragma unroll
+  for (int it = 0; it < IT; ++it) asm volatile("" : "+v"(v[it]));  // loaded here, not sunk past the test below
+#pragma unroll
+  for (int j = 0; j < HIST_PER; ++j) asm volatile("" : "+v"(hc[j]));
+  const int64_t n = visible(pos, P.m, P.cap);
+  if (n <= P.k || c0 >= n) return;
+  const int64_t c1 = c0 + CAND_CHUNK < n ? c0 + CAND_CHUNK : n;
+  const int bstar = threshold_bin(hc, P.k, s_part);
   if (blockIdx.x == 0 && tid == 0) {  // for the final select: the known top bits
     P.csel[2 * b] = bstar;
     P.csel[2 * b + 1] = s_part[5];
@@ -374,8 +392,37 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   __shared__ int s_sel[2];
   __shared__ int s_part[34];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  const int64_t n = visible(query_pos(P, b, 0), P.m, P.cap);
+  const int64_t pos = P.pos_dev[b];  // decode: positions on the device
   int32_t* out = P.idx + static_cast<size_t>(b) * P.k;
+  // the row's chunk counts and bases (every chunk slot of the row; those past
+  // the visible entries are dropped below) and its whole candidate list are
+  // read beside the position, not after it; slots past the row's candidate
+  // count hold older values and are not used
+  const size_t rb = static_cast<size_t>(b) * P.nch;
+  const size_t cb0 = static_cast<size_t>(b) * CAND_CAP;
+  constexpr int CL = CAND_CAP / 1024;
+  int32_t cid[CL];
+  uint32_t ckv[CL];
+  int cc[CPT], cbv[CPT];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) {
+    const int j = min(tid * CPT + u, P.nch - 1);
+    cc[u] = P.ccnt[rb + j];
+    cbv[u] = P.cbase[rb + j];
+  }
+#pragma unroll
+  for (int u = 0; u < CL; ++u) {
+    cid[u] = P.cidx[cb0 + tid + 1024 * u];
+    ckv[u] = P.ckey[cb0 + tid + 1024 * u];
+  }
+  // the histogram bin of the k-th key and the count above it (the candidate
+  // pass's chunk 0 wrote them)
+  uint32_t bstar = static_cast<uint32_t>(P.csel[2 * b]);
+  int above = P.csel[2 * b + 1];
+#pragma unroll
+  for (int u = 0; u < CPT; ++u) asm volatile("" : "+v"(cc[u]), "+v"(cbv[u]));  // loaded here, not sunk past the test below
+  asm volatile("" : "+s"(bstar), "+s"(above));
+  const int64_t n = visible(pos, P.m, P.cap);
   // a fused decode step over a paged KV cache: each selected entry's pool
   // row as well, the list its sparse attention reads (-1 on a page outside
   // the pool, like the padding).  The sequence's block-table row is staged
@@ -416,27 +463,14 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   // where each chunk's candidates go in index order: prefix of the chunk
   // counts (their sum is the row's candidate count)
   const int nch = static_cast<int>((n + CAND_CHUNK - 1) / CAND_CHUNK);
-  const size_t rb = static_cast<size_t>(b) * P.nch;
-  // (the whole candidate list is read at once, beside the counts: slots past
-  // the row's count hold older values and are not used)
-  const size_t cb0 = static_cast<size_t>(b) * CAND_CAP;
-  constexpr int CL = CAND_CAP / 1024;
-  int32_t cid[CL];
-  uint32_t ckv[CL];
-  int cc[CPT], loc = 0;
+  int loc = 0;
 #pragma unroll
   for (int u = 0; u < CPT; ++u) {
     const int j = tid * CPT + u;
-    cc[u] = j < nch ? P.ccnt[rb + j] : 0;
-    if (j < nch) s_cb[j] = P.cbase[rb + j];
+    if (j < nch) s_cb[j] = cbv[u];
+    else cc[u] = 0;
+    loc += cc[u];
   }
-#pragma unroll
-  for (int u = 0; u < CL; ++u) {
-    cid[u] = P.cidx[cb0 + tid + 1024 * u];
-    ckv[u] = P.ckey[cb0 + tid + 1024 * u];
-  }
-#pragma unroll
-  for (int u = 0; u < CPT; ++u) loc += cc[u];
   int pre, unused, c, unused_tot;
   block_scan2(loc, 0, s_part, &pre, &unused, &c, &unused_tot);
   if (c > CAND_CAP) {  // too many candidates: exact select over the whole row
@@ -467,8 +501,6 @@ __global__ void __launch_bounds__(1024) topk_final_kernel(IndexParams P, int key
   uint32_t prefix, pmask;
   int remaining;
   auto key_of = [](int64_t i) { return s_key[i]; };
-  const uint32_t bstar = static_cast<uint32_t>(P.csel[2 * b]);
-  const int above = P.csel[2 * b + 1];
   radix_threshold(key_of, c, P.k - above, key_bits, hist, s_sel, &prefix, &pmask, &remaining,
                   bstar << (32 - HIST_BITS), ~0u << (32 - HIST_BITS), 32 - HIST_BITS - 8);
   stage_tab();  // ordered_take's workgroup scan (barriers) precedes its first output
