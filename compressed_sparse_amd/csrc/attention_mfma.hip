@@ -38,7 +38,7 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 // 128w + 32mb + 8jq + 4 (lane / 32) .. +4.  Grid (32 blocks (w, mb, nb), B),
 // 256 threads: thread (jq, lane) reads one 8-byte piece of every split (2 KB
 // contiguous per split and workgroup), the weights of the block's 32 heads
-// are formed once in LDS.  S >= splits is a power of two: every thread's S
+// are formed once in LDS (8 threads per head).  S >= splits is a power of two: every thread's S
 // loads (clamped to the last split) are issued before the weights are known.
 template <int S>
 __global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams P, int splits, const void* part, int B) {
@@ -56,25 +56,35 @@ __global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams P, int split
     v[sp] = *reinterpret_cast<const uint2*>(po + static_cast<size_t>(min(sp, splits - 1)) * NH * DN);
   const float* pl = reinterpret_cast<const float*>(static_cast<const bf16_t*>(part) + static_cast<size_t>(B) * splits * (NH * DN)) +
                     static_cast<size_t>(b) * splits * NH;
-  // the log2 weight sums of the block's 32 heads for every split, then each
-  // head's weights (thread = head)
-  for (int i = tid; i < 32 * S; i += 256) {
-    const int hh = i & 31, sp = i >> 5;
-    s_f[hh][sp] = sp < splits ? pl[sp * NH + 32 * nb + hh] : -INFINITY;
-  }
-  __syncthreads();
-  if (tid < 32) {
-    float M = -INFINITY;
-    for (int sp = 0; sp < S; ++sp) M = fmaxf(M, s_f[tid][sp]);
+  // each head's split weights: 8 threads per head (head tid / 8), thread
+  // tid % 8 taking splits tid % 8, tid % 8 + 8, ..; maximum and sum over the
+  // 8 by lane exchanges
+  {
+    constexpr int PS = S < 8 ? 1 : S / 8;  // splits per thread
+    const int hh = tid >> 3, sub = tid & 7;
+    float ls[PS], M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < PS; ++u) {
+      const int sp = sub + 8 * u;
+      ls[u] = sp < splits ? pl[sp * NH + 32 * nb + hh] : -INFINITY;
+      M = fmaxf(M, ls[u]);
+    }
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) M = fmaxf(M, __shfl_xor(M, o));
     float L = 0.0f;
-    for (int sp = 0; sp < S; ++sp) {
-      const float ls = s_f[tid][sp];
-      const float f = ls != -INFINITY ? exp2f(ls - M) : 0.0f;  // 0 past the last split and for empty splits
-      s_f[tid][sp] = f;
+#pragma unroll
+    for (int u = 0; u < PS; ++u) {
+      const int sp = sub + 8 * u;
+      const float f = ls[u] != -INFINITY ? exp2f(ls[u] - M) : 0.0f;  // 0 past the last split and for empty splits
+      if (sp < S) s_f[hh][sp] = f;
       L += f;
     }
-    s_L[tid] = L;
-    s_M[tid] = M;
+#pragma unroll
+    for (int o = 1; o < 8; o <<= 1) L += __shfl_xor(L, o);
+    if (sub == 0) {
+      s_L[hh] = L;
+      s_M[hh] = M;
+    }
   }
   __syncthreads();
   const float L = s_L[hl];
