@@ -192,7 +192,9 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
   // the wave index is uniform: saying so keeps the loops below scalar
   const int tid = threadIdx.x, lane = tid & 63, w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int b = blockIdx.y;
-  const int t0 = blockIdx.x * QG;
+  // longest rows first (a query's visible entries grow with t): the last
+  // workgroups to start are the short ones, so the launch ends on a short tail
+  const int t0 = (gridDim.x - 1 - blockIdx.x) * QG;
   // visible entries of query t0 + q (0 past the end of the rows): one 64-bit
   // division per workgroup, (pos0 + t0 + 1) = qb m + rb
   const int64_t base = P.pos0 + t0 + 1;
