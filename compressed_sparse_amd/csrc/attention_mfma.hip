@@ -38,8 +38,9 @@ __device__ __forceinline__ uint32_t pack2_bf16(float a, float b) {
 // 128w + 32mb + 8jq + 4 (lane / 32) .. +4.  Grid (32 blocks (w, mb, nb), B),
 // 256 threads: thread (jq, lane) reads one 8-byte piece of every split (2 KB
 // contiguous per split and workgroup), the weights of the block's 32 heads
-// are formed once in LDS (8 threads per head).  S >= splits is a power of two: every thread's S
-// loads (clamped to the last split) are issued before the weights are known.
+// are formed once in LDS (8 threads per head).  S >= splits is a power of
+// two: every thread's S loads (clamped to the last split) are issued before
+// the weights are known.
 template <int S>
 __global__ void __launch_bounds__(256) attn_merge_kernel(AttnParams P, int splits, const void* part, int B) {
   __shared__ float s_f[32][S + 1];
