@@ -4,11 +4,16 @@
 // dims BF16, rest FP8); [读完这篇] §三 压缩机制 (per-dimension weights, 4 W +
 // 2 B).
 //
-// One workgroup builds one entry: each thread owns channels j, j+256, ...,
-// runs an online softmax over the 2m (or m) logits of its channel and keeps
-// the weighted value; the entry then sits in LDS for the RoPE turn and the
-// FP8 / MXFP4 scale reductions.  HBM traffic is the 2m rows in and one entry
-// out; the kernel is bandwidth-bound and tiny next to attention.
+// Prefill: compress_prefill_wave_kernel gives each entry a group of lanes (a
+// whole wave for 576-wide entries, 8 lanes for 64-wide indexer keys); lane l
+// owns 8 consecutive channels and RoPE pair l, folds the 2m (or m) window
+// rows into a per-channel online softmax in batches of rows, turns its RoPE
+// pair in registers and reduces the FP8 / MXFP4 scales across lanes.
+// compress_prefill_kernel (one workgroup per entry, one thread per channel)
+// serves entry shapes outside that lane map.  Decode: one workgroup per
+// sequence, one thread per channel, the window's older rows from the
+// staging ring.  HBM traffic is the window rows in and one entry out; the
+// kernels are bandwidth-bound and small next to attention.
 #include "compress_store.hpp"
 #include "index_prep.hpp"
 

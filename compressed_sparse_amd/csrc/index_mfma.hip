@@ -5,10 +5,12 @@
 //   I[s] = sum_h w[h] * ReLU(qI[h] . K[s])
 //
 // index_prefill_fused_kernel: 4 consecutive queries per workgroup, i.e. 64
-//   MFMA rows (query x head) against 32-entry column blocks
-//   (v_mfma_f32_32x32x16_bf16, keys loaded straight from L2 as the B
-//   operand).  The 4 score rows stay in LDS (4 x 8192 fp32) and each wave
-//   then radix-selects one row's top-k, so scores never reach HBM.
+//   MFMA rows (query x head) against 16-entry column blocks
+//   (v_mfma_f32_16x16x32_bf16; keys read by coalesced loads and passed
+//   through a per-wave LDS stage into the B operand's layout; MXFP4: 32-entry
+//   blocks on the scaled FP4 MFMA).  The 4 score rows stay in LDS (4 x 8192
+//   fp32) and two waves per row then select its top-k (binned threshold,
+//   exact ranking inside the threshold bin), so scores never reach HBM.
 // index_scan_kernel: one query row against a 1024-entry chunk per
 //   workgroup (v_mfma_f32_16x16x32_bf16, rows = the 16 heads); the decode
 //   scan and the fallback for long prefill rows, BF16 or FP8 keys.  FP8

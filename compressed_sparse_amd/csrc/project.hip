@@ -9,9 +9,11 @@
 //
 // project_gemm_kernel: one workgroup computes a 256-token x 256-column tile of
 // Y (128 columns when the projected width needs it) with
-// v_mfma_f32_32x32x16_bf16, 4 waves of 128 x 128 (x 64); both operands reach
-// LDS by direct-to-LDS buffer loads, double-buffered in 64-wide K steps, the
-// 16-byte chunks of each 128-byte row XOR-swizzled by the row.  Columns of a
+// v_mfma_f32_32x32x16_bf16, 4 waves of 128 x 128 (x 64); both operands are
+// read by 16-byte buffer loads into registers two K steps ahead and written
+// to one of two LDS buffers one step ahead (64-wide K steps, the loads and
+// writes spread over the MFMA stream), the 16-byte chunks of each 128-byte
+// row XOR-swizzled by the row.  Columns of a
 // tile are the NT projections of consecutive channels, so the
 // epilogue finds every input of its entries' channels in the tile: Y goes to
 // LDS in 64-column passes (fp32, never rounded) and each (entry, channel) runs the compressor's
