@@ -80,7 +80,8 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 // fused prefill: scores of 4 queries in LDS, then two waves per row select
 // ---------------------------------------------------------------------------
 
-constexpr int FW = 8;           // waves per fused workgroup
+constexpr int FW = 8;           // select waves per fused workgroup (two per row)
+constexpr int SW = 12;          // scoring waves (three per SIMD; the first FW then select)
 constexpr int SEL_BINS = 2048;  // value-range bins of the fused select (16-bit counts, two per word)
 constexpr int SEL_HW = SEL_BINS / 2;  // histogram words per row
 constexpr int SEL_CBH = 128;    // threshold-bin entries ranked directly, per half row
@@ -178,17 +179,20 @@ __device__ __forceinline__ void wave_radix_select(const float* row, int n, int k
 // sums and one cross-half swap per MFMA, lanes 0..31 hold queries 0 and 2,
 // lanes 32..63 queries 1 and 3.
 template <bool KFP8, bool FROM_WS, bool MX = false>
-__global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexParams P) {
+__global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fused_kernel(IndexParams P) {
+  // waves of the launch: SW score the keys, FW of them select (a select-only
+  // launch, FROM_WS, has FW)
+  constexpr int NWG = FROM_WS ? FW : SW;
   __shared__ __align__(16) float srow[QG][FUSED_NMAX];
   // select state (histograms, bin-B candidates, ranks); while scoring, the
   // same bytes stage each wave's key block
   __shared__ __align__(16) int sel_mem[QG * SEL_HW + 3 * QG * 2 * SEL_CBH];
-  static_assert(sizeof(sel_mem) >= FW * 2048, "key stage");
+  static_assert(sizeof(sel_mem) >= SW * 2048, "key stage");
   int (*hist)[SEL_HW] = reinterpret_cast<int (*)[SEL_HW]>(sel_mem);
   int (*cidx)[2][SEL_CBH] = reinterpret_cast<int (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW);
   uint32_t (*ckey)[2][SEL_CBH] = reinterpret_cast<uint32_t (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW + QG * 2 * SEL_CBH);
   int (*crank)[2][SEL_CBH] = reinterpret_cast<int (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW + 2 * QG * 2 * SEL_CBH);
-  __shared__ float s_mm[FW][QG][2];  // per wave and row: min, max of the scores it wrote
+  __shared__ float s_mm[SW][QG][2];  // per wave and row: min, max of the scores it wrote
   __shared__ int s_cnt[QG][2][2];    // per row and half: bin-B entries, entries above B
   __shared__ int s_sink[FW][64];     // stores of lanes with nothing to store
   // the wave index is uniform: saying so keeps the loops below scalar
@@ -300,15 +304,15 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
     u32x4 kr[MXD];
     uint32_t kss[MXD];
 #pragma unroll
-    for (int i = 0; i < MXD; ++i) loadk(min(w + FW * i, nb32 - 1), kr[i], kss[i]);
-    for (int cb = w; cb < nb32; cb += FW * MXD) {
+    for (int i = 0; i < MXD; ++i) loadk(min(w + NWG * i, nb32 - 1), kr[i], kss[i]);
+    for (int cb = w; cb < nb32; cb += NWG * MXD) {
 #pragma unroll
       for (int i = 0; i < MXD; ++i) {
-        const int c = cb + FW * i;
+        const int c = cb + NWG * i;
         const i32x8 kv = {static_cast<int>(kr[i][0]), static_cast<int>(kr[i][1]), static_cast<int>(kr[i][2]),
                           static_cast<int>(kr[i][3]), 0, 0, 0, 0};
         const int ksc = static_cast<int>(kss[i]);
-        loadk(min(c + FW * MXD, nb32 - 1), kr[i], kss[i]);
+        loadk(min(c + NWG * MXD, nb32 - 1), kr[i], kss[i]);
         if (c < nb32) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
@@ -383,17 +387,21 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
     // 128-byte rows) or c ^ ((r/4)%4) (FP8, 64-byte rows): both the writes
     // and the reads of 16 lanes then cover distinct bank groups.
     uint8_t* stage = reinterpret_cast<uint8_t*>(sel_mem) + 2048 * w;
+    // the sequence's key rows from a workgroup-uniform base, with 32-bit lane
+    // offsets (entries below nmax <= FUSED_NMAX)
+    const uint8_t* kbase = static_cast<const uint8_t*>(P.knope) + seq * (KFP8 ? DI : 2 * DI);
+    const float* sbase = static_cast<const float*>(P.kscale) + (KFP8 ? seq : 0);
     auto loadk = [&](int cb, u32x4 (&kr)[2], float& ksc) {
       if (KFP8) {
         const int s = min(cb * 16 + (lane >> 2), nmax - 1);
-        kr[0] = *reinterpret_cast<const u32x4*>(static_cast<const uint8_t*>(P.knope) + (seq + s) * DI + 16 * (lane & 3));
+        kr[0] = *reinterpret_cast<const u32x4*>(kbase + static_cast<uint32_t>(s * DI + 16 * (lane & 3)));
         kr[1] = kr[0];
-        ksc = static_cast<const float*>(P.kscale)[seq + min(cb * 16 + e16, nmax - 1)];
+        ksc = sbase[static_cast<uint32_t>(min(cb * 16 + e16, nmax - 1))];
       } else {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int s = min(cb * 16 + 8 * i + (lane >> 3), nmax - 1);
-          kr[i] = *reinterpret_cast<const u32x4*>(static_cast<const bf16_t*>(P.knope) + (seq + s) * DI + 8 * (lane & 7));
+          kr[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<uint32_t>(s * 2 * DI + 16 * (lane & 7)));
         }
         ksc = 1.0f;
       }
@@ -422,6 +430,10 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
           kb[ks] = *reinterpret_cast<const u32x4*>(stage + 128 * e16 + 16 * ((4 * ks + g) ^ ((e16 >> 1) & 7)));
       }
     };
+    // the extremes are kept of the unrounded scores and rounded once at the
+    // end (RNE is monotonic, so they are the BF16 scores' extremes); the
+    // fp32 results of the sums need no canonicalising for fminf / fmaxf
+    const bool rb = P.score_dt == CSA_BF16;
     auto compute = [&](int cb, const u32x4 (&kb)[2], float ksc) {
       f32x4 acc[4];
 #pragma unroll
@@ -435,35 +447,45 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
       for (int j = 0; j < 4; ++j)
 #pragma unroll
         for (int i = 0; i < 4; ++i) val = fmaf(wv[4 * j + i], relu(acc[j][i] * ksc), val);
-      if (P.score_dt == CSA_BF16) val = round_bf16(val);
       const int s = cb * 16 + e16;
       if (s < nv) {
-        srow[g][s] = val;
+        srow[g][s] = rb ? round_bf16(val) : val;
         mnv = fminf(mnv, val);
         mxv = fmaxf(mxv, val);
       }
     };
-    // KD blocks of keys in flight per wave: block c + FW KD loads into the
+    // KD blocks of keys in flight per wave: block c + NWG KD loads into the
     // registers block c has just staged (a block past the end re-reads the
     // last one, so no load sits under a branch)
-    u32x4 kr[KD][2];
-    float ks[KD];
-    const int lastb = nblocks - 1;
-#pragma unroll
-    for (int i = 0; i < KD; ++i) loadk(min(w + FW * i, lastb), kr[i], ks[i]);
-    for (int cb = w; cb < nblocks; cb += FW * KD) {
+    {
+      u32x4 kr[KD][2];
+      float ks[KD];
+      const int lastb = nblocks - 1;
+      // issued in block order (the scheduler would otherwise reorder them, and
+      // the loop's first wait would then have to drain them all)
 #pragma unroll
       for (int i = 0; i < KD; ++i) {
-        const int c = cb + FW * i;
-        if (c < nblocks) {
+        loadk(min(w + NWG * i, lastb), kr[i], ks[i]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      for (int cb = w; cb < nblocks; cb += NWG * KD) {
+#pragma unroll
+        for (int i = 0; i < KD; ++i) {
+          const int c = cb + NWG * i;
+          // every load and stage step is unconditional (past the last block
+          // they repeat it), so the loads keep their issue order and each
+          // block waits for its own loads only; the uniform branch holds no
+          // memory load
           u32x4 kb[2];
           restage(kr[i], kb);
           const float ksc = ks[i];
-          loadk(min(c + FW * KD, lastb), kr[i], ks[i]);
-          compute(c, kb, ksc);
-        } else {
-          loadk(min(c + FW * KD, lastb), kr[i], ks[i]);
+          loadk(min(c + NWG * KD, lastb), kr[i], ks[i]);
+          if (c < nblocks) compute(c, kb, ksc);
         }
+      }
+      if (rb) {
+        mnv = round_bf16(mnv);
+        mxv = round_bf16(mxv);
       }
     }
     // per-row extremes of this wave's scores (the 16 lanes of query g)
@@ -481,8 +503,9 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
   __syncthreads();
 
   // ---- select: row q, half hf; every wave passes the same barriers ----
+  // waves FW.. only pass the barriers (no row)
   const int q = w & 3, hf = w >> 2;
-  const bool live = t0 + q < P.T;
+  const bool live = w < FW && t0 + q < P.T;
   const int k = P.k;
   const int n = live ? __builtin_amdgcn_readfirstlane(nvis(q)) : 0;
   int32_t* out = P.idx + (row0 + q) * k;
@@ -490,7 +513,7 @@ __global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexPa
   float mn = INFINITY, mx = -INFINITY;
   if (n > k) {
 #pragma unroll
-    for (int j = 0; j < FW; ++j) {
+    for (int j = 0; j < NWG; ++j) {
       mn = fminf(mn, s_mm[j][q][0]);
       mx = fmaxf(mx, s_mm[j][q][1]);
     }
@@ -1093,11 +1116,11 @@ int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
   if (P.qk_dt == CSA_MXFP4) {
     const int st = launch_index_mx_prep(P, B * P.T, s);
     if (st != CSA_OK) return st;
-    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false, true>), grid, dim3(64 * FW), 0, s, P);
+    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false, true>), grid, dim3(64 * SW), 0, s, P);
   } else if (P.key_dt == CSA_FP8E4M3) {
-    hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * FW), 0, s, P);
+    hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * SW), 0, s, P);
   } else {
-    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * FW), 0, s, P);
+    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * SW), 0, s, P);
   }
   return check_launch("index_prefill_fused_kernel");
 }
