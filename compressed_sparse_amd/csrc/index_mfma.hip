@@ -66,6 +66,18 @@ __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_wave_barrier();
 }
 
+// Buffer descriptor of `bytes` bytes from `base` (wave-uniform; read back
+// from lane 0 so that it is built in scalar registers); loads past the range
+// return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t key_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  const int nb = __builtin_amdgcn_readfirstlane(static_cast<int>(bytes));
+  void* ub = reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(ub, static_cast<short>(0), nb, 0x00020000);
+}
+
 // ReLU as an integer max: every negative float, -0 included, becomes +0
 // (one instruction; the float max would first quiet NaNs)
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
@@ -387,22 +399,24 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
     // 128-byte rows) or c ^ ((r/4)%4) (FP8, 64-byte rows): both the writes
     // and the reads of 16 lanes then cover distinct bank groups.
     uint8_t* stage = reinterpret_cast<uint8_t*>(sel_mem) + 2048 * w;
-    // the sequence's key rows from a workgroup-uniform base, with 32-bit lane
-    // offsets (entries below nmax <= FUSED_NMAX)
-    const uint8_t* kbase = static_cast<const uint8_t*>(P.knope) + seq * (KFP8 ? DI : 2 * DI);
-    const float* sbase = static_cast<const float*>(P.kscale) + (KFP8 ? seq : 0);
+    // the sequence's first nmax key rows as a buffer (rows past them read as
+    // zero; their scores are dropped): each load is a fixed lane offset plus
+    // the block's start (nmax <= FUSED_NMAX rows, so 32-bit offsets)
+    constexpr int KROW = KFP8 ? DI : 2 * DI;  // bytes per key row
+    const __amdgpu_buffer_rsrc_t krs =
+        key_rsrc(static_cast<const uint8_t*>(P.knope) + seq * KROW, static_cast<uint32_t>(nmax) * KROW);
+    const __amdgpu_buffer_rsrc_t srs =
+        key_rsrc(KFP8 ? static_cast<const float*>(P.kscale) + seq : nullptr, KFP8 ? static_cast<uint32_t>(nmax) * 4 : 0);
+    // BF16: lane l reads row 8i + l/8, chunk l%8; FP8: row l/4, chunk l%4
+    const uint32_t lo0 = KFP8 ? (lane >> 2) * DI + 16 * (lane & 3) : (lane >> 3) * KROW + 16 * (lane & 7);
     auto loadk = [&](int cb, u32x4 (&kr)[2], float& ksc) {
+      const uint32_t b0 = static_cast<uint32_t>(cb) * 16 * KROW;
+      kr[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo0 + b0, 0, 0));
       if (KFP8) {
-        const int s = min(cb * 16 + (lane >> 2), nmax - 1);
-        kr[0] = *reinterpret_cast<const u32x4*>(kbase + static_cast<uint32_t>(s * DI + 16 * (lane & 3)));
         kr[1] = kr[0];
-        ksc = sbase[static_cast<uint32_t>(min(cb * 16 + e16, nmax - 1))];
+        ksc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(srs, 4 * (cb * 16 + e16), 0, 0));
       } else {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int s = min(cb * 16 + 8 * i + (lane >> 3), nmax - 1);
-          kr[i] = *reinterpret_cast<const u32x4*>(kbase + static_cast<uint32_t>(s * 2 * DI + 16 * (lane & 7)));
-        }
+        kr[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, lo0 + b0 + 8 * KROW, 0, 0));
         ksc = 1.0f;
       }
     };
@@ -441,12 +455,14 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j][0], as_bf16x8(kb[0]), f32x4{}, 0, 0, 0);
         acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[j][1], as_bf16x8(kb[1]), acc[j], 0, 0, 0);
       }
-      // heads 0..15 in order
+      // heads 0..15 in order; the positive FP8 entry scale commutes with the
+      // ReLU and multiplies the head sum (one product instead of sixteen)
       float val = 0.0f;
 #pragma unroll
       for (int j = 0; j < 4; ++j)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) val = fmaf(wv[4 * j + i], relu(acc[j][i] * ksc), val);
+        for (int i = 0; i < 4; ++i) val = fmaf(wv[4 * j + i], relu(acc[j][i]), val);
+      if (KFP8) val *= ksc;
       const int s = cb * 16 + e16;
       if (s < nv) {
         srow[g][s] = rb ? round_bf16(val) : val;
