@@ -92,12 +92,11 @@ __device__ __forceinline__ uint32_t order_key(float x) {
 // fused prefill: scores of 4 queries in LDS, then two waves per row select
 // ---------------------------------------------------------------------------
 
-constexpr int FW = 8;           // select waves per fused workgroup (two per row)
-constexpr int SW = 12;          // scoring waves (three per SIMD; the first FW then select)
+constexpr int FW = 8;           // waves per fused workgroup (two per SIMD; two per row in the select)
 constexpr int SEL_BINS = 2048;  // value-range bins of the fused select (16-bit counts, two per word)
 constexpr int SEL_HW = SEL_BINS / 2;  // histogram words per row
 constexpr int SEL_CBH = 128;    // threshold-bin entries ranked directly, per half row
-constexpr int KD = 8;           // key blocks in flight per wave (scoring)
+constexpr int KD = 4;           // key blocks in flight per wave (scoring)
 constexpr int HSTEPS = FUSED_NMAX / 512;  // 256-entry steps in half a row, at most
 
 __device__ __forceinline__ int mbcnt(unsigned long long m) {
@@ -191,20 +190,17 @@ __device__ __forceinline__ void wave_radix_select(const float* row, int n, int k
 // sums and one cross-half swap per MFMA, lanes 0..31 hold queries 0 and 2,
 // lanes 32..63 queries 1 and 3.
 template <bool KFP8, bool FROM_WS, bool MX = false>
-__global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fused_kernel(IndexParams P) {
-  // waves of the launch: SW score the keys, FW of them select (a select-only
-  // launch, FROM_WS, has FW)
-  constexpr int NWG = FROM_WS ? FW : SW;
+__global__ void __launch_bounds__(64 * FW, 1) index_prefill_fused_kernel(IndexParams P) {
   __shared__ __align__(16) float srow[QG][FUSED_NMAX];
   // select state (histograms, bin-B candidates, ranks); while scoring, the
   // same bytes stage each wave's key block
   __shared__ __align__(16) int sel_mem[QG * SEL_HW + 3 * QG * 2 * SEL_CBH];
-  static_assert(sizeof(sel_mem) >= SW * 2048, "key stage");
+  static_assert(sizeof(sel_mem) >= FW * 2048, "key stage");
   int (*hist)[SEL_HW] = reinterpret_cast<int (*)[SEL_HW]>(sel_mem);
   int (*cidx)[2][SEL_CBH] = reinterpret_cast<int (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW);
   uint32_t (*ckey)[2][SEL_CBH] = reinterpret_cast<uint32_t (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW + QG * 2 * SEL_CBH);
   int (*crank)[2][SEL_CBH] = reinterpret_cast<int (*)[2][SEL_CBH]>(sel_mem + QG * SEL_HW + 2 * QG * 2 * SEL_CBH);
-  __shared__ float s_mm[SW][QG][2];  // per wave and row: min, max of the scores it wrote
+  __shared__ float s_mm[FW][QG][2];  // per wave and row: min, max of the scores it wrote
   __shared__ int s_cnt[QG][2][2];    // per row and half: bin-B entries, entries above B
   __shared__ int s_sink[FW][64];     // stores of lanes with nothing to store
   // the wave index is uniform: saying so keeps the loops below scalar
@@ -316,15 +312,15 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
     u32x4 kr[MXD];
     uint32_t kss[MXD];
 #pragma unroll
-    for (int i = 0; i < MXD; ++i) loadk(min(w + NWG * i, nb32 - 1), kr[i], kss[i]);
-    for (int cb = w; cb < nb32; cb += NWG * MXD) {
+    for (int i = 0; i < MXD; ++i) loadk(min(w + FW * i, nb32 - 1), kr[i], kss[i]);
+    for (int cb = w; cb < nb32; cb += FW * MXD) {
 #pragma unroll
       for (int i = 0; i < MXD; ++i) {
-        const int c = cb + NWG * i;
+        const int c = cb + FW * i;
         const i32x8 kv = {static_cast<int>(kr[i][0]), static_cast<int>(kr[i][1]), static_cast<int>(kr[i][2]),
                           static_cast<int>(kr[i][3]), 0, 0, 0, 0};
         const int ksc = static_cast<int>(kss[i]);
-        loadk(min(c + NWG * MXD, nb32 - 1), kr[i], kss[i]);
+        loadk(min(c + FW * MXD, nb32 - 1), kr[i], kss[i]);
         if (c < nb32) {
 #pragma unroll
           for (int p = 0; p < 2; ++p) {
@@ -470,7 +466,7 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
         mxv = fmaxf(mxv, val);
       }
     };
-    // KD blocks of keys in flight per wave: block c + NWG KD loads into the
+    // KD blocks of keys in flight per wave: block c + FW KD loads into the
     // registers block c has just staged (a block past the end re-reads the
     // last one, so no load sits under a branch)
     {
@@ -481,13 +477,13 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
       // the loop's first wait would then have to drain them all)
 #pragma unroll
       for (int i = 0; i < KD; ++i) {
-        loadk(min(w + NWG * i, lastb), kr[i], ks[i]);
+        loadk(min(w + FW * i, lastb), kr[i], ks[i]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      for (int cb = w; cb < nblocks; cb += NWG * KD) {
+      for (int cb = w; cb < nblocks; cb += FW * KD) {
 #pragma unroll
         for (int i = 0; i < KD; ++i) {
-          const int c = cb + NWG * i;
+          const int c = cb + FW * i;
           // every load and stage step is unconditional (past the last block
           // they repeat it), so the loads keep their issue order and each
           // block waits for its own loads only; the uniform branch holds no
@@ -495,7 +491,7 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
           u32x4 kb[2];
           restage(kr[i], kb);
           const float ksc = ks[i];
-          loadk(min(c + NWG * KD, lastb), kr[i], ks[i]);
+          loadk(min(c + FW * KD, lastb), kr[i], ks[i]);
           if (c < nblocks) compute(c, kb, ksc);
         }
       }
@@ -519,9 +515,8 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
   __syncthreads();
 
   // ---- select: row q, half hf; every wave passes the same barriers ----
-  // waves FW.. only pass the barriers (no row)
   const int q = w & 3, hf = w >> 2;
-  const bool live = w < FW && t0 + q < P.T;
+  const bool live = t0 + q < P.T;
   const int k = P.k;
   const int n = live ? __builtin_amdgcn_readfirstlane(nvis(q)) : 0;
   int32_t* out = P.idx + (row0 + q) * k;
@@ -529,7 +524,7 @@ __global__ void __launch_bounds__(64 * (FROM_WS ? FW : SW), 1) index_prefill_fus
   float mn = INFINITY, mx = -INFINITY;
   if (n > k) {
 #pragma unroll
-    for (int j = 0; j < NWG; ++j) {
+    for (int j = 0; j < FW; ++j) {
       mn = fminf(mn, s_mm[j][q][0]);
       mx = fmaxf(mx, s_mm[j][q][1]);
     }
@@ -1132,11 +1127,11 @@ int launch_index_fused_prefill(const IndexParams& P, int B, hipStream_t s) {
   if (P.qk_dt == CSA_MXFP4) {
     const int st = launch_index_mx_prep(P, B * P.T, s);
     if (st != CSA_OK) return st;
-    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false, true>), grid, dim3(64 * SW), 0, s, P);
+    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false, true>), grid, dim3(64 * FW), 0, s, P);
   } else if (P.key_dt == CSA_FP8E4M3) {
-    hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * SW), 0, s, P);
+    hipLaunchKernelGGL((index_prefill_fused_kernel<true, false>), grid, dim3(64 * FW), 0, s, P);
   } else {
-    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * SW), 0, s, P);
+    hipLaunchKernelGGL((index_prefill_fused_kernel<false, false>), grid, dim3(64 * FW), 0, s, P);
   }
   return check_launch("index_prefill_fused_kernel");
 }
